@@ -1,0 +1,248 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the forward pass of one mixture-of-experts
+ * layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (sources by page title and section):
+ *   gating      p_e(x) = softmax(g(x))_e, g(x) = W_r x (+ b)
+ *               ["MoE技术演进", "Adaptive Mixtures of Local Experts", gating equation]
+ *   selection   top-k experts per token, optionally inside the best groups
+ *               ["MoE技术演进", "DeepSeek-V2" item 3, device-limited routing]
+ *               or per routing head inside the head's own expert partition
+ *               ["多头 LatentMoE 与 Head Parallel", 方法论 items 1-2]
+ *   keep rule   capacity C per expert, overflow through the residual
+ *               ["MoE技术演进", "GShard" item 1]; or keep the best 90 % per
+ *               expert by affinity ["MoE技术演进", "DeepSeek-V2" item 5];
+ *               or no dropping ["MoE技术演进", "DeepSeek-V3" item 5]
+ *   experts     FFN_e(u) = W2 relu(W1 u)  ["MoE技术演进", "GShard" item 3]
+ *               or W2 (SiLU(W1 u) * W3 u) ["大语言模型并行策略（七）：专家并行",
+ *               "MoE 模型的参数量分析": 3 d_model x d_moe matrices]
+ *   combine     h = sum_shared FFN_i(u) + sum_kept g_e FFN_e(u) + u
+ *               ["MoE技术演进", "DeepSeekMoE" item 2, shared-expert equation]
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless marked [host].  Matrices are
+ *     row-major; weights use the [out, in] layout, so both operands of every
+ *     product are contiguous along the contracted dimension.
+ *   - The caller allocates every buffer, the workspace included.  The library
+ *     never allocates or frees device memory, never synchronises the stream
+ *     and keeps no pointer after a call returns.  Calls are reentrant.
+ *   - Every call is asynchronous on `stream` and returns a moe_status.  All
+ *     argument checks run on the host before anything is launched: a failed
+ *     check launches nothing.  A launch failure returns MOE_ERR_HIP.
+ *   - Row counts that depend on routing (R = kept assignments) are never read
+ *     back to the host: buffers sized by R use moe_rows_upper_bound(), and
+ *     the true R is offsets[E] on the device.
+ *   - "act" tensors (activations and expert weights) have cfg->act_dtype;
+ *     the router weight has cfg->router_dtype; gates, logits, bias and the
+ *     aux loss are float32; indices are int32.
+ *   - The workspace `ws` must hold at least moe_workspace_bytes(cfg) bytes and
+ *     be 256-byte aligned; its contents need not be initialised.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,          /* null pointer, bad size or inconsistent config */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid request outside what the kernels support */
+  MOE_ERR_WORKSPACE = -3,    /* ws_bytes < moe_workspace_bytes(cfg) or misaligned */
+  MOE_ERR_HIP = -4           /* a HIP launch reported an error */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_ACT_RELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+typedef enum { MOE_DROP_NONE = 0, MOE_DROP_CAPACITY = 1, MOE_DROP_AFFINITY = 2 } moe_drop;
+typedef enum {
+  MOE_LOGITS_COMPUTE = 0,        /* compute scores from x and W_r; logits buffer unused (may be NULL) */
+  MOE_LOGITS_COMPUTE_STORE = 1,  /* compute, and also write them to `logits` */
+  MOE_LOGITS_LOAD = 2            /* read final scores (bias included) from `logits`; x, W_r, bias unused */
+} moe_logits_mode;
+
+/* [host] Layer shape and rules.  All fields are int32 so the layout is fixed. */
+typedef struct moe_config {
+  int32_t T;            /* tokens, >= 0 (T == 0: every call is a no-op returning MOE_OK) */
+  int32_t d_model;      /* width of x and y; multiple of 64 */
+  int32_t n_heads;      /* H >= 1 routing heads */
+  int32_t d_head;       /* expert input width d_e; multiple of 64; with H == 1 and no latent
+                           projection it equals d_model; otherwise H*d_head is the latent width */
+  int32_t n_experts;    /* E routed experts in total, E = H * E_h, 1 <= E_h <= 256, E <= 1024 */
+  int32_t top_k;        /* experts chosen per head, 1 <= top_k <= min(E_h, 8) */
+  int32_t n_groups;     /* group-limited routing: groups per head (0 = off); divides E_h, <= 32 */
+  int32_t topk_groups;  /* groups kept per token, 1..n_groups; top_k <= topk_groups*(E_h/n_groups) */
+  int32_t renorm;       /* 1: chosen gates divided by their sum */
+  int32_t drop;         /* moe_drop */
+  int32_t capacity;     /* MOE_DROP_CAPACITY: integer C >= 0 (computed by the caller) */
+  int32_t keep_num;     /* MOE_DROP_AFFINITY: keep ceil(keep_num*n_e/keep_den) of expert e's */
+  int32_t keep_den;     /*   n_e assignments; 0 < keep_num <= keep_den */
+  int32_t d_ff;         /* expert hidden width; multiple of 64 */
+  int32_t act;          /* moe_act */
+  int32_t n_shared;     /* always-active shared experts (H == 1 only), each d_ff wide */
+  int32_t latent_proj;  /* 1: z = x W_in^T before routing and o W_out^T + x after */
+  int32_t residual;     /* 1: combine adds the layer input (ignored with latent_proj: the
+                           residual is added after the output projection) */
+  int32_t act_dtype;    /* moe_dtype of activations and expert weights */
+  int32_t router_dtype; /* moe_dtype of W_r; MOE_BF16 requires act_dtype == MOE_BF16 */
+} moe_config;
+
+/* Weights of one layer (device pointers; [out, in] layout). */
+typedef struct moe_weights {
+  const void *w_router;     /* [E, d_head] (== [H, E_h, d_head]), router_dtype */
+  const float *router_bias; /* [E] or NULL: added to the scores before softmax and selection */
+  const void *w1;           /* [E, d_ff, d_head]  gate projection (the only one for ReLU) */
+  const void *w3;           /* [E, d_ff, d_head]  up projection (SwiGLU) or NULL (ReLU) */
+  const void *w2;           /* [E, d_head, d_ff]  down projection */
+  const void *ws1;          /* [n_shared*d_ff, d_model] shared experts, hidden widths concatenated */
+  const void *ws3;          /* [n_shared*d_ff, d_model] (SwiGLU) or NULL */
+  const void *ws2;          /* [d_model, n_shared*d_ff] */
+  const void *w_in;         /* [H*d_head, d_model] latent in-projection, or NULL */
+  const void *w_out;        /* [d_model, H*d_head] latent out-projection, or NULL */
+} moe_weights;
+
+/* Optional outputs and intermediates of moe_layer_fwd.  Every pointer may be
+ * NULL; a NULL intermediate lives in the workspace instead.  Shapes use
+ * K = H*top_k assignments per token and R_max = moe_rows_upper_bound(cfg). */
+typedef struct moe_layer_io {
+  float *logits;            /* [T, E] float32; role set by logits_mode */
+  int32_t logits_mode;      /* moe_logits_mode; LOAD requires logits != NULL */
+  int32_t *topk_idx;        /* [T, K] */
+  float *topk_w;            /* [T, K] */
+  int32_t *demand;          /* [E]  assignments per expert before the keep rule */
+  int32_t *counts;          /* [E]  kept assignments per expert */
+  int32_t *offsets;         /* [E+1] exclusive prefix sum of counts; offsets[E] = R */
+  int32_t *row_of;          /* [T, K] row of each assignment in x_perm, -1 if dropped */
+  int32_t *src_of;          /* [R_max] flat assignment (t*K + j) held by each row */
+  float *aux_loss;          /* [1] GShard auxiliary loss (H == 1 only) */
+  void *z;                  /* [T, H*d_head] act: latent (latent_proj only) */
+  void *x_perm;             /* [R_max, d_head] act: expert-contiguous expert inputs */
+  void *y_perm;             /* [R_max, d_head] act: expert outputs, same row order */
+  void *shared_out;         /* [T, d_model] act: sum of the shared experts (n_shared > 0) */
+  void *o;                  /* [T, H*d_head] act: combined head outputs (latent_proj only) */
+} moe_layer_io;
+
+/* [host] Workspace bytes every call below needs for `cfg` (0 for an invalid cfg). */
+size_t moe_workspace_bytes(const moe_config *cfg);
+
+/* [host] Upper bound on R, the number of kept assignments:
+ * T*H*top_k for MOE_DROP_NONE / MOE_DROP_AFFINITY, min(T*top_k, E*C) for
+ * MOE_DROP_CAPACITY.  -1 for an invalid cfg. */
+int64_t moe_rows_upper_bound(const moe_config *cfg);
+
+/* [host] Static string naming a moe_status value. */
+const char *moe_status_str(int status);
+
+/* [host] MOE_OK if `cfg` is valid and supported, else the error moe_* calls would return. */
+int moe_check_config(const moe_config *cfg);
+
+/*
+ * moe_route -- scores, softmax, top-k and gates of every token.
+ * ["MoE技术演进", "Adaptive Mixtures of Local Experts" (gating equation and
+ * top-K selector); "GShard" item 1 (aux-loss equation); "DeepSeek-V2" item 3
+ * (device-limited routing, here over expert groups); "多头 LatentMoE 与 Head
+ * Parallel", 方法论 item 2 (per-head choice within a fixed partition)]
+ *
+ *   x         [T, H*d_head] act: router input (the latent z when latent_proj)
+ *   w_router  [E, d_head] router_dtype; head h uses rows [h*E_h, (h+1)*E_h)
+ *             and reads columns [h*d_head, (h+1)*d_head) of x
+ *   bias      [E] float32 or NULL
+ *   logits    [T, E] float32, per `mode`
+ *   topk_idx  [T, H*top_k] out: global expert ids (h*E_h + local); the k
+ *             entries of a head are ordered by score descending, lower expert
+ *             index first on equal scores (-0.0 and +0.0 are equal)
+ *   topk_w    [T, H*top_k] out: softmax probability of each chosen expert over
+ *             its head's E_h experts, divided by the chosen sum if cfg->renorm
+ *   aux_loss  [1] float32 out or NULL: sum_e m_e * c_e / T with m_e the mean
+ *             probability and c_e the number of choices of e; H == 1 only
+ *             (MOE_ERR_UNSUPPORTED otherwise)
+ * Scores must be finite; non-finite scores give unspecified routing.
+ */
+int moe_route(const moe_config *cfg, const void *x, const void *w_router, const float *bias,
+              float *logits, int mode, int32_t *topk_idx, float *topk_w, float *aux_loss,
+              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_dispatch -- keep rule and permutation of tokens into an expert-contiguous buffer.
+ * ["MoE技术演进", "GShard" item 1 (capacity C, overflow through the residual);
+ * "DeepSeek-V2" item 5 (keep the top 90 % by affinity); "DeepSeek-V3" item 5
+ * (no dropping); "大语言模型并行策略（七）：专家并行", "MoE 中的 all-to-all 通信"
+ * (count tokens per expert, then fill each expert's buffer)]
+ *
+ * Flat assignment a = t*K + j (K = H*top_k), expert e(a) = topk_idx[a].
+ *   NONE      every assignment kept
+ *   CAPACITY  a kept iff fewer than C earlier assignments (smaller a) chose e(a)
+ *   AFFINITY  per expert, the ceil(keep_num*n_e/keep_den) assignments with the
+ *             largest topk_w are kept (equal gates: smaller a first)
+ *
+ *   topk_idx  [T, K] in, values in [0, E) (out-of-range values: undefined behaviour)
+ *   topk_w    [T, K] in; read only for AFFINITY (may be NULL otherwise)
+ *   x         [T, H*d_head] act: expert inputs (x, or z when latent_proj)
+ *   demand    [E] out, counts [E] out, offsets [E+1] out (offsets[E] = R)
+ *   row_of    [T, K] out: row of a in x_perm, or -1 if dropped
+ *   src_of    [R_max] out: rows [0, R) hold the flat index of their assignment;
+ *             rows of expert e are [offsets[e], offsets[e+1]) in ascending a
+ *   x_perm    [R_max, d_head] act out: row r = columns [h*d_head, (h+1)*d_head)
+ *             of x[src_of[r] / K], h = e(src_of[r]) / E_h (bitwise copy)
+ * Results are deterministic (integer work only, no order-dependent atomics).
+ */
+int moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, const float *topk_w,
+                 const void *x, int32_t *demand, int32_t *counts, int32_t *offsets,
+                 int32_t *row_of, int32_t *src_of, void *x_perm,
+                 void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn -- every routed expert on its rows of x_perm, plus the shared experts.
+ * ["MoE技术演进", "GShard" item 3 (FFN_e); "DeepSeekMoE" item 2 (shared experts);
+ * "大语言模型并行策略（七）：专家并行", "MoE 模型的参数量分析" (SwiGLU, 3 matrices)]
+ *
+ *   x_perm     [R_max, d_head] act, offsets [E+1] (from moe_dispatch)
+ *   w1, w3, w2 per-expert weights (moe_weights layout); w3 NULL for ReLU
+ *   y_perm     [R_max, d_head] act out: row r = FFN_e(x_perm[r]) for the expert
+ *              e owning row r; rows >= offsets[E] untouched
+ *   x_shared   [T, d_model] act (the layer input) or NULL when n_shared == 0
+ *   ws1, ws3, ws2, shared_out [T, d_model] act out: sum over shared experts
+ * Products accumulate in float32; the hidden activation is rounded to act_dtype.
+ */
+int moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *offsets,
+                   const void *w1, const void *w3, const void *w2, void *y_perm,
+                   const void *x_shared, const void *ws1, const void *ws3, const void *ws2,
+                   void *shared_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_combine -- gate-weighted sum of the expert outputs, plus shared output and residual.
+ * ["MoE技术演进", "GShard" item 3 (y_s = sum_e G_{s,e} FFN_e(x_s)); "DeepSeekMoE"
+ * items 1-2 (+ u_t and the ungated shared experts)]
+ *
+ * For column c of head h = c / d_head:
+ *   y[t, c] = residual[t, c] + shared_out[t, c]
+ *             + sum_{j in head h, row_of[t,j] >= 0} topk_w[t,j] * y_perm[row_of[t,j], c - h*d_head]
+ * accumulated in float32 in that order (residual, shared, then j ascending)
+ * and rounded once.  A dropped assignment adds nothing.
+ *   y_perm [R_max, d_head], row_of [T, K], topk_w [T, K]
+ *   residual [T, H*d_head] act or NULL, shared_out [T, H*d_head] act or NULL
+ *   y [T, H*d_head] act out (the layer output when H == 1; o when latent_proj)
+ */
+int moe_combine(const moe_config *cfg, const void *y_perm, const int32_t *row_of,
+                const float *topk_w, const void *residual, const void *shared_out, void *y,
+                hipStream_t stream);
+
+/*
+ * moe_layer_fwd -- the whole layer: [z = x W_in^T] -> route -> dispatch ->
+ * expert FFN (+ shared) -> combine -> [y = o W_out^T + x].  One stream, no host
+ * synchronisation.  x [T, d_model] act in, y [T, d_model] act out (distinct
+ * from x).  `io` may be NULL.  Sources as for the four calls above, and
+ * "多头 LatentMoE 与 Head Parallel", 方法论 item 1 (latent routing space).
+ */
+int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
+                  moe_layer_io *io, void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

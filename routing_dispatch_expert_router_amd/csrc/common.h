@@ -1,0 +1,80 @@
+// Internal helpers shared by the gfx950 kernels of libmoe.so (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------- bf16 <-> f32
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// round to nearest, ties to even (inputs here are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// storage type traits: activations / weights are either bf16 (uint16 bits) or f32
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+  static constexpr int kPer16B = 8;  // elements per 16-byte chunk
+  __device__ __forceinline__ static float load(const uint16_t *p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static uint16_t from_f32(float f) { return f32_to_bf16(f); }
+  __device__ __forceinline__ static float to_f32(uint16_t v) { return bf16_to_f32(v); }
+};
+template <> struct Elem<float> {
+  static constexpr int kPer16B = 4;
+  __device__ __forceinline__ static float load(const float *p) { return *p; }
+  __device__ __forceinline__ static float from_f32(float f) { return f; }
+  __device__ __forceinline__ static float to_f32(float v) { return v; }
+};
+
+// ---------------------------------------------------------------- MFMA
+// One 16x16 output block, contraction over the 16 bytes each lane holds of A
+// and B (8 bf16 or 4 f32).  Lane l holds A row (l % 16) and B column (l % 16);
+// which k each byte stands for does not matter as long as A and B agree.
+// Result layout: acc[i] = C[4*(l/16) + i][l % 16].
+__device__ __forceinline__ f32x4 mma16(const u32x4 &a, const u32x4 &b, f32x4 acc, uint16_t) {
+  bf16x8 av = __builtin_bit_cast(bf16x8, a);
+  bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(const u32x4 &a, const u32x4 &b, f32x4 acc, float) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), acc, 0, 0, 0);
+  return acc;
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+
+// order-preserving key of a float score: larger float -> larger key; -0.0 == +0.0
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+__device__ __forceinline__ float group_sum_fixed(float v, int width) {
+  // butterfly: every lane of the group ends with the same value, and the
+  // association order is fixed by the lane pattern (deterministic)
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI host code (moe_api.cpp) and the kernel
+// files.  Launchers return 0, -2 (unsupported shape) or -4 (launch error).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Validated, normalised layer shape.
+struct Shape {
+  int T, d, H, dh, E, Eh, k, K;  // K = H * k assignments per token
+  int n_groups, topk_groups, renorm;
+  int drop, C, keep_num, keep_den;
+  int dff, act, n_shared, latent, residual;
+  bool act_f32, router_f32;
+  long R_max;                     // upper bound on kept rows
+};
+
+// ---------------------------------------------------------------- route
+struct RouteGeom {
+  int Epad, nf, nplanes, mw, tb, ksplit, kchunk_per_split;
+  int L, epl, sel_blocks;
+};
+RouteGeom route_geometry(const Shape &s);
+bool route_supported(const Shape &s);
+size_t route_ws_bytes(const Shape &s);
+int launch_route(const Shape &s, const void *x, const void *w_router, const float *bias, float *logits,
+                 int mode, int32_t *topk_idx, float *topk_w, float *aux_loss, void *ws, hipStream_t st);
+
+// ---------------------------------------------------------------- dispatch
+size_t dispatch_ws_bytes(const Shape &s);
+int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w, const void *x,
+                    int32_t *demand, int32_t *counts, int32_t *offsets, int32_t *row_of, int32_t *src_of,
+                    void *x_perm, void *ws, hipStream_t st);
+
+// ---------------------------------------------------------------- grouped GEMM / expert FFN
+size_t ffn_ws_bytes(const Shape &s);
+int launch_expert_ffn(const Shape &s, const void *x_perm, const int32_t *offsets, const void *w1,
+                      const void *w3, const void *w2, void *y_perm, const void *x_shared, const void *ws1,
+                      const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st);
+// dense C[M,N] = A[M,K] B[N,K]^T (+ residual R[M,N]), act dtype, float32 accumulate
+size_t dense_ws_bytes();
+int launch_dense(bool f32, const void *A, const void *B, void *C, const void *residual, int M, int N, int K,
+                 void *ws, hipStream_t st);
+
+// ---------------------------------------------------------------- combine
+int launch_combine(const Shape &s, const void *y_perm, const int32_t *row_of, const float *topk_w,
+                   const void *residual, const void *shared_out, void *y, hipStream_t st);
+
+}  // namespace moe
