@@ -1,0 +1,229 @@
+"""Benchmark: MoE layer forward tokens/s on one MI355X, with roofline fractions.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1|c2|c3|c4|c0] [--no-cpu]
+
+Prints ONE JSON line on stdout (progress goes to stderr).  A step is one
+moe_layer_fwd call (route -> dispatch -> expert FFN -> combine, plus the latent
+projections for the multi-head workload) over one batch of synthetic tokens
+already resident in HBM.  K steps run back to back on one stream between two
+device synchronisations; value = T * K / elapsed.
+
+Per-stage times come from HIP events recorded on the stream the kernels run
+on, around separate calls of moe_route / moe_dispatch / moe_expert_ffn /
+moe_combine on the same data.  The roofline object is for the grouped GEMM of
+the expert FFN (its two launches: gate/up with the SwiGLU epilogue, then
+down), the dominant kernel: achieved = algorithmic FLOPs of the kept rows and
+shared experts / measured stage time, against the bf16 dense MFMA peak.
+The CPU baseline is the float64 numpy oracle on a bounded sample of the same
+workload (routing of every token, expert FFN and combine for a token sample).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+METRIC = "MoE layer fwd tokens/s on 1 MI355X; grouped-GEMM MFMA % + route/dispatch HBM %"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c1")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: automatic)")
+    ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, R):
+    """Algorithmic bytes (HBM) and FLOPs of each step, for R kept rows."""
+    a = 4 if cfg.act_dtype == 0 else 2
+    r = 4 if cfg.router_dtype == 0 else 2
+    T, d, H, dh, E, K = cfg.T, cfg.d_model, cfg.n_heads, cfg.d_head, cfg.n_experts, cfg.k_total
+    m = 3 if cfg.act == 1 else 2
+    out = {}
+    out["route_bytes"] = T * H * dh * a + E * dh * r + T * K * 8
+    out["dispatch_bytes"] = T * H * dh * a + R * dh * a + T * K * 8 + R * 4 + (T * K * 4 if cfg.drop == 2 else 0)
+    out["combine_bytes"] = R * dh * a + T * K * 8 + T * H * dh * a * (1 + (cfg.residual and not cfg.latent_proj)
+                                                                        + (cfg.n_shared > 0))
+    out["ffn_flops"] = 2 * R * dh * m * cfg.d_ff + 2 * T * d * m * cfg.n_shared * cfg.d_ff
+    out["proj_flops"] = (2 * 2 * T * d * H * dh) if cfg.latent_proj else 0
+    return out
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        n = len(os.sched_getaffinity(0))
+    return int(n)
+
+
+def cpu_baseline(cfg, inp, sample):
+    import oracle
+    toks = np.linspace(0, cfg.T - 1, sample).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.forward(cfg, inp, tokens=toks)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"float64 numpy oracle: routing + keep rule of all {cfg.T} tokens, expert FFN and "
+                      f"combine for {sample} evenly spaced tokens; {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import routing_dispatch_expert_router_amd as moe
+    from moe_inputs import CONFIGS, generate
+
+    names = {"c0": 0, "c1": 1, "c2": 2, "c3": 3, "c4": 4}
+    cfg = CONFIGS[names[args.config]] if args.config in names else next(c for c in CONFIGS if c.name == args.config)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev_name = torch.cuda.get_device_properties(0).name
+    log(f"[bench] {cfg.name} on {dev_name}: generating inputs")
+    t0 = time.perf_counter()
+    inp = generate(cfg)
+    log(f"[bench] inputs in {time.perf_counter() - t0:.1f} s; moving to HBM")
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    W = dict(w_router=dev(inp.w_router), router_bias=dev(inp.bias), w1=dev(inp.w1), w3=dev(inp.w3),
+             w2=dev(inp.w2), ws1=dev(inp.ws1), ws3=dev(inp.ws3), ws2=dev(inp.ws2), w_in=dev(inp.w_in),
+             w_out=dev(inp.w_out))
+    x = dev(inp.x)
+    y = torch.empty_like(x)
+    T, K, E, dh = cfg.T, cfg.k_total, cfg.n_experts, cfg.d_head
+    Rm = moe.moe_rows_upper_bound(cfg)
+    adt = torch.bfloat16 if cfg.act_dtype == 1 else torch.float32
+    io = dict(topk_idx=torch.empty(T, K, dtype=torch.int32, device="cuda"),
+              topk_w=torch.empty(T, K, dtype=torch.float32, device="cuda"),
+              demand=torch.empty(E, dtype=torch.int32, device="cuda"),
+              counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+              offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+              row_of=torch.empty(T, K, dtype=torch.int32, device="cuda"),
+              src_of=torch.empty(Rm, dtype=torch.int32, device="cuda"),
+              x_perm=torch.empty(Rm, dh, dtype=adt, device="cuda"),
+              y_perm=torch.empty(Rm, dh, dtype=adt, device="cuda"),
+              shared_out=torch.empty(T, cfg.d_model, dtype=adt, device="cuda") if cfg.n_shared else None,
+              z=torch.empty(T, cfg.d_latent, dtype=adt, device="cuda") if cfg.latent_proj else None,
+              o=torch.empty(T, cfg.d_latent, dtype=adt, device="cuda") if cfg.latent_proj else None)
+    ws = moe.workspace(cfg)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_layer_fwd(cfg, W, x, y, io, ws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    R = int(io["offsets"][E].item())
+    log(f"[bench] R = {R} kept rows; timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {ms_step:.3f} ms/step (events), {wall / args.steps * 1e3:.3f} ms/step (wall)")
+
+    # ---- per-stage times: the four C-ABI calls on the same data, HIP events on this stream
+    xin = io["z"] if cfg.latent_proj else x
+    reps = max(5, min(50, args.steps))
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3  # seconds
+
+    st = {}
+    st["route"] = timed(lambda: moe.moe_route(cfg, xin, W["w_router"], W["router_bias"], None,
+                                              moe.MOE_LOGITS_COMPUTE, io["topk_idx"], io["topk_w"], None, ws))
+    st["dispatch"] = timed(lambda: moe.moe_dispatch(cfg, io["topk_idx"], io["topk_w"], xin, io["demand"],
+                                                    io["counts"], io["offsets"], io["row_of"], io["src_of"],
+                                                    io["x_perm"], ws))
+    st["expert_ffn"] = timed(lambda: moe.moe_expert_ffn(cfg, io["x_perm"], io["offsets"], W["w1"], W["w3"],
+                                                        W["w2"], io["y_perm"], x if cfg.n_shared else None,
+                                                        W["ws1"], W["ws3"], W["ws2"], io["shared_out"], ws))
+    st["combine"] = timed(lambda: moe.moe_combine(cfg, io["y_perm"], io["row_of"], io["topk_w"],
+                                                  x if (cfg.residual and not cfg.latent_proj) else None,
+                                                  io["shared_out"], io["o"] if cfg.latent_proj else y))
+    alg = algorithmic(cfg, R)
+    peak = PEAK_F32_TFLOPS if cfg.act_dtype == 0 else PEAK_BF16_TFLOPS
+    ffn_tf = alg["ffn_flops"] / st["expert_ffn"] / 1e12
+    stages = {
+        "route": {"us": st["route"] * 1e6, "GBs": alg["route_bytes"] / st["route"] / 1e9},
+        "dispatch": {"us": st["dispatch"] * 1e6, "GBs": alg["dispatch_bytes"] / st["dispatch"] / 1e9},
+        "expert_ffn": {"us": st["expert_ffn"] * 1e6, "TFLOPs": ffn_tf},
+        "combine": {"us": st["combine"] * 1e6, "GBs": alg["combine_bytes"] / st["combine"] / 1e9},
+    }
+    for k in ("route", "dispatch", "combine"):
+        stages[k]["hbm_frac"] = stages[k]["GBs"] / PEAK_HBM_GBS
+    stages["expert_ffn"]["mfma_frac"] = ffn_tf / peak
+    for k, v in stages.items():
+        log(f"[bench]   {k:10s} " + "  ".join(f"{a}={b:.4g}" for a, b in v.items()))
+
+    value = T / (ms_step * 1e-3)
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if cfg.act_dtype == 0 else "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "d_model": cfg.d_model, "n_experts": E, "top_k": cfg.top_k,
+                   "n_heads": cfg.n_heads, "d_ff": cfg.d_ff, "n_shared": cfg.n_shared, "kept_rows": R,
+                   "act": "swiglu" if cfg.act == 1 else "relu",
+                   "drop": ["none", "capacity", "affinity"][cfg.drop], "parallelism": "single GPU"},
+        "roofline": {"kernel": "grouped_gemm_kernel, expert FFN (SwiGLU gate/up launch + down launch)",
+                     "bound": "mfma", "achieved": ffn_tf, "peak": peak, "unit": "TFLOP/s", "frac": ffn_tf / peak,
+                     "traffic": None},
+        "stages": stages,
+        "device": dev_name,
+    }
+    if not args.no_cpu:
+        sample = args.cpu_tokens or {0: 256, 1: 384, 2: 1024, 3: 96, 4: 2048}[names.get(args.config, 1)]
+        log(f"[bench] oracle CPU baseline on {sample} tokens")
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, sample)
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(s + "\n")
+
+
+if __name__ == "__main__":
+    main()
