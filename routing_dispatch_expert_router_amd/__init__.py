@@ -6,7 +6,7 @@ stream through the C ABI declared in include/moe.h, with the same names and
 argument order.  PyTorch provides device memory and streams.
 
 Importing fails loudly if the library has not been built
-(``python -m routing_dispatch_expert_router_amd.build``).
+(``python routing_dispatch_expert_router_amd/build.py``).
 """
 import ctypes
 import os
@@ -56,7 +56,7 @@ class MoeError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m routing_dispatch_expert_router_amd.build`")
+                          "`python routing_dispatch_expert_router_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, S, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.POINTER(MoeConfig)
     sig = {

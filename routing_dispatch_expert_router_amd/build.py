@@ -1,6 +1,8 @@
 """Build libmoe.so (gfx950 code objects + C-ABI host code) in-tree with hipcc.
 
-    python -m routing_dispatch_expert_router_amd.build [-v]
+    python routing_dispatch_expert_router_amd/build.py [-v]
+
+(run it by path: importing the package loads the library it builds)
 
 Every source is compiled on each call (object files go to _build/ at the repo
 root); the shared library is written next to this file and replaced atomically.
@@ -52,6 +54,13 @@ def build(verbose=False):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # a kernel template whose host-side instantiation failed leaves its launch
+    # stub undefined; refuse such a library instead of failing at load time
+    nm = subprocess.run(["nm", "-DC", "--undefined-only", tmp], capture_output=True, text=True)
+    bad = [l.strip() for l in nm.stdout.splitlines() if "moe::" in l]
+    if bad:
+        os.remove(tmp)
+        raise RuntimeError("libmoe.so has undefined library symbols:\n" + "\n".join(bad[:20]))
     os.replace(tmp, LIB)
     return LIB
 

@@ -21,7 +21,6 @@
 namespace moe {
 
 enum { EPI_PLAIN = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_RESID = 3 };
-constexpr int BM = 128, BN = 128;
 
 struct GemmArgs {
   const void *A; long lda;                    // routed: A rows indexed by offsets
@@ -33,15 +32,18 @@ struct GemmArgs {
   const void *Bx; const void *Bx2; long ldbx;
   void *Cx; long ldcx;
   int Mx, Nx, Kx, has_x;
+  long Mr_bound;                              // upper bound on the routed rows (sum over experts)
   const void *res; long ldres;                // EPI_RESID: added to the extra group's output
   const int32_t *prefix;                      // [G+1] tile prefix
   int G;
 };
 
-template <int EPI> __host__ __device__ inline int n_tiles(int N) { return EPI == EPI_SWIGLU ? N / 64 : (N + BN - 1) / BN; }
+template <int EPI, int BN_> __host__ __device__ inline int n_tiles(int N) {
+  return EPI == EPI_SWIGLU ? (N + BN_ / 2 - 1) / (BN_ / 2) : (N + BN_ - 1) / BN_;
+}
 
 // tile prefix over groups: tiles_g = ceil(M_g / BM) * n_tiles(N_g)
-template <int EPI>
+template <int EPI, int BM_, int BN_>
 __global__ __launch_bounds__(1024) void gemm_prep_kernel(const int32_t *__restrict__ offsets, int E, int N,
                                                          int has_x, int Mx, int Nx, int32_t *__restrict__ prefix) {
   __shared__ int s[1024];
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(1024) void gemm_prep_kernel(const int32_t *__restri
     if (g < G) {
       int M = (g < E) ? offsets[g + 1] - offsets[g] : Mx;
       int nn = (g < E) ? N : Nx;
-      v = (M + BM - 1) / BM * n_tiles<EPI>(nn);
+      v = (M + BM_ - 1) / BM_ * n_tiles<EPI, BN_>(nn);
     }
     loc[i] = v;
     sum += v;
@@ -78,12 +80,37 @@ __global__ __launch_bounds__(1024) void gemm_prep_kernel(const int32_t *__restri
   if (tid == 1023) prefix[G] = s[1023];
 }
 
-template <typename TE, int EPI>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
+// Tile BM x BN outputs (SwiGLU: BN/2 hidden columns, the B tile holding BN/2
+// gate rows then BN/2 up rows); WGM x WGN waves, each (BM/WGM) x (BN/WGN);
+// k-chunks of KS 16-byte slots per row (KS = 8: 128 B, KS = 4: 64 B) in a ring
+// of STAGES LDS buffers, so global loads run STAGES-1 chunks ahead of the
+// MFMAs.  Operands go global -> LDS with global_load_lds_dwordx4 (no VGPR
+// staging): each wave instruction fills 64 consecutive 16-byte LDS slots, so
+// every lane fetches the global chunk that belongs in its slot.  Slots are
+// XOR-swizzled within a row so the 16 rows one ds_read_b128 touches fall in
+// distinct banks.
+template <int KS>
+__device__ __forceinline__ int swz(int row, int q) {
+  if constexpr (KS == 8) return q ^ (row & 7);
+  else return q ^ (((row >> 1) ^ (row >> 3)) & 3);
+}
+
+template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES, int PFA>
+__global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p) {
+  constexpr int NT = 64 * WGM * WGN;    // threads
   constexpr int EPC = 16 / sizeof(TE);  // elements per 16-byte slot
-  constexpr int BKE = 8 * EPC;          // elements per 128-byte k-chunk
-  __shared__ u32x4 sA[2][BM * 8];
-  __shared__ u32x4 sB[2][BN * 8];
+  constexpr int BKE = KS * EPC;         // elements per k-chunk
+  constexpr int WM = BM_ / WGM, WN = BN_ / WGN, MF = WM / 16, NF = WN / 16;
+  constexpr int SA = BM_ * KS, SB = BN_ * KS;  // 16-byte slots per stage
+  constexpr int LA = SA / NT, LB = SB / NT;    // slots per thread per stage
+  constexpr int NKS = KS / 4;                  // MFMA k-steps per chunk
+  static_assert(LA * NT == SA && LB * NT == SB, "tile / thread mismatch");
+  static_assert(STAGES == 2 && NKS == 2, "pipeline below is written for 2 stages of 2 k-steps");
+  constexpr int NPF = (BM_ + BN_ + NT - 1) / NT;  // L2-prefetch loads per thread per chunk
+  extern __shared__ u32x4 smem[];
+  u32x4 *sA = smem;                  // [STAGES][SA]
+  u32x4 *sB = smem + STAGES * SA;    // [STAGES][SB]
+  u32x4 *sPF = sB + STAGES * SB;     // [waves][16]: landing area of the L2 prefetches
 
   const int total = p.prefix[p.G];
   const int b = blockIdx.x;
@@ -98,7 +125,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
     if (p.prefix[mid] <= lt) lo = mid; else hi = mid - 1;
   }
   const int g = lo;
-  int local = lt - p.prefix[g];
+  const int local = lt - p.prefix[g];
 
   const TE *A, *B, *B2;
   TE *C;
@@ -118,7 +145,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
     A = (const TE *)p.Ax; B = (const TE *)p.Bx; B2 = (const TE *)p.Bx2; C = (TE *)p.Cx;
   }
   // grouped raster inside the group: bands of GM m-tiles, n outer, m inner
-  const int mt = (M + BM - 1) / BM, nt = n_tiles<EPI>(N);
+  const int mt = (M + BM_ - 1) / BM_, nt = n_tiles<EPI, BN_>(N);
   constexpr int GM = 8;
   const int band = local / (GM * nt);
   const int first_m = band * GM;
@@ -126,110 +153,146 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
   const int in_band = local - band * GM * nt;
   const int tm = first_m + in_band % gsm;
   const int tn = in_band / gsm;
-  const int m0 = tm * BM;
+  const int m0 = tm * BM_;
+  constexpr int HB = BN_ / 2;  // SwiGLU: hidden columns per tile
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv / WGN, wn = wv % WGN;
   const int cq = lane >> 4, l16 = lane & 15;
 
-  // global -> LDS assignment: 1024 16-byte slots per operand tile, 4 per thread
-  const TE *pa[4];
-  const TE *pb[4];
-  int slot[4];
+  // global source of each LDS slot s = i*NT + tid this thread fills
+  const TE *pa[LA];
+  const TE *pb[LB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 3) + 32 * i, q = tid & 7;
-    slot[i] = row * 8 + (q ^ (row & 7));
+  for (int i = 0; i < LA; ++i) {
+    const int s = i * NT + tid, row = s / KS, q = swz<KS>(row, s % KS);
     pa[i] = A + (size_t)min(m0 + row, M - 1) * lda + q * EPC;
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int s = i * NT + tid, row = s / KS, q = swz<KS>(row, s % KS);
     if (EPI == EPI_SWIGLU) {
-      const int hn = tn * 64 + (row & 63);
-      pb[i] = ((row < 64) ? B : B2) + (size_t)hn * ldb + q * EPC;
+      const int hn = min(tn * HB + (row % HB), N - 1);
+      pb[i] = ((row < HB) ? B : B2) + (size_t)hn * ldb + q * EPC;
     } else {
-      pb[i] = B + (size_t)min(tn * BN + row, N - 1) * ldb + q * EPC;
+      pb[i] = B + (size_t)min(tn * BN_ + row, N - 1) * ldb + q * EPC;
     }
   }
   const int nk = K / BKE;
-
-  f32x4 acc[4][4];
+  // L2 prefetch: thread t touches tile rows t, t+NT, ... (A rows, then B rows)
+  // of the chunk PFA chunks after the one whose LDS loads it issues
+  const TE *ppf[NPF];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 ra[4], rb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = *reinterpret_cast<const u32x4 *>(pa[i]);
-    rb[i] = *reinterpret_cast<const u32x4 *>(pb[i]);
+  for (int i = 0; i < NPF; ++i) {
+    const int row = min(i * NT + tid, BM_ + BN_ - 1);
+    if (row < BM_) {
+      ppf[i] = A + (size_t)min(m0 + row, M - 1) * lda;
+    } else {
+      const int r = row - BM_;
+      if (EPI == EPI_SWIGLU)
+        ppf[i] = ((r < HB) ? B : B2) + (size_t)min(tn * HB + (r % HB), N - 1) * ldb;
+      else
+        ppf[i] = B + (size_t)min(tn * BN_ + r, N - 1) * ldb;
+    }
   }
+
+  f32x4 acc[MF][NF];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sA[0][slot[i]] = ra[i];
-    sB[0][slot[i]] = rb[i];
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // LDS slot offsets (within a stage) of this lane's fragments, per k-step
+  int aoff[NKS][MF], boff[NKS][NF];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int qs = cq + 4 * ks;
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int r = wm * WM + i * 16 + l16;
+      aoff[ks][i] = r * KS + swz<KS>(r, qs);
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int r = (EPI == EPI_SWIGLU)
+                        ? ((f < NF / 2) ? wn * (HB / WGN) + f * 16 : HB + wn * (HB / WGN) + (f - NF / 2) * 16) + l16
+                        : wn * WN + f * 16 + l16;
+      boff[ks][f] = r * KS + swz<KS>(r, qs);
+    }
   }
+
+  auto issue = [&](int kc, int st) {
+    const size_t ko = (size_t)kc * BKE;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) load_lds16(pa[i] + ko, sA + st * SA + i * NT + wv * 64);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) load_lds16(pb[i] + ko, sB + st * SB + i * NT + wv * 64);
+    if constexpr (PFA > 0) {
+      // always issued (clamped to the last chunk) so the vmcnt arithmetic holds
+      const size_t kp = (size_t)min(kc + PFA, nk - 1) * BKE;
+#pragma unroll
+      for (int i = 0; i < NPF; ++i) load_lds4(ppf[i] + kp, sPF + wv * 16);
+    }
+  };
+  constexpr int NPFI = PFA > 0 ? NPF : 0;  // prefetch loads issued after each chunk's LDS loads
+  auto read = [&](int st, int ks, u32x4 *fa, u32x4 *fb) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i) fa[i] = sA[st * SA + aoff[ks][i]];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) fb[f] = sB[st * SB + boff[ks][f]];
+  };
+  auto mfma = [&](const u32x4 *fa, const u32x4 *fb) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[i][f] = mma16(fa[i], fb[f], acc[i][f], TE());
+  };
+
+  // Software pipeline over k-steps: the LDS reads of the next k-step are in
+  // flight while the MFMAs of the current one run.  Chunk kc+2 is loaded into
+  // the stage of chunk kc once every wave has read chunk kc (barrier).
+  u32x4 fa0[MF], fb0[NF], fa1[MF], fb1[NF];
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  if (nk > 1) wait_vmcnt<LA + LB + 2 * NPFI>(); else wait_vmcnt<NPFI>();
   __syncthreads();
-
-  // B-tile row of this wave's n-fragment f
-  int brow[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f)
-    brow[f] = (EPI == EPI_SWIGLU) ? ((f < 2) ? wn * 32 + f * 16 : 64 + wn * 32 + (f - 2) * 16) + l16
-                                  : wn * 64 + f * 16 + l16;
-
+  read(0, 0, fa0, fb0);
   for (int kc = 0; kc < nk; ++kc) {
     const int st = kc & 1;
+    read(st, 1, fa1, fb1);
+    mfma(fa0, fb0);
     if (kc + 1 < nk) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4 *>(pa[i] + (size_t)(kc + 1) * BKE);
-        rb[i] = *reinterpret_cast<const u32x4 *>(pb[i] + (size_t)(kc + 1) * BKE);
-      }
+      // chunk kc+1 landed for this wave (only its trailing L2 prefetches may
+      // still be in flight); this wave's reads of stage st are done
+      wait_vmcnt<NPFI>();
+      wait_lgkmcnt0();
+      __syncthreads();
+      if (kc + 2 < nk) issue(kc + 2, st);
+      read(st ^ 1, 0, fa0, fb0);
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int qs = cq + 4 * ks;
-      u32x4 fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + l16;
-        fa[i] = sA[st][r * 8 + (qs ^ (r & 7))];
-      }
-#pragma unroll
-      for (int f = 0; f < 4; ++f) fb[f] = sB[st][brow[f] * 8 + (qs ^ (brow[f] & 7))];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int f = 0; f < 4; ++f) acc[i][f] = mma16(fa[i], fb[f], acc[i][f], TE());
-    }
-    if (kc + 1 < nk) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sA[st ^ 1][slot[i]] = ra[i];
-        sB[st ^ 1][slot[i]] = rb[i];
-      }
-    }
-    __syncthreads();
+    mfma(fa1, fb1);
   }
 
-  // epilogue: acc[i][f][v] = C[wm*64 + i*16 + 4*cq + v][n-fragment f, column l16]
+  // epilogue: acc[i][f][v] = C[wm*WM + i*16 + 4*cq + v][n-fragment f, column l16]
   const TE *R = (EPI == EPI_RESID) ? (const TE *)p.res : nullptr;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MF; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int row = m0 + wm * 64 + i * 16 + 4 * cq + v;
+      const int row = m0 + wm * WM + i * 16 + 4 * cq + v;
       if (row >= M) continue;
       if (EPI == EPI_SWIGLU) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int col = tn * 64 + wn * 32 + f * 16 + l16;
-          const float gt = acc[i][f][v], up = acc[i][f + 2][v];
+        for (int f = 0; f < NF / 2; ++f) {
+          const int col = tn * HB + wn * (HB / WGN) + f * 16 + l16;
+          if (col >= N) continue;
+          const float gt = acc[i][f][v], up = acc[i][f + NF / 2][v];
           const float h = gt / (1.0f + __expf(-gt)) * up;
           C[(size_t)row * ldc + col] = Elem<TE>::from_f32(h);
         }
       } else {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const int col = tn * BN + wn * 64 + f * 16 + l16;
+        for (int f = 0; f < NF; ++f) {
+          const int col = tn * BN_ + wn * WN + f * 16 + l16;
           if (col >= N) continue;
           float o = acc[i][f][v];
           if (EPI == EPI_RELU) o = fmaxf(o, 0.0f);
@@ -241,20 +304,55 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------- host
-static long max_tiles(long rows_bound, int groups, int n_tiles_) {
-  return ((rows_bound + BM - 1) / BM + groups) * n_tiles_;
+// Tile shapes with an instantiated kernel.
+enum TileCfg {
+  TILE_128x128 = 0,     // 4 waves (2 x 2), wave tile 64 x 64
+  TILE_256x256_W8 = 1,  // 8 waves (2 x 4), wave tile 128 x 64
+  TILE_256x128_W8 = 2,  // 8 waves (4 x 2), wave tile 64 x 64
+  TILE_128x256_W8 = 3,  // 8 waves (2 x 4), wave tile 64 x 64
+  TILE_128x128_W8 = 4,  // 8 waves (2 x 4), wave tile 64 x 32
+  TILE_64x256_W4 = 5,   // 4 waves (1 x 4), wave tile 64 x 64
+};
+
+static long max_tiles(long rows_bound, int groups, int bm, int ntiles) {
+  return ((rows_bound + bm - 1) / bm + groups) * ntiles;
+}
+
+template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES, int PFA>
+static int run_gemm_t(GemmArgs a, int32_t *prefix, hipStream_t st) {
+  a.prefix = prefix;
+  hipLaunchKernelGGL((gemm_prep_kernel<EPI, BM_, BN_>), dim3(1), dim3(1024), 0, st, a.offsets, a.E, a.N, a.has_x,
+                     a.Mx, a.Nx, prefix);
+  if (hipGetLastError() != hipSuccess) return -4;
+  long grid = (a.E ? max_tiles(a.Mr_bound, a.E, BM_, n_tiles<EPI, BN_>(a.N)) : 0) +
+              (a.has_x ? max_tiles(a.Mx, 0, BM_, n_tiles<EPI, BN_>(a.Nx)) : 0);
+  if (grid <= 0) return 0;
+  // dynamic LDS up to the device's per-workgroup limit (160 KiB on gfx950)
+  constexpr size_t lds = (size_t)STAGES * (BM_ + BN_) * KS * 16 + (size_t)WGM * WGN * 256;
+  static_assert(lds <= 160 * 1024, "LDS per workgroup");
+  hipLaunchKernelGGL((grouped_gemm_kernel<TE, EPI, BM_, BN_, WGM, WGN, KS, STAGES, PFA>), dim3(grid),
+                     dim3(64 * WGM * WGN), lds, st, a);
+  if (hipGetLastError() != hipSuccess) return -4;
+  return 0;
 }
 
 template <typename TE, int EPI>
-static int run_gemm(GemmArgs a, long grid, int prepN, int prepNx, int32_t *prefix, hipStream_t st) {
-  a.prefix = prefix;
-  hipLaunchKernelGGL((gemm_prep_kernel<EPI>), dim3(1), dim3(1024), 0, st, a.offsets, a.E, prepN, a.has_x, a.Mx,
-                     prepNx, prefix);
-  if (hipGetLastError() != hipSuccess) return -4;
-  if (grid <= 0) return 0;
-  hipLaunchKernelGGL((grouped_gemm_kernel<TE, EPI>), dim3(grid), dim3(256), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return -4;
-  return 0;
+static int run_gemm(GemmArgs a, int tile, int32_t *prefix, hipStream_t st) {
+  if constexpr (sizeof(TE) == 4) return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 0>(a, prefix, st);
+  switch (tile) {
+    case TILE_256x256_W8: return run_gemm_t<TE, EPI, 256, 256, 2, 4, 8, 2, 0>(a, prefix, st);
+    case TILE_256x128_W8: return run_gemm_t<TE, EPI, 256, 128, 4, 2, 8, 2, 0>(a, prefix, st);
+    case TILE_128x256_W8: return run_gemm_t<TE, EPI, 128, 256, 2, 4, 8, 2, 0>(a, prefix, st);
+    case TILE_128x128_W8: return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 0>(a, prefix, st);
+    case TILE_64x256_W4: return run_gemm_t<TE, EPI, 64, 256, 1, 4, 8, 2, 0>(a, prefix, st);
+    default: return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 0>(a, prefix, st);
+  }
+}
+
+// tile shape for a launch: large tiles when the groups are tall enough to fill them
+static int pick_tile(long rows, int groups) {
+  long avg = groups > 0 ? rows / groups : rows;
+  return avg >= 1024 ? TILE_256x256_W8 : TILE_128x128_W8;
 }
 
 size_t ffn_ws_bytes(const Shape &s) {
@@ -284,45 +382,36 @@ static int ffn_typed(const Shape &s, const void *x_perm, const int32_t *offsets,
   int32_t *pre2 = (int32_t *)p;
   const bool glu = s.act == 1;
   const int has_x = s.n_shared ? 1 : 0;
+  // f32 layers are parity-sized: the small tile is plenty
+  const int tile = sizeof(TE) == 4 ? TILE_128x128 : pick_tile(s.R_max, s.E);
 
   GemmArgs a{};
   // ---- GEMM 1: H = act(x_perm W1^T [, x_perm W3^T])
   a.A = x_perm; a.lda = s.dh;
   a.B = w1; a.B2 = glu ? w3 : nullptr; a.ldb = s.dh; a.bstride = (long)s.dff * s.dh;
   a.C = H; a.ldc = s.dff;
-  a.offsets = offsets; a.E = s.E; a.N = s.dff; a.K = s.dh;
+  a.offsets = offsets; a.E = s.E; a.N = s.dff; a.K = s.dh; a.Mr_bound = s.R_max;
   a.has_x = has_x;
   if (has_x) {
     a.Ax = x_shared; a.ldax = s.d; a.Bx = ws1; a.Bx2 = glu ? ws3 : nullptr; a.ldbx = s.d;
     a.Cx = Hs; a.ldcx = fs; a.Mx = s.T; a.Nx = fs; a.Kx = s.d;
   }
   a.G = s.E + has_x;
-  int rc;
-  if (glu) {
-    long grid = max_tiles(s.R_max, s.E, n_tiles<EPI_SWIGLU>(s.dff)) +
-                (has_x ? max_tiles(s.T, 0, n_tiles<EPI_SWIGLU>(fs)) : 0);
-    rc = run_gemm<TE, EPI_SWIGLU>(a, grid, s.dff, fs, pre1, st);
-  } else {
-    long grid = max_tiles(s.R_max, s.E, n_tiles<EPI_RELU>(s.dff)) +
-                (has_x ? max_tiles(s.T, 0, n_tiles<EPI_RELU>(fs)) : 0);
-    rc = run_gemm<TE, EPI_RELU>(a, grid, s.dff, fs, pre1, st);
-  }
+  int rc = glu ? run_gemm<TE, EPI_SWIGLU>(a, tile, pre1, st) : run_gemm<TE, EPI_RELU>(a, tile, pre1, st);
   if (rc) return rc;
   // ---- GEMM 2: y_perm = H W2^T ; shared_out = Hs Ws2^T
   GemmArgs b{};
   b.A = H; b.lda = s.dff;
   b.B = w2; b.B2 = nullptr; b.ldb = s.dff; b.bstride = (long)s.dh * s.dff;
   b.C = y_perm; b.ldc = s.dh;
-  b.offsets = offsets; b.E = s.E; b.N = s.dh; b.K = s.dff;
+  b.offsets = offsets; b.E = s.E; b.N = s.dh; b.K = s.dff; b.Mr_bound = s.R_max;
   b.has_x = has_x;
   if (has_x) {
     b.Ax = Hs; b.ldax = fs; b.Bx = ws2; b.Bx2 = nullptr; b.ldbx = fs;
     b.Cx = shared_out; b.ldcx = s.d; b.Mx = s.T; b.Nx = s.d; b.Kx = fs;
   }
   b.G = s.E + has_x;
-  long grid2 = max_tiles(s.R_max, s.E, n_tiles<EPI_PLAIN>(s.dh)) +
-               (has_x ? max_tiles(s.T, 0, n_tiles<EPI_PLAIN>(s.d)) : 0);
-  return run_gemm<TE, EPI_PLAIN>(b, grid2, s.dh, s.d, pre2, st);
+  return run_gemm<TE, EPI_PLAIN>(b, tile, pre2, st);
 }
 
 int launch_expert_ffn(const Shape &s, const void *x_perm, const int32_t *offsets, const void *w1, const void *w3,
@@ -341,12 +430,12 @@ int launch_dense(bool f32, const void *A, const void *B, void *C, const void *re
   a.E = 0; a.has_x = 1; a.G = 1;
   a.Ax = A; a.ldax = K; a.Bx = B; a.ldbx = K; a.Cx = C; a.ldcx = N; a.Mx = M; a.Nx = N; a.Kx = K;
   a.res = residual; a.ldres = N;
-  long grid = max_tiles(M, 0, n_tiles<EPI_PLAIN>(N));
   int32_t *pre = (int32_t *)ws;
   if (f32)
-    return residual ? run_gemm<float, EPI_RESID>(a, grid, 0, N, pre, st) : run_gemm<float, EPI_PLAIN>(a, grid, 0, N, pre, st);
-  return residual ? run_gemm<uint16_t, EPI_RESID>(a, grid, 0, N, pre, st)
-                  : run_gemm<uint16_t, EPI_PLAIN>(a, grid, 0, N, pre, st);
+    return residual ? run_gemm<float, EPI_RESID>(a, TILE_128x128, pre, st)
+                    : run_gemm<float, EPI_PLAIN>(a, TILE_128x128, pre, st);
+  const int tile = pick_tile(M, 1);
+  return residual ? run_gemm<uint16_t, EPI_RESID>(a, tile, pre, st) : run_gemm<uint16_t, EPI_PLAIN>(a, tile, pre, st);
 }
 
 }  // namespace moe
