@@ -95,7 +95,7 @@ __device__ __forceinline__ int swz(int row, int q) {
   else return q ^ (((row >> 1) ^ (row >> 3)) & 3);
 }
 
-template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES, int PFA>
+template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES>
 __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int NT = 64 * WGM * WGN;    // threads
   constexpr int EPC = 16 / sizeof(TE);  // elements per 16-byte slot
@@ -106,11 +106,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   constexpr int NKS = KS / 4;                  // MFMA k-steps per chunk
   static_assert(LA * NT == SA && LB * NT == SB, "tile / thread mismatch");
   static_assert(STAGES == 2 && NKS == 2, "pipeline below is written for 2 stages of 2 k-steps");
-  constexpr int NPF = (BM_ + BN_ + NT - 1) / NT;  // L2-prefetch loads per thread per chunk
   extern __shared__ u32x4 smem[];
   u32x4 *sA = smem;                  // [STAGES][SA]
   u32x4 *sB = smem + STAGES * SA;    // [STAGES][SB]
-  u32x4 *sPF = sB + STAGES * SB;     // [waves][16]: landing area of the L2 prefetches
 
   const int total = p.prefix[p.G];
   const int b = blockIdx.x;
@@ -159,86 +157,64 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv / WGN, wn = wv % WGN;
   const int cq = lane >> 4, l16 = lane & 15;
 
-  // global source of each LDS slot s = i*NT + tid this thread fills
-  const TE *pa[LA];
-  const TE *pb[LB];
+  // global source of each LDS slot s = i*NT + tid this thread fills, as a
+  // 32-bit element offset from the operand base (a group's operand is < 2^31
+  // elements); SwiGLU B rows past HB come from the up projection
+  uint32_t oa[LA], ob[LB];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int s = i * NT + tid, row = s / KS, q = swz<KS>(row, s % KS);
-    pa[i] = A + (size_t)min(m0 + row, M - 1) * lda + q * EPC;
+    oa[i] = (uint32_t)((size_t)min(m0 + row, M - 1) * lda + q * EPC);
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
     const int s = i * NT + tid, row = s / KS, q = swz<KS>(row, s % KS);
     if (EPI == EPI_SWIGLU) {
       const int hn = min(tn * HB + (row % HB), N - 1);
-      pb[i] = ((row < HB) ? B : B2) + (size_t)hn * ldb + q * EPC;
+      ob[i] = (uint32_t)((size_t)hn * ldb + q * EPC);
     } else {
-      pb[i] = B + (size_t)min(tn * BN_ + row, N - 1) * ldb + q * EPC;
+      ob[i] = (uint32_t)((size_t)min(tn * BN_ + row, N - 1) * ldb + q * EPC);
     }
   }
+  auto bsrc = [&](int i) -> const TE * {  // which projection slot i reads
+    const int row = (i * NT + tid) / KS;
+    return (EPI == EPI_SWIGLU && row >= HB) ? B2 : B;
+  };
   const int nk = K / BKE;
-  // L2 prefetch: thread t touches tile rows t, t+NT, ... (A rows, then B rows)
-  // of the chunk PFA chunks after the one whose LDS loads it issues
-  const TE *ppf[NPF];
-#pragma unroll
-  for (int i = 0; i < NPF; ++i) {
-    const int row = min(i * NT + tid, BM_ + BN_ - 1);
-    if (row < BM_) {
-      ppf[i] = A + (size_t)min(m0 + row, M - 1) * lda;
-    } else {
-      const int r = row - BM_;
-      if (EPI == EPI_SWIGLU)
-        ppf[i] = ((r < HB) ? B : B2) + (size_t)min(tn * HB + (r % HB), N - 1) * ldb;
-      else
-        ppf[i] = B + (size_t)min(tn * BN_ + r, N - 1) * ldb;
-    }
-  }
-
   f32x4 acc[MF][NF];
 #pragma unroll
   for (int i = 0; i < MF; ++i)
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // LDS slot offsets (within a stage) of this lane's fragments, per k-step
-  int aoff[NKS][MF], boff[NKS][NF];
+  // LDS slot of this lane's fragments: fragment rows are multiples of 16 plus
+  // l16, so row & 7 == l16 & 7 and the swizzled slot depends only on the
+  // k-step; the per-fragment part is a compile-time offset
+  static_assert(KS == 8, "fragment addressing assumes 128-byte k-chunks");
+  int abase[NKS], bbase[NKS];
+  const int bwoff = (EPI == EPI_SWIGLU) ? wn * (HB / WGN) : wn * WN;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    const int qs = cq + 4 * ks;
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      const int r = wm * WM + i * 16 + l16;
-      aoff[ks][i] = r * KS + swz<KS>(r, qs);
-    }
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int r = (EPI == EPI_SWIGLU)
-                        ? ((f < NF / 2) ? wn * (HB / WGN) + f * 16 : HB + wn * (HB / WGN) + (f - NF / 2) * 16) + l16
-                        : wn * WN + f * 16 + l16;
-      boff[ks][f] = r * KS + swz<KS>(r, qs);
-    }
+    const int sw = (cq + 4 * ks) ^ (l16 & 7);
+    abase[ks] = (wm * WM + l16) * KS + sw;
+    bbase[ks] = (bwoff + l16) * KS + sw;
   }
+  auto brow_off = [](int f) {  // B-tile row of n-fragment f, relative to bwoff
+    return (EPI == EPI_SWIGLU) ? ((f < NF / 2) ? f * 16 : HB + (f - NF / 2) * 16) : f * 16;
+  };
 
   auto issue = [&](int kc, int st) {
     const size_t ko = (size_t)kc * BKE;
 #pragma unroll
-    for (int i = 0; i < LA; ++i) load_lds16(pa[i] + ko, sA + st * SA + i * NT + wv * 64);
+    for (int i = 0; i < LA; ++i) load_lds16(A + oa[i] + ko, sA + st * SA + i * NT + wv * 64);
 #pragma unroll
-    for (int i = 0; i < LB; ++i) load_lds16(pb[i] + ko, sB + st * SB + i * NT + wv * 64);
-    if constexpr (PFA > 0) {
-      // always issued (clamped to the last chunk) so the vmcnt arithmetic holds
-      const size_t kp = (size_t)min(kc + PFA, nk - 1) * BKE;
-#pragma unroll
-      for (int i = 0; i < NPF; ++i) load_lds4(ppf[i] + kp, sPF + wv * 16);
-    }
+    for (int i = 0; i < LB; ++i) load_lds16(bsrc(i) + ob[i] + ko, sB + st * SB + i * NT + wv * 64);
   };
-  constexpr int NPFI = PFA > 0 ? NPF : 0;  // prefetch loads issued after each chunk's LDS loads
   auto read = [&](int st, int ks, u32x4 *fa, u32x4 *fb) {
 #pragma unroll
-    for (int i = 0; i < MF; ++i) fa[i] = sA[st * SA + aoff[ks][i]];
+    for (int i = 0; i < MF; ++i) fa[i] = sA[st * SA + abase[ks] + i * 16 * KS];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) fb[f] = sB[st * SB + boff[ks][f]];
+    for (int f = 0; f < NF; ++f) fb[f] = sB[st * SB + bbase[ks] + brow_off(f) * KS];
   };
   auto mfma = [&](const u32x4 *fa, const u32x4 *fb) {
 #pragma unroll
@@ -253,7 +229,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   u32x4 fa0[MF], fb0[NF], fa1[MF], fb1[NF];
   issue(0, 0);
   if (nk > 1) issue(1, 1);
-  if (nk > 1) wait_vmcnt<LA + LB + 2 * NPFI>(); else wait_vmcnt<NPFI>();
+  if (nk > 1) wait_vmcnt<LA + LB>(); else wait_vmcnt0();
   __syncthreads();
   read(0, 0, fa0, fb0);
   for (int kc = 0; kc < nk; ++kc) {
@@ -261,9 +237,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
     read(st, 1, fa1, fb1);
     mfma(fa0, fb0);
     if (kc + 1 < nk) {
-      // chunk kc+1 landed for this wave (only its trailing L2 prefetches may
-      // still be in flight); this wave's reads of stage st are done
-      wait_vmcnt<NPFI>();
+      // chunk kc+1 landed for this wave; this wave's reads of stage st are done
+      wait_vmcnt0();
       wait_lgkmcnt0();
       __syncthreads();
       if (kc + 2 < nk) issue(kc + 2, st);
@@ -318,7 +293,7 @@ static long max_tiles(long rows_bound, int groups, int bm, int ntiles) {
   return ((rows_bound + bm - 1) / bm + groups) * ntiles;
 }
 
-template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES, int PFA>
+template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES>
 static int run_gemm_t(GemmArgs a, int32_t *prefix, hipStream_t st) {
   a.prefix = prefix;
   hipLaunchKernelGGL((gemm_prep_kernel<EPI, BM_, BN_>), dim3(1), dim3(1024), 0, st, a.offsets, a.E, a.N, a.has_x,
@@ -328,9 +303,9 @@ static int run_gemm_t(GemmArgs a, int32_t *prefix, hipStream_t st) {
               (a.has_x ? max_tiles(a.Mx, 0, BM_, n_tiles<EPI, BN_>(a.Nx)) : 0);
   if (grid <= 0) return 0;
   // dynamic LDS up to the device's per-workgroup limit (160 KiB on gfx950)
-  constexpr size_t lds = (size_t)STAGES * (BM_ + BN_) * KS * 16 + (size_t)WGM * WGN * 256;
+  constexpr size_t lds = (size_t)STAGES * (BM_ + BN_) * KS * 16;
   static_assert(lds <= 160 * 1024, "LDS per workgroup");
-  hipLaunchKernelGGL((grouped_gemm_kernel<TE, EPI, BM_, BN_, WGM, WGN, KS, STAGES, PFA>), dim3(grid),
+  hipLaunchKernelGGL((grouped_gemm_kernel<TE, EPI, BM_, BN_, WGM, WGN, KS, STAGES>), dim3(grid),
                      dim3(64 * WGM * WGN), lds, st, a);
   if (hipGetLastError() != hipSuccess) return -4;
   return 0;
@@ -338,14 +313,17 @@ static int run_gemm_t(GemmArgs a, int32_t *prefix, hipStream_t st) {
 
 template <typename TE, int EPI>
 static int run_gemm(GemmArgs a, int tile, int32_t *prefix, hipStream_t st) {
-  if constexpr (sizeof(TE) == 4) return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 0>(a, prefix, st);
+  if constexpr (sizeof(TE) == 4) {
+    return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2>(a, prefix, st);
+  } else {
   switch (tile) {
-    case TILE_256x256_W8: return run_gemm_t<TE, EPI, 256, 256, 2, 4, 8, 2, 0>(a, prefix, st);
-    case TILE_256x128_W8: return run_gemm_t<TE, EPI, 256, 128, 4, 2, 8, 2, 0>(a, prefix, st);
-    case TILE_128x256_W8: return run_gemm_t<TE, EPI, 128, 256, 2, 4, 8, 2, 0>(a, prefix, st);
-    case TILE_128x128_W8: return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 0>(a, prefix, st);
-    case TILE_64x256_W4: return run_gemm_t<TE, EPI, 64, 256, 1, 4, 8, 2, 0>(a, prefix, st);
-    default: return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 0>(a, prefix, st);
+    case TILE_256x256_W8: return run_gemm_t<TE, EPI, 256, 256, 2, 4, 8, 2>(a, prefix, st);
+    case TILE_256x128_W8: return run_gemm_t<TE, EPI, 256, 128, 4, 2, 8, 2>(a, prefix, st);
+    case TILE_128x256_W8: return run_gemm_t<TE, EPI, 128, 256, 2, 4, 8, 2>(a, prefix, st);
+    case TILE_128x128_W8: return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2>(a, prefix, st);
+    case TILE_64x256_W4: return run_gemm_t<TE, EPI, 64, 256, 1, 4, 8, 2>(a, prefix, st);
+    default: return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2>(a, prefix, st);
+  }
   }
 }
 
