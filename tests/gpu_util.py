@@ -77,4 +77,9 @@ def routing_margin(cfg, l32):
             gap = np.minimum(gap, s[:, k - 1] - s[:, k])
         if k > 1:
             gap = np.minimum(gap, np.min(s[:, :k - 1] - s[:, 1:k], axis=1))
+        if cfg.n_groups:
+            g = np.sort(l32[:, h * Eh:(h + 1) * Eh].astype(np.float64).reshape(T, cfg.n_groups, -1).max(axis=2),
+                        axis=1)[:, ::-1]
+            if cfg.topk_groups < cfg.n_groups:
+                gap = np.minimum(gap, g[:, cfg.topk_groups - 1] - g[:, cfg.topk_groups])
     return gap
