@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: automatic)")
     ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many MiB (a known-size "
+                         "reference for the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -65,6 +68,22 @@ def algorithmic(cfg, R):
     out["ffn_flops"] = 2 * R * dh * m * cfg.d_ff + 2 * T * d * m * cfg.n_shared * cfg.d_ff
     out["proj_flops"] = (2 * 2 * T * d * H * dh) if cfg.latent_proj else 0
     return out
+
+
+def measured_traffic(cfg):
+    """HBM bytes per expert-FFN call measured with rocprofv3 for this workload, if the
+    grouped-GEMM source is unchanged since the measurement (else None)."""
+    import hashlib
+    f = os.path.join(ROOT, "profiles", f"traffic__grouped_gemm__{cfg.name}.json")
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        rec = json.load(fh)
+    src = os.path.join(ROOT, "routing_dispatch_expert_router_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as fh:
+        if hashlib.sha256(fh.read()).hexdigest() != rec.get("gemm_source_sha256"):
+            return None
+    return rec["traffic_bytes"]
 
 
 def cpu_threads():
@@ -184,6 +203,14 @@ def main():
     st["combine"] = timed(lambda: moe.moe_combine(cfg, io["y_perm"], io["row_of"], io["topk_w"],
                                                   x if (cfg.residual and not cfg.latent_proj) else None,
                                                   io["shared_out"], io["o"] if cfg.latent_proj else y))
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     alg = algorithmic(cfg, R)
     peak = PEAK_F32_TFLOPS if cfg.act_dtype == 0 else PEAK_BF16_TFLOPS
     ffn_tf = alg["ffn_flops"] / st["expert_ffn"] / 1e12
@@ -210,7 +237,8 @@ def main():
                    "drop": ["none", "capacity", "affinity"][cfg.drop], "parallelism": "single GPU"},
         "roofline": {"kernel": "grouped_gemm_kernel, expert FFN (SwiGLU gate/up launch + down launch)",
                      "bound": "mfma", "achieved": ffn_tf, "peak": peak, "unit": "TFLOP/s", "frac": ffn_tf / peak,
-                     "traffic": None},
+                     "traffic": measured_traffic(cfg), "traffic_unit": "bytes per call (2 launches)",
+                     "algorithmic_flops": alg["ffn_flops"]},
         "stages": stages,
         "device": dev_name,
     }

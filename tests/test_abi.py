@@ -1,0 +1,149 @@
+"""The C ABI without a GPU: the library loads, exports what include/moe.h declares,
+and its host-side helpers and argument checks behave as documented (every
+call here is rejected before anything would be launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import routing_dispatch_expert_router_amd as moe
+from moe_inputs import CONFIGS, SMALL, MoEConfig
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:[A-Za-z_][\w ]*[\s\*]+)(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_five_calls_and_helpers():
+    names = declared()
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_fwd",
+              "moe_workspace_bytes", "moe_rows_upper_bound", "moe_status_str", "moe_check_config"):
+        assert n in names
+    assert sorted(moe.SYMBOLS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    for n in declared():
+        assert n in exported, n
+        assert hasattr(moe._lib, n)
+    # no undefined library symbols (a failed kernel-template instantiation would show here)
+    und = subprocess.run(["nm", "-DC", "--undefined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
+    assert "moe::" not in und
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert moe.status_str(s).startswith("MOE_")
+    assert "unknown" in moe.status_str(7)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS + SMALL, ids=lambda c: c.name)
+def test_workloads_are_supported(cfg):
+    assert moe.moe_check_config(cfg) == moe.MOE_OK
+    assert moe.moe_workspace_bytes(cfg) > 0
+
+
+def test_rows_upper_bound_formula():
+    for cfg in CONFIGS:
+        tk = cfg.T * cfg.k_total
+        want = min(tk, cfg.n_experts * cfg.capacity) if cfg.drop == 1 else tk
+        assert moe.moe_rows_upper_bound(cfg) == want
+    assert moe.moe_rows_upper_bound(CONFIGS[0]) == 512
+
+
+def test_workspace_grows_with_tokens():
+    base = CONFIGS[2]
+    sizes = [moe.moe_workspace_bytes(base.with_(T=t, capacity=(t * 6 + 63) // 64)) for t in (64, 512, 4096, 8192)]
+    assert sizes == sorted(sizes) and sizes[0] < sizes[-1]
+
+
+def _bad(**kw):
+    return CONFIGS[2].with_(**kw)
+
+
+@pytest.mark.parametrize("cfg,status", [
+    (_bad(d_model=100, d_head=100), moe.MOE_ERR_ARG),           # not a multiple of 64
+    (_bad(top_k=0), moe.MOE_ERR_ARG),
+    (_bad(top_k=65), moe.MOE_ERR_ARG),                          # more than E_h
+    (_bad(top_k=9), moe.MOE_ERR_UNSUPPORTED),                   # kernel limit 8
+    (_bad(n_groups=3, topk_groups=1), moe.MOE_ERR_ARG),         # 64 % 3 != 0
+    (_bad(n_groups=8, topk_groups=1, top_k=9), moe.MOE_ERR_ARG),  # k > groups * group size
+    (_bad(drop=1, capacity=-1), moe.MOE_ERR_ARG),
+    (_bad(drop=2, keep_num=11, keep_den=10), moe.MOE_ERR_ARG),
+    (_bad(d_ff=100), moe.MOE_ERR_ARG),
+    (_bad(act=3), moe.MOE_ERR_ARG),
+    (_bad(act_dtype=0, router_dtype=1), moe.MOE_ERR_UNSUPPORTED),
+    (_bad(n_heads=2, d_head=1024, n_experts=64), moe.MOE_ERR_UNSUPPORTED),  # shared experts need H == 1
+    (_bad(n_experts=2048), moe.MOE_ERR_ARG),                    # top_k fine, E_h > 256 -> unsupported or arg
+    (_bad(T=-1), moe.MOE_ERR_ARG),
+])
+def test_invalid_configs_rejected(cfg, status):
+    got = moe.moe_check_config(cfg)
+    if cfg.n_experts == 2048:
+        assert got in (moe.MOE_ERR_ARG, moe.MOE_ERR_UNSUPPORTED)
+    else:
+        assert got == status
+    assert moe.moe_workspace_bytes(cfg) == 0
+    assert moe.moe_rows_upper_bound(cfg) == -1
+
+
+def test_calls_reject_bad_arguments_before_launching():
+    lib = moe._lib
+    c = moe.config_struct(CONFIGS[2])
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
+    # null config
+    assert lib.moe_route(None, fake, fake, None, None, 0, fake, fake, None, fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    # missing outputs
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 0, None, fake, None, fake, 1 << 40, None) \
+        == moe.MOE_ERR_ARG
+    # LOAD mode needs logits
+    assert lib.moe_route(ctypes.byref(c), None, None, None, None, 2, fake, fake, None, fake, 1 << 40, None) \
+        == moe.MOE_ERR_ARG
+    # bad mode
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 5, fake, fake, None, fake, 1 << 40, None) \
+        == moe.MOE_ERR_ARG
+    # workspace too small / misaligned
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 0, fake, fake, None, fake, 16, None) \
+        == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 0, fake, fake, None, ctypes.c_void_p(0x1001),
+                         1 << 40, None) == moe.MOE_ERR_WORKSPACE
+    # aux loss is defined for one head only
+    c4 = moe.config_struct(CONFIGS[4])
+    assert lib.moe_route(ctypes.byref(c4), fake, fake, None, None, 0, fake, fake, fake, fake, 1 << 40, None) \
+        == moe.MOE_ERR_UNSUPPORTED
+    # affinity keep needs the gates
+    c3 = moe.config_struct(CONFIGS[3])
+    assert lib.moe_dispatch(ctypes.byref(c3), fake, None, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 40,
+                            None) == moe.MOE_ERR_ARG
+    # SwiGLU needs w3; shared experts need their weights
+    assert lib.moe_expert_ffn(ctypes.byref(c), fake, fake, fake, None, fake, fake, fake, fake, fake, fake, fake,
+                              fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    assert lib.moe_expert_ffn(ctypes.byref(c), fake, fake, fake, fake, fake, fake, None, fake, fake, fake, fake,
+                              fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    # combine: missing outputs
+    assert lib.moe_combine(ctypes.byref(c), fake, fake, fake, None, None, None, None) == moe.MOE_ERR_ARG
+    # layer: y aliasing x, missing weights
+    w = moe.MoeWeights()
+    assert lib.moe_layer_fwd(ctypes.byref(c), ctypes.byref(w), fake, fake, None, fake, 1 << 40, None) \
+        == moe.MOE_ERR_ARG
+    assert lib.moe_layer_fwd(ctypes.byref(c), None, fake, ctypes.c_void_p(0x2000), None, fake, 1 << 40, None) \
+        == moe.MOE_ERR_ARG
+
+
+def test_config_struct_layout_matches_header():
+    # 20 int32 fields, in header order
+    assert ctypes.sizeof(moe.MoeConfig) == 20 * 4
+    src = open(HEADER).read()
+    body = src[src.index("typedef struct moe_config {"):src.index("} moe_config;")]
+    fields = re.findall(r"int32_t\s+([^;]+);", body)
+    names = [n.strip() for f in fields for n in f.split(",")]
+    assert names == moe.CONFIG_FIELDS
