@@ -36,7 +36,20 @@ struct GemmArgs {
   const void *res; long ldres;                // EPI_RESID: added to the extra group's output
   const int32_t *prefix;                      // [G+1] tile prefix
   int G;
+  int split;  // 0: all rows of a group; 1: rows [0, cut); 2: rows [cut, M) (see row_window)
 };
+
+// Rows of a group a launch covers.  With split launches, a group's rows are
+// cut where the last 256-row tile would hold at most 128 rows: the head goes
+// to 256-row tiles, the short tail to 128-row tiles in a second launch.
+constexpr int SPLIT_BM = 256;
+__host__ __device__ inline void row_window(int split, int M, int *beg, int *len) {
+  const int rem = M % SPLIT_BM;
+  const int cut = (rem == 0 || rem > SPLIT_BM / 2) ? M : M - rem;
+  if (split == 1) { *beg = 0; *len = cut; }
+  else if (split == 2) { *beg = cut; *len = M - cut; }
+  else { *beg = 0; *len = M; }
+}
 
 template <int EPI, int BN_> __host__ __device__ inline int n_tiles(int N) {
   return EPI == EPI_SWIGLU ? (N + BN_ / 2 - 1) / (BN_ / 2) : (N + BN_ - 1) / BN_;
@@ -45,7 +58,8 @@ template <int EPI, int BN_> __host__ __device__ inline int n_tiles(int N) {
 // tile prefix over groups: tiles_g = ceil(M_g / BM) * n_tiles(N_g)
 template <int EPI, int BM_, int BN_>
 __global__ __launch_bounds__(1024) void gemm_prep_kernel(const int32_t *__restrict__ offsets, int E, int N,
-                                                         int has_x, int Mx, int Nx, int32_t *__restrict__ prefix) {
+                                                         int has_x, int Mx, int Nx, int split,
+                                                         int32_t *__restrict__ prefix) {
   __shared__ int s[1024];
   const int G = E + has_x;
   const int tid = threadIdx.x;
@@ -57,6 +71,8 @@ __global__ __launch_bounds__(1024) void gemm_prep_kernel(const int32_t *__restri
     int v = 0;
     if (g < G) {
       int M = (g < E) ? offsets[g + 1] - offsets[g] : Mx;
+      int beg;
+      row_window(split, M, &beg, &M);
       int nn = (g < E) ? N : Nx;
       v = (M + BM_ - 1) / BM_ * n_tiles<EPI, BN_>(nn);
     }
@@ -95,7 +111,7 @@ __device__ __forceinline__ int swz(int row, int q) {
   else return q ^ (((row >> 1) ^ (row >> 3)) & 3);
 }
 
-template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES>
+template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES, bool SG>
 __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int NT = 64 * WGM * WGN;    // threads
   constexpr int EPC = 16 / sizeof(TE);  // elements per 16-byte slot
@@ -129,19 +145,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   TE *C;
   long lda, ldb, ldc;
   int M, N, K;
+  int r0;
   if (g < p.E) {
-    const int r0 = p.offsets[g];
+    r0 = p.offsets[g];
     M = p.offsets[g + 1] - r0;
     lda = p.lda; ldb = p.ldb; ldc = p.ldc; N = p.N; K = p.K;
-    A = (const TE *)p.A + (size_t)r0 * lda;
+    A = (const TE *)p.A;
     B = (const TE *)p.B + (size_t)g * p.bstride;
     B2 = p.B2 ? (const TE *)p.B2 + (size_t)g * p.bstride : nullptr;
-    C = (TE *)p.C + (size_t)r0 * ldc;
+    C = (TE *)p.C;
   } else {
+    r0 = 0;
     M = p.Mx; N = p.Nx; K = p.Kx;
     lda = p.ldax; ldb = p.ldbx; ldc = p.ldcx;
     A = (const TE *)p.Ax; B = (const TE *)p.Bx; B2 = (const TE *)p.Bx2; C = (TE *)p.Cx;
   }
+  int wbeg;
+  row_window(p.split, M, &wbeg, &M);
+  r0 += wbeg;
+  A += (size_t)r0 * lda;
+  C += (size_t)r0 * ldc;
   // grouped raster inside the group: bands of GM m-tiles, n outer, m inner
   const int mt = (M + BM_ - 1) / BM_, nt = n_tiles<EPI, BN_>(N);
   constexpr int GM = 8;
@@ -232,23 +255,40 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   if (nk > 1) wait_vmcnt<LA + LB>(); else wait_vmcnt0();
   __syncthreads();
   read(0, 0, fa0, fb0);
+  // scheduling hint (SG): interleave the LDS reads of the next k-step with the
+  // MFMAs of the current one
+  auto interleave = [&]() {
+    if constexpr (SG) {
+      constexpr int NR = MF + NF, NM = MF * NF;
+      constexpr int PER = NM / NR > 0 ? NM / NR : 1;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // then PER MFMAs
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    }
+  };
   for (int kc = 0; kc < nk; ++kc) {
     const int st = kc & 1;
     read(st, 1, fa1, fb1);
     mfma(fa0, fb0);
+    interleave();
     if (kc + 1 < nk) {
       // chunk kc+1 landed for this wave; this wave's reads of stage st are done
       wait_vmcnt0();
       wait_lgkmcnt0();
       __syncthreads();
       if (kc + 2 < nk) issue(kc + 2, st);
-      read(st ^ 1, 0, fa0, fb0);
     }
+    // on the last chunk this reads stage data that is never used
+    read(st ^ 1, 0, fa0, fb0);
     mfma(fa1, fb1);
+    interleave();
   }
 
   // epilogue: acc[i][f][v] = C[wm*WM + i*16 + 4*cq + v][n-fragment f, column l16]
-  const TE *R = (EPI == EPI_RESID) ? (const TE *)p.res : nullptr;
+  const TE *R = (EPI == EPI_RESID) ? (const TE *)p.res + (size_t)r0 * p.ldres : nullptr;
 #pragma unroll
   for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -287,37 +327,63 @@ enum TileCfg {
   TILE_128x256_W8 = 3,  // 8 waves (2 x 4), wave tile 64 x 64
   TILE_128x128_W8 = 4,  // 8 waves (2 x 4), wave tile 64 x 32
   TILE_64x256_W4 = 5,   // 4 waves (1 x 4), wave tile 64 x 64
+  TILE_256x256_W8_SG = 6,  // as 1, LDS reads interleaved with MFMAs by scheduling hints
+  TILE_128x128_W8_SG = 7,  // as 4, same
 };
 
 static long max_tiles(long rows_bound, int groups, int bm, int ntiles) {
   return ((rows_bound + bm - 1) / bm + groups) * ntiles;
 }
 
-template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES>
+template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES, bool SG = false>
 static int run_gemm_t(GemmArgs a, int32_t *prefix, hipStream_t st) {
   a.prefix = prefix;
   hipLaunchKernelGGL((gemm_prep_kernel<EPI, BM_, BN_>), dim3(1), dim3(1024), 0, st, a.offsets, a.E, a.N, a.has_x,
-                     a.Mx, a.Nx, prefix);
+                     a.Mx, a.Nx, a.split, prefix);
   if (hipGetLastError() != hipSuccess) return -4;
-  long grid = (a.E ? max_tiles(a.Mr_bound, a.E, BM_, n_tiles<EPI, BN_>(a.N)) : 0) +
-              (a.has_x ? max_tiles(a.Mx, 0, BM_, n_tiles<EPI, BN_>(a.Nx)) : 0);
+  // tail launches hold at most one tile row per group
+  long grid;
+  if (a.split == 2)
+    grid = (long)a.E * n_tiles<EPI, BN_>(a.N) + (a.has_x ? n_tiles<EPI, BN_>(a.Nx) : 0);
+  else
+    grid = (a.E ? max_tiles(a.Mr_bound, a.E, BM_, n_tiles<EPI, BN_>(a.N)) : 0) +
+           (a.has_x ? max_tiles(a.Mx, 0, BM_, n_tiles<EPI, BN_>(a.Nx)) : 0);
   if (grid <= 0) return 0;
   // dynamic LDS up to the device's per-workgroup limit (160 KiB on gfx950)
   constexpr size_t lds = (size_t)STAGES * (BM_ + BN_) * KS * 16;
   static_assert(lds <= 160 * 1024, "LDS per workgroup");
-  hipLaunchKernelGGL((grouped_gemm_kernel<TE, EPI, BM_, BN_, WGM, WGN, KS, STAGES>), dim3(grid),
+  hipLaunchKernelGGL((grouped_gemm_kernel<TE, EPI, BM_, BN_, WGM, WGN, KS, STAGES, SG>), dim3(grid),
                      dim3(64 * WGM * WGN), lds, st, a);
   if (hipGetLastError() != hipSuccess) return -4;
   return 0;
 }
 
 template <typename TE, int EPI>
+static int run_gemm_one(GemmArgs a, int tile, int32_t *prefix, hipStream_t st);
+
+// 256-row tiles run as a head launch plus a tail launch of 128-row tiles
+template <typename TE, int EPI>
 static int run_gemm(GemmArgs a, int tile, int32_t *prefix, hipStream_t st) {
+  if (tile == TILE_256x256_W8_SG) {
+    GemmArgs h = a, t = a;
+    h.split = 1;
+    t.split = 2;
+    int rc = run_gemm_one<TE, EPI>(h, TILE_256x256_W8_SG, prefix, st);
+    if (rc) return rc;
+    return run_gemm_one<TE, EPI>(t, TILE_128x128_W8_SG, prefix + (a.E + 2), st);
+  }
+  return run_gemm_one<TE, EPI>(a, tile, prefix, st);
+}
+
+template <typename TE, int EPI>
+static int run_gemm_one(GemmArgs a, int tile, int32_t *prefix, hipStream_t st) {
   if constexpr (sizeof(TE) == 4) {
     return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2>(a, prefix, st);
   } else {
   switch (tile) {
     case TILE_256x256_W8: return run_gemm_t<TE, EPI, 256, 256, 2, 4, 8, 2>(a, prefix, st);
+    case TILE_256x256_W8_SG: return run_gemm_t<TE, EPI, 256, 256, 2, 4, 8, 2, true>(a, prefix, st);
+    case TILE_128x128_W8_SG: return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, true>(a, prefix, st);
     case TILE_256x128_W8: return run_gemm_t<TE, EPI, 256, 128, 4, 2, 8, 2>(a, prefix, st);
     case TILE_128x256_W8: return run_gemm_t<TE, EPI, 128, 256, 2, 4, 8, 2>(a, prefix, st);
     case TILE_128x128_W8: return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2>(a, prefix, st);
@@ -330,14 +396,14 @@ static int run_gemm(GemmArgs a, int tile, int32_t *prefix, hipStream_t st) {
 // tile shape for a launch: large tiles when the groups are tall enough to fill them
 static int pick_tile(long rows, int groups) {
   long avg = groups > 0 ? rows / groups : rows;
-  return avg >= 1024 ? TILE_256x256_W8 : TILE_128x128_W8;
+  return avg >= 1024 ? TILE_256x256_W8_SG : TILE_128x128_W8_SG;
 }
 
 size_t ffn_ws_bytes(const Shape &s) {
   const int esz = s.act_f32 ? 4 : 2;
   size_t b = align_up((size_t)s.R_max * s.dff * esz, 256);                       // hidden H
   if (s.n_shared) b += align_up((size_t)s.T * s.n_shared * s.dff * esz, 256);    // shared hidden
-  b += 2 * align_up((size_t)(s.E + 2) * 4, 256);                                  // tile prefixes
+  b += 2 * align_up((size_t)2 * (s.E + 2) * 4, 256);                              // tile prefixes
   return b;
 }
 
@@ -355,8 +421,8 @@ static int ffn_typed(const Shape &s, const void *x_perm, const int32_t *offsets,
     Hs = (TE *)p;
     p += align_up((size_t)s.T * fs * esz, 256);
   }
-  int32_t *pre1 = (int32_t *)p;
-  p += align_up((size_t)(s.E + 2) * 4, 256);
+  int32_t *pre1 = (int32_t *)p;  // [2][E+2]: head and tail launches
+  p += align_up((size_t)2 * (s.E + 2) * 4, 256);
   int32_t *pre2 = (int32_t *)p;
   const bool glu = s.act == 1;
   const int has_x = s.n_shared ? 1 : 0;
@@ -400,7 +466,7 @@ int launch_expert_ffn(const Shape &s, const void *x_perm, const int32_t *offsets
   return ffn_typed<uint16_t>(s, x_perm, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws, st);
 }
 
-size_t dense_ws_bytes() { return 256; }
+size_t dense_ws_bytes() { return 256; }  // two tile prefixes of 3 ints
 
 int launch_dense(bool f32, const void *A, const void *B, void *C, const void *residual, int M, int N, int K,
                  void *ws, hipStream_t st) {
