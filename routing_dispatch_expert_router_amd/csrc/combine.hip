@@ -13,69 +13,98 @@
 
 namespace moe {
 
-template <typename TA>
+// One thread per 16 bytes of an output row (grid-stride over T x chunks).  KH
+// (>= the choices per head) is a compile-time bound so every expert-row load
+// of the token is issued before the first add.
+template <typename TA, int KH>
 __global__ __launch_bounds__(256) void combine_kernel(
     const TA *__restrict__ y_perm, const int32_t *__restrict__ row_of, const float *__restrict__ topk_w,
     const TA *__restrict__ res, const TA *__restrict__ sh, TA *__restrict__ y, int T, int H, int k, int dh,
-    int tokens_per_block, long r_max) {
+    long r_max) {
   constexpr int EPC = 16 / sizeof(TA);
   const int width = H * dh;
   const int cpr = width / EPC;  // 16-byte chunks per row
-  const long t0 = (long)blockIdx.x * tokens_per_block;
-  const int nt = (int)min((long)tokens_per_block, (long)T - t0);
   const int K = H * k;
-  for (int i = threadIdx.x; i < nt * cpr; i += 256) {
-    const int tt = i / cpr, q = i - tt * cpr;
-    const long t = t0 + tt;
+  const long total = (long)T * cpr;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const long t = i / cpr;
+    const int q = (int)(i - t * cpr);
     const int c0 = q * EPC;
     const int h = c0 / dh;
+    int row[KH];
+    float w[KH];
+#pragma unroll
+    for (int j = 0; j < KH; ++j) {
+      row[j] = -1;
+      w[j] = 0.f;
+      if (j < k) {
+        const int r = row_of[t * K + h * k + j];
+        row[j] = (r >= 0 && r < r_max) ? r : -1;
+        w[j] = topk_w[t * K + h * k + j];
+      }
+    }
+    u32x4 v[KH];
+#pragma unroll
+    for (int j = 0; j < KH; ++j)
+      v[j] = row[j] >= 0 ? reinterpret_cast<const u32x4 *>(y_perm + (size_t)row[j] * dh + (c0 - h * dh))[0]
+                         : u32x4{0u, 0u, 0u, 0u};
+    u32x4 rv = res ? reinterpret_cast<const u32x4 *>(res + (size_t)t * width)[q] : u32x4{0u, 0u, 0u, 0u};
+    u32x4 sv = sh ? reinterpret_cast<const u32x4 *>(sh + (size_t)t * width)[q] : u32x4{0u, 0u, 0u, 0u};
     float acc[EPC];
 #pragma unroll
-    for (int v = 0; v < EPC; ++v) acc[v] = 0.f;
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+    // fixed order: residual, shared, then the head's choices j ascending
     if (res) {
-      u32x4 r = reinterpret_cast<const u32x4 *>(res + (size_t)t * width)[q];
-      const TA *rv = reinterpret_cast<const TA *>(&r);
+      const TA *p = reinterpret_cast<const TA *>(&rv);
 #pragma unroll
-      for (int v = 0; v < EPC; ++v) acc[v] += Elem<TA>::to_f32(rv[v]);
+      for (int e = 0; e < EPC; ++e) acc[e] += Elem<TA>::to_f32(p[e]);
     }
     if (sh) {
-      u32x4 r = reinterpret_cast<const u32x4 *>(sh + (size_t)t * width)[q];
-      const TA *rv = reinterpret_cast<const TA *>(&r);
+      const TA *p = reinterpret_cast<const TA *>(&sv);
 #pragma unroll
-      for (int v = 0; v < EPC; ++v) acc[v] += Elem<TA>::to_f32(rv[v]);
+      for (int e = 0; e < EPC; ++e) acc[e] += Elem<TA>::to_f32(p[e]);
     }
-    for (int j = h * k; j < (h + 1) * k; ++j) {
-      const int row = row_of[t * K + j];
-      if (row < 0 || row >= r_max) continue;
-      const float w = topk_w[t * K + j];
-      u32x4 r = reinterpret_cast<const u32x4 *>(y_perm + (size_t)row * dh + (c0 - h * dh))[0];
-      const TA *rv = reinterpret_cast<const TA *>(&r);
 #pragma unroll
-      for (int v = 0; v < EPC; ++v) acc[v] += w * Elem<TA>::to_f32(rv[v]);
+    for (int j = 0; j < KH; ++j) {
+      if (row[j] < 0) continue;
+      const TA *p = reinterpret_cast<const TA *>(&v[j]);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += w[j] * Elem<TA>::to_f32(p[e]);
     }
     u32x4 o;
     TA *ov = reinterpret_cast<TA *>(&o);
 #pragma unroll
-    for (int v = 0; v < EPC; ++v) ov[v] = Elem<TA>::from_f32(acc[v]);
+    for (int e = 0; e < EPC; ++e) ov[e] = Elem<TA>::from_f32(acc[e]);
     reinterpret_cast<u32x4 *>(y + (size_t)t * width)[q] = o;
   }
 }
 
+template <typename TA, int KH>
+static void launch_c(const Shape &s, const void *y_perm, const int32_t *row_of, const float *topk_w,
+                     const void *residual, const void *shared_out, void *y, hipStream_t st) {
+  const long total = (long)s.T * (s.H * s.dh * (long)sizeof(TA) / 16);
+  long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL((combine_kernel<TA, KH>), dim3(blocks), dim3(256), 0, st, (const TA *)y_perm, row_of, topk_w,
+                     (const TA *)residual, (const TA *)shared_out, (TA *)y, s.T, s.H, s.k, s.dh, s.R_max);
+}
+
+template <typename TA>
+static void launch_typed(const Shape &s, const void *y_perm, const int32_t *row_of, const float *topk_w,
+                         const void *residual, const void *shared_out, void *y, hipStream_t st) {
+  if (s.k <= 1) launch_c<TA, 1>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
+  else if (s.k <= 2) launch_c<TA, 2>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
+  else if (s.k <= 4) launch_c<TA, 4>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
+  else launch_c<TA, 8>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
+}
+
 int launch_combine(const Shape &s, const void *y_perm, const int32_t *row_of, const float *topk_w,
                    const void *residual, const void *shared_out, void *y, hipStream_t st) {
-  const int esz = s.act_f32 ? 4 : 2;
-  const long row_bytes = (long)s.H * s.dh * esz;
-  long tpb_ = 32768 / row_bytes;
-  const int tpb = tpb_ < 1 ? 1 : (int)tpb_;
-  const long blocks = ((long)s.T + tpb - 1) / tpb;
-  if (blocks == 0) return 0;
+  if (s.T == 0) return 0;
   if (s.act_f32)
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float *)y_perm, row_of, topk_w,
-                       (const float *)residual, (const float *)shared_out, (float *)y, s.T, s.H, s.k, s.dh, tpb, s.R_max);
+    launch_typed<float>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
   else
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st, (const uint16_t *)y_perm, row_of,
-                       topk_w, (const uint16_t *)residual, (const uint16_t *)shared_out, (uint16_t *)y, s.T, s.H,
-                       s.k, s.dh, tpb, s.R_max);
+    launch_typed<uint16_t>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

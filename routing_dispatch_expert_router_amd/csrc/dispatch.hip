@@ -8,15 +8,17 @@
 //
 // Pipeline (flat assignment a = t*K + j, chunks of CH consecutive a):
 //   hist      per-chunk expert histogram (LDS integer atomics: order-free)
-//   scan      per-expert prefix over chunks -> chunk bases; demand; keep rule
-//             -> counts; offsets = exclusive scan of counts
-//   rank      stable rank of every a among the earlier a of its expert, from
-//             the chunk base + per-wave prefix + in-wave ballot match; writes
-//             row_of / src_of (NONE, CAPACITY) or the expert-sorted segment
-//             list (AFFINITY)
+//   rank      each chunk's block sums the earlier chunks' histograms (its base
+//             per expert), applies the keep rule to the demand and scans the
+//             kept counts into offsets (block 0 writes demand, counts,
+//             offsets); then the stable rank of every a among the earlier a of
+//             its expert = chunk base + per-wave prefix + in-wave ballot
+//             match; writes row_of / src_of (NONE, CAPACITY) or the
+//             expert-sorted segment list (AFFINITY)
 //   affinity  one block per expert: radix select of the keep-th largest gate,
 //             then two ordered scans -> row_of / src_of
-//   scatter   row r <- x[src_of[r] / K] (head slice), 16-byte copies
+//   scatter   token-major copy: each 16 bytes of x are read once and stored
+//             to every kept row of their token (head slice)
 // Every count is an integer and every order is fixed by a, so the result is
 // bit-reproducible.
 #include "common.h"
@@ -24,7 +26,7 @@
 
 namespace moe {
 
-constexpr int CH = 4096;  // assignments per chunk (256 threads x 16)
+constexpr int CH = 1024;  // assignments per chunk (256 threads x 4)
 
 __global__ __launch_bounds__(256) void disp_hist_kernel(const int32_t *__restrict__ idx, long n, int E,
                                                         int32_t *__restrict__ hist) {
@@ -40,50 +42,36 @@ __global__ __launch_bounds__(256) void disp_hist_kernel(const int32_t *__restric
   for (int e = threadIdx.x; e < E; e += 256) hist[(long)blockIdx.x * E + e] = h[e];
 }
 
-// one block of 1024 threads; E <= 1024
-__global__ __launch_bounds__(1024) void disp_scan_kernel(
-    int32_t *__restrict__ hist /* in: counts, out: chunk bases */, int nchunks, int E, int drop, int C,
-    int keep_num, int keep_den, int32_t *__restrict__ demand, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ all_off) {
-  __shared__ int32_t sc[1024];
-  __shared__ int32_t sd[1024];
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      int v = hist[(long)c * E + e];
-      hist[(long)c * E + e] = run;
-      run += v;
-    }
+// exclusive scan of v[0..E) by a 256-thread block (E <= 1024, 4 per thread),
+// in integers and a fixed order; returns the total
+__device__ int block_scan_experts(const int *v, int *out, int E, int *tmp) {
+  const int tid = threadIdx.x;
+  int loc[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    loc[i] = e < E ? v[e] : 0;
+    sum += loc[i];
   }
-  int cnt = 0;
-  if (e < E) {
-    if (drop == 0) cnt = run;
-    else if (drop == 1) cnt = min(run, C);
-    else cnt = (int)(((long)keep_num * run + keep_den - 1) / keep_den);
-    demand[e] = run;
-    counts[e] = cnt;
-  }
-  sc[e] = (e < E) ? cnt : 0;
-  sd[e] = (e < E) ? run : 0;
+  tmp[tid] = sum;
   __syncthreads();
-  // Hillis-Steele inclusive scans (integers: exact)
-  for (int o = 1; o < 1024; o <<= 1) {
-    int v1 = (e >= o) ? sc[e - o] : 0;
-    int v2 = (e >= o) ? sd[e - o] : 0;
+  for (int o = 1; o < 256; o <<= 1) {
+    int u = tid >= o ? tmp[tid - o] : 0;
     __syncthreads();
-    sc[e] += v1;
-    sd[e] += v2;
+    tmp[tid] += u;
     __syncthreads();
   }
-  if (e < E) {
-    offsets[e] = sc[e] - cnt;
-    if (all_off) all_off[e] = sd[e] - run;
+  int run = tmp[tid] - sum;
+  const int total = tmp[255];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < E) out[e] = run;
+    run += loc[i];
   }
-  if (e == 0) {
-    offsets[E] = sc[1023];
-    if (all_off) all_off[E] = sd[1023];
-  }
+  __syncthreads();
+  return total;
 }
 
 // lanes of this wave holding the same expert id (E <= 1024 -> 10 bits)
@@ -97,15 +85,53 @@ __device__ __forceinline__ uint64_t match_mask(int e, bool active) {
   return active ? m : 0ull;
 }
 
-// block 256 = 4 waves per chunk; wave w owns a in [a0 + w*CH/4, a0 + (w+1)*CH/4)
+// One block (4 waves) per chunk; wave w owns a in [a0 + w*CH/4, a0 + (w+1)*CH/4).
 __global__ __launch_bounds__(256) void disp_rank_kernel(
-    const int32_t *__restrict__ idx, long n, int E, const int32_t *__restrict__ base,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ all_off, int drop, int C,
-    int32_t *__restrict__ row_of, int32_t *__restrict__ src_of, int32_t *__restrict__ seg) {
-  extern __shared__ int32_t cnt[];  // [4][E]: per-wave counts, then running counters
+    const int32_t *__restrict__ idx, long n, int E, int nchunks, const int32_t *__restrict__ hist, int drop,
+    int C, int keep_num, int keep_den, int32_t *__restrict__ demand, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ all_off_out, int32_t *__restrict__ row_of,
+    int32_t *__restrict__ src_of, int32_t *__restrict__ seg) {
+  extern __shared__ int32_t sm[];
+  int32_t *cnt = sm;            // [4][E] per-wave counts, then running ranks
+  int32_t *base = sm + 4 * E;   // [E] this chunk's base per expert
+  int32_t *dem = base + E;      // [E] demand
+  int32_t *kept = dem + E;      // [E] kept counts
+  int32_t *off = kept + E;      // [E] first row of each expert
+  int32_t *aoff = off + E;      // [E] first slot of each expert in the affinity segments
+  __shared__ int tmp[256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = blockIdx.x;
+  for (int e = tid; e < E; e += 256) {
+    int b = 0, tot = 0;
+#pragma unroll 8
+    for (int q = 0; q < nchunks; ++q) {
+      const int v = hist[(long)q * E + e];
+      b += q < c ? v : 0;
+      tot += v;
+    }
+    base[e] = b;
+    dem[e] = tot;
+    kept[e] = drop == 0 ? tot
+              : drop == 1 ? min(tot, C)
+                          : (int)(((long)keep_num * tot + keep_den - 1) / keep_den);
+  }
+  __syncthreads();
+  const int R = block_scan_experts(kept, off, E, tmp);
+  if (drop == 2) block_scan_experts(dem, aoff, E, tmp);
+  if (c == 0) {
+    for (int e = tid; e < E; e += 256) {
+      demand[e] = dem[e];
+      counts[e] = kept[e];
+      offsets[e] = off[e];
+      if (drop == 2) all_off_out[e] = aoff[e];
+    }
+    if (tid == 0) {
+      offsets[E] = R;
+      if (drop == 2) all_off_out[E] = (int)n;
+    }
+  }
   constexpr int SUB = CH / 4;
-  const long a0 = (long)blockIdx.x * CH + (long)w * SUB;
+  const long a0 = (long)c * CH + (long)w * SUB;
   for (int i = tid; i < 4 * E; i += 256) cnt[i] = 0;
   __syncthreads();
   for (int i = lane; i < SUB; i += 64) {
@@ -113,9 +139,9 @@ __global__ __launch_bounds__(256) void disp_rank_kernel(
     if (a < n) atomicAdd(&cnt[w * E + idx[a]], 1);
   }
   __syncthreads();
-  // exclusive prefix over waves, plus the chunk base
+  // exclusive prefix over the block's waves, plus the chunk base
   for (int e = tid; e < E; e += 256) {
-    int run = base[(long)blockIdx.x * E + e];
+    int run = base[e];
     for (int q = 0; q < 4; ++q) {
       int v = cnt[q * E + e];
       cnt[q * E + e] = run;
@@ -137,12 +163,12 @@ __global__ __launch_bounds__(256) void disp_rank_kernel(
     if (leader) cnt[w * E + e] = rank + 1;
     if (act) {
       if (drop == 2) {
-        seg[all_off[e] + rank] = (int32_t)a;
+        seg[aoff[e] + rank] = (int32_t)a;
       } else {
-        bool kept = (drop == 0) || rank < C;
-        int row = kept ? offsets[e] + rank : -1;
+        bool kp = (drop == 0) || rank < C;
+        int row = kp ? off[e] + rank : -1;
         row_of[a] = row;
-        if (kept) src_of[row] = (int32_t)a;
+        if (kp) src_of[row] = (int32_t)a;
       }
     }
   }
@@ -166,10 +192,18 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
   return incl - v;
 }
 
+// One block per expert.  The expert's gate keys (up to AFF_LDS of them) are
+// staged in LDS; a 4-pass radix select (8 bits per pass, digit found by a
+// suffix scan over the 256 bins) gives the keep-th largest key; two ordered
+// scans then pick the kept assignments and their rows.
+constexpr int AFF_LDS = 2048;
+
 __global__ __launch_bounds__(256) void disp_affinity_kernel(
     const int32_t *__restrict__ seg, const int32_t *__restrict__ all_off, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, const float *__restrict__ topk_w, int32_t *__restrict__ row_of,
     int32_t *__restrict__ src_of) {
+  __shared__ uint32_t skey[AFF_LDS];
+  __shared__ int sa[AFF_LDS];
   __shared__ int hist[256];
   __shared__ int tmp[256];
   __shared__ uint32_t s_prefix;
@@ -179,27 +213,36 @@ __global__ __launch_bounds__(256) void disp_affinity_kernel(
   const int keep = counts[e];
   const int out0 = offsets[e];
   if (n == 0) return;
-  // threshold key: the keep-th largest gate bit pattern (gates are >= 0, so
-  // their float bits order like the values)
+  const bool staged = n <= AFF_LDS;
+  if (staged) {
+    for (int i = tid; i < n; i += 256) {
+      const int a = seg[beg + i];
+      sa[i] = a;
+      skey[i] = __float_as_uint(topk_w[a]);  // gates are >= 0: their bits order like the values
+    }
+    __syncthreads();
+  }
+  auto key_of = [&](int i) -> uint32_t { return staged ? skey[i] : __float_as_uint(topk_w[seg[beg + i]]); };
+  auto a_of = [&](int i) -> int { return staged ? sa[i] : seg[beg + i]; };
   uint32_t prefix = 0, pmask = 0;
-  int need = keep;  // how many still to take from keys matching prefix
+  int need = keep;  // how many keys still to take among those matching prefix
   if (keep < n) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       hist[tid] = 0;
       __syncthreads();
       for (int i = tid; i < n; i += 256) {
-        uint32_t key = __float_as_uint(topk_w[seg[beg + i]]);
+        const uint32_t key = key_of(i);
         if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
       }
       __syncthreads();
-      if (tid == 0) {
-        int acc = 0, d = 255;
-        for (; d > 0; --d) {
-          if (acc + hist[d] >= need) break;
-          acc += hist[d];
-        }
+      // thread t looks at digit d = 255 - t; `above` = keys with a larger digit
+      const int d = 255 - tid;
+      const int v = hist[d];
+      int tot;
+      const int above = block_excl_scan(v, tmp, &tot);
+      if (above < need && above + v >= need) {
         s_prefix = prefix | ((uint32_t)d << shift);
-        s_need = need - acc;
+        s_need = need - above;
       }
       __syncthreads();
       prefix = s_prefix;
@@ -211,25 +254,25 @@ __global__ __launch_bounds__(256) void disp_affinity_kernel(
   // kept iff key > thr, or key == thr and among the first `need` equal keys (by a)
   int eq_seen = 0, kept_seen = 0;
   for (int i0 = 0; i0 < n; i0 += 256) {
-    int i = i0 + tid;
-    bool act = i < n;
-    int a = act ? seg[beg + i] : 0;
-    uint32_t key = act ? __float_as_uint(topk_w[a]) : 0u;
+    const int i = i0 + tid;
+    const bool act = i < n;
+    const int a = act ? a_of(i) : 0;
+    const uint32_t key = act ? key_of(i) : 0u;
     bool kept;
     int tot;
     if (keep >= n) {
       kept = act;
     } else {
-      bool eq = act && key == prefix;
-      int eq_before = block_excl_scan(eq ? 1 : 0, tmp, &tot);
+      const bool eq = act && key == prefix;
+      const int eq_before = block_excl_scan(eq ? 1 : 0, tmp, &tot);
       kept = act && (key > prefix || (eq && eq_seen + eq_before < need));
       eq_seen += tot;
     }
-    int kb = block_excl_scan(kept ? 1 : 0, tmp, &tot);
+    const int kb = block_excl_scan(kept ? 1 : 0, tmp, &tot);
     if (act) {
       // never past this expert's `keep` rows, even if the selection were off
       kept = kept && (kept_seen + kb < keep);
-      int row = kept ? out0 + kept_seen + kb : -1;
+      const int row = kept ? out0 + kept_seen + kb : -1;
       row_of[a] = row;
       if (kept) src_of[row] = a;
     }
@@ -237,28 +280,31 @@ __global__ __launch_bounds__(256) void disp_affinity_kernel(
   }
 }
 
-// ---------------------------------------------------------------- row gather
-template <typename TA>
+// ---------------------------------------------------------------- row copy (token-major)
+// One thread per 16 bytes of a token's row (grid-stride): read once, stored to
+// every kept row of the token's head.
+template <typename TA, int KH>
 __global__ __launch_bounds__(256) void disp_scatter_kernel(
-    const TA *__restrict__ x, const int32_t *__restrict__ src_of, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ offsets, TA *__restrict__ x_perm, int E, int K, int Eh, int dh, int ldx,
-    int rows_per_block, long n_assign) {
-  const int R = offsets[E];
-  const long r0 = (long)blockIdx.x * rows_per_block;
-  if (r0 >= R) return;
-  const int nrows = (int)min((long)rows_per_block, (long)R - r0);
-  const int cpr = dh * (int)sizeof(TA) / 16;  // 16-byte chunks per row
-  const int total = nrows * cpr;
-  for (int i = threadIdx.x; i < total; i += 256) {
-    int rr = i / cpr, q = i - rr * cpr;
-    long r = r0 + rr;
-    int a = src_of[r];
-    if (a < 0 || a >= n_assign) continue;  // defensive: rows are always written
-    int t = a / K;
-    int h = idx[a] / Eh;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t)t * ldx + (size_t)h * dh);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(x_perm + (size_t)r * dh);
-    dst[q] = src[q];
+    const TA *__restrict__ x, const int32_t *__restrict__ row_of, TA *__restrict__ x_perm, int T, int H, int k,
+    int dh, long r_max) {
+  constexpr int EPC = 16 / sizeof(TA);
+  const int width = H * dh;
+  const int cpr = width / EPC;
+  const int K = H * k;
+  const long total = (long)T * cpr;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const long t = i / cpr;
+    const int q = (int)(i - t * cpr);
+    const int c0 = q * EPC;
+    const int h = c0 / dh;
+    int row[KH];
+#pragma unroll
+    for (int j = 0; j < KH; ++j) row[j] = j < k ? row_of[t * K + h * k + j] : -1;
+    const u32x4 v = reinterpret_cast<const u32x4 *>(x + (size_t)t * width)[q];
+#pragma unroll
+    for (int j = 0; j < KH; ++j)
+      if (row[j] >= 0 && row[j] < r_max)
+        reinterpret_cast<u32x4 *>(x_perm + (size_t)row[j] * dh + (c0 - h * dh))[0] = v;
   }
 }
 
@@ -266,10 +312,25 @@ __global__ __launch_bounds__(256) void disp_scatter_kernel(
 static long n_chunks(const Shape &s) { return ((long)s.T * s.K + CH - 1) / CH; }
 
 size_t dispatch_ws_bytes(const Shape &s) {
-  size_t b = align_up((size_t)n_chunks(s) * s.E * 4, 256);  // chunk hist / bases
+  size_t b = align_up((size_t)n_chunks(s) * s.E * 4, 256);  // chunk histograms
   b += align_up((size_t)(s.E + 1) * 4, 256);                  // all_off
   if (s.drop == 2) b += align_up((size_t)s.T * s.K * 4, 256);  // expert-sorted segments
   return b;
+}
+
+template <typename TA>
+static void launch_scatter(const Shape &s, const void *x, const int32_t *row_of, void *x_perm, hipStream_t st) {
+  const long total = (long)s.T * (s.H * s.dh * (long)sizeof(TA) / 16);
+  long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+#define SC(KH_)                                                                                              \
+  hipLaunchKernelGGL((disp_scatter_kernel<TA, KH_>), dim3(blocks), dim3(256), 0, st, (const TA *)x, row_of, \
+                     (TA *)x_perm, s.T, s.H, s.k, s.dh, s.R_max)
+  if (s.k <= 1) SC(1);
+  else if (s.k <= 2) SC(2);
+  else if (s.k <= 4) SC(4);
+  else SC(8);
+#undef SC
 }
 
 int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w, const void *x,
@@ -286,28 +347,17 @@ int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w
 
   hipLaunchKernelGGL(disp_hist_kernel, dim3(nc), dim3(256), s.E * 4, st, topk_idx, n, s.E, hist);
   if (hipGetLastError() != hipSuccess) return -4;
-  hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(1024), 0, st, hist, (int)nc, s.E, s.drop, s.C,
-                     s.keep_num, s.keep_den, demand, counts, offsets, s.drop == 2 ? all_off : nullptr);
-  if (hipGetLastError() != hipSuccess) return -4;
-  hipLaunchKernelGGL(disp_rank_kernel, dim3(nc), dim3(256), 4 * s.E * 4, st, topk_idx, n, s.E, hist,
-                     offsets, all_off, s.drop, s.C, row_of, src_of, seg);
+  hipLaunchKernelGGL(disp_rank_kernel, dim3(nc), dim3(256), 9 * s.E * 4, st, topk_idx, n, s.E, (int)nc, hist,
+                     s.drop, s.C, s.keep_num, s.keep_den, demand, counts, offsets, all_off, row_of, src_of, seg);
   if (hipGetLastError() != hipSuccess) return -4;
   if (s.drop == 2) {
     hipLaunchKernelGGL(disp_affinity_kernel, dim3(s.E), dim3(256), 0, st, seg, all_off, counts, offsets,
                        topk_w, row_of, src_of);
     if (hipGetLastError() != hipSuccess) return -4;
   }
-  const int esz = s.act_f32 ? 4 : 2;
-  long rpb_ = 32768 / ((long)s.dh * esz);
-  int rpb = rpb_ < 1 ? 1 : (int)rpb_;
-  long blocks = (s.R_max + rpb - 1) / rpb;
-  if (blocks > 0) {
-    if (s.act_f32)
-      hipLaunchKernelGGL(disp_scatter_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float *)x, src_of,
-                         topk_idx, offsets, (float *)x_perm, s.E, s.K, s.Eh, s.dh, s.H * s.dh, rpb, n);
-    else
-      hipLaunchKernelGGL(disp_scatter_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st, (const uint16_t *)x,
-                         src_of, topk_idx, offsets, (uint16_t *)x_perm, s.E, s.K, s.Eh, s.dh, s.H * s.dh, rpb, n);
+  if (x_perm) {
+    if (s.act_f32) launch_scatter<float>(s, x, row_of, x_perm, st);
+    else launch_scatter<uint16_t>(s, x, row_of, x_perm, st);
     if (hipGetLastError() != hipSuccess) return -4;
   }
   return 0;

@@ -44,8 +44,10 @@ __global__ void route_split_w_kernel(const float *__restrict__ w, uint16_t *__re
 
 // ------------------------------------------------------------------ logits (MFMA)
 // grid (ceil(T/TB), H, KSPLIT), block 256.  TB = 64*MW tokens; wave w owns
-// tokens [w*16*MW, (w+1)*16*MW) of the tile.  W rows of the head: NPL planes
-// x NF*16 rows, staged per 128-byte k-chunk in LDS (XOR-swizzled 16-byte slots).
+// tokens [w*16*MW, (w+1)*16*MW) of the tile.  The head's W rows (NPL planes x
+// NF*16 rows, rows past E_h read row 0 and are never stored) are staged per
+// 128-byte k-chunk in LDS with global_load_lds (XOR-swizzled 16-byte slots,
+// two stages); x goes straight into MFMA fragments, loaded one chunk ahead.
 template <typename TIN, typename TW, int NF, int NPL, int MW>
 __global__ __launch_bounds__(256) void route_logits_kernel(
     const TIN *__restrict__ x, const TW *__restrict__ w, float *__restrict__ part,
@@ -53,7 +55,10 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
   constexpr int EPC = 16 / sizeof(TIN);            // elements per 16 bytes
   constexpr int CHUNK = 8 * EPC;                   // elements per 128-byte row chunk
   constexpr int ROWS = NPL * NF * 16;
-  __shared__ u32x4 lds[ROWS * 8];
+  constexpr int NWI = (ROWS * 8 + 255) / 256;      // W load instructions per thread per chunk
+  constexpr int STAGE = NWI * 256;                 // slots per stage (padded to whole instructions)
+  constexpr int NL = NWI + 2 * MW;                 // vector-memory instructions per thread per chunk
+  __shared__ u32x4 lds[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int h = blockIdx.y, ks = blockIdx.z;
   const int tok0 = blockIdx.x * (64 * MW);
@@ -63,6 +68,33 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
   const int c1 = min(nchunks, c0 + kchunk_per_split);
   const TW *wh = w + (size_t)h * w_head_stride;
   const TIN *xh = x + (size_t)h * dh;
+  const int cq = lane >> 4, l16 = lane & 15;
+
+  // W source of each staged slot (row 0 for padding rows and padding slots)
+  uint32_t woff[NWI];
+#pragma unroll
+  for (int i = 0; i < NWI; ++i) {
+    const int sl = i * 256 + tid;
+    const int r = sl >> 3, q = (sl & 7) ^ (r & 7);
+    const int pl = r / Epad, e = r - pl * Epad;
+    woff[i] = (sl < ROWS * 8 && e < Eh) ? (uint32_t)(pl * w_plane_stride + (long)e * dh + q * (16 / sizeof(TW)))
+                                        : (uint32_t)(q * (16 / sizeof(TW)));
+  }
+  int arow[MW];
+#pragma unroll
+  for (int i = 0; i < MW; ++i) arow[i] = min(T - 1, tok0 + wv * 16 * MW + i * 16 + l16);
+
+  auto issue = [&](int c, int st, u32x4 (&xa)[MW][2]) {
+#pragma unroll
+    for (int i = 0; i < NWI; ++i)
+      load_lds16(wh + woff[i] + (size_t)c * (8 * 16 / sizeof(TW)), lds + st * STAGE + i * 256 + wv * 64);
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(xh + (size_t)arow[i] * ldx + (size_t)c * CHUNK);
+      xa[i][0] = src[cq];
+      xa[i][1] = src[cq + 4];
+    }
+  };
 
   f32x4 acc[MW][NF];
 #pragma unroll
@@ -70,43 +102,35 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int arow[MW];
-#pragma unroll
-  for (int i = 0; i < MW; ++i) arow[i] = min(T - 1, tok0 + wv * 16 * MW + i * 16 + (lane & 15));
-  const int cq = lane >> 4;  // 0..3
-
-  for (int c = c0; c < c1; ++c) {
-    __syncthreads();
-    for (int s = tid; s < ROWS * 8; s += 256) {
-      int r = s >> 3, q = s & 7;
-      int pl = r / Epad, e = r - pl * Epad;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (e < Eh)
-        v = reinterpret_cast<const u32x4 *>(wh + (size_t)pl * w_plane_stride + (size_t)e * dh +
-                                            (size_t)c * CHUNK)[q];
-      lds[r * 8 + (q ^ (r & 7))] = v;
-    }
-    __syncthreads();
-    u32x4 a0[MW], a1[MW];
-#pragma unroll
-    for (int i = 0; i < MW; ++i) {
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(xh + (size_t)arow[i] * ldx + (size_t)c * CHUNK);
-      a0[i] = src[cq];
-      a1[i] = src[cq + 4];
-    }
+  auto compute = [&](int st, const u32x4 (&xa)[MW][2]) {
 #pragma unroll
     for (int p = 0; p < NPL; ++p)
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        int r = p * Epad + f * 16 + (lane & 15);
-        u32x4 b0 = lds[r * 8 + (cq ^ (r & 7))];
-        u32x4 b1 = lds[r * 8 + ((cq + 4) ^ (r & 7))];
+        const int r = p * Epad + f * 16 + l16;
+        const u32x4 b0 = lds[st * STAGE + r * 8 + (cq ^ (r & 7))];
+        const u32x4 b1 = lds[st * STAGE + r * 8 + ((cq + 4) ^ (r & 7))];
 #pragma unroll
         for (int i = 0; i < MW; ++i) {
-          acc[i][f] = mma16(a0[i], b0, acc[i][f], TW());
-          acc[i][f] = mma16(a1[i], b1, acc[i][f], TW());
+          acc[i][f] = mma16(xa[i][0], b0, acc[i][f], TW());
+          acc[i][f] = mma16(xa[i][1], b1, acc[i][f], TW());
         }
       }
+  };
+
+  // two register sets for x, alternating; chunk c+1 is in flight during chunk c
+  u32x4 xa0[MW][2], xa1[MW][2];
+  if (c0 < c1) issue(c0, 0, xa0);
+  for (int c = c0; c < c1; c += 2) {
+    if (c + 1 < c1) { issue(c + 1, 1, xa1); wait_vmcnt<NL>(); } else { wait_vmcnt0(); }
+    __syncthreads();
+    compute(0, xa0);
+    __syncthreads();
+    if (c + 1 >= c1) break;
+    if (c + 2 < c1) { issue(c + 2, 0, xa0); wait_vmcnt<NL>(); } else { wait_vmcnt0(); }
+    __syncthreads();
+    compute(1, xa1);
+    __syncthreads();
   }
   // store partial scores: acc[i][f][v] = C[row 4*(lane/16)+v][col lane%16]
   float *out = part + (size_t)ks * T * E;
@@ -114,7 +138,7 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
   for (int i = 0; i < MW; ++i)
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      int e = f * 16 + (lane & 15);
+      int e = f * 16 + l16;
       if (e >= Eh) continue;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -170,20 +194,21 @@ __global__ __launch_bounds__(256) void route_select_kernel(
 
   // group-limited: allowed-group bitmask (groups of consecutive experts)
   uint32_t allowed = 0xFFFFFFFFu;
+  int grp[EPL];  // group of each owned expert (groups are consecutive experts)
   if (n_groups > 0) {
     // group score = largest score in the group; keep the topk_groups best
     // groups (higher score first, lower group index on ties)
     const int gsz = Eh / n_groups;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) grp[i] = (j + L * i) / gsz;
     uint32_t gkey[32];
 #pragma unroll
     for (int g = 0; g < 32; ++g) {
       float v = NEG;
       if (g < n_groups) {
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-          int e = j + L * i;
-          if (e < Eh && e / gsz == g) v = fmaxf(v, lv[i]);
-        }
+        for (int i = 0; i < EPL; ++i)
+          if (j + L * i < Eh && grp[i] == g) v = fmaxf(v, lv[i]);
         v = wave_max(v, L);
       }
       gkey[g] = score_key(v);
@@ -205,7 +230,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   for (int i = 0; i < EPL; ++i) {
     int e = j + L * i;
     bool ok = e < Eh;
-    if (ok && n_groups > 0) ok = (allowed >> (e / (Eh / n_groups))) & 1u;
+    if (ok && n_groups > 0) ok = (allowed >> grp[i]) & 1u;
     kk[i] = ok ? (((uint64_t)score_key(lv[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)) : 0ull;
   }
   int sel_e[KMAX];
@@ -355,17 +380,25 @@ static int dispatch_logits(const Shape &s, const RouteGeom &g, const void *x, co
     case 4: launch_logits<TIN, TW, 4, NPL, 1>(s, g, x, w, part, st); break;
     case 5: launch_logits<TIN, TW, 5, NPL, 1>(s, g, x, w, part, st); break;
     case 6: launch_logits<TIN, TW, 6, NPL, 1>(s, g, x, w, part, st); break;
-    case 8: launch_logits<TIN, TW, 8, NPL, 2>(s, g, x, w, part, st); break;
-    case 10: launch_logits<TIN, TW, 10, NPL, 2>(s, g, x, w, part, st); break;
-    case 12: launch_logits<TIN, TW, 12, NPL, 2>(s, g, x, w, part, st); break;
-    case 16: launch_logits<TIN, TW, 16, NPL, 2>(s, g, x, w, part, st); break;
-    default: return -2;
+    default:
+      if constexpr (NPL == 1) {
+        switch (g.nf) {
+          case 8: launch_logits<TIN, TW, 8, NPL, 2>(s, g, x, w, part, st); return 0;
+          case 10: launch_logits<TIN, TW, 10, NPL, 2>(s, g, x, w, part, st); return 0;
+          case 12: launch_logits<TIN, TW, 12, NPL, 2>(s, g, x, w, part, st); return 0;
+          case 16: launch_logits<TIN, TW, 16, NPL, 2>(s, g, x, w, part, st); return 0;
+        }
+      }
+      return -2;
   }
   return 0;
 }
 
 bool route_supported(const Shape &s) {
   RouteGeom g = route_geometry(s);
+  // the three-plane (fp32 router, bf16 activations) form stages 3x the rows:
+  // instantiated up to 6 fragments (E_h <= 96)
+  if (g.nplanes == 3 && g.nf > 6) return false;
   return g.nf > 0 && g.epl <= 16;
 }
 

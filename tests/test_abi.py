@@ -84,6 +84,7 @@ def _bad(**kw):
     (_bad(act_dtype=0, router_dtype=1), moe.MOE_ERR_UNSUPPORTED),
     (_bad(n_heads=2, d_head=1024, n_experts=64), moe.MOE_ERR_UNSUPPORTED),  # shared experts need H == 1
     (_bad(n_experts=2048), moe.MOE_ERR_ARG),                    # top_k fine, E_h > 256 -> unsupported or arg
+    (CONFIGS[1].with_(n_experts=128), moe.MOE_ERR_UNSUPPORTED),  # fp32 router beyond 96 experts per head
     (_bad(T=-1), moe.MOE_ERR_ARG),
 ])
 def test_invalid_configs_rejected(cfg, status):
