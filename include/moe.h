@@ -28,7 +28,11 @@
  *     and keeps no pointer after a call returns.  Calls are reentrant.
  *   - Every call is asynchronous on `stream` and returns a moe_status.  All
  *     argument checks run on the host before anything is launched: a failed
- *     check launches nothing.  A launch failure returns MOE_ERR_HIP.
+ *     check launches nothing.  A launch failure returns MOE_ERR_HIP; with the
+ *     environment variable MOE_DEBUG set, the failing launch and HIP's
+ *     reason are also written to stderr.  A call clears HIP's last-error
+ *     state (hipGetLastError) before its first launch, so an error that an
+ *     earlier, unrelated HIP call left there is neither reported nor kept.
  *   - Row counts that depend on routing (R = kept assignments) are never read
  *     back to the host: buffers sized by R use moe_rows_upper_bound(), and
  *     the true R is offsets[E] on the device.

@@ -11,6 +11,16 @@ Importing fails loudly if the library has not been built
 import ctypes
 import os
 
+# One HIP runtime per process.  torch ships its own libamdhip64 (same soname,
+# libamdhip64.so.7, but requested by torch under the unversioned name): if
+# libmoe.so were loaded first, it would bring in /opt/rocm's copy and torch
+# would then load a second one, and the two runtimes do not share the device.
+# Importing torch first makes libmoe.so bind to torch's runtime.
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:  # plain ctypes use without torch: /opt/rocm's runtime
+    _torch = None
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 

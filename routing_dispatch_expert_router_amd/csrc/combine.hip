@@ -105,7 +105,7 @@ int launch_combine(const Shape &s, const void *y_perm, const int32_t *row_of, co
     launch_typed<float>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
   else
     launch_typed<uint16_t>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
-  return hipGetLastError() == hipSuccess ? 0 : -4;
+  return launch_status("combine");
 }
 
 }  // namespace moe

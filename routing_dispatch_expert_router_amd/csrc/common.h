@@ -100,6 +100,8 @@ __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC
 
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+// wave index in the workgroup, as a scalar (wave-uniform) value
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE); }
 
 // order-preserving key of a float score: larger float -> larger key; -0.0 == +0.0
 __device__ __forceinline__ uint32_t score_key(float f) {

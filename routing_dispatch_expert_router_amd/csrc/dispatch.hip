@@ -346,19 +346,19 @@ int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w
   int32_t *seg = (s.drop == 2) ? (int32_t *)p : nullptr;
 
   hipLaunchKernelGGL(disp_hist_kernel, dim3(nc), dim3(256), s.E * 4, st, topk_idx, n, s.E, hist);
-  if (hipGetLastError() != hipSuccess) return -4;
+  if (int rc = launch_status("dispatch histogram")) return rc;
   hipLaunchKernelGGL(disp_rank_kernel, dim3(nc), dim3(256), 9 * s.E * 4, st, topk_idx, n, s.E, (int)nc, hist,
                      s.drop, s.C, s.keep_num, s.keep_den, demand, counts, offsets, all_off, row_of, src_of, seg);
-  if (hipGetLastError() != hipSuccess) return -4;
+  if (int rc = launch_status("dispatch rank")) return rc;
   if (s.drop == 2) {
     hipLaunchKernelGGL(disp_affinity_kernel, dim3(s.E), dim3(256), 0, st, seg, all_off, counts, offsets,
                        topk_w, row_of, src_of);
-    if (hipGetLastError() != hipSuccess) return -4;
+    if (int rc = launch_status("dispatch affinity")) return rc;
   }
   if (x_perm) {
     if (s.act_f32) launch_scatter<float>(s, x, row_of, x_perm, st);
     else launch_scatter<uint16_t>(s, x, row_of, x_perm, st);
-    if (hipGetLastError() != hipSuccess) return -4;
+    if (int rc = launch_status("dispatch scatter")) return rc;
   }
   return 0;
 }

@@ -11,10 +11,19 @@
 // C[M_g, N] = A_g[M_g, K] * B_g[N, K]^T for groups g: routed expert e owns rows
 // [offsets[e], offsets[e+1]) of A and C; an optional extra group (shared
 // experts, or a plain dense product) has its own pointers and sizes.  Both
-// operands are K-contiguous.  Tiles: 128 x 128 outputs (SwiGLU: 128 rows x 64
-// hidden columns, whose gate and up halves make the 128 B rows), k-chunk of
-// 128 bytes, 4 waves each 64 x 64, LDS double buffer with XOR-swizzled 16-byte
-// slots, one barrier per k-chunk.
+// operands are K-contiguous.  Tiles: 256 x 256 outputs with 8 waves (tall
+// groups; a group's short tail goes to a second launch of 128 x 128 tiles) or
+// 128 x 128 with 8 waves (SwiGLU: half the tile's B rows are gate rows, half
+// up rows, so the output tile is BN/2 hidden columns wide); k-chunks of 128
+// bytes per row in LDS rings with XOR-swizzled 16-byte slots, one barrier per
+// k-chunk.  Waves whose rows lie past a group's end skip their MFMAs.
+//
+// What bounds it (measured on MI355X): with the global loads removed the MFMA
+// + LDS-read loop runs at 75-85 % of the bf16 peak; the global -> LDS stream
+// alone takes 70-90 % of the kernel's time, its L2 misses (the weights,
+// streamed once from HBM, and re-fetched row tiles) setting the pace.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -40,8 +49,10 @@ struct GemmArgs {
 };
 
 // Rows of a group a launch covers.  With split launches, a group's rows are
-// cut where the last 256-row tile would hold at most 128 rows: the head goes
-// to 256-row tiles, the short tail to 128-row tiles in a second launch.
+// cut where its last 256-row tile would hold at most 128 rows: the head goes
+// to 256-row tiles, the short tail to 128-row tiles in a second launch (a tail
+// tile in the head launch would hold a CU for nearly as long as a full tile,
+// since the tile's time goes to streaming its weight columns).
 constexpr int SPLIT_BM = 256;
 __host__ __device__ inline void row_window(int split, int M, int *beg, int *len) {
   const int rem = M % SPLIT_BM;
@@ -98,20 +109,21 @@ __global__ __launch_bounds__(1024) void gemm_prep_kernel(const int32_t *__restri
 
 // Tile BM x BN outputs (SwiGLU: BN/2 hidden columns, the B tile holding BN/2
 // gate rows then BN/2 up rows); WGM x WGN waves, each (BM/WGM) x (BN/WGN);
-// k-chunks of KS 16-byte slots per row (KS = 8: 128 B, KS = 4: 64 B) in a ring
-// of STAGES LDS buffers, so global loads run STAGES-1 chunks ahead of the
-// MFMAs.  Operands go global -> LDS with global_load_lds_dwordx4 (no VGPR
+// k-chunks of KS = 8 16-byte slots (128 B) per row.  The A and B chunks sit
+// in rings of STA and STB LDS buffers, so the global loads of an operand run
+// STA-1 (STB-1) chunks ahead of the MFMAs; the deeper ring goes to the
+// operand whose loads miss L2 more.  Operands go global -> LDS with global_load_lds_dwordx4 (no VGPR
 // staging): each wave instruction fills 64 consecutive 16-byte LDS slots, so
 // every lane fetches the global chunk that belongs in its slot.  Slots are
 // XOR-swizzled within a row so the 16 rows one ds_read_b128 touches fall in
 // distinct banks.
 template <int KS>
 __device__ __forceinline__ int swz(int row, int q) {
-  if constexpr (KS == 8) return q ^ (row & 7);
-  else return q ^ (((row >> 1) ^ (row >> 3)) & 3);
+  static_assert(KS == 8, "128-byte k-chunks");
+  return q ^ (row & 7);
 }
 
-template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES, bool SG>
+template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STA, int STB, bool SG>
 __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int NT = 64 * WGM * WGN;    // threads
   constexpr int EPC = 16 / sizeof(TE);  // elements per 16-byte slot
@@ -121,10 +133,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   constexpr int LA = SA / NT, LB = SB / NT;    // slots per thread per stage
   constexpr int NKS = KS / 4;                  // MFMA k-steps per chunk
   static_assert(LA * NT == SA && LB * NT == SB, "tile / thread mismatch");
-  static_assert(STAGES == 2 && NKS == 2, "pipeline below is written for 2 stages of 2 k-steps");
+  static_assert(STA >= 2 && STB >= 2 && NKS == 2, "two k-steps per chunk, two or more stages");
   extern __shared__ u32x4 smem[];
-  u32x4 *sA = smem;                  // [STAGES][SA]
-  u32x4 *sB = smem + STAGES * SA;    // [STAGES][SB]
+  u32x4 *sA = smem;               // [STA][SA]
+  u32x4 *sB = smem + STA * SA;    // [STB][SB]
 
   const int total = p.prefix[p.G];
   const int b = blockIdx.x;
@@ -218,7 +230,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   const int bwoff = (EPI == EPI_SWIGLU) ? wn * (HB / WGN) : wn * WN;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    const int sw = (cq + 4 * ks) ^ (l16 & 7);
+    const int sw = swz<KS>(l16, cq + 4 * ks);
     abase[ks] = (wm * WM + l16) * KS + sw;
     bbase[ks] = (bwoff + l16) * KS + sw;
   }
@@ -226,40 +238,40 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
     return (EPI == EPI_SWIGLU) ? ((f < NF / 2) ? f * 16 : HB + (f - NF / 2) * 16) : f * 16;
   };
 
-  auto issue = [&](int kc, int st) {
+  auto issue_a = [&](int kc, int st) {
     const size_t ko = (size_t)kc * BKE;
 #pragma unroll
     for (int i = 0; i < LA; ++i) load_lds16(A + oa[i] + ko, sA + st * SA + i * NT + wv * 64);
+  };
+  auto issue_b = [&](int kc, int st) {
+    const size_t ko = (size_t)kc * BKE;
 #pragma unroll
     for (int i = 0; i < LB; ++i) load_lds16(bsrc(i) + ob[i] + ko, sB + st * SB + i * NT + wv * 64);
   };
-  auto read = [&](int st, int ks, u32x4 *fa, u32x4 *fb) {
+  // NL: m-fragments of this wave that hold rows (the rest of a ragged tile is
+  // skipped: no LDS reads, no MFMAs)
+  auto read = [&](auto nl, int sa, int sb, int ks, u32x4 *fa, u32x4 *fb) {
+    constexpr int NL = decltype(nl)::value;
+    if constexpr (NL > 0) {
 #pragma unroll
-    for (int i = 0; i < MF; ++i) fa[i] = sA[st * SA + abase[ks] + i * 16 * KS];
+      for (int i = 0; i < NL; ++i) fa[i] = sA[sa * SA + abase[ks] + i * 16 * KS];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) fb[f] = sB[st * SB + bbase[ks] + brow_off(f) * KS];
+      for (int f = 0; f < NF; ++f) fb[f] = sB[sb * SB + bbase[ks] + brow_off(f) * KS];
+    }
   };
-  auto mfma = [&](const u32x4 *fa, const u32x4 *fb) {
+  auto mfma = [&](auto nl, const u32x4 *fa, const u32x4 *fb) {
+    constexpr int NL = decltype(nl)::value;
 #pragma unroll
-    for (int i = 0; i < MF; ++i)
+    for (int i = 0; i < NL; ++i)
 #pragma unroll
       for (int f = 0; f < NF; ++f) acc[i][f] = mma16(fa[i], fb[f], acc[i][f], TE());
   };
-
-  // Software pipeline over k-steps: the LDS reads of the next k-step are in
-  // flight while the MFMAs of the current one run.  Chunk kc+2 is loaded into
-  // the stage of chunk kc once every wave has read chunk kc (barrier).
-  u32x4 fa0[MF], fb0[NF], fa1[MF], fb1[NF];
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
-  if (nk > 1) wait_vmcnt<LA + LB>(); else wait_vmcnt0();
-  __syncthreads();
-  read(0, 0, fa0, fb0);
   // scheduling hint (SG): interleave the LDS reads of the next k-step with the
   // MFMAs of the current one
-  auto interleave = [&]() {
-    if constexpr (SG) {
-      constexpr int NR = MF + NF, NM = MF * NF;
+  auto interleave = [&](auto nl) {
+    constexpr int NL = decltype(nl)::value;
+    if constexpr (SG && NL > 0) {
+      constexpr int NR = NL + NF, NM = NL * NF;
       constexpr int PER = NM / NR > 0 ? NM / NR : 1;
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
@@ -269,23 +281,57 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
       __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
     }
   };
-  for (int kc = 0; kc < nk; ++kc) {
-    const int st = kc & 1;
-    read(st, 1, fa1, fb1);
-    mfma(fa0, fb0);
-    interleave();
-    if (kc + 1 < nk) {
-      // chunk kc+1 landed for this wave; this wave's reads of stage st are done
-      wait_vmcnt0();
-      wait_lgkmcnt0();
-      __syncthreads();
-      if (kc + 2 < nk) issue(kc + 2, st);
+
+  // Software pipeline.  Step kc (after its barrier) loads A chunk kc+STA into
+  // the A stage of chunk kc and B chunk kc+STB into the B stage of chunk kc;
+  // the LDS reads of each k-step overlap the MFMAs of the one before.  The
+  // prologue issues the loads of the steps before step 0 in the same order.
+  // Vector-memory loads complete in order, so "chunk c has landed" is a wait
+  // until no more than the loads issued after it are outstanding:
+  constexpr int SMAX = STA > STB ? STA : STB, SMIN = STA < STB ? STA : STB;
+  constexpr int LAFTER = (STA < STB ? LB : 0) + (SMIN - 2) * (LA + LB);
+  auto wait_chunk = [&](int c) {  // chunk c landed (all chunks < c + SMAX - 1 issued, if they exist)
+    if (c + SMAX - 2 < nk) wait_vmcnt<LAFTER>(); else wait_vmcnt0();
+  };
+  auto pipeline = [&](auto nl) {
+    u32x4 fa0[MF], fb0[NF], fa1[MF], fb1[NF];
+    for (int i = -SMAX; i < 0; ++i) {
+      if (i + STA >= 0 && i + STA < nk) issue_a(i + STA, i + STA);
+      if (i + STB >= 0 && i + STB < nk) issue_b(i + STB, i + STB);
     }
-    // on the last chunk this reads stage data that is never used
-    read(st ^ 1, 0, fa0, fb0);
-    mfma(fa1, fb1);
-    interleave();
-  }
+    wait_chunk(0);
+    __syncthreads();
+    read(nl, 0, 0, 0, fa0, fb0);
+    int sa = 0, sb = 0;
+    for (int kc = 0; kc < nk; ++kc) {
+      read(nl, sa, sb, 1, fa1, fb1);
+      mfma(nl, fa0, fb0);
+      interleave(nl);
+      const int san = (sa + 1 == STA) ? 0 : sa + 1, sbn = (sb + 1 == STB) ? 0 : sb + 1;
+      if (kc + 1 < nk) {
+        // chunk kc+1 landed for this wave; this wave's reads of chunk kc are done
+        wait_chunk(kc + 1);
+        wait_lgkmcnt0();
+        __syncthreads();
+        if (kc + STA < nk) issue_a(kc + STA, sa);
+        if (kc + STB < nk) issue_b(kc + STB, sb);
+      }
+      // on the last chunk this reads stage data that is never used
+      read(nl, san, sbn, 0, fa0, fb0);
+      mfma(nl, fa1, fb1);
+      interleave(nl);
+      sa = san;
+      sb = sbn;
+    }
+  };
+  // live m-fragments of this wave, rounded up to MF, MF/2, MF/4 or 0 (the
+  // rows past M in a group's last tile); wave-uniform, so every wave still
+  // takes part in the loads and barriers
+  const int live = min(max(M - m0 - wave_id() / WGN * WM, 0), WM);
+  if (live > WM / 2) pipeline(std::integral_constant<int, MF>{});
+  else if (MF >= 4 && live > WM / 4) pipeline(std::integral_constant<int, (MF >= 4 ? MF / 2 : MF)>{});
+  else if (live > 0) pipeline(std::integral_constant<int, (MF >= 4 ? MF / 4 : MF)>{});
+  else pipeline(std::integral_constant<int, 0>{});
 
   // epilogue: acc[i][f][v] = C[wm*WM + i*16 + 4*cq + v][n-fragment f, column l16]
   const TE *R = (EPI == EPI_RESID) ? (const TE *)p.res + (size_t)r0 * p.ldres : nullptr;
@@ -321,27 +367,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
 // ---------------------------------------------------------------- host
 // Tile shapes with an instantiated kernel.
 enum TileCfg {
-  TILE_128x128 = 0,     // 4 waves (2 x 2), wave tile 64 x 64
-  TILE_256x256_W8 = 1,  // 8 waves (2 x 4), wave tile 128 x 64
-  TILE_256x128_W8 = 2,  // 8 waves (4 x 2), wave tile 64 x 64
-  TILE_128x256_W8 = 3,  // 8 waves (2 x 4), wave tile 64 x 64
-  TILE_128x128_W8 = 4,  // 8 waves (2 x 4), wave tile 64 x 32
-  TILE_64x256_W4 = 5,   // 4 waves (1 x 4), wave tile 64 x 64
-  TILE_256x256_W8_SG = 6,  // as 1, LDS reads interleaved with MFMAs by scheduling hints
-  TILE_128x128_W8_SG = 7,  // as 4, same
+  TILE_128x128 = 0,     // 4 waves (2 x 2), wave tile 64 x 64 (also the float32 tile)
+  TILE_256x256_W8 = 1,  // 8 waves (2 x 4), wave tile 128 x 64; head + tail launches
+  TILE_128x128_W8 = 2,  // 8 waves (2 x 4), wave tile 64 x 32
 };
 
 static long max_tiles(long rows_bound, int groups, int bm, int ntiles) {
   return ((rows_bound + bm - 1) / bm + groups) * ntiles;
 }
 
-template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STAGES, bool SG = false>
+template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STA, int STB, bool SG = false>
 static int run_gemm_t(GemmArgs a, int32_t *prefix, hipStream_t st) {
   a.prefix = prefix;
   hipLaunchKernelGGL((gemm_prep_kernel<EPI, BM_, BN_>), dim3(1), dim3(1024), 0, st, a.offsets, a.E, a.N, a.has_x,
                      a.Mx, a.Nx, a.split, prefix);
-  if (hipGetLastError() != hipSuccess) return -4;
-  // tail launches hold at most one tile row per group
+  if (int rc = launch_status("gemm tile prefix")) return rc;
+  // grid: an upper bound of the tile count; blocks past the device-built
+  // prefix total exit at once.  A tail launch holds at most one tile row per
+  // group.
   long grid;
   if (a.split == 2)
     grid = (long)a.E * n_tiles<EPI, BN_>(a.N) + (a.has_x ? n_tiles<EPI, BN_>(a.Nx) : 0);
@@ -350,53 +393,46 @@ static int run_gemm_t(GemmArgs a, int32_t *prefix, hipStream_t st) {
            (a.has_x ? max_tiles(a.Mx, 0, BM_, n_tiles<EPI, BN_>(a.Nx)) : 0);
   if (grid <= 0) return 0;
   // dynamic LDS up to the device's per-workgroup limit (160 KiB on gfx950)
-  constexpr size_t lds = (size_t)STAGES * (BM_ + BN_) * KS * 16;
+  constexpr size_t lds = (size_t)(STA * BM_ + STB * BN_) * KS * 16;
   static_assert(lds <= 160 * 1024, "LDS per workgroup");
-  hipLaunchKernelGGL((grouped_gemm_kernel<TE, EPI, BM_, BN_, WGM, WGN, KS, STAGES, SG>), dim3(grid),
+  hipLaunchKernelGGL((grouped_gemm_kernel<TE, EPI, BM_, BN_, WGM, WGN, KS, STA, STB, SG>), dim3(grid),
                      dim3(64 * WGM * WGN), lds, st, a);
-  if (hipGetLastError() != hipSuccess) return -4;
+  if (int rc = launch_status("grouped gemm")) return rc;
   return 0;
-}
-
-template <typename TE, int EPI>
-static int run_gemm_one(GemmArgs a, int tile, int32_t *prefix, hipStream_t st);
-
-// 256-row tiles run as a head launch plus a tail launch of 128-row tiles
-template <typename TE, int EPI>
-static int run_gemm(GemmArgs a, int tile, int32_t *prefix, hipStream_t st) {
-  if (tile == TILE_256x256_W8_SG) {
-    GemmArgs h = a, t = a;
-    h.split = 1;
-    t.split = 2;
-    int rc = run_gemm_one<TE, EPI>(h, TILE_256x256_W8_SG, prefix, st);
-    if (rc) return rc;
-    return run_gemm_one<TE, EPI>(t, TILE_128x128_W8_SG, prefix + (a.E + 2), st);
-  }
-  return run_gemm_one<TE, EPI>(a, tile, prefix, st);
 }
 
 template <typename TE, int EPI>
 static int run_gemm_one(GemmArgs a, int tile, int32_t *prefix, hipStream_t st) {
   if constexpr (sizeof(TE) == 4) {
-    return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2>(a, prefix, st);
+    return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 2>(a, prefix, st);
   } else {
-  switch (tile) {
-    case TILE_256x256_W8: return run_gemm_t<TE, EPI, 256, 256, 2, 4, 8, 2>(a, prefix, st);
-    case TILE_256x256_W8_SG: return run_gemm_t<TE, EPI, 256, 256, 2, 4, 8, 2, true>(a, prefix, st);
-    case TILE_128x128_W8_SG: return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, true>(a, prefix, st);
-    case TILE_256x128_W8: return run_gemm_t<TE, EPI, 256, 128, 4, 2, 8, 2>(a, prefix, st);
-    case TILE_128x256_W8: return run_gemm_t<TE, EPI, 128, 256, 2, 4, 8, 2>(a, prefix, st);
-    case TILE_128x128_W8: return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2>(a, prefix, st);
-    case TILE_64x256_W4: return run_gemm_t<TE, EPI, 64, 256, 1, 4, 8, 2>(a, prefix, st);
-    default: return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2>(a, prefix, st);
+    switch (tile) {
+      case TILE_256x256_W8: return run_gemm_t<TE, EPI, 256, 256, 2, 4, 8, 2, 2, true>(a, prefix, st);
+      case TILE_128x128_W8: return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 2, true>(a, prefix, st);
+      default: return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 2>(a, prefix, st);
+    }
   }
+}
+
+// 256-row tiles run as a head launch plus a tail launch of 128-row tiles;
+// prefix holds two tile prefixes of E + 2 entries
+template <typename TE, int EPI>
+static int run_gemm(GemmArgs a, int tile, int32_t *prefix, hipStream_t st) {
+  if (tile == TILE_256x256_W8) {
+    GemmArgs h = a, t = a;
+    h.split = 1;
+    t.split = 2;
+    int rc = run_gemm_one<TE, EPI>(h, TILE_256x256_W8, prefix, st);
+    if (rc) return rc;
+    return run_gemm_one<TE, EPI>(t, TILE_128x128_W8, prefix + (a.E + 2), st);
   }
+  return run_gemm_one<TE, EPI>(a, tile, prefix, st);
 }
 
 // tile shape for a launch: large tiles when the groups are tall enough to fill them
 static int pick_tile(long rows, int groups) {
   long avg = groups > 0 ? rows / groups : rows;
-  return avg >= 1024 ? TILE_256x256_W8_SG : TILE_128x128_W8_SG;
+  return avg >= 1024 ? TILE_256x256_W8 : TILE_128x128_W8;
 }
 
 size_t ffn_ws_bytes(const Shape &s) {
@@ -421,7 +457,7 @@ static int ffn_typed(const Shape &s, const void *x_perm, const int32_t *offsets,
     Hs = (TE *)p;
     p += align_up((size_t)s.T * fs * esz, 256);
   }
-  int32_t *pre1 = (int32_t *)p;  // [2][E+2]: head and tail launches
+  int32_t *pre1 = (int32_t *)p;  // [2][E+2] per GEMM: head and tail launches
   p += align_up((size_t)2 * (s.E + 2) * 4, 256);
   int32_t *pre2 = (int32_t *)p;
   const bool glu = s.act == 1;

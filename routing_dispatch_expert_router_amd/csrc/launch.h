@@ -7,6 +7,11 @@
 
 namespace moe {
 
+// Status of the launches since the last check: 0, or -4 (MOE_ERR_HIP) after
+// writing HIP's reason and the launch name to stderr when the MOE_DEBUG
+// environment variable is set.
+int launch_status(const char *what);
+
 // Validated, normalised layer shape.
 struct Shape {
   int T, d, H, dh, E, Eh, k, K;  // K = H * k assignments per token

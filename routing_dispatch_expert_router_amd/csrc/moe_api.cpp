@@ -2,12 +2,21 @@
 // Host code only: validation, workspace layout and launch order.  Every check
 // runs before the first launch, so a rejected call launches nothing.
 #include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/moe.h"
 #include "launch.h"
 
 using moe::Shape;
+
+int moe::launch_status(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return 0;
+  if (getenv("MOE_DEBUG")) fprintf(stderr, "moe: %s launch failed: %s\n", what, hipGetErrorString(e));
+  return -4;
+}
 
 namespace {
 
@@ -101,6 +110,11 @@ int check_ws(const Shape &s, const void *ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
+// HIP's last-error state also holds errors of earlier, unrelated runtime
+// calls of the caller; clear it before our first launch so that the checks
+// after each launch see only our own launches
+void clear_stale_error() { (void)hipGetLastError(); }
+
 int rc_of(int launcher_rc) {
   if (launcher_rc == -2) return MOE_ERR_UNSUPPORTED;
   if (launcher_rc != 0) return MOE_ERR_HIP;
@@ -152,6 +166,7 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router, const 
   if (aux_loss && s.H != 1) return MOE_ERR_UNSUPPORTED;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   if (s.T == 0) return MOE_OK;
+  clear_stale_error();
   return rc_of(moe::launch_route(s, x, w_router, bias, logits, mode, topk_idx, topk_w, aux_loss, ws, stream));
 }
 
@@ -165,6 +180,7 @@ int moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, const float *to
   if (s.drop == MOE_DROP_AFFINITY && !topk_w) return MOE_ERR_ARG;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   if (s.T == 0) return MOE_OK;
+  clear_stale_error();
   return rc_of(moe::launch_dispatch(s, topk_idx, topk_w, x, demand, counts, offsets, row_of, src_of, x_perm, ws,
                                     stream));
 }
@@ -183,6 +199,7 @@ int moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *off
   }
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   if (s.T == 0) return MOE_OK;
+  clear_stale_error();
   return rc_of(moe::launch_expert_ffn(s, x_perm, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out,
                                       ws, stream));
 }
@@ -194,6 +211,7 @@ int moe_combine(const moe_config *cfg, const void *y_perm, const int32_t *row_of
   if (rc) return rc;
   if (!y_perm || !row_of || !topk_w || !y) return MOE_ERR_ARG;
   if (s.T == 0) return MOE_OK;
+  clear_stale_error();
   return rc_of(moe::launch_combine(s, y_perm, row_of, topk_w, residual, shared_out, y, stream));
 }
 
@@ -234,6 +252,7 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
   void *o = s.latent ? pick(io->o, L.o) : nullptr;
   void *scratch = base + L.scratch;
 
+  clear_stale_error();
   const void *xin = x;  // router and expert input
   if (s.latent) {
     if ((rc = rc_of(moe::launch_dense(s.act_f32, x, w->w_in, z, nullptr, s.T, s.H * s.dh, s.d, scratch, stream))))

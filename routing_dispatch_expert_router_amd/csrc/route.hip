@@ -356,7 +356,7 @@ size_t route_ws_bytes(const Shape &s) {
   return b;
 }
 
-#define LAUNCH_CHECK() do { if (hipGetLastError() != hipSuccess) return -4; } while (0)
+#define LAUNCH_CHECK() do { if (int rc_ = launch_status("route")) return rc_; } while (0)
 
 template <typename TIN, typename TW, int NF, int NPL, int MW>
 static void launch_logits(const Shape &s, const RouteGeom &g, const void *x, const void *w, float *part,

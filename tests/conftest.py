@@ -6,6 +6,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+# a failed launch names itself and HIP's reason on stderr
+os.environ.setdefault("MOE_DEBUG", "1")
 
 
 def pytest_configure(config):

@@ -148,3 +148,11 @@ def test_config_struct_layout_matches_header():
     fields = re.findall(r"int32_t\s+([^;]+);", body)
     names = [n.strip() for f in fields for n in f.split(",")]
     assert names == moe.CONFIG_FIELDS
+
+
+def test_one_hip_runtime_in_process():
+    """libmoe.so and torch share one HIP runtime (two copies do not share the device)."""
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read()
+    libs = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(libs) == 1, libs
