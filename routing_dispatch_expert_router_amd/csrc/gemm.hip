@@ -408,7 +408,15 @@ static int run_gemm_one(GemmArgs a, int tile, int32_t *prefix, hipStream_t st) {
   } else {
     switch (tile) {
       case TILE_256x256_W8: return run_gemm_t<TE, EPI, 256, 256, 2, 4, 8, 2, 2, true>(a, prefix, st);
-      case TILE_128x128_W8: return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 2, true>(a, prefix, st);
+      case TILE_128x128_W8:
+        // the down projection (long K, few row tiles per weight tile) keeps a
+        // third weight chunk in flight; measured: -27 % on a tail launch of
+        // a few short groups, -6 % on 160 experts of ~280 rows; no gain for
+        // the gate/up launch, which streams at HBM rate
+        if constexpr (EPI == EPI_PLAIN || EPI == EPI_RESID)
+          return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 3, true>(a, prefix, st);
+        else
+          return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 2, true>(a, prefix, st);
       default: return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 2>(a, prefix, st);
     }
   }
