@@ -117,6 +117,32 @@ __global__ __launch_bounds__(1024) void gemm_prep_kernel(const int32_t *__restri
 // every lane fetches the global chunk that belongs in its slot.  Slots are
 // XOR-swizzled within a row so the 16 rows one ds_read_b128 touches fall in
 // distinct banks.
+// Four consecutive elements of a row as one access (the caller keeps them
+// inside the row and 8-byte (bf16) / 16-byte (fp32) aligned).
+template <typename TE> struct Quad;
+template <> struct Quad<uint16_t> {
+  __device__ __forceinline__ static void load(const uint16_t *p, float o[4]) {
+    const uint2 u = *(const uint2 *)p;
+    o[0] = bf16_to_f32((uint16_t)(u.x & 0xFFFFu)); o[1] = bf16_to_f32((uint16_t)(u.x >> 16));
+    o[2] = bf16_to_f32((uint16_t)(u.y & 0xFFFFu)); o[3] = bf16_to_f32((uint16_t)(u.y >> 16));
+  }
+  __device__ __forceinline__ static void store(uint16_t *p, const float o[4]) {
+    uint2 u;
+    u.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+    u.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+    *(uint2 *)p = u;
+  }
+};
+template <> struct Quad<float> {
+  __device__ __forceinline__ static void load(const float *p, float o[4]) {
+    const float4 u = *(const float4 *)p;
+    o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w;
+  }
+  __device__ __forceinline__ static void store(float *p, const float o[4]) {
+    *(float4 *)p = make_float4(o[0], o[1], o[2], o[3]);
+  }
+};
+
 template <int KS>
 __device__ __forceinline__ int swz(int row, int q) {
   static_assert(KS == 8, "128-byte k-chunks");
@@ -264,7 +290,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
 #pragma unroll
     for (int i = 0; i < NL; ++i)
 #pragma unroll
-      for (int f = 0; f < NF; ++f) acc[i][f] = mma16(fa[i], fb[f], acc[i][f], TE());
+      for (int f = 0; f < NF; ++f) acc[i][f] = mma16(fb[f], fa[i], acc[i][f], TE());
   };
   // scheduling hint (SG): interleave the LDS reads of the next k-step with the
   // MFMAs of the current one
@@ -333,35 +359,47 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   else if (live > 0) pipeline(std::integral_constant<int, (MF >= 4 ? MF / 4 : MF)>{});
   else pipeline(std::integral_constant<int, 0>{});
 
-  // epilogue: acc[i][f][v] = C[wm*WM + i*16 + 4*cq + v][n-fragment f, column l16]
+  // epilogue.  The MFMAs take the B fragment as their first operand, so they
+  // produce C^T blocks: acc[i][f][v] = C[row wm*WM + i*16 + l16][column
+  // (n-fragment f) + 4*cq + v], four consecutive columns of one row per lane,
+  // written (and, for the residual, read) as one 8-byte (bf16) or 16-byte
+  // (fp32) access.  Every N here is a multiple of 64, so a quad is either
+  // wholly inside N or wholly outside.
   const TE *R = (EPI == EPI_RESID) ? (const TE *)p.res + (size_t)r0 * p.ldres : nullptr;
 #pragma unroll
-  for (int i = 0; i < MF; ++i)
+  for (int i = 0; i < MF; ++i) {
+    const int row = m0 + wm * WM + i * 16 + l16;
+    if (row >= M) continue;
+    if (EPI == EPI_SWIGLU) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = m0 + wm * WM + i * 16 + 4 * cq + v;
-      if (row >= M) continue;
-      if (EPI == EPI_SWIGLU) {
+      for (int f = 0; f < NF / 2; ++f) {
+        const int col = tn * HB + wn * (HB / WGN) + f * 16 + 4 * cq;
+        if (col >= N) continue;
+        float h[4];
 #pragma unroll
-        for (int f = 0; f < NF / 2; ++f) {
-          const int col = tn * HB + wn * (HB / WGN) + f * 16 + l16;
-          if (col >= N) continue;
+        for (int v = 0; v < 4; ++v) {
           const float gt = acc[i][f][v], up = acc[i][f + NF / 2][v];
-          const float h = gt / (1.0f + __expf(-gt)) * up;
-          C[(size_t)row * ldc + col] = Elem<TE>::from_f32(h);
+          h[v] = gt / (1.0f + __expf(-gt)) * up;
         }
-      } else {
+        Quad<TE>::store(C + (size_t)row * ldc + col, h);
+      }
+    } else {
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const int col = tn * BN_ + wn * WN + f * 16 + l16;
-          if (col >= N) continue;
-          float o = acc[i][f][v];
-          if (EPI == EPI_RELU) o = fmaxf(o, 0.0f);
-          if (EPI == EPI_RESID) o += Elem<TE>::to_f32(R[(size_t)row * p.ldres + col]);
-          C[(size_t)row * ldc + col] = Elem<TE>::from_f32(o);
+      for (int f = 0; f < NF; ++f) {
+        const int col = tn * BN_ + wn * WN + f * 16 + 4 * cq;
+        if (col >= N) continue;
+        float o[4], r[4] = {0.f, 0.f, 0.f, 0.f};
+        if (EPI == EPI_RESID) Quad<TE>::load(R + (size_t)row * p.ldres + col, r);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          o[v] = acc[i][f][v];
+          if (EPI == EPI_RELU) o[v] = fmaxf(o[v], 0.0f);
+          if (EPI == EPI_RESID) o[v] += r[v];
         }
+        Quad<TE>::store(C + (size_t)row * ldc + col, o);
       }
     }
+  }
 }
 
 // ---------------------------------------------------------------- host
