@@ -8,12 +8,14 @@ projections for the multi-head workload) over one batch of synthetic tokens
 already resident in HBM.  K steps run back to back on one stream between two
 device synchronisations; value = T * K / elapsed.
 
-Per-stage times come from HIP events recorded on the stream the kernels run
-on, around separate calls of moe_route / moe_dispatch / moe_expert_ffn /
+The layer runs without an x_perm buffer: dispatch moves indices only and the
+expert FFN gathers each row from x inside its GEMM operand loads.  Per-stage
+times come from HIP events recorded on the stream the kernels run on, around
+separate calls of moe_route / moe_dispatch / moe_expert_ffn_gather /
 moe_combine on the same data.  The roofline object is for the grouped GEMM of
-the expert FFN (its two launches: gate/up with the SwiGLU epilogue, then
-down), the dominant kernel: achieved = algorithmic FLOPs of the kept rows and
-shared experts / measured stage time, against the bf16 dense MFMA peak.
+the expert FFN (its gate/up launches with the SwiGLU epilogue, then its down
+launches), the dominant kernel: achieved = algorithmic FLOPs of the kept rows
+and shared experts / measured stage time, against the bf16 dense MFMA peak.
 The CPU baseline is the float64 numpy oracle on a bounded sample of the same
 workload (routing of every token, expert FFN and combine for a token sample).
 """
@@ -62,7 +64,8 @@ def algorithmic(cfg, R):
     m = 3 if cfg.act == 1 else 2
     out = {}
     out["route_bytes"] = T * H * dh * a + E * dh * r + T * K * 8
-    out["dispatch_bytes"] = T * H * dh * a + R * dh * a + T * K * 8 + R * 4 + (T * K * 4 if cfg.drop == 2 else 0)
+    # dispatch moves indices only: the expert FFN gathers its rows from x itself
+    out["dispatch_bytes"] = T * K * 8 + R * 4 + (T * K * 4 if cfg.drop == 2 else 0)
     out["combine_bytes"] = R * dh * a + T * K * 8 + T * H * dh * a * (1 + (cfg.residual and not cfg.latent_proj)
                                                                         + (cfg.n_shared > 0))
     out["ffn_flops"] = 2 * R * dh * m * cfg.d_ff + 2 * T * d * m * cfg.n_shared * cfg.d_ff
@@ -147,7 +150,6 @@ def main():
               offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
               row_of=torch.empty(T, K, dtype=torch.int32, device="cuda"),
               src_of=torch.empty(Rm, dtype=torch.int32, device="cuda"),
-              x_perm=torch.empty(Rm, dh, dtype=adt, device="cuda"),
               y_perm=torch.empty(Rm, dh, dtype=adt, device="cuda"),
               shared_out=torch.empty(T, cfg.d_model, dtype=adt, device="cuda") if cfg.n_shared else None,
               z=torch.empty(T, cfg.d_latent, dtype=adt, device="cuda") if cfg.latent_proj else None,
@@ -194,12 +196,13 @@ def main():
     st = {}
     st["route"] = timed(lambda: moe.moe_route(cfg, xin, W["w_router"], W["router_bias"], None,
                                               moe.MOE_LOGITS_COMPUTE, io["topk_idx"], io["topk_w"], None, ws))
-    st["dispatch"] = timed(lambda: moe.moe_dispatch(cfg, io["topk_idx"], io["topk_w"], xin, io["demand"],
+    st["dispatch"] = timed(lambda: moe.moe_dispatch(cfg, io["topk_idx"], io["topk_w"], None, io["demand"],
                                                     io["counts"], io["offsets"], io["row_of"], io["src_of"],
-                                                    io["x_perm"], ws))
-    st["expert_ffn"] = timed(lambda: moe.moe_expert_ffn(cfg, io["x_perm"], io["offsets"], W["w1"], W["w3"],
-                                                        W["w2"], io["y_perm"], x if cfg.n_shared else None,
-                                                        W["ws1"], W["ws3"], W["ws2"], io["shared_out"], ws))
+                                                    None, ws))
+    st["expert_ffn"] = timed(lambda: moe.moe_expert_ffn_gather(cfg, xin, io["src_of"], io["offsets"], W["w1"],
+                                                               W["w3"], W["w2"], io["y_perm"],
+                                                               x if cfg.n_shared else None, W["ws1"], W["ws3"],
+                                                               W["ws2"], io["shared_out"], ws))
     st["combine"] = timed(lambda: moe.moe_combine(cfg, io["y_perm"], io["row_of"], io["topk_w"],
                                                   x if (cfg.residual and not cfg.latent_proj) else None,
                                                   io["shared_out"], io["o"] if cfg.latent_proj else y))
@@ -235,9 +238,9 @@ def main():
                    "n_heads": cfg.n_heads, "d_ff": cfg.d_ff, "n_shared": cfg.n_shared, "kept_rows": R,
                    "act": "swiglu" if cfg.act == 1 else "relu",
                    "drop": ["none", "capacity", "affinity"][cfg.drop], "parallelism": "single GPU"},
-        "roofline": {"kernel": "grouped_gemm_kernel, expert FFN (SwiGLU gate/up launch + down launch)",
+        "roofline": {"kernel": "grouped_gemm_kernel, expert FFN (gate/up and down launches, rows gathered from x)",
                      "bound": "mfma", "achieved": ffn_tf, "peak": peak, "unit": "TFLOP/s", "frac": ffn_tf / peak,
-                     "traffic": measured_traffic(cfg), "traffic_unit": "bytes per call (2 launches)",
+                     "traffic": measured_traffic(cfg), "traffic_unit": "HBM bytes per expert-FFN call (all its launches)",
                      "algorithmic_flops": alg["ffn_flops"]},
         "stages": stages,
         "device": dev_name,

@@ -35,7 +35,8 @@
  *     earlier, unrelated HIP call left there is neither reported nor kept.
  *   - Row counts that depend on routing (R = kept assignments) are never read
  *     back to the host: buffers sized by R use moe_rows_upper_bound(), and
- *     the true R is offsets[E] on the device.
+ *     the true R is offsets[E] on the device.  When that bound is 0 (capacity
+ *     0), the buffers sized by it may be NULL.
  *   - "act" tensors (activations and expert weights) have cfg->act_dtype;
  *     the router weight has cfg->router_dtype; gates, logits, bias and the
  *     aux loss are float32; indices are int32.
@@ -125,7 +126,9 @@ typedef struct moe_layer_io {
   int32_t *src_of;          /* [R_max] flat assignment (t*K + j) held by each row */
   float *aux_loss;          /* [1] GShard auxiliary loss (H == 1 only) */
   void *z;                  /* [T, H*d_head] act: latent (latent_proj only) */
-  void *x_perm;             /* [R_max, d_head] act: expert-contiguous expert inputs */
+  void *x_perm;             /* [R_max, d_head] act: expert-contiguous expert inputs; if
+                               NULL, none is written and the expert FFN reads its rows
+                               from x (or z) directly (moe_expert_ffn_gather) */
   void *y_perm;             /* [R_max, d_head] act: expert outputs, same row order */
   void *shared_out;         /* [T, d_model] act: sum of the shared experts (n_shared > 0) */
   void *o;                  /* [T, H*d_head] act: combined head outputs (latent_proj only) */
@@ -192,7 +195,8 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router, const 
  *   src_of    [R_max] out: rows [0, R) hold the flat index of their assignment;
  *             rows of expert e are [offsets[e], offsets[e+1]) in ascending a
  *   x_perm    [R_max, d_head] act out: row r = columns [h*d_head, (h+1)*d_head)
- *             of x[src_of[r] / K], h = e(src_of[r]) / E_h (bitwise copy)
+ *             of x[src_of[r] / K], h = e(src_of[r]) / E_h (bitwise copy); may be
+ *             NULL: then nothing is copied and x is not read (may be NULL too)
  * Results are deterministic (integer work only, no order-dependent atomics).
  */
 int moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, const float *topk_w,
@@ -219,6 +223,27 @@ int moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *off
                    void *shared_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_expert_ffn_gather -- moe_expert_ffn with the token-to-expert copy fused
+ * into the expert kernel's operand loads: no x_perm is read or written.
+ * ["多头 LatentMoE 与 Head Parallel", 方法论 item 4 (IO-aware kernels: the
+ * token-to-expert transfer is batched and fused with the expert computation,
+ * cutting memory copies)]
+ *
+ *   x        [T, H*d_head] act: the expert inputs moe_dispatch was given (x, or z)
+ *   src_of   [R_max], offsets [E+1] (from moe_dispatch, whose x_perm may be NULL)
+ * Row r of expert e is read from x[src_of[r] / K], columns [h*d_head,
+ * (h+1)*d_head), h = e / E_h: the row x_perm[r] would hold.  y_perm and
+ * shared_out are bitwise those of moe_expert_ffn on that x_perm.  Other
+ * arguments and errors as for moe_expert_ffn; additionally T * H * d_head
+ * must be below 2^31 (MOE_ERR_UNSUPPORTED otherwise).
+ */
+int moe_expert_ffn_gather(const moe_config *cfg, const void *x, const int32_t *src_of,
+                          const int32_t *offsets, const void *w1, const void *w3, const void *w2,
+                          void *y_perm, const void *x_shared, const void *ws1, const void *ws3,
+                          const void *ws2, void *shared_out, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
  * moe_combine -- gate-weighted sum of the expert outputs, plus shared output and residual.
  * ["MoE技术演进", "GShard" item 3 (y_s = sum_e G_{s,e} FFN_e(x_s)); "DeepSeekMoE"
  * items 1-2 (+ u_t and the ungated shared experts)]
@@ -239,7 +264,8 @@ int moe_combine(const moe_config *cfg, const void *y_perm, const int32_t *row_of
 /*
  * moe_layer_fwd -- the whole layer: [z = x W_in^T] -> route -> dispatch ->
  * expert FFN (+ shared) -> combine -> [y = o W_out^T + x].  One stream, no host
- * synchronisation.  x [T, d_model] act in, y [T, d_model] act out (distinct
+ * synchronisation.  Without io->x_perm the expert FFN gathers its rows from the
+ * expert input directly (as moe_expert_ffn_gather); y is the same either way.  x [T, d_model] act in, y [T, d_model] act out (distinct
  * from x).  `io` may be NULL.  Sources as for the four calls above, and
  * "多头 LatentMoE 与 Head Parallel", 方法论 item 1 (latent routing space).
  */

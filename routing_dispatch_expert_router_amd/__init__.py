@@ -36,7 +36,7 @@ CONFIG_FIELDS = ["T", "d_model", "n_heads", "d_head", "n_experts", "top_k", "n_g
 
 # exported symbols, as declared in include/moe.h
 SYMBOLS = ["moe_workspace_bytes", "moe_rows_upper_bound", "moe_status_str", "moe_check_config",
-           "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_fwd"]
+           "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd"]
 
 
 class MoeConfig(ctypes.Structure):
@@ -77,6 +77,7 @@ def _load():
         "moe_route": (I, [Z, P, P, P, P, I, P, P, P, P, S, P]),
         "moe_dispatch": (I, [Z, P, P, P, P, P, P, P, P, P, P, S, P]),
         "moe_expert_ffn": (I, [Z, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
+        "moe_expert_ffn_gather": (I, [Z, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
         "moe_combine": (I, [Z, P, P, P, P, P, P, P]),
         "moe_layer_fwd": (I, [Z, ctypes.POINTER(MoeWeights), P, P, ctypes.POINTER(MoeLayerIO), P, S, P]),
     }
@@ -167,6 +168,15 @@ def moe_expert_ffn(cfg, x_perm, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3,
     return _check(_lib.moe_expert_ffn(ctypes.byref(c), _p(x_perm), _p(offsets), _p(w1), _p(w3), _p(w2),
                                       _p(y_perm), _p(x_shared), _p(ws1), _p(ws3), _p(ws2), _p(shared_out),
                                       _p(ws), _nbytes(ws), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_expert_ffn_gather(cfg, x, src_of, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws,
+                          stream=None):
+    c = _c(cfg)
+    return _check(_lib.moe_expert_ffn_gather(ctypes.byref(c), _p(x), _p(src_of), _p(offsets), _p(w1), _p(w3),
+                                             _p(w2), _p(y_perm), _p(x_shared), _p(ws1), _p(ws3), _p(ws2),
+                                             _p(shared_out), _p(ws), _nbytes(ws), _stream(stream)),
+                  "moe_expert_ffn_gather")
 
 
 def moe_combine(cfg, y_perm, row_of, topk_w, residual, shared_out, y, stream=None):

@@ -33,6 +33,8 @@ enum { EPI_PLAIN = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_RESID = 3 };
 
 struct GemmArgs {
   const void *A; long lda;                    // routed: A rows indexed by offsets
+  const int32_t *gather;                      // routed A row r = A[gather[r] / gK] + (e / gEh) * gdh, or NULL
+  int gK, gEh, gdh;
   const void *B; const void *B2; long ldb; long bstride;
   void *C; long ldc;
   const int32_t *offsets;
@@ -184,11 +186,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   long lda, ldb, ldc;
   int M, N, K;
   int r0;
+  const int32_t *gat = nullptr;  // routed rows gathered from the expert input
   if (g < p.E) {
     r0 = p.offsets[g];
     M = p.offsets[g + 1] - r0;
     lda = p.lda; ldb = p.ldb; ldc = p.ldc; N = p.N; K = p.K;
     A = (const TE *)p.A;
+    if (p.gather) {
+      gat = p.gather;
+      A += (size_t)(g / p.gEh) * p.gdh;
+    }
     B = (const TE *)p.B + (size_t)g * p.bstride;
     B2 = p.B2 ? (const TE *)p.B2 + (size_t)g * p.bstride : nullptr;
     C = (TE *)p.C;
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   int wbeg;
   row_window(p.split, M, &wbeg, &M);
   r0 += wbeg;
-  A += (size_t)r0 * lda;
+  if (!gat) A += (size_t)r0 * lda;
   C += (size_t)r0 * ldc;
   // grouped raster inside the group: bands of GM m-tiles, n outer, m inner
   const int mt = (M + BM_ - 1) / BM_, nt = n_tiles<EPI, BN_>(N);
@@ -225,7 +232,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int s = i * NT + tid, row = s / KS, q = swz<KS>(row, s % KS);
-    oa[i] = (uint32_t)((size_t)min(m0 + row, M - 1) * lda + q * EPC);
+    const int ar = min(m0 + row, M - 1);
+    const size_t arow = gat ? (size_t)(gat[r0 + ar] / p.gK) : (size_t)ar;
+    oa[i] = (uint32_t)(arow * lda + q * EPC);
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
@@ -490,9 +499,9 @@ size_t ffn_ws_bytes(const Shape &s) {
 }
 
 template <typename TE>
-static int ffn_typed(const Shape &s, const void *x_perm, const int32_t *offsets, const void *w1, const void *w3,
-                     const void *w2, void *y_perm, const void *x_shared, const void *ws1, const void *ws3,
-                     const void *ws2, void *shared_out, void *ws, hipStream_t st) {
+static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets,
+                     const void *w1, const void *w3, const void *w2, void *y_perm, const void *x_shared,
+                     const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st) {
   const int esz = sizeof(TE);
   char *p = (char *)ws;
   TE *H = (TE *)p;
@@ -513,7 +522,8 @@ static int ffn_typed(const Shape &s, const void *x_perm, const int32_t *offsets,
 
   GemmArgs a{};
   // ---- GEMM 1: H = act(x_perm W1^T [, x_perm W3^T])
-  a.A = x_perm; a.lda = s.dh;
+  a.A = xin; a.lda = gather ? (long)s.H * s.dh : s.dh;
+  a.gather = gather; a.gK = s.K; a.gEh = s.Eh; a.gdh = s.dh;
   a.B = w1; a.B2 = glu ? w3 : nullptr; a.ldb = s.dh; a.bstride = (long)s.dff * s.dh;
   a.C = H; a.ldc = s.dff;
   a.offsets = offsets; a.E = s.E; a.N = s.dff; a.K = s.dh; a.Mr_bound = s.R_max;
@@ -540,12 +550,13 @@ static int ffn_typed(const Shape &s, const void *x_perm, const int32_t *offsets,
   return run_gemm<TE, EPI_PLAIN>(b, tile, pre2, st);
 }
 
-int launch_expert_ffn(const Shape &s, const void *x_perm, const int32_t *offsets, const void *w1, const void *w3,
-                      const void *w2, void *y_perm, const void *x_shared, const void *ws1, const void *ws3,
-                      const void *ws2, void *shared_out, void *ws, hipStream_t st) {
+int launch_expert_ffn(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets,
+                      const void *w1, const void *w3, const void *w2, void *y_perm, const void *x_shared,
+                      const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st) {
   if (s.act_f32)
-    return ffn_typed<float>(s, x_perm, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws, st);
-  return ffn_typed<uint16_t>(s, x_perm, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws, st);
+    return ffn_typed<float>(s, xin, gather, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws, st);
+  return ffn_typed<uint16_t>(s, xin, gather, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws,
+                             st);
 }
 
 size_t dense_ws_bytes() { return 256; }  // two tile prefixes of 3 ints

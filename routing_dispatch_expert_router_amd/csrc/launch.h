@@ -41,9 +41,12 @@ int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w
 
 // ---------------------------------------------------------------- grouped GEMM / expert FFN
 size_t ffn_ws_bytes(const Shape &s);
-int launch_expert_ffn(const Shape &s, const void *x_perm, const int32_t *offsets, const void *w1,
-                      const void *w3, const void *w2, void *y_perm, const void *x_shared, const void *ws1,
-                      const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st);
+// gather == NULL: `xin` is x_perm (row r of the routed operand is xin[r]);
+// else `xin` is the expert input x and row r is read from x[gather[r] / K]
+// at column offset (e / E_h) * d_head
+int launch_expert_ffn(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets,
+                      const void *w1, const void *w3, const void *w2, void *y_perm, const void *x_shared,
+                      const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st);
 // dense C[M,N] = A[M,K] B[N,K]^T (+ residual R[M,N]), act dtype, float32 accumulate
 size_t dense_ws_bytes();
 int launch_dense(bool f32, const void *A, const void *B, void *C, const void *residual, int M, int N, int K,

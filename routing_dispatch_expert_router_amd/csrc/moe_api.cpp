@@ -78,7 +78,7 @@ size_t scratch_bytes(const Shape &s) {
 
 // intermediates of moe_layer_fwd, in workspace order
 struct LayerBufs {
-  size_t topk_idx, topk_w, demand, counts, offsets, row_of, src_of, aux, z, x_perm, y_perm, shared, o, scratch, total;
+  size_t topk_idx, topk_w, demand, counts, offsets, row_of, src_of, aux, z, y_perm, shared, o, scratch, total;
 };
 
 LayerBufs layer_layout(const Shape &s) {
@@ -95,7 +95,6 @@ LayerBufs layer_layout(const Shape &s) {
   b.src_of = o; o += al((size_t)s.R_max * 4);
   b.aux = o; o += al(4);
   b.z = o; o += s.latent ? al((size_t)s.T * s.H * s.dh * esz) : 0;
-  b.x_perm = o; o += al((size_t)s.R_max * s.dh * esz);
   b.y_perm = o; o += al((size_t)s.R_max * s.dh * esz);
   b.shared = o; o += s.n_shared ? al((size_t)s.T * s.d * esz) : 0;
   b.o = o; o += s.latent ? al((size_t)s.T * s.H * s.dh * esz) : 0;
@@ -114,6 +113,9 @@ int check_ws(const Shape &s, const void *ws, size_t ws_bytes) {
 // calls of the caller; clear it before our first launch so that the checks
 // after each launch see only our own launches
 void clear_stale_error() { (void)hipGetLastError(); }
+
+// the gathered operand rows are addressed with 32-bit element offsets into x
+bool gather_supported(const Shape &s) { return (long)s.T * s.H * s.dh < (1L << 31); }
 
 int rc_of(int launcher_rc) {
   if (launcher_rc == -2) return MOE_ERR_UNSUPPORTED;
@@ -176,7 +178,8 @@ int moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, const float *to
   Shape s;
   int rc = make_shape(cfg, &s);
   if (rc) return rc;
-  if (!topk_idx || !x || !demand || !counts || !offsets || !row_of || !src_of || !x_perm) return MOE_ERR_ARG;
+  if (!topk_idx || !demand || !counts || !offsets || !row_of || (!src_of && s.R_max) || (x_perm && !x))
+    return MOE_ERR_ARG;
   if (s.drop == MOE_DROP_AFFINITY && !topk_w) return MOE_ERR_ARG;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   if (s.T == 0) return MOE_OK;
@@ -191,7 +194,7 @@ int moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *off
   Shape s;
   int rc = make_shape(cfg, &s);
   if (rc) return rc;
-  if (!x_perm || !offsets || !w1 || !w2 || !y_perm) return MOE_ERR_ARG;
+  if (((!x_perm || !y_perm) && s.R_max) || !offsets || !w1 || !w2) return MOE_ERR_ARG;
   if ((s.act == MOE_ACT_SWIGLU) != (w3 != nullptr)) return MOE_ERR_ARG;
   if (s.n_shared) {
     if (!x_shared || !ws1 || !ws2 || !shared_out) return MOE_ERR_ARG;
@@ -200,8 +203,29 @@ int moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *off
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   if (s.T == 0) return MOE_OK;
   clear_stale_error();
-  return rc_of(moe::launch_expert_ffn(s, x_perm, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out,
-                                      ws, stream));
+  return rc_of(moe::launch_expert_ffn(s, x_perm, nullptr, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2,
+                                      shared_out, ws, stream));
+}
+
+int moe_expert_ffn_gather(const moe_config *cfg, const void *x, const int32_t *src_of, const int32_t *offsets,
+                          const void *w1, const void *w3, const void *w2, void *y_perm, const void *x_shared,
+                          const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, &s);
+  if (rc) return rc;
+  if (((!x || !src_of || !y_perm) && s.R_max) || !offsets || !w1 || !w2) return MOE_ERR_ARG;
+  if ((s.act == MOE_ACT_SWIGLU) != (w3 != nullptr)) return MOE_ERR_ARG;
+  if (s.n_shared) {
+    if (!x_shared || !ws1 || !ws2 || !shared_out) return MOE_ERR_ARG;
+    if ((s.act == MOE_ACT_SWIGLU) != (ws3 != nullptr)) return MOE_ERR_ARG;
+  }
+  if (!gather_supported(s)) return MOE_ERR_UNSUPPORTED;
+  if ((rc = check_ws(s, ws, ws_bytes))) return rc;
+  if (s.T == 0) return MOE_OK;
+  clear_stale_error();
+  return rc_of(moe::launch_expert_ffn(s, x, src_of, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2,
+                                      shared_out, ws, stream));
 }
 
 int moe_combine(const moe_config *cfg, const void *y_perm, const int32_t *row_of, const float *topk_w,
@@ -232,6 +256,7 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
   if (s.n_shared && (!w->ws1 || !w->ws2 || ((s.act == MOE_ACT_SWIGLU) != (w->ws3 != nullptr)))) return MOE_ERR_ARG;
   if (s.latent && (!w->w_in || !w->w_out)) return MOE_ERR_ARG;
   if (io->aux_loss && s.H != 1) return MOE_ERR_UNSUPPORTED;
+  if (!io->x_perm && !gather_supported(s)) return MOE_ERR_UNSUPPORTED;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   if (s.T == 0) return MOE_OK;
 
@@ -245,7 +270,7 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
   int32_t *offsets = (int32_t *)pick(io->offsets, L.offsets);
   int32_t *row_of = (int32_t *)pick(io->row_of, L.row_of);
   int32_t *src_of = (int32_t *)pick(io->src_of, L.src_of);
-  void *x_perm = pick(io->x_perm, L.x_perm);
+  void *x_perm = io->x_perm;  // NULL: the expert FFN gathers rows from xin
   void *y_perm = pick(io->y_perm, L.y_perm);
   void *shared = s.n_shared ? pick(io->shared_out, L.shared) : nullptr;
   void *z = s.latent ? pick(io->z, L.z) : nullptr;
@@ -265,8 +290,9 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
   if ((rc = rc_of(moe::launch_dispatch(s, topk_idx, topk_w, xin, demand, counts, offsets, row_of, src_of, x_perm,
                                        scratch, stream))))
     return rc;
-  if ((rc = rc_of(moe::launch_expert_ffn(s, x_perm, offsets, w->w1, w->w3, w->w2, y_perm, x, w->ws1, w->ws3, w->ws2,
-                                         shared, scratch, stream))))
+  if ((rc = rc_of(moe::launch_expert_ffn(s, x_perm ? x_perm : xin, x_perm ? nullptr : src_of, offsets, w->w1,
+                                         w->w3, w->w2, y_perm, x, w->ws1, w->ws3, w->ws2, shared, scratch,
+                                         stream))))
     return rc;
   const void *res = (!s.latent && s.residual) ? x : nullptr;
   if ((rc = rc_of(moe::launch_combine(s, y_perm, row_of, topk_w, res, shared, s.latent ? o : y, stream))))

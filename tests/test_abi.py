@@ -23,7 +23,7 @@ def declared():
 
 def test_header_declares_the_five_calls_and_helpers():
     names = declared()
-    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_fwd",
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd",
               "moe_workspace_bytes", "moe_rows_upper_bound", "moe_status_str", "moe_check_config"):
         assert n in names
     assert sorted(moe.SYMBOLS) == names
@@ -130,6 +130,14 @@ def test_calls_reject_bad_arguments_before_launching():
                               fake, 1 << 40, None) == moe.MOE_ERR_ARG
     assert lib.moe_expert_ffn(ctypes.byref(c), fake, fake, fake, fake, fake, fake, None, fake, fake, fake, fake,
                               fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    # gather FFN: missing x or src_of
+    assert lib.moe_expert_ffn_gather(ctypes.byref(c), None, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                     fake, fake, fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    assert lib.moe_expert_ffn_gather(ctypes.byref(c), fake, None, fake, fake, fake, fake, fake, fake, fake, fake,
+                                     fake, fake, fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    # dispatch: an x_perm to fill needs x
+    assert lib.moe_dispatch(ctypes.byref(c), fake, fake, None, fake, fake, fake, fake, fake, fake, fake, 1 << 40,
+                            None) == moe.MOE_ERR_ARG
     # combine: missing outputs
     assert lib.moe_combine(ctypes.byref(c), fake, fake, fake, None, None, None, None) == moe.MOE_ERR_ARG
     # layer: y aliasing x, missing weights

@@ -22,7 +22,7 @@ FULL = CONFIGS[1:]
 SAMPLE = 24
 
 
-def _run(cfg, inp, logits_load):
+def _run(cfg, inp, logits_load, with_xperm=True):
     T, K, E = cfg.T, cfg.k_total, cfg.n_experts
     Rm = moe.moe_rows_upper_bound(cfg)
     adt = torch.bfloat16 if cfg.act_dtype == 1 else torch.float32
@@ -33,7 +33,7 @@ def _run(cfg, inp, logits_load):
               offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
               row_of=torch.empty(T, K, dtype=torch.int32, device="cuda"),
               src_of=torch.empty(Rm, dtype=torch.int32, device="cuda"),
-              x_perm=torch.empty(Rm, cfg.d_head, dtype=adt, device="cuda"),
+              x_perm=torch.empty(Rm, cfg.d_head, dtype=adt, device="cuda") if with_xperm else None,
               z=torch.empty(T, cfg.d_latent, dtype=adt, device="cuda") if cfg.latent_proj else None)
     if logits_load is not None:
         io["logits"] = dev(logits_load)
@@ -118,3 +118,19 @@ def test_fullsize_free_running_routing(cfg):
     log(f"  max|dl| {err:.3g} (max|l| {lmax:.3g}); tokens routed differently: {len(diff)}")
     assert err <= 1e-5 * lmax
     assert np.all(margin[diff] <= 4 * err), "routing differs at a token that is not a near-tie"
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
+def test_fullsize_gather_equals_xperm_path(cfg):
+    """Without x_perm the expert FFN gathers its rows inside the GEMM: the layer
+    output is bitwise that of the copy path (the path the benchmark times)."""
+    log(f"full-size gather vs x_perm {cfg.name}")
+    inp = cached_inputs(cfg)
+    y1, io1, _ = _run(cfg, inp, None, with_xperm=True)
+    y2, io2, _ = _run(cfg, inp, None, with_xperm=False)
+    for k in ("topk_idx", "offsets", "row_of"):
+        assert torch.equal(io1[k], io2[k])
+    R = int(io1["offsets"][-1].item())
+    assert torch.equal(io1["src_of"][:R], io2["src_of"][:R])  # rows past R are not written
+    b = (lambda t: t.view(torch.int16)) if y1.dtype == torch.bfloat16 else (lambda t: t.view(torch.int32))
+    assert torch.equal(b(y1), b(y2))
