@@ -45,7 +45,8 @@ struct GemmArgs {
   int Mx, Nx, Kx, has_x;
   long Mr_bound;                              // upper bound on the routed rows (sum over experts)
   const void *res; long ldres;                // EPI_RESID: added to the extra group's output
-  const int32_t *prefix;                      // [G+1] tile prefix
+  const int32_t *prefix;                      // [G+1] tile prefix, or NULL: E == 0 and fixed_tiles tiles
+  int fixed_tiles;
   int G;
   int split;  // 0: all rows of a group; 1: rows [0, cut); 2: rows [cut, M) (see row_window)
 };
@@ -68,13 +69,23 @@ template <int EPI, int BN_> __host__ __device__ inline int n_tiles(int N) {
   return EPI == EPI_SWIGLU ? (N + BN_ / 2 - 1) / (BN_ / 2) : (N + BN_ - 1) / BN_;
 }
 
-// tile prefix over groups: tiles_g = ceil(M_g / BM) * n_tiles(N_g)
-template <int EPI, int BM_, int BN_>
-__global__ __launch_bounds__(1024) void gemm_prep_kernel(const int32_t *__restrict__ offsets, int E, int N,
-                                                         int has_x, int Mx, int Nx, int split,
-                                                         int32_t *__restrict__ prefix) {
+// Tile prefixes over groups for up to four launches at once (one block per
+// launch): tiles_g = ceil(rows of g in the launch's window / bm) * nt_g.
+struct PrepCfg {
+  int bm, split, nt, ntx;  // row tile, row window, n-tiles of a routed / the extra group
+};
+struct PrepArgs {
+  PrepCfg c[4];
+  const int32_t *offsets;
+  int E, has_x, Mx;
+  int32_t *prefix;  // [launch][E + 2]
+};
+
+__global__ __launch_bounds__(1024) void gemm_prep_kernel(PrepArgs a) {
   __shared__ int s[1024];
-  const int G = E + has_x;
+  const PrepCfg c = a.c[blockIdx.x];
+  int32_t *prefix = a.prefix + (size_t)blockIdx.x * (a.E + 2);
+  const int E = a.E, G = E + a.has_x;
   const int tid = threadIdx.x;
   const int per = (G + 1023) / 1024;
   int loc[2] = {0, 0};
@@ -83,11 +94,10 @@ __global__ __launch_bounds__(1024) void gemm_prep_kernel(const int32_t *__restri
     int g = tid * per + i;
     int v = 0;
     if (g < G) {
-      int M = (g < E) ? offsets[g + 1] - offsets[g] : Mx;
+      int M = (g < E) ? a.offsets[g + 1] - a.offsets[g] : a.Mx;
       int beg;
-      row_window(split, M, &beg, &M);
-      int nn = (g < E) ? N : Nx;
-      v = (M + BM_ - 1) / BM_ * n_tiles<EPI, BN_>(nn);
+      row_window(c.split, M, &beg, &M);
+      v = (M + c.bm - 1) / c.bm * ((g < E) ? c.nt : c.ntx);
     }
     loc[i] = v;
     sum += v;
@@ -166,20 +176,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   u32x4 *sA = smem;               // [STA][SA]
   u32x4 *sB = smem + STA * SA;    // [STB][SB]
 
-  const int total = p.prefix[p.G];
+  // tile count: the device-built prefix, or (no routed groups: a plain
+  // product whose size the host knows) the fixed count
+  const int total = p.prefix ? p.prefix[p.G] : p.fixed_tiles;
   const int b = blockIdx.x;
   if (b >= total) return;
   // blocks go round-robin to the 8 XCDs; give each XCD a contiguous run of
   // tiles so tiles sharing operands share an L2
   const int q8 = total >> 3;
   const int lt = (b < 8 * q8) ? (b & 7) * q8 + (b >> 3) : b;
-  int lo = 0, hi = p.G - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (p.prefix[mid] <= lt) lo = mid; else hi = mid - 1;
+  int g = 0, local = lt;
+  if (p.prefix) {
+    int lo = 0, hi = p.G - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (p.prefix[mid] <= lt) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    local = lt - p.prefix[g];
   }
-  const int g = lo;
-  const int local = lt - p.prefix[g];
 
   const TE *A, *B, *B2;
   TE *C;
@@ -423,17 +438,17 @@ static long max_tiles(long rows_bound, int groups, int bm, int ntiles) {
   return ((rows_bound + bm - 1) / bm + groups) * ntiles;
 }
 
+// The kernel launch of one tile shape.  a.prefix: the device tile prefix
+// (routed groups), or NULL with a.fixed_tiles set (a plain product).
 template <typename TE, int EPI, int BM_, int BN_, int WGM, int WGN, int KS, int STA, int STB, bool SG = false>
-static int run_gemm_t(GemmArgs a, int32_t *prefix, hipStream_t st) {
-  a.prefix = prefix;
-  hipLaunchKernelGGL((gemm_prep_kernel<EPI, BM_, BN_>), dim3(1), dim3(1024), 0, st, a.offsets, a.E, a.N, a.has_x,
-                     a.Mx, a.Nx, a.split, prefix);
-  if (int rc = launch_status("gemm tile prefix")) return rc;
+static int run_gemm_t(GemmArgs a, hipStream_t st) {
   // grid: an upper bound of the tile count; blocks past the device-built
   // prefix total exit at once.  A tail launch holds at most one tile row per
   // group.
   long grid;
-  if (a.split == 2)
+  if (!a.prefix)
+    grid = a.fixed_tiles;
+  else if (a.split == 2)
     grid = (long)a.E * n_tiles<EPI, BN_>(a.N) + (a.has_x ? n_tiles<EPI, BN_>(a.Nx) : 0);
   else
     grid = (a.E ? max_tiles(a.Mr_bound, a.E, BM_, n_tiles<EPI, BN_>(a.N)) : 0) +
@@ -444,47 +459,55 @@ static int run_gemm_t(GemmArgs a, int32_t *prefix, hipStream_t st) {
   static_assert(lds <= 160 * 1024, "LDS per workgroup");
   hipLaunchKernelGGL((grouped_gemm_kernel<TE, EPI, BM_, BN_, WGM, WGN, KS, STA, STB, SG>), dim3(grid),
                      dim3(64 * WGM * WGN), lds, st, a);
-  if (int rc = launch_status("grouped gemm")) return rc;
-  return 0;
+  return launch_status("grouped gemm");
 }
 
 template <typename TE, int EPI>
-static int run_gemm_one(GemmArgs a, int tile, int32_t *prefix, hipStream_t st) {
+static int run_gemm_one(GemmArgs a, int tile, hipStream_t st) {
   if constexpr (sizeof(TE) == 4) {
-    return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 2>(a, prefix, st);
+    return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 2>(a, st);
   } else {
     switch (tile) {
-      case TILE_256x256_W8: return run_gemm_t<TE, EPI, 256, 256, 2, 4, 8, 2, 2, true>(a, prefix, st);
+      case TILE_256x256_W8: return run_gemm_t<TE, EPI, 256, 256, 2, 4, 8, 2, 2, true>(a, st);
       case TILE_128x128_W8:
         // the down projection (long K, few row tiles per weight tile) keeps a
         // third weight chunk in flight; measured: -27 % on a tail launch of
         // a few short groups, -6 % on 160 experts of ~280 rows; no gain for
         // the gate/up launch, which streams at HBM rate
         if constexpr (EPI == EPI_PLAIN || EPI == EPI_RESID)
-          return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 3, true>(a, prefix, st);
+          return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 3, true>(a, st);
         else
-          return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 2, true>(a, prefix, st);
-      default: return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 2>(a, prefix, st);
+          return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 2, true>(a, st);
+      default: return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 2>(a, st);
     }
   }
 }
 
-// 256-row tiles run as a head launch plus a tail launch of 128-row tiles;
-// prefix holds two tile prefixes of E + 2 entries
-template <typename TE, int EPI>
-static int run_gemm(GemmArgs a, int tile, int32_t *prefix, hipStream_t st) {
+// One launch of a product: its tile shape and row window.  256-row tiles run
+// as a head launch (split 1) plus a tail launch of 128-row tiles (split 2).
+struct Launch {
+  int tile, split;
+};
+static int plan_launches(int tile, Launch out[2]) {
   if (tile == TILE_256x256_W8) {
-    GemmArgs h = a, t = a;
-    h.split = 1;
-    t.split = 2;
-    int rc = run_gemm_one<TE, EPI>(h, TILE_256x256_W8, prefix, st);
-    if (rc) return rc;
-    return run_gemm_one<TE, EPI>(t, TILE_128x128_W8, prefix + (a.E + 2), st);
+    out[0] = {TILE_256x256_W8, 1};
+    out[1] = {TILE_128x128_W8, 2};
+    return 2;
   }
-  return run_gemm_one<TE, EPI>(a, tile, prefix, st);
+  out[0] = {tile, 0};
+  return 1;
+}
+static int tile_rows(int tile) { return tile == TILE_256x256_W8 ? 256 : 128; }
+static int tile_cols(int tile) { return tile == TILE_256x256_W8 ? 256 : 128; }
+static int col_tiles(int epi, int tile, int N) {
+  const int bn = tile_cols(tile);
+  return epi == EPI_SWIGLU ? (N + bn / 2 - 1) / (bn / 2) : (N + bn - 1) / bn;
+}
+static PrepCfg prep_cfg(int epi, const Launch &l, int N, int Nx) {
+  return PrepCfg{tile_rows(l.tile), l.split, col_tiles(epi, l.tile, N), col_tiles(epi, l.tile, Nx)};
 }
 
-// tile shape for a launch: large tiles when the groups are tall enough to fill them
+// tile shape for a product: large tiles when the groups are tall enough to fill them
 static int pick_tile(long rows, int groups) {
   long avg = groups > 0 ? rows / groups : rows;
   return avg >= 1024 ? TILE_256x256_W8 : TILE_128x128_W8;
@@ -494,7 +517,7 @@ size_t ffn_ws_bytes(const Shape &s) {
   const int esz = s.act_f32 ? 4 : 2;
   size_t b = align_up((size_t)s.R_max * s.dff * esz, 256);                       // hidden H
   if (s.n_shared) b += align_up((size_t)s.T * s.n_shared * s.dff * esz, 256);    // shared hidden
-  b += 2 * align_up((size_t)2 * (s.E + 2) * 4, 256);                              // tile prefixes
+  b += align_up((size_t)4 * (s.E + 2) * 4, 256);                                  // tile prefixes
   return b;
 }
 
@@ -512,13 +535,14 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
     Hs = (TE *)p;
     p += align_up((size_t)s.T * fs * esz, 256);
   }
-  int32_t *pre1 = (int32_t *)p;  // [2][E+2] per GEMM: head and tail launches
-  p += align_up((size_t)2 * (s.E + 2) * 4, 256);
-  int32_t *pre2 = (int32_t *)p;
+  int32_t *pre = (int32_t *)p;  // [launch][E+2]: tile prefixes of the (up to four) launches
   const bool glu = s.act == 1;
   const int has_x = s.n_shared ? 1 : 0;
   // f32 layers are parity-sized: the small tile is plenty
   const int tile = sizeof(TE) == 4 ? TILE_128x128 : pick_tile(s.R_max, s.E);
+  const int epi1 = glu ? EPI_SWIGLU : EPI_RELU;
+  Launch l[2];
+  const int nl = plan_launches(tile, l);
 
   GemmArgs a{};
   // ---- GEMM 1: H = act(x_perm W1^T [, x_perm W3^T])
@@ -533,8 +557,6 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
     a.Cx = Hs; a.ldcx = fs; a.Mx = s.T; a.Nx = fs; a.Kx = s.d;
   }
   a.G = s.E + has_x;
-  int rc = glu ? run_gemm<TE, EPI_SWIGLU>(a, tile, pre1, st) : run_gemm<TE, EPI_RELU>(a, tile, pre1, st);
-  if (rc) return rc;
   // ---- GEMM 2: y_perm = H W2^T ; shared_out = Hs Ws2^T
   GemmArgs b{};
   b.A = H; b.lda = s.dff;
@@ -547,7 +569,28 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
     b.Cx = shared_out; b.ldcx = s.d; b.Mx = s.T; b.Nx = s.d; b.Kx = fs;
   }
   b.G = s.E + has_x;
-  return run_gemm<TE, EPI_PLAIN>(b, tile, pre2, st);
+
+  // one launch builds the tile prefixes of every launch of both GEMMs
+  PrepArgs pa{};
+  pa.offsets = offsets; pa.E = s.E; pa.has_x = has_x; pa.Mx = s.T; pa.prefix = pre;
+  for (int i = 0; i < nl; ++i) {
+    pa.c[i] = prep_cfg(epi1, l[i], a.N, a.Nx);
+    pa.c[nl + i] = prep_cfg(EPI_PLAIN, l[i], b.N, b.Nx);
+  }
+  hipLaunchKernelGGL(gemm_prep_kernel, dim3(2 * nl), dim3(1024), 0, st, pa);
+  if (int rc = launch_status("gemm tile prefix")) return rc;
+  for (int i = 0; i < nl; ++i) {
+    a.split = l[i].split;
+    a.prefix = pre + (size_t)i * (s.E + 2);
+    int rc = glu ? run_gemm_one<TE, EPI_SWIGLU>(a, l[i].tile, st) : run_gemm_one<TE, EPI_RELU>(a, l[i].tile, st);
+    if (rc) return rc;
+  }
+  for (int i = 0; i < nl; ++i) {
+    b.split = l[i].split;
+    b.prefix = pre + (size_t)(nl + i) * (s.E + 2);
+    if (int rc = run_gemm_one<TE, EPI_PLAIN>(b, l[i].tile, st)) return rc;
+  }
+  return 0;
 }
 
 int launch_expert_ffn(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets,
@@ -559,20 +602,37 @@ int launch_expert_ffn(const Shape &s, const void *xin, const int32_t *gather, co
                              st);
 }
 
-size_t dense_ws_bytes() { return 256; }  // two tile prefixes of 3 ints
+size_t dense_ws_bytes() { return 0; }  // the tile counts come from the host
 
+// C[M, N] = A[M, K] B[N, K]^T (+ residual): one plain group, its tile count
+// known on the host (no prefix launch; a launch with no tiles is skipped)
 int launch_dense(bool f32, const void *A, const void *B, void *C, const void *residual, int M, int N, int K,
                  void *ws, hipStream_t st) {
+  (void)ws;
   GemmArgs a{};
   a.E = 0; a.has_x = 1; a.G = 1;
   a.Ax = A; a.ldax = K; a.Bx = B; a.ldbx = K; a.Cx = C; a.ldcx = N; a.Mx = M; a.Nx = N; a.Kx = K;
   a.res = residual; a.ldres = N;
-  int32_t *pre = (int32_t *)ws;
-  if (f32)
-    return residual ? run_gemm<float, EPI_RESID>(a, TILE_128x128, pre, st)
-                    : run_gemm<float, EPI_PLAIN>(a, TILE_128x128, pre, st);
-  const int tile = pick_tile(M, 1);
-  return residual ? run_gemm<uint16_t, EPI_RESID>(a, tile, pre, st) : run_gemm<uint16_t, EPI_PLAIN>(a, tile, pre, st);
+  const int epi = residual ? EPI_RESID : EPI_PLAIN;
+  const int tile = f32 ? TILE_128x128 : pick_tile(M, 1);
+  Launch l[2];
+  const int nl = plan_launches(tile, l);
+  for (int i = 0; i < nl; ++i) {
+    int beg, len;
+    row_window(l[i].split, M, &beg, &len);
+    a.split = l[i].split;
+    a.prefix = nullptr;
+    a.fixed_tiles = (len + tile_rows(l[i].tile) - 1) / tile_rows(l[i].tile) * col_tiles(epi, l[i].tile, N);
+    if (a.fixed_tiles == 0) continue;
+    int rc;
+    if (f32)
+      rc = residual ? run_gemm_one<float, EPI_RESID>(a, l[i].tile, st) : run_gemm_one<float, EPI_PLAIN>(a, l[i].tile, st);
+    else
+      rc = residual ? run_gemm_one<uint16_t, EPI_RESID>(a, l[i].tile, st)
+                    : run_gemm_one<uint16_t, EPI_PLAIN>(a, l[i].tile, st);
+    if (rc) return rc;
+  }
+  return 0;
 }
 
 }  // namespace moe
