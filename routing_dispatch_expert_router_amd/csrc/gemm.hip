@@ -513,6 +513,25 @@ static int pick_tile(long rows, int groups) {
   return avg >= 1024 ? TILE_256x256_W8 : TILE_128x128_W8;
 }
 
+// A plain product (one group, no routed rows: a.E == 0, a.has_x == 1): the
+// tile count of each launch is known on the host; launches with no tiles are
+// skipped.
+template <typename TE, int EPI>
+static int run_plain(GemmArgs a, int tile, hipStream_t st) {
+  Launch l[2];
+  const int nl = plan_launches(tile, l);
+  for (int i = 0; i < nl; ++i) {
+    int beg, len;
+    row_window(l[i].split, a.Mx, &beg, &len);
+    a.split = l[i].split;
+    a.prefix = nullptr;
+    a.fixed_tiles = (len + tile_rows(l[i].tile) - 1) / tile_rows(l[i].tile) * col_tiles(EPI, l[i].tile, a.Nx);
+    if (a.fixed_tiles == 0) continue;
+    if (int rc = run_gemm_one<TE, EPI>(a, l[i].tile, st)) return rc;
+  }
+  return 0;
+}
+
 size_t ffn_ws_bytes(const Shape &s) {
   const int esz = s.act_f32 ? 4 : 2;
   size_t b = align_up((size_t)s.R_max * s.dff * esz, 256);                       // hidden H
@@ -551,31 +570,21 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
   a.B = w1; a.B2 = glu ? w3 : nullptr; a.ldb = s.dh; a.bstride = (long)s.dff * s.dh;
   a.C = H; a.ldc = s.dff;
   a.offsets = offsets; a.E = s.E; a.N = s.dff; a.K = s.dh; a.Mr_bound = s.R_max;
-  a.has_x = has_x;
-  if (has_x) {
-    a.Ax = x_shared; a.ldax = s.d; a.Bx = ws1; a.Bx2 = glu ? ws3 : nullptr; a.ldbx = s.d;
-    a.Cx = Hs; a.ldcx = fs; a.Mx = s.T; a.Nx = fs; a.Kx = s.d;
-  }
-  a.G = s.E + has_x;
-  // ---- GEMM 2: y_perm = H W2^T ; shared_out = Hs Ws2^T
+  a.has_x = 0; a.G = s.E;
+  // ---- GEMM 2: y_perm = H W2^T
   GemmArgs b{};
   b.A = H; b.lda = s.dff;
   b.B = w2; b.B2 = nullptr; b.ldb = s.dff; b.bstride = (long)s.dh * s.dff;
   b.C = y_perm; b.ldc = s.dh;
   b.offsets = offsets; b.E = s.E; b.N = s.dh; b.K = s.dff; b.Mr_bound = s.R_max;
-  b.has_x = has_x;
-  if (has_x) {
-    b.Ax = Hs; b.ldax = fs; b.Bx = ws2; b.Bx2 = nullptr; b.ldbx = fs;
-    b.Cx = shared_out; b.ldcx = s.d; b.Mx = s.T; b.Nx = s.d; b.Kx = fs;
-  }
-  b.G = s.E + has_x;
+  b.has_x = 0; b.G = s.E;
 
-  // one launch builds the tile prefixes of every launch of both GEMMs
+  // one launch builds the tile prefixes of every routed launch of both GEMMs
   PrepArgs pa{};
-  pa.offsets = offsets; pa.E = s.E; pa.has_x = has_x; pa.Mx = s.T; pa.prefix = pre;
+  pa.offsets = offsets; pa.E = s.E; pa.has_x = 0; pa.Mx = 0; pa.prefix = pre;
   for (int i = 0; i < nl; ++i) {
-    pa.c[i] = prep_cfg(epi1, l[i], a.N, a.Nx);
-    pa.c[nl + i] = prep_cfg(EPI_PLAIN, l[i], b.N, b.Nx);
+    pa.c[i] = prep_cfg(epi1, l[i], a.N, 0);
+    pa.c[nl + i] = prep_cfg(EPI_PLAIN, l[i], b.N, 0);
   }
   hipLaunchKernelGGL(gemm_prep_kernel, dim3(2 * nl), dim3(1024), 0, st, pa);
   if (int rc = launch_status("gemm tile prefix")) return rc;
@@ -590,7 +599,25 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
     b.prefix = pre + (size_t)(nl + i) * (s.E + 2);
     if (int rc = run_gemm_one<TE, EPI_PLAIN>(b, l[i].tile, st)) return rc;
   }
-  return 0;
+  if (!has_x) return 0;
+
+  // ---- shared experts ("MoE技术演进", "DeepSeekMoE" item 2): a plain
+  // product over all T tokens, concatenated experts of width n_shared*d_ff,
+  // in its own launches with tiles sized for T rows (in the routed launch
+  // its tiles took the routed experts' small tile and ran at the end of the
+  // tile list on two XCDs, re-reading its operands many times)
+  const int tile_s = sizeof(TE) == 4 ? TILE_128x128 : pick_tile(s.T, 1);
+  GemmArgs sa{};
+  sa.E = 0; sa.has_x = 1; sa.G = 1;
+  sa.Ax = x_shared; sa.ldax = s.d; sa.Bx = ws1; sa.Bx2 = glu ? ws3 : nullptr; sa.ldbx = s.d;
+  sa.Cx = Hs; sa.ldcx = fs; sa.Mx = s.T; sa.Nx = fs; sa.Kx = s.d;
+  int rc = glu ? run_plain<TE, EPI_SWIGLU>(sa, tile_s, st) : run_plain<TE, EPI_RELU>(sa, tile_s, st);
+  if (rc) return rc;
+  GemmArgs sb{};
+  sb.E = 0; sb.has_x = 1; sb.G = 1;
+  sb.Ax = Hs; sb.ldax = fs; sb.Bx = ws2; sb.Bx2 = nullptr; sb.ldbx = fs;
+  sb.Cx = shared_out; sb.ldcx = s.d; sb.Mx = s.T; sb.Nx = s.d; sb.Kx = fs;
+  return run_plain<TE, EPI_PLAIN>(sb, tile_s, st);
 }
 
 int launch_expert_ffn(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets,
@@ -613,26 +640,10 @@ int launch_dense(bool f32, const void *A, const void *B, void *C, const void *re
   a.E = 0; a.has_x = 1; a.G = 1;
   a.Ax = A; a.ldax = K; a.Bx = B; a.ldbx = K; a.Cx = C; a.ldcx = N; a.Mx = M; a.Nx = N; a.Kx = K;
   a.res = residual; a.ldres = N;
-  const int epi = residual ? EPI_RESID : EPI_PLAIN;
-  const int tile = f32 ? TILE_128x128 : pick_tile(M, 1);
-  Launch l[2];
-  const int nl = plan_launches(tile, l);
-  for (int i = 0; i < nl; ++i) {
-    int beg, len;
-    row_window(l[i].split, M, &beg, &len);
-    a.split = l[i].split;
-    a.prefix = nullptr;
-    a.fixed_tiles = (len + tile_rows(l[i].tile) - 1) / tile_rows(l[i].tile) * col_tiles(epi, l[i].tile, N);
-    if (a.fixed_tiles == 0) continue;
-    int rc;
-    if (f32)
-      rc = residual ? run_gemm_one<float, EPI_RESID>(a, l[i].tile, st) : run_gemm_one<float, EPI_PLAIN>(a, l[i].tile, st);
-    else
-      rc = residual ? run_gemm_one<uint16_t, EPI_RESID>(a, l[i].tile, st)
-                    : run_gemm_one<uint16_t, EPI_PLAIN>(a, l[i].tile, st);
-    if (rc) return rc;
-  }
-  return 0;
+  if (f32)
+    return residual ? run_plain<float, EPI_RESID>(a, TILE_128x128, st) : run_plain<float, EPI_PLAIN>(a, TILE_128x128, st);
+  const int tile = pick_tile(M, 1);
+  return residual ? run_plain<uint16_t, EPI_RESID>(a, tile, st) : run_plain<uint16_t, EPI_PLAIN>(a, tile, st);
 }
 
 }  // namespace moe
