@@ -36,7 +36,8 @@ CONFIG_FIELDS = ["T", "d_model", "n_heads", "d_head", "n_experts", "top_k", "n_g
 
 # exported symbols, as declared in include/moe.h
 SYMBOLS = ["moe_workspace_bytes", "moe_rows_upper_bound", "moe_status_str", "moe_check_config",
-           "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd"]
+           "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd",
+           "moe_backward_workspace_bytes", "moe_transpose_weights", "moe_layer_bwd"]
 
 
 class MoeConfig(ctypes.Structure):
@@ -55,6 +56,14 @@ class MoeLayerIO(ctypes.Structure):
                 ("src_of", ctypes.c_void_p), ("aux_loss", ctypes.c_void_p), ("z", ctypes.c_void_p),
                 ("x_perm", ctypes.c_void_p), ("y_perm", ctypes.c_void_p), ("shared_out", ctypes.c_void_p),
                 ("o", ctypes.c_void_p)]
+
+
+class MoeWeightsT(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w13t", "w2t", "ws13t", "ws2t")]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dx", "dw_router", "dbias", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2")]
 
 
 class MoeError(RuntimeError):
@@ -80,6 +89,10 @@ def _load():
         "moe_expert_ffn_gather": (I, [Z, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
         "moe_combine": (I, [Z, P, P, P, P, P, P, P]),
         "moe_layer_fwd": (I, [Z, ctypes.POINTER(MoeWeights), P, P, ctypes.POINTER(MoeLayerIO), P, S, P]),
+        "moe_backward_workspace_bytes": (S, [Z]),
+        "moe_transpose_weights": (I, [Z, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeightsT), P]),
+        "moe_layer_bwd": (I, [Z, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeightsT), P, P, ctypes.c_float,
+                              ctypes.POINTER(MoeLayerIO), ctypes.POINTER(MoeGrads), P, S, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -197,3 +210,45 @@ def moe_layer_fwd(cfg, weights, x, y, io=None, ws=None, stream=None):
     return _check(_lib.moe_layer_fwd(ctypes.byref(c), ctypes.byref(w), _p(x), _p(y),
                                      ctypes.byref(iob) if iob is not None else None, _p(ws), _nbytes(ws),
                                      _stream(stream)), "moe_layer_fwd")
+
+
+# ---------------------------------------------------------------- backward
+def moe_backward_workspace_bytes(cfg):
+    return int(_lib.moe_backward_workspace_bytes(ctypes.byref(_c(cfg))))
+
+
+def backward_workspace(cfg, device="cuda"):
+    """A uint8 device tensor of moe_backward_workspace_bytes(cfg) bytes (256-byte aligned)."""
+    import torch
+    n = moe_backward_workspace_bytes(cfg)
+    if n == 0:
+        raise MoeError(MOE_ERR_UNSUPPORTED, "backward_workspace")
+    t = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-t.data_ptr()) % 256
+    return t[off:off + n]
+
+
+def _weights(weights):
+    return MoeWeights(**{k: (v.data_ptr() if v is not None else None) for k, v in weights.items()})
+
+
+def moe_transpose_weights(cfg, weights, wt, stream=None):
+    """weights: moe_weights field names -> tensors; wt: moe_weights_t field names -> tensors."""
+    c = _c(cfg)
+    w = _weights(weights)
+    t = MoeWeightsT(**{k: (v.data_ptr() if v is not None else None) for k, v in wt.items()})
+    return _check(_lib.moe_transpose_weights(ctypes.byref(c), ctypes.byref(w), ctypes.byref(t), _stream(stream)),
+                  "moe_transpose_weights")
+
+
+def moe_layer_bwd(cfg, weights, wt, x, dy, aux_weight, io, grads, ws, stream=None):
+    """io: the forward's moe_layer_io tensors (dict); grads: moe_grads field names -> tensors."""
+    c = _c(cfg)
+    w = _weights(weights)
+    t = MoeWeightsT(**{k: (v.data_ptr() if v is not None else None) for k, v in wt.items()})
+    kw = {k: (v.data_ptr() if v is not None else None) for k, v in io.items() if k != "logits_mode"}
+    iob = MoeLayerIO(logits_mode=int(io.get("logits_mode", MOE_LOGITS_COMPUTE)), **kw)
+    g = MoeGrads(**{k: (v.data_ptr() if v is not None else None) for k, v in grads.items()})
+    return _check(_lib.moe_layer_bwd(ctypes.byref(c), ctypes.byref(w), ctypes.byref(t), _p(x), _p(dy),
+                                     float(aux_weight), ctypes.byref(iob), ctypes.byref(g), _p(ws), _nbytes(ws),
+                                     _stream(stream)), "moe_layer_bwd")

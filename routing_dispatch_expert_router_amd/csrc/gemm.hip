@@ -29,7 +29,11 @@
 
 namespace moe {
 
-enum { EPI_PLAIN = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_RESID = 3 };
+enum { EPI_PLAIN = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_RESID = 3, EPI_SWIGLU_BWD = 4, EPI_RELU_BWD = 5 };
+// epilogues whose B tile pairs gate rows with up rows (SwiGLU forward, and its backward)
+static_assert(GEMM_EPI_PLAIN == EPI_PLAIN && GEMM_EPI_SWIGLU_BWD == EPI_SWIGLU_BWD &&
+                  GEMM_EPI_RELU_BWD == EPI_RELU_BWD, "epilogue ids");
+template <int EPI> constexpr bool kPair = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD);
 
 struct GemmArgs {
   const void *A; long lda;                    // routed: A rows indexed by offsets
@@ -45,6 +49,11 @@ struct GemmArgs {
   int Mx, Nx, Kx, has_x;
   long Mr_bound;                              // upper bound on the routed rows (sum over experts)
   const void *res; long ldres;                // EPI_RESID: added to the extra group's output
+  const void *dh; long lddh;                  // *_BWD: upstream gradient of the hidden activation (rows as C)
+  void *hout; long ldh;                       // *_BWD: the recomputed hidden activation (rows as C)
+  const int32_t *kwin;                        // K-grouped mode: group g contracts columns [kwin[g], kwin[g+1])
+  long cstride;                               //   of A and B (both [M or N][ld]); its C block at C + g * cstride
+  int Mk;                                     //   rows of A in that mode
   const int32_t *prefix;                      // [G+1] tile prefix, or NULL: E == 0 and fixed_tiles tiles
   int fixed_tiles;
   int G;
@@ -66,7 +75,7 @@ __host__ __device__ inline void row_window(int split, int M, int *beg, int *len)
 }
 
 template <int EPI, int BN_> __host__ __device__ inline int n_tiles(int N) {
-  return EPI == EPI_SWIGLU ? (N + BN_ / 2 - 1) / (BN_ / 2) : (N + BN_ - 1) / BN_;
+  return kPair<EPI> ? (N + BN_ / 2 - 1) / (BN_ / 2) : (N + BN_ - 1) / BN_;
 }
 
 // Tile prefixes over groups for up to four launches at once (one block per
@@ -186,7 +195,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   const int q8 = total >> 3;
   const int lt = (b < 8 * q8) ? (b & 7) * q8 + (b >> 3) : b;
   int g = 0, local = lt;
-  if (p.prefix) {
+  if (p.kwin) {
+    // K-grouped: every group has the same (Mk x N) tile grid
+    const int tpg = ((p.Mk + BM_ - 1) / BM_) * n_tiles<EPI, BN_>(p.N);
+    g = lt / tpg;
+    local = lt - g * tpg;
+  } else if (p.prefix) {
     int lo = 0, hi = p.G - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
@@ -202,7 +216,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   int M, N, K;
   int r0;
   const int32_t *gat = nullptr;  // routed rows gathered from the expert input
-  if (g < p.E) {
+  if (p.kwin) {
+    const int k0 = p.kwin[g];
+    r0 = 0;
+    M = p.Mk; N = p.N; K = p.kwin[g + 1] - k0;
+    lda = p.lda; ldb = p.ldb; ldc = p.ldc;
+    A = (const TE *)p.A + k0;
+    B = (const TE *)p.B + k0;
+    B2 = nullptr;
+    C = (TE *)p.C + (size_t)g * p.cstride;
+  } else if (g < p.E) {
     r0 = p.offsets[g];
     M = p.offsets[g + 1] - r0;
     lda = p.lda; ldb = p.ldb; ldc = p.ldc; N = p.N; K = p.K;
@@ -254,7 +277,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
     const int s = i * NT + tid, row = s / KS, q = swz<KS>(row, s % KS);
-    if (EPI == EPI_SWIGLU) {
+    if (kPair<EPI>) {
       const int hn = min(tn * HB + (row % HB), N - 1);
       ob[i] = (uint32_t)((size_t)hn * ldb + q * EPC);
     } else {
@@ -263,7 +286,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   }
   auto bsrc = [&](int i) -> const TE * {  // which projection slot i reads
     const int row = (i * NT + tid) / KS;
-    return (EPI == EPI_SWIGLU && row >= HB) ? B2 : B;
+    return (kPair<EPI> && row >= HB) ? B2 : B;
   };
   const int nk = K / BKE;
   f32x4 acc[MF][NF];
@@ -277,7 +300,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   // k-step; the per-fragment part is a compile-time offset
   static_assert(KS == 8, "fragment addressing assumes 128-byte k-chunks");
   int abase[NKS], bbase[NKS];
-  const int bwoff = (EPI == EPI_SWIGLU) ? wn * (HB / WGN) : wn * WN;
+  const int bwoff = kPair<EPI> ? wn * (HB / WGN) : wn * WN;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const int sw = swz<KS>(l16, cq + 4 * ks);
@@ -285,7 +308,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
     bbase[ks] = (bwoff + l16) * KS + sw;
   }
   auto brow_off = [](int f) {  // B-tile row of n-fragment f, relative to bwoff
-    return (EPI == EPI_SWIGLU) ? ((f < NF / 2) ? f * 16 : HB + (f - NF / 2) * 16) : f * 16;
+    return kPair<EPI> ? ((f < NF / 2) ? f * 16 : HB + (f - NF / 2) * 16) : f * 16;
   };
 
   auto issue_a = [&](int kc, int st) {
@@ -390,11 +413,51 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   // (fp32) access.  Every N here is a multiple of 64, so a quad is either
   // wholly inside N or wholly outside.
   const TE *R = (EPI == EPI_RESID) ? (const TE *)p.res + (size_t)r0 * p.ldres : nullptr;
+  const TE *DHp = (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) ? (const TE *)p.dh + (size_t)r0 * p.lddh : nullptr;
+  TE *HO = (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) ? (TE *)p.hout + (size_t)r0 * p.ldh : nullptr;
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
     const int row = m0 + wm * WM + i * 16 + l16;
     if (row >= M) continue;
-    if (EPI == EPI_SWIGLU) {
+    if (EPI == EPI_SWIGLU_BWD) {
+      // recomputed gate g and up u with the upstream dH: dA = dH * u * SiLU'(g),
+      // dB = dH * SiLU(g) (C[row][col] and C[row][N + col]), H = SiLU(g) * u
+#pragma unroll
+      for (int f = 0; f < NF / 2; ++f) {
+        const int col = tn * HB + wn * (HB / WGN) + f * 16 + 4 * cq;
+        if (col >= N) continue;
+        float dh[4], da[4], db[4], h[4];
+        Quad<TE>::load(DHp + (size_t)row * p.lddh + col, dh);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gt = acc[i][f][v], up = acc[i][f + NF / 2][v];
+          const float sg = 1.0f / (1.0f + __expf(-gt)), si = gt * sg;
+          da[v] = dh[v] * up * (sg * (1.0f + gt * (1.0f - sg)));
+          db[v] = dh[v] * si;
+          h[v] = si * up;
+        }
+        Quad<TE>::store(C + (size_t)row * ldc + col, da);
+        Quad<TE>::store(C + (size_t)row * ldc + N + col, db);
+        Quad<TE>::store(HO + (size_t)row * p.ldh + col, h);
+      }
+    } else if (EPI == EPI_RELU_BWD) {
+      // recomputed a = W1 v with the upstream dH: dA = dH * [a > 0], H = max(a, 0)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int col = tn * BN_ + wn * WN + f * 16 + 4 * cq;
+        if (col >= N) continue;
+        float dh[4], da[4], h[4];
+        Quad<TE>::load(DHp + (size_t)row * p.lddh + col, dh);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float a = acc[i][f][v];
+          da[v] = a > 0.0f ? dh[v] : 0.0f;
+          h[v] = fmaxf(a, 0.0f);
+        }
+        Quad<TE>::store(C + (size_t)row * ldc + col, da);
+        Quad<TE>::store(HO + (size_t)row * p.ldh + col, h);
+      }
+    } else if (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int f = 0; f < NF / 2; ++f) {
         const int col = tn * HB + wn * (HB / WGN) + f * 16 + 4 * cq;
@@ -501,7 +564,7 @@ static int tile_rows(int tile) { return tile == TILE_256x256_W8 ? 256 : 128; }
 static int tile_cols(int tile) { return tile == TILE_256x256_W8 ? 256 : 128; }
 static int col_tiles(int epi, int tile, int N) {
   const int bn = tile_cols(tile);
-  return epi == EPI_SWIGLU ? (N + bn / 2 - 1) / (bn / 2) : (N + bn - 1) / bn;
+  return (epi == EPI_SWIGLU || epi == EPI_SWIGLU_BWD) ? (N + bn / 2 - 1) / (bn / 2) : (N + bn - 1) / bn;
 }
 static PrepCfg prep_cfg(int epi, const Launch &l, int N, int Nx) {
   return PrepCfg{tile_rows(l.tile), l.split, col_tiles(epi, l.tile, N), col_tiles(epi, l.tile, Nx)};
@@ -530,6 +593,81 @@ static int run_plain(GemmArgs a, int tile, hipStream_t st) {
     if (int rc = run_gemm_one<TE, EPI>(a, l[i].tile, st)) return rc;
   }
   return 0;
+}
+
+// ---------------------------------------------------------------- backward products
+template <typename TE>
+static int run_epi(int epi, const GemmArgs &a, int tile, hipStream_t st) {
+  switch (epi) {
+    case EPI_PLAIN: return run_gemm_one<TE, EPI_PLAIN>(a, tile, st);
+    case EPI_SWIGLU_BWD: return run_gemm_one<TE, EPI_SWIGLU_BWD>(a, tile, st);
+    case EPI_RELU_BWD: return run_gemm_one<TE, EPI_RELU_BWD>(a, tile, st);
+    default: return -2;
+  }
+}
+
+// C[R, N] = A[R, K] B_e[N, K]^T over the rows of every routed expert e
+// (A rows gathered from the expert input when `gather`), epilogue `epi`
+int gemm_routed(const Shape &s, int epi, const void *A, long lda, const int32_t *gather, const void *B,
+                const void *B2, long ldb, long bstride, void *C, long ldc, int N, int K, const int32_t *offsets,
+                const void *dh, long lddh, void *hout, long ldh, int32_t *prefix, hipStream_t st) {
+  GemmArgs a{};
+  a.A = A; a.lda = lda; a.gather = gather; a.gK = s.K; a.gEh = s.Eh; a.gdh = s.dh;
+  a.B = B; a.B2 = B2; a.ldb = ldb; a.bstride = bstride; a.C = C; a.ldc = ldc;
+  a.offsets = offsets; a.E = s.E; a.N = N; a.K = K; a.Mr_bound = s.R_max; a.G = s.E;
+  a.dh = dh; a.lddh = lddh; a.hout = hout; a.ldh = ldh;
+  const int tile = s.act_f32 ? TILE_128x128 : pick_tile(s.R_max, s.E);
+  Launch l[2];
+  const int nl = plan_launches(tile, l);
+  PrepArgs pa{};
+  pa.offsets = offsets; pa.E = s.E; pa.has_x = 0; pa.Mx = 0; pa.prefix = prefix;
+  for (int i = 0; i < nl; ++i) pa.c[i] = prep_cfg(epi, l[i], N, 0);
+  hipLaunchKernelGGL(gemm_prep_kernel, dim3(nl), dim3(1024), 0, st, pa);
+  if (int rc = launch_status("gemm tile prefix")) return rc;
+  for (int i = 0; i < nl; ++i) {
+    a.split = l[i].split;
+    a.prefix = prefix + (size_t)i * (s.E + 2);
+    const int rc = s.act_f32 ? run_epi<float>(epi, a, l[i].tile, st) : run_epi<uint16_t>(epi, a, l[i].tile, st);
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+// C[M, N] = A[M, K] B[N, K]^T, one plain group
+int gemm_plain(bool f32, int epi, const void *A, long lda, const void *B, const void *B2, long ldb, void *C,
+               long ldc, int M, int N, int K, const void *dh, long lddh, void *hout, long ldh, hipStream_t st) {
+  GemmArgs a{};
+  a.E = 0; a.has_x = 1; a.G = 1;
+  a.Ax = A; a.ldax = lda; a.Bx = B; a.Bx2 = B2; a.ldbx = ldb; a.Cx = C; a.ldcx = ldc; a.Mx = M; a.Nx = N; a.Kx = K;
+  a.dh = dh; a.lddh = lddh; a.hout = hout; a.ldh = ldh;
+  const int tile = f32 ? TILE_128x128 : pick_tile(M, 1);
+  Launch l[2];
+  const int nl = plan_launches(tile, l);
+  for (int i = 0; i < nl; ++i) {
+    int beg, len;
+    row_window(l[i].split, M, &beg, &len);
+    a.split = l[i].split;
+    a.prefix = nullptr;
+    a.fixed_tiles = (len + tile_rows(l[i].tile) - 1) / tile_rows(l[i].tile) * col_tiles(epi, l[i].tile, N);
+    if (a.fixed_tiles == 0) continue;
+    const int rc = f32 ? run_epi<float>(epi, a, l[i].tile, st) : run_epi<uint16_t>(epi, a, l[i].tile, st);
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+// Weight gradients: for g < G, C_g[M, N] = A[:, kwin[g]..kwin[g+1]] B[:, same]^T
+// (A [M][lda], B [N][ldb], both contracted along their rows' columns; every
+// window a multiple of the k-chunk); C_g at C + g * cstride, ldc
+int gemm_kgrouped(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long ldc, long cstride, int G,
+                  int M, int N, const int32_t *kwin, hipStream_t st) {
+  if (G <= 0 || M <= 0 || N <= 0) return 0;
+  GemmArgs a{};
+  a.A = A; a.lda = lda; a.B = B; a.ldb = ldb; a.C = C; a.ldc = ldc; a.cstride = cstride;
+  a.kwin = kwin; a.Mk = M; a.N = N; a.E = G; a.G = G; a.split = 0; a.prefix = nullptr;
+  const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
+  a.fixed_tiles = G * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
+  return f32 ? run_gemm_one<float, EPI_PLAIN>(a, tile, st) : run_gemm_one<uint16_t, EPI_PLAIN>(a, tile, st);
 }
 
 size_t ffn_ws_bytes(const Shape &s) {

@@ -39,6 +39,30 @@ int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w
                     int32_t *demand, int32_t *counts, int32_t *offsets, int32_t *row_of, int32_t *src_of,
                     void *x_perm, void *ws, hipStream_t st);
 
+// ---------------------------------------------------------------- backward
+// grouped-GEMM epilogues the backward selects at run time
+enum { GEMM_EPI_PLAIN = 0, GEMM_EPI_SWIGLU_BWD = 4, GEMM_EPI_RELU_BWD = 5 };
+int gemm_routed(const Shape &s, int epi, const void *A, long lda, const int32_t *gather, const void *B,
+                const void *B2, long ldb, long bstride, void *C, long ldc, int N, int K, const int32_t *offsets,
+                const void *dh, long lddh, void *hout, long ldh, int32_t *prefix, hipStream_t st);
+int gemm_plain(bool f32, int epi, const void *A, long lda, const void *B, const void *B2, long ldb, void *C,
+               long ldc, int M, int N, int K, const void *dh, long lddh, void *hout, long ldh, hipStream_t st);
+int gemm_kgrouped(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long ldc, long cstride, int G,
+                  int M, int N, const int32_t *kwin, hipStream_t st);
+int launch_transpose(bool f32, const void *src, long ld_src, long bs_src, const int32_t *rmap, long nvalid,
+                     long njcols, int ncols, int coff, void *dst, long ld_dst, long bs_dst, int batches,
+                     hipStream_t st);
+int launch_bwd_rows(const Shape &s, const void *dy, const void *y_perm, const float *gates, const int32_t *src_of,
+                    const int32_t *offsets, void *dY, float *dg, hipStream_t st);
+int launch_bwd_pad(const Shape &s, const int32_t *offsets, const int32_t *src_of, int32_t *poff, int32_t *pmap_r,
+                   int32_t *pmap_x, long npad, hipStream_t st);
+int launch_router_bwd(const Shape &s, const float *logits, const int32_t *topk_idx, const float *gates,
+                      const float *dg, const int32_t *demand, float lam, const void *x, float *dl, float *dw_router,
+                      float *dbias, hipStream_t st);
+int launch_bwd_dx(const Shape &s, const void *dy, const void *dxs, const void *dXr, const int32_t *row_of,
+                  const float *dl, const void *w_router, void *dx, hipStream_t st);
+int launch_set_kwin(int32_t *kwin, int tpad, hipStream_t st);
+
 // ---------------------------------------------------------------- grouped GEMM / expert FFN
 size_t ffn_ws_bytes(const Shape &s);
 // gather == NULL: `xin` is x_perm (row r of the routed operand is xin[r]);

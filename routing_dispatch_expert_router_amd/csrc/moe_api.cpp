@@ -123,6 +123,55 @@ int rc_of(int launcher_rc) {
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- backward
+bool bwd_supported(const Shape &s) { return s.H == 1 && !s.latent && gather_supported(s); }
+
+// columns of the per-expert padded, transposed activations: every expert's
+// rows rounded up to 64 (the GEMM k-chunk), and a multiple of 64 overall so
+// rows of the transposed buffers stay 16-byte aligned
+long rpad_bound(const Shape &s) { return (s.R_max + 63) / 64 * 64 + 64L * s.E; }
+long tpad(const Shape &s) { return (s.T + 63) / 64 * 64; }
+
+struct BwdBufs {
+  size_t dg, dl, dY, dH, dAB, Hr, dXr, poff, pmap_r, pmap_x, Xt, dYt, dABt, Ht, prefix, kwin;
+  size_t dHs, dABs, Hs, dxs, dyt, xt, dABst, Hst, total;
+};
+
+BwdBufs bwd_layout(const Shape &s) {
+  const size_t esz = s.act_f32 ? 4 : 2, m = s.act == MOE_ACT_SWIGLU ? 2 : 1;
+  const size_t R = s.R_max, Rp = rpad_bound(s), Tp = tpad(s), fs = (size_t)s.n_shared * s.dff;
+  BwdBufs b{};
+  size_t o = 0;
+  b.dg = o; o += al((size_t)s.T * s.K * 4);
+  b.dl = o; o += al((size_t)s.T * s.E * 4);
+  b.dY = o; o += al(R * s.dh * esz);
+  b.dH = o; o += al(R * s.dff * esz);
+  b.dAB = o; o += al(R * m * s.dff * esz);
+  b.Hr = o; o += al(R * s.dff * esz);
+  b.dXr = o; o += al(R * s.dh * esz);
+  b.poff = o; o += al((size_t)(s.E + 1) * 4);
+  b.pmap_r = o; o += al(Rp * 4);
+  b.pmap_x = o; o += al(Rp * 4);
+  b.Xt = o; o += al((size_t)s.dh * Rp * esz);
+  b.dYt = o; o += al((size_t)s.dh * Rp * esz);
+  b.dABt = o; o += al(m * s.dff * Rp * esz);
+  b.Ht = o; o += al((size_t)s.dff * Rp * esz);
+  b.prefix = o; o += al((size_t)2 * (s.E + 2) * 4);
+  b.kwin = o; o += al(2 * 4);
+  if (fs) {
+    b.dHs = o; o += al((size_t)s.T * fs * esz);
+    b.dABs = o; o += al((size_t)s.T * m * fs * esz);
+    b.Hs = o; o += al((size_t)s.T * fs * esz);
+    b.dxs = o; o += al((size_t)s.T * s.d * esz);
+    b.dyt = o; o += al((size_t)s.d * Tp * esz);
+    b.xt = o; o += al((size_t)s.d * Tp * esz);
+    b.dABst = o; o += al(m * fs * Tp * esz);
+    b.Hst = o; o += al(fs * Tp * esz);
+  }
+  b.total = o;
+  return b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -302,6 +351,156 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
       return rc;
   }
   return MOE_OK;
+}
+
+size_t moe_backward_workspace_bytes(const moe_config *cfg) {
+  Shape s;
+  if (make_shape(cfg, &s) != MOE_OK || !bwd_supported(s)) return 0;
+  return bwd_layout(s).total;
+}
+
+int moe_transpose_weights(const moe_config *cfg, const moe_weights *w, const moe_weights_t *wt, hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, &s);
+  if (rc) return rc;
+  if (!w || !wt || !w->w1 || !w->w2 || !wt->w13t || !wt->w2t) return MOE_ERR_ARG;
+  const bool glu = s.act == MOE_ACT_SWIGLU;
+  if (glu && !w->w3) return MOE_ERR_ARG;
+  if (s.n_shared && (!w->ws1 || !w->ws2 || (glu && !w->ws3) || !wt->ws13t || !wt->ws2t)) return MOE_ERR_ARG;
+  const long m = glu ? 2 : 1, esz = s.act_f32 ? 4 : 2, dff = s.dff, dh = s.dh;
+  clear_stale_error();
+  // w13t[e][c][0..dff) = W1[e][..][c], [dff..2dff) = W3[e][..][c]
+  if ((rc = rc_of(moe::launch_transpose(s.act_f32, w->w1, dh, dff * dh, nullptr, dff, dff, (int)dh, 0, wt->w13t,
+                                        m * dff, dh * m * dff, s.E, stream))))
+    return rc;
+  if (glu && (rc = rc_of(moe::launch_transpose(s.act_f32, w->w3, dh, dff * dh, nullptr, dff, dff, (int)dh, 0,
+                                               (char *)wt->w13t + dff * esz, m * dff, dh * m * dff, s.E, stream))))
+    return rc;
+  if ((rc = rc_of(moe::launch_transpose(s.act_f32, w->w2, dff, dh * dff, nullptr, dh, dh, (int)dff, 0, wt->w2t, dh,
+                                        dff * dh, s.E, stream))))
+    return rc;
+  if (s.n_shared) {
+    const long fs = (long)s.n_shared * dff, d = s.d;
+    if ((rc = rc_of(moe::launch_transpose(s.act_f32, w->ws1, d, 0, nullptr, fs, fs, (int)d, 0, wt->ws13t, m * fs,
+                                          0, 1, stream))))
+      return rc;
+    if (glu && (rc = rc_of(moe::launch_transpose(s.act_f32, w->ws3, d, 0, nullptr, fs, fs, (int)d, 0,
+                                                 (char *)wt->ws13t + fs * esz, m * fs, 0, 1, stream))))
+      return rc;
+    if ((rc = rc_of(moe::launch_transpose(s.act_f32, w->ws2, fs, 0, nullptr, d, d, (int)fs, 0, wt->ws2t, d, 0, 1,
+                                          stream))))
+      return rc;
+  }
+  return MOE_OK;
+}
+
+int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights_t *wt, const void *x,
+                  const void *dy, float aux_weight, const moe_layer_io *io, moe_grads *g, void *ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, &s);
+  if (rc) return rc;
+  if (!w || !wt || !x || !dy || !io || !g) return MOE_ERR_ARG;
+  if (!bwd_supported(s)) return MOE_ERR_UNSUPPORTED;
+  const bool glu = s.act == MOE_ACT_SWIGLU;
+  if (!w->w_router || !w->w1 || !w->w2 || (glu && !w->w3) || !wt->w13t || !wt->w2t) return MOE_ERR_ARG;
+  if (!io->logits || !io->topk_idx || !io->topk_w || !io->demand || !io->offsets || !io->row_of ||
+      ((!io->src_of || !io->y_perm) && s.R_max))
+    return MOE_ERR_ARG;
+  if (!g->dx || !g->dw_router || !g->dw1 || !g->dw2 || (glu && !g->dw3)) return MOE_ERR_ARG;
+  if (s.n_shared && (!w->ws1 || !w->ws2 || (glu && !w->ws3) || !wt->ws13t || !wt->ws2t || !g->dws1 || !g->dws2 ||
+                     (glu && !g->dws3)))
+    return MOE_ERR_ARG;
+  const BwdBufs L = bwd_layout(s);
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (s.T == 0) return MOE_OK;
+
+  char *base = (char *)ws;
+  auto at = [&](size_t off) { return (void *)(base + off); };
+  float *dg = (float *)at(L.dg), *dl = (float *)at(L.dl);
+  void *dY = at(L.dY), *dH = at(L.dH), *dAB = at(L.dAB), *Hr = at(L.Hr), *dXr = at(L.dXr);
+  int32_t *poff = (int32_t *)at(L.poff), *pmap_r = (int32_t *)at(L.pmap_r), *pmap_x = (int32_t *)at(L.pmap_x);
+  void *Xt = at(L.Xt), *dYt = at(L.dYt), *dABt = at(L.dABt), *Ht = at(L.Ht);
+  int32_t *prefix = (int32_t *)at(L.prefix), *kwin = (int32_t *)at(L.kwin);
+  const bool f32 = s.act_f32;
+  const long m = glu ? 2 : 1, esz = f32 ? 4 : 2, dh = s.dh, dff = s.dff, d = s.d, Rp = rpad_bound(s), Tp = tpad(s);
+  const int epi_bwd = glu ? moe::GEMM_EPI_SWIGLU_BWD : moe::GEMM_EPI_RELU_BWD;
+  const int32_t *offsets = io->offsets, *src_of = io->src_of;
+
+  clear_stale_error();
+  // gate gradients dg = <dy, y_perm>, scaled row gradients dY = g * dy
+  if ((rc = rc_of(moe::launch_bwd_rows(s, dy, io->y_perm, io->topk_w, src_of, offsets, dY, dg, stream)))) return rc;
+  if ((rc = rc_of(moe::launch_bwd_pad(s, offsets, src_of, poff, pmap_r, pmap_x, Rp, stream)))) return rc;
+  // dH = dY W2  (B = W2^T rows)
+  if ((rc = rc_of(moe::gemm_routed(s, moe::GEMM_EPI_PLAIN, dY, dh, nullptr, wt->w2t, nullptr, dh, dff * dh, dH, dff,
+                                   (int)dff, (int)dh, offsets, nullptr, 0, nullptr, 0, prefix, stream))))
+    return rc;
+  // recompute the gate/up products from x, with the backward epilogue: dA|dB, H
+  if ((rc = rc_of(moe::gemm_routed(s, epi_bwd, x, d, src_of, w->w1, glu ? w->w3 : nullptr, dh, dff * dh, dAB,
+                                   m * dff, (int)dff, (int)dh, offsets, dH, dff, Hr, dff, prefix, stream))))
+    return rc;
+  // dX rows = [dA dB] [W1; W3]
+  if ((rc = rc_of(moe::gemm_routed(s, moe::GEMM_EPI_PLAIN, dAB, m * dff, nullptr, wt->w13t, nullptr, m * dff,
+                                   dh * m * dff, dXr, dh, (int)dh, (int)(m * dff), offsets, nullptr, 0, nullptr, 0,
+                                   prefix, stream))))
+    return rc;
+  // transposed, per-expert padded activations for the weight gradients
+  if ((rc = rc_of(moe::launch_transpose(f32, x, d, 0, pmap_x, 0, Rp, (int)dh, 0, Xt, Rp, 0, 1, stream)))) return rc;
+  if ((rc = rc_of(moe::launch_transpose(f32, dY, dh, 0, pmap_r, 0, Rp, (int)dh, 0, dYt, Rp, 0, 1, stream)))) return rc;
+  if ((rc = rc_of(moe::launch_transpose(f32, dAB, m * dff, 0, pmap_r, 0, Rp, (int)(m * dff), 0, dABt, Rp, 0, 1,
+                                        stream))))
+    return rc;
+  if ((rc = rc_of(moe::launch_transpose(f32, Hr, dff, 0, pmap_r, 0, Rp, (int)dff, 0, Ht, Rp, 0, 1, stream)))) return rc;
+  // dW2_e = dY_e^T H_e, dW1_e = dA_e^T X_e, dW3_e = dB_e^T X_e
+  if ((rc = rc_of(moe::gemm_kgrouped(f32, dYt, Rp, Ht, Rp, g->dw2, dff, dh * dff, s.E, (int)dh, (int)dff, poff,
+                                     stream))))
+    return rc;
+  if ((rc = rc_of(moe::gemm_kgrouped(f32, dABt, Rp, Xt, Rp, g->dw1, dh, dff * dh, s.E, (int)dff, (int)dh, poff,
+                                     stream))))
+    return rc;
+  if (glu && (rc = rc_of(moe::gemm_kgrouped(f32, (char *)dABt + dff * Rp * esz, Rp, Xt, Rp, g->dw3, dh, dff * dh,
+                                            s.E, (int)dff, (int)dh, poff, stream))))
+    return rc;
+  // router: dl, dW_r, dbias
+  if ((rc = rc_of(moe::launch_router_bwd(s, io->logits, io->topk_idx, io->topk_w, dg, io->demand, aux_weight, x, dl,
+                                         g->dw_router, g->dbias, stream))))
+    return rc;
+  // shared experts: the same MLP backward over all T tokens with gate 1
+  void *dxs = nullptr;
+  if (s.n_shared) {
+    const long fs = (long)s.n_shared * dff;
+    void *dHs = at(L.dHs), *dABs = at(L.dABs), *Hs = at(L.Hs), *dyt = at(L.dyt), *xt = at(L.xt);
+    void *dABst = at(L.dABst), *Hst = at(L.Hst);
+    dxs = at(L.dxs);
+    if ((rc = rc_of(moe::gemm_plain(f32, moe::GEMM_EPI_PLAIN, dy, d, wt->ws2t, nullptr, d, dHs, fs, s.T, (int)fs,
+                                    (int)d, nullptr, 0, nullptr, 0, stream))))
+      return rc;
+    if ((rc = rc_of(moe::gemm_plain(f32, epi_bwd, x, d, w->ws1, glu ? w->ws3 : nullptr, d, dABs, m * fs, s.T,
+                                    (int)fs, (int)d, dHs, fs, Hs, fs, stream))))
+      return rc;
+    if ((rc = rc_of(moe::gemm_plain(f32, moe::GEMM_EPI_PLAIN, dABs, m * fs, wt->ws13t, nullptr, m * fs, dxs, d, s.T,
+                                    (int)d, (int)(m * fs), nullptr, 0, nullptr, 0, stream))))
+      return rc;
+    if ((rc = rc_of(moe::launch_transpose(f32, dy, d, 0, nullptr, s.T, Tp, (int)d, 0, dyt, Tp, 0, 1, stream))))
+      return rc;
+    if ((rc = rc_of(moe::launch_transpose(f32, x, d, 0, nullptr, s.T, Tp, (int)d, 0, xt, Tp, 0, 1, stream))))
+      return rc;
+    if ((rc = rc_of(moe::launch_transpose(f32, dABs, m * fs, 0, nullptr, s.T, Tp, (int)(m * fs), 0, dABst, Tp, 0, 1,
+                                          stream))))
+      return rc;
+    if ((rc = rc_of(moe::launch_transpose(f32, Hs, fs, 0, nullptr, s.T, Tp, (int)fs, 0, Hst, Tp, 0, 1, stream))))
+      return rc;
+    if ((rc = rc_of(moe::launch_set_kwin(kwin, (int)Tp, stream)))) return rc;
+    if ((rc = rc_of(moe::gemm_kgrouped(f32, dyt, Tp, Hst, Tp, g->dws2, fs, 0, 1, (int)d, (int)fs, kwin, stream))))
+      return rc;
+    if ((rc = rc_of(moe::gemm_kgrouped(f32, dABst, Tp, xt, Tp, g->dws1, d, 0, 1, (int)fs, (int)d, kwin, stream))))
+      return rc;
+    if (glu && (rc = rc_of(moe::gemm_kgrouped(f32, (char *)dABst + fs * Tp * esz, Tp, xt, Tp, g->dws3, d, 0, 1,
+                                              (int)fs, (int)d, kwin, stream))))
+      return rc;
+  }
+  // dx = [dy] + [dxs] + sum_j dX rows + dl W_r
+  return rc_of(moe::launch_bwd_dx(s, dy, dxs, dXr, io->row_of, dl, w->w_router, g->dx, stream));
 }
 
 }  // extern "C"

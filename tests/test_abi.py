@@ -164,3 +164,26 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     libs = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
     assert len(libs) == 1, libs
+
+
+def test_backward_workspace_and_support():
+    for cfg in CONFIGS[:4] + SMALL[:4]:
+        assert moe.moe_backward_workspace_bytes(cfg) > 0, cfg.name
+    assert moe.moe_backward_workspace_bytes(CONFIGS[4]) == 0   # multi-head latent: no backward
+    assert moe.moe_backward_workspace_bytes(SMALL[4]) == 0
+
+
+def test_backward_rejects_bad_arguments_before_launching():
+    lib = moe._lib
+    c = moe.config_struct(CONFIGS[2])
+    fake = ctypes.c_void_p(0x1000)
+    w, wt, io, g = moe.MoeWeights(), moe.MoeWeightsT(), moe.MoeLayerIO(), moe.MoeGrads()
+    # missing weights / io / grads
+    assert lib.moe_layer_bwd(ctypes.byref(c), ctypes.byref(w), ctypes.byref(wt), fake, fake, 0.0, ctypes.byref(io),
+                             ctypes.byref(g), fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    assert lib.moe_layer_bwd(ctypes.byref(c), None, ctypes.byref(wt), fake, fake, 0.0, ctypes.byref(io),
+                             ctypes.byref(g), fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    c4 = moe.config_struct(CONFIGS[4])
+    assert lib.moe_layer_bwd(ctypes.byref(c4), ctypes.byref(w), ctypes.byref(wt), fake, fake, 0.0, ctypes.byref(io),
+                             ctypes.byref(g), fake, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_transpose_weights(ctypes.byref(c), ctypes.byref(w), ctypes.byref(wt), None) == moe.MOE_ERR_ARG
