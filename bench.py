@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: automatic)")
     ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB (a known-size "
                          "reference for the HBM byte counters of a profiler run)")
@@ -87,6 +88,55 @@ def measured_traffic(cfg):
         if hashlib.sha256(fh.read()).hexdigest() != rec.get("gemm_source_sha256"):
             return None
     return rec["traffic_bytes"]
+
+
+def time_backward(cfg, moe, W, x, inp, args, stream):
+    """moe_layer_bwd on the same batch (dy synthetic, aux weight 0.01): ms per step, and the
+    forward + backward step as tokens/s.  Algorithmic FLOPs of the backward: twice the
+    forward's expert FLOPs (input and weight gradients); the gate/up recompute the
+    backward does on top is not counted."""
+    import torch
+    T, K, E, dh, F, d = cfg.T, cfg.k_total, cfg.n_experts, cfg.d_head, cfg.d_ff, cfg.d_model
+    Rm = moe.moe_rows_upper_bound(cfg)
+    adt = torch.bfloat16 if cfg.act_dtype == 1 else torch.float32
+    m = 2 if cfg.act == 1 else 1
+    fs = cfg.n_shared * F
+    e = lambda *shape, dt=adt: torch.empty(*shape, dtype=dt, device="cuda")
+    io = dict(logits=e(T, E, dt=torch.float32), logits_mode=moe.MOE_LOGITS_COMPUTE_STORE,
+              topk_idx=e(T, K, dt=torch.int32), topk_w=e(T, K, dt=torch.float32), demand=e(E, dt=torch.int32),
+              counts=e(E, dt=torch.int32), offsets=e(E + 1, dt=torch.int32), row_of=e(T, K, dt=torch.int32),
+              src_of=e(max(Rm, 1), dt=torch.int32), y_perm=e(max(Rm, 1), dh),
+              shared_out=e(T, d) if fs else None)
+    y = torch.empty_like(x)
+    moe.moe_layer_fwd(cfg, W, x, y, io, moe.workspace(cfg))
+    wt = dict(w13t=e(E, dh, m * F), w2t=e(E, F, dh), ws13t=e(d, m * fs) if fs else None,
+              ws2t=e(fs, d) if fs else None)
+    moe.moe_transpose_weights(cfg, W, wt)
+    g = dict(dx=e(T, d), dw_router=e(E, dh, dt=torch.float32), dbias=e(E, dt=torch.float32), dw1=e(E, F, dh),
+             dw3=e(E, F, dh) if cfg.act == 1 else None, dw2=e(E, dh, F), dws1=e(fs, d) if fs else None,
+             dws3=e(fs, d) if (fs and cfg.act == 1) else None, dws2=e(d, fs) if fs else None)
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    dy = torch.randn(T, d, device="cuda", generator=gen).to(adt)
+    ws = moe.backward_workspace(cfg)
+    step = lambda: moe.moe_layer_bwd(cfg, W, wt, x, dy, 0.01, io, g, ws)
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    n = max(3, min(args.steps, 20))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    R = int(io["offsets"][E].item())
+    flops = 2 * algorithmic(cfg, R)["ffn_flops"]
+    tf = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_F32_TFLOPS if cfg.act_dtype == 0 else PEAK_BF16_TFLOPS
+    log(f"[bench] backward {ms:.3f} ms/step, {tf:.4g} TFLOP/s ({tf / peak:.1%} of peak)")
+    return {"ms_per_step": ms, "steps": n, "algorithmic_flops": flops, "TFLOPs": tf, "mfma_frac": tf / peak,
+            "aux_weight": 0.01}
 
 
 def cpu_threads():
@@ -206,6 +256,9 @@ def main():
     st["combine"] = timed(lambda: moe.moe_combine(cfg, io["y_perm"], io["row_of"], io["topk_w"],
                                                   x if (cfg.residual and not cfg.latent_proj) else None,
                                                   io["shared_out"], io["o"] if cfg.latent_proj else y))
+    bwd = None
+    if not args.no_backward and moe.moe_backward_workspace_bytes(cfg) > 0:
+        bwd = time_backward(cfg, moe, W, x, inp, args, stream)
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -243,8 +296,11 @@ def main():
                      "traffic": measured_traffic(cfg), "traffic_unit": "HBM bytes per expert-FFN call (all its launches)",
                      "algorithmic_flops": alg["ffn_flops"]},
         "stages": stages,
+        "backward": bwd,
         "device": dev_name,
     }
+    if bwd is not None:
+        bwd["fwd_bwd_tokens_per_s"] = T / ((ms_step + bwd["ms_per_step"]) * 1e-3)
     if not args.no_cpu:
         sample = args.cpu_tokens or {0: 256, 1: 384, 2: 1024, 3: 96, 4: 2048}[names.get(args.config, 1)]
         log(f"[bench] oracle CPU baseline on {sample} tokens")

@@ -212,3 +212,70 @@ def backward(cfg, P, topk_idx, kept, dy, lam=0.0):
                 dws3[i * f:(i + 1) * f] += b
     return dict(dx=dx, dw_router=dw_router, dbias=dbias, dw1=dw1, dw3=dw3, dw2=dw2,
                 dws1=dws1, dws3=dws3, dws2=dws2, dg=dg, dl=dl)
+
+
+def _gates_and_p(cfg, P, xt, idx_t):
+    l = xt @ P["w_router"].T
+    if P["bias"] is not None:
+        l = l + P["bias"]
+    p = softmax(l)
+    pc = np.take_along_axis(p, idx_t.astype(np.int64), axis=-1)
+    g = pc / pc.sum(axis=-1, keepdims=True) if cfg.renorm else pc
+    return p, pc, g
+
+
+def backward_tokens(cfg, P, topk_idx, kept, dy, lam, tokens, demand):
+    """dx of the given tokens only: the same chain rule as `backward`, evaluated per
+    token (a token's input gradient depends on its own choices, and on the other
+    tokens only through the aux loss's demand counts `demand` [E])."""
+    _check_cfg(cfg)
+    k, T = cfg.top_k, cfg.T
+    keep2 = np.asarray(kept).reshape(T, k)
+    out = []
+    for t in np.asarray(tokens, np.int64):
+        xt = P["x"][t:t + 1]
+        idx_t = topk_idx[t:t + 1].astype(np.int64)
+        p, pc, g = _gates_and_p(cfg, P, xt, idx_t)
+        dyt = np.asarray(dy[t:t + 1], np.float64)
+        dx = dyt.copy() if cfg.residual else np.zeros_like(dyt)
+        dg = np.zeros((1, k))
+        for j in range(k):
+            if not keep2[t, j]:
+                continue
+            e = int(idx_t[0, j])
+            w3 = P["w3"][e] if P["w3"] is not None else None
+            dg[0, j] = float(np.sum(dyt * _ffn(cfg, P, e, xt)))
+            dv, _, _, _ = _mlp_backward(cfg.act, xt, P["w1"][e], w3, P["w2"][e], g[0, j] * dyt)
+            dx += dv
+        dp = np.zeros_like(p)
+        dpc = (dg - np.sum(dg * g, axis=1, keepdims=True)) / pc.sum(axis=1, keepdims=True) if cfg.renorm else dg
+        np.add.at(dp, (np.zeros(k, np.int64), idx_t[0]), dpc[0])
+        if lam:
+            dp += lam * np.asarray(demand, np.float64)[None, :] / (T * T)
+        dl = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+        dx += dl @ P["w_router"]
+        for i in range(cfg.n_shared):
+            w1, w3, w2 = _shared_slices(cfg, P, i)
+            dv, _, _, _ = _mlp_backward(cfg.act, xt, w1, w3, w2, dyt)
+            dx += dv
+        out.append(dx[0])
+    return np.array(out)
+
+
+def backward_expert(cfg, P, e, topk_idx, kept, dy, hidden=None):
+    """dW1, dW3, dW2 of expert e alone: the sums over its kept rows in `backward`.
+
+    `hidden` (index array) restricts them to those hidden units -- rows of dW1
+    and dW3, columns of dW2: F = sum_f W2[:, f] h_f, so a unit's weight
+    gradients depend on that unit only (and the upstream dF)."""
+    _check_cfg(cfg)
+    T, k = cfg.T, cfg.top_k
+    idx = topk_idx.astype(np.int64)
+    rows, cols = np.nonzero((idx == e) & np.asarray(kept).reshape(T, k))
+    xv = P["x"][rows]
+    _, _, g = _gates_and_p(cfg, P, xv, idx[rows])
+    dF = g[np.arange(len(rows)), cols][:, None] * np.asarray(dy, np.float64)[rows]
+    hs = slice(None) if hidden is None else np.asarray(hidden, np.int64)
+    w3 = P["w3"][e][hs] if P["w3"] is not None else None
+    _, dW1, dW3, dW2 = _mlp_backward(cfg.act, xv, P["w1"][e][hs], w3, P["w2"][e][:, hs], dF)
+    return dW1, dW3, dW2

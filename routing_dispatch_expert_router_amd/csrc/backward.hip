@@ -200,71 +200,162 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float *__restrict
   }
 }
 
-// dW_r[e][c] = sum_t dl[t][e] x[t][c] (float32, t ascending); block y == 0
-// also writes dbias[e] = sum_t dl[t][e].  A block owns 64 columns and all E.
-template <typename TX>
-__global__ __launch_bounds__(512) void router_wgrad_kernel(const float *__restrict__ dl, const TX *__restrict__ x,
-                                                           long ldx, int T, int E, int d, float *__restrict__ dw,
-                                                           float *__restrict__ dbias) {
-  constexpr int TC = 32;         // tokens per staged chunk
-  __shared__ float sdl[TC][257];
-  __shared__ float sx[TC][64];
-  const int c0 = blockIdx.x * 64, tid = threadIdx.x, c = tid & 63, eg = tid >> 6;  // 8 expert groups
-  float acc[32], accb[32];
+// ---------------------------------------------------------------- float32 tile
+// acc += sum_{k in [k_beg, k_end)} a(k, m) b(k, n) for the 64 x 64 output tile at
+// (m0, n0); thread (tm, tn) = (tid / 16, tid % 16) owns m0 + 4 tm + i, n0 + 4 tn + j.
+// b(k, n) = B[k ldb + n]; a(k, m) = A[k lda + m], or A[m lda + k] when A_MK (the
+// operand is staged transposed into LDS).  k ascends: the order is fixed.
+struct TileSmem {
+  __align__(16) float a[32][68];
+  __align__(16) float b[32][68];
+};
+
+template <bool A_MK, typename TA_, typename TB_>
+__device__ __forceinline__ void tile_outer(float (&acc)[4][4], TileSmem &sm, const TA_ *__restrict__ A, long lda,
+                                           int M, const TB_ *__restrict__ B, long ldb, int N, int m0, int n0,
+                                           int k_beg, int k_end) {
+  const int tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
+  for (int k0 = k_beg; k0 < k_end; k0 += 32) {
+    const int nk = min(32, k_end - k0);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = accb[i] = 0.f;
-  for (int t0 = 0; t0 < T; t0 += TC) {
-    const int nt = min(TC, T - t0);
-    for (int i = tid; i < TC * E; i += 512) {
-      const int tt = i / E, e = i % E;
-      sdl[tt][e] = tt < nt ? dl[(size_t)(t0 + tt) * E + e] : 0.f;
-    }
-    for (int i = tid; i < TC * 64; i += 512) {
-      const int tt = i / 64, cc = i % 64;
-      sx[tt][cc] = (tt < nt && c0 + cc < d) ? Elem<TX>::to_f32(x[(size_t)(t0 + tt) * ldx + c0 + cc]) : 0.f;
-    }
-    __syncthreads();
-    for (int tt = 0; tt < nt; ++tt) {
-      const float xv = sx[tt][c];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int e = eg + 8 * i;
-        if (e < E) {
-          acc[i] += sdl[tt][e] * xv;
-          accb[i] += sdl[tt][e];
-        }
+    for (int r = 0; r < 8; ++r) {
+      const int i = tid + 256 * r;
+      int kk, mm;
+      if (A_MK) {
+        kk = i & 31;
+        mm = i >> 5;
+      } else {
+        kk = i >> 6;
+        mm = i & 63;
       }
+      float av = 0.f;
+      if (kk < nk && m0 + mm < M)
+        av = Elem<TA_>::to_f32(A_MK ? A[(size_t)(m0 + mm) * lda + k0 + kk] : A[(size_t)(k0 + kk) * lda + m0 + mm]);
+      sm.a[kk][mm] = av;
+      const int kb = i >> 6, nb = i & 63;
+      sm.b[kb][nb] = (kb < nk && n0 + nb < N) ? Elem<TB_>::to_f32(B[(size_t)(k0 + kb) * ldb + n0 + nb]) : 0.f;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < nk; ++kk) {
+      const float4 av = *(const float4 *)&sm.a[kk][4 * tm];
+      const float4 bv = *(const float4 *)&sm.b[kk][4 * tn];
+      const float am[4] = {av.x, av.y, av.z, av.w}, bn[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += am[i] * bn[j];
     }
     __syncthreads();
   }
+}
+
+// dW_r = dl^T x in float32: m = expert, n = column, k = token.  Block (eb, cb,
+// ts) covers token range ts of gridDim.z and writes part[ts][e][c]; a second
+// pass adds the ranges in ascending order (fixed order: reproducible).
+template <typename TX>
+__global__ __launch_bounds__(256) void router_wgrad_kernel(const float *__restrict__ dl, const TX *__restrict__ x,
+                                                           long ldx, int T, int E, int d, float *__restrict__ part) {
+  __shared__ TileSmem sm;
+  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64, ts = blockIdx.z;
+  const int per = (T + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int t_beg = min(T, ts * per), t_end = min(T, t_beg + per);
+  float acc[4][4] = {};
+  tile_outer<false>(acc, sm, dl, E, E, x, ldx, d, m0, n0, t_beg, t_end);
+  const int tm = threadIdx.x >> 4, tn = threadIdx.x & 15;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int e = eg + 8 * i;
-    if (e < E && c0 + c < d) dw[(size_t)e * d + c0 + c] = acc[i];
-    if (e < E && blockIdx.x == 0 && c == 0 && dbias) dbias[e] = accb[i];
+  for (int i = 0; i < 4; ++i) {
+    const int e = m0 + 4 * tm + i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = n0 + 4 * tn + j;
+      if (e < E && c < d) part[((size_t)ts * E + e) * d + c] = acc[i][j];
+    }
   }
+}
+
+__global__ void router_wgrad_sum_kernel(const float *__restrict__ part, long n, int nsplit, float *__restrict__ dw) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int ts = 0; ts < nsplit; ++ts) s += part[(size_t)ts * n + i];
+    dw[i] = s;
+  }
+}
+
+// dbias[e] = sum_t dl[t][e]: one block per expert, strided partials then a
+// fixed-order tree
+__global__ __launch_bounds__(256) void router_dbias_kernel(const float *__restrict__ dl, int T, int E,
+                                                           float *__restrict__ dbias) {
+  __shared__ float s[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  float v = 0.f;
+  for (int t = tid; t < T; t += 256) v += dl[(size_t)t * E + e];
+  s[tid] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) s[tid] += s[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) dbias[e] = s[0];
 }
 
 // ---------------------------------------------------------------- input gradient
 // dx[t][c] = [dy[t][c]] + [dxs[t][c]] + sum_j dXr[row_of[t][j]][c] + sum_e dl[t][e] W_r[e][c],
-// float32 in that order, rounded once.
+// float32 in that order (the router term over experts ascending), rounded
+// once.  A thread owns one column of DX_TOK consecutive tokens: every global
+// access of a wave covers 64 consecutive columns, and the dl reads have
+// block-uniform addresses (scalar loads).
+constexpr int DX_TOK = 8;
 template <typename TA, typename TR>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const TA *__restrict__ dy, const TA *__restrict__ dxs,
                                                      const TA *__restrict__ dXr, const int32_t *__restrict__ row_of,
                                                      const float *__restrict__ dl, const TR *__restrict__ w_r, int T,
                                                      int d, int K, int E, int residual, TA *__restrict__ dx) {
-  const long n = (long)T * d;
-  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-    const int t = (int)(i / d), c = (int)(i % d);
-    float s = residual ? Elem<TA>::to_f32(dy[i]) : 0.f;
-    if (dxs) s += Elem<TA>::to_f32(dxs[i]);
-    for (int j = 0; j < K; ++j) {
-      const int r = row_of[(size_t)t * K + j];
-      if (r >= 0) s += Elem<TA>::to_f32(dXr[(size_t)r * d + c]);
+  const int t0 = blockIdx.x * DX_TOK, c = blockIdx.y * 256 + threadIdx.x;
+  if (c >= d) return;
+  const int nt = min(DX_TOK, T - t0);
+  float acc[DX_TOK];
+#pragma unroll
+  for (int i = 0; i < DX_TOK; ++i) {
+    float v = 0.f;
+    if (i < nt) {
+      const int t = t0 + i;
+      const size_t o = (size_t)t * d + c;
+      if (residual) v = Elem<TA>::to_f32(dy[o]);
+      if (dxs) v += Elem<TA>::to_f32(dxs[o]);
+      for (int q = 0; q < K; ++q) {
+        const int r = row_of[(size_t)t * K + q];
+        if (r >= 0) v += Elem<TA>::to_f32(dXr[(size_t)r * d + c]);
+      }
     }
-    for (int e = 0; e < E; ++e) s += dl[(size_t)t * E + e] * Elem<TR>::to_f32(w_r[(size_t)e * d + c]);
-    dx[i] = Elem<TA>::from_f32(s);
+    acc[i] = v;
   }
+  const float *dlb = dl + (size_t)t0 * E;
+  if (nt == DX_TOK && (E & 3) == 0) {
+    // dl rows are 16-byte aligned (the buffer is, and E % 4 == 0)
+    for (int e = 0; e < E; e += 4) {
+      float w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = Elem<TR>::to_f32(w_r[(size_t)(e + u) * d + c]);
+#pragma unroll
+      for (int i = 0; i < DX_TOK; ++i) {
+        const float4 l = *(const float4 *)(dlb + (size_t)i * E + e);
+        acc[i] += l.x * w[0];
+        acc[i] += l.y * w[1];
+        acc[i] += l.z * w[2];
+        acc[i] += l.w * w[3];
+      }
+    }
+  } else {
+    for (int e = 0; e < E; ++e) {
+      const float w = Elem<TR>::to_f32(w_r[(size_t)e * d + c]);
+#pragma unroll
+      for (int i = 0; i < DX_TOK; ++i)
+        if (i < nt) acc[i] += dlb[(size_t)i * E + e] * w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < DX_TOK; ++i)
+    if (i < nt) dx[(size_t)(t0 + i) * d + c] = Elem<TA>::from_f32(acc[i]);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -316,18 +407,27 @@ int launch_bwd_pad(const Shape &s, const int32_t *offsets, const int32_t *src_of
 }
 
 int launch_router_bwd(const Shape &s, const float *logits, const int32_t *topk_idx, const float *gates,
-                      const float *dg, const int32_t *demand, float lam, const void *x, float *dl, float *dw_router,
-                      float *dbias, hipStream_t st) {
+                      const float *dg, const int32_t *demand, float lam, const void *x, float *dl, float *part,
+                      float *dw_router, float *dbias, hipStream_t st) {
   hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((s.T + 3) / 4)), dim3(256), 0, st, logits, topk_idx, gates,
                      dg, demand, s.T, s.E, s.K, s.renorm, lam, dl);
   if (int rc = launch_status("router backward")) return rc;
-  const unsigned grid = (unsigned)((s.d + 63) / 64);
+  if (dbias) {
+    hipLaunchKernelGGL(router_dbias_kernel, dim3((unsigned)s.E), dim3(256), 0, st, dl, s.T, s.E, dbias);
+    if (int rc = launch_status("router bias gradient")) return rc;
+  }
+  const int nsplit = router_wgrad_split(s.E, s.d);
+  const dim3 grid((unsigned)((s.E + 63) / 64), (unsigned)((s.d + 63) / 64), (unsigned)nsplit);
   if (s.act_f32)
-    hipLaunchKernelGGL((router_wgrad_kernel<float>), dim3(grid), dim3(512), 0, st, dl, (const float *)x, (long)s.d,
-                       s.T, s.E, s.d, dw_router, dbias);
+    hipLaunchKernelGGL((router_wgrad_kernel<float>), grid, dim3(256), 0, st, dl, (const float *)x, (long)s.d, s.T,
+                       s.E, s.d, part);
   else
-    hipLaunchKernelGGL((router_wgrad_kernel<uint16_t>), dim3(grid), dim3(512), 0, st, dl, (const uint16_t *)x,
-                       (long)s.d, s.T, s.E, s.d, dw_router, dbias);
+    hipLaunchKernelGGL((router_wgrad_kernel<uint16_t>), grid, dim3(256), 0, st, dl, (const uint16_t *)x, (long)s.d,
+                       s.T, s.E, s.d, part);
+  if (int rc = launch_status("router weight gradient")) return rc;
+  const long n = (long)s.E * s.d;
+  hipLaunchKernelGGL(router_wgrad_sum_kernel, dim3((unsigned)std::min<long>((n + 255) / 256, 4096)), dim3(256), 0,
+                     st, part, n, nsplit, dw_router);
   return launch_status("router weight gradient");
 }
 
@@ -345,8 +445,8 @@ int launch_set_kwin(int32_t *kwin, int tpad, hipStream_t st) {
 
 int launch_bwd_dx(const Shape &s, const void *dy, const void *dxs, const void *dXr, const int32_t *row_of,
                   const float *dl, const void *w_router, void *dx, hipStream_t st) {
-  const long n = (long)s.T * s.d;
-  const unsigned grid = (unsigned)std::min<long>((n + 255) / 256, 65536);
+  if (s.T == 0 || s.d == 0) return 0;
+  const dim3 grid((unsigned)((s.T + DX_TOK - 1) / DX_TOK), (unsigned)((s.d + 255) / 256));
   if (s.act_f32) {
     hipLaunchKernelGGL((bwd_dx_kernel<float, float>), dim3(grid), dim3(256), 0, st, (const float *)dy,
                        (const float *)dxs, (const float *)dXr, row_of, dl, (const float *)w_router, s.T, s.d, s.K,

@@ -133,7 +133,7 @@ long rpad_bound(const Shape &s) { return (s.R_max + 63) / 64 * 64 + 64L * s.E; }
 long tpad(const Shape &s) { return (s.T + 63) / 64 * 64; }
 
 struct BwdBufs {
-  size_t dg, dl, dY, dH, dAB, Hr, dXr, poff, pmap_r, pmap_x, Xt, dYt, dABt, Ht, prefix, kwin;
+  size_t dg, dl, rpart, dY, dH, dAB, Hr, dXr, poff, pmap_r, pmap_x, Xt, dYt, dABt, Ht, prefix, kwin;
   size_t dHs, dABs, Hs, dxs, dyt, xt, dABst, Hst, total;
 };
 
@@ -144,6 +144,7 @@ BwdBufs bwd_layout(const Shape &s) {
   size_t o = 0;
   b.dg = o; o += al((size_t)s.T * s.K * 4);
   b.dl = o; o += al((size_t)s.T * s.E * 4);
+  b.rpart = o; o += al((size_t)moe::router_wgrad_split(s.E, s.d) * s.E * s.d * 4);
   b.dY = o; o += al(R * s.dh * esz);
   b.dH = o; o += al(R * s.dff * esz);
   b.dAB = o; o += al(R * m * s.dff * esz);
@@ -463,7 +464,7 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
     return rc;
   // router: dl, dW_r, dbias
   if ((rc = rc_of(moe::launch_router_bwd(s, io->logits, io->topk_idx, io->topk_w, dg, io->demand, aux_weight, x, dl,
-                                         g->dw_router, g->dbias, stream))))
+                                         (float *)at(L.rpart), g->dw_router, g->dbias, stream))))
     return rc;
   // shared experts: the same MLP backward over all T tokens with gate 1
   void *dxs = nullptr;

@@ -126,4 +126,27 @@ def check_special_cases():
     assert np.all(G["dw1"] == 0) and np.all(G["dw2"] == 0) and np.any(G["dw_router"] != 0)
 
 
-ALL = [check_fd_all, check_fd_aux_only, check_forward_fixed_matches_oracle, check_special_cases]
+def check_restricted_forms():
+    """backward_tokens and backward_expert (used at full size) equal the full backward."""
+    B, O = _mods()
+    for cfg in tiny_cfgs():
+        inp, out, P, dy = _setup(cfg)
+        idx, kept = out["topk_idx"], out["kept"]
+        G = B.backward(cfg, P, idx, kept, dy, 0.37)
+        toks = np.arange(0, cfg.T, 3)
+        dx = B.backward_tokens(cfg, P, idx, kept, dy, 0.37, toks, out["demand"])
+        assert np.allclose(dx, G["dx"][toks], rtol=1e-10, atol=1e-12), cfg.name
+        for e in range(cfg.n_experts):
+            dW1, dW3, dW2 = B.backward_expert(cfg, P, e, idx, kept, dy)
+            assert np.allclose(dW1, G["dw1"][e], rtol=1e-10, atol=1e-12), (cfg.name, e)
+            assert np.allclose(dW2, G["dw2"][e], rtol=1e-10, atol=1e-12), (cfg.name, e)
+            if dW3 is not None:
+                assert np.allclose(dW3, G["dw3"][e], rtol=1e-10, atol=1e-12), (cfg.name, e)
+            hid = np.arange(1, cfg.d_ff, 3)
+            h1, h3, h2 = B.backward_expert(cfg, P, e, idx, kept, dy, hidden=hid)
+            assert np.allclose(h1, G["dw1"][e][hid], rtol=1e-10, atol=1e-12), (cfg.name, e)
+            assert np.allclose(h2, G["dw2"][e][:, hid], rtol=1e-10, atol=1e-12), (cfg.name, e)
+
+
+ALL = [check_fd_all, check_fd_aux_only, check_forward_fixed_matches_oracle, check_special_cases,
+       check_restricted_forms]

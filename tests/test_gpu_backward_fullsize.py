@@ -1,0 +1,102 @@
+"""Backward at the full workload sizes (one routing head), in the launch configuration the
+benchmark times, against the float64 backward oracle on samples it evaluates cheaply:
+dx of sampled tokens (a token's input gradient needs only its own experts and the
+demand counts), and the weight gradients of one expert restricted to sampled hidden
+units (they decompose over hidden units).  Router gradients: every token's logit
+gradient sums to zero over the experts (softmax Jacobian), so sum_e dbias_e and
+every column sum of dW_router vanish.  Plus finiteness and bitwise reproducibility.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.moe_backward as OB
+import routing_dispatch_expert_router_amd as moe
+from moe_inputs import CONFIGS, bf16_bits_from_f32
+from tests.gpu_util import log, dev, f64, tol, weights_dev, cached_inputs
+
+pytestmark = pytest.mark.gpu
+
+FULL = [c for c in CONFIGS[1:] if c.n_heads == 1 and not c.latent_proj]
+LAM = 0.01
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
+def test_fullsize_backward(cfg):
+    log(f"full-size backward {cfg.name}")
+    inp = cached_inputs(cfg)
+    T, K, E, dh, F, d = cfg.T, cfg.k_total, cfg.n_experts, cfg.d_head, cfg.d_ff, cfg.d_model
+    Rm = moe.moe_rows_upper_bound(cfg)
+    adt = torch.bfloat16
+    m = 2 if cfg.act == 1 else 1
+    fs = cfg.n_shared * F
+    e_ = lambda *s, dt=adt: torch.empty(*s, dtype=dt, device="cuda")
+    io = dict(logits=e_(T, E, dt=torch.float32), logits_mode=moe.MOE_LOGITS_COMPUTE_STORE,
+              topk_idx=e_(T, K, dt=torch.int32), topk_w=e_(T, K, dt=torch.float32), demand=e_(E, dt=torch.int32),
+              counts=e_(E, dt=torch.int32), offsets=e_(E + 1, dt=torch.int32), row_of=e_(T, K, dt=torch.int32),
+              src_of=e_(Rm, dt=torch.int32), y_perm=e_(Rm, dh))
+    W = weights_dev(cfg, inp)
+    x = dev(inp.x)
+    y = torch.empty_like(x)
+    moe.moe_layer_fwd(cfg, W, x, y, io, moe.workspace(cfg))
+    wt = dict(w13t=e_(E, dh, m * F), w2t=e_(E, F, dh), ws13t=e_(d, m * fs) if fs else None,
+              ws2t=e_(fs, d) if fs else None)
+    moe.moe_transpose_weights(cfg, W, wt)
+    rng = np.random.default_rng([5, cfg.tag])
+    dy_h = bf16_bits_from_f32(rng.standard_normal((T, d)).astype(np.float32))
+    dy = dev(dy_h)
+
+    def grads():
+        return dict(dx=e_(T, d), dw_router=e_(E, dh, dt=torch.float32), dbias=e_(E, dt=torch.float32),
+                    dw1=e_(E, F, dh), dw3=e_(E, F, dh) if cfg.act == 1 else None, dw2=e_(E, dh, F),
+                    dws1=e_(fs, d) if fs else None, dws3=e_(fs, d) if (fs and cfg.act == 1) else None,
+                    dws2=e_(d, fs) if fs else None)
+
+    ws = moe.backward_workspace(cfg)
+    G1, G2 = grads(), grads()
+    log("  GPU backward x2")
+    moe.moe_layer_bwd(cfg, W, wt, x, dy, LAM, io, G1, ws)
+    moe.moe_layer_bwd(cfg, W, wt, x, dy, LAM, io, G2, ws)
+    torch.cuda.synchronize()
+    for k in G1:
+        if G1[k] is not None:
+            assert torch.isfinite(G1[k].float()).all(), k
+            assert torch.equal(_bits(G1[k]), _bits(G2[k])), k
+    # router gradients: zero sums over experts
+    db = G1["dbias"].double()
+    assert abs(float(db.sum())) <= 1e-4 * float(db.abs().sum())
+    dwr = G1["dw_router"].double()
+    assert float(dwr.sum(0).abs().max()) <= 1e-4 * float(dwr.abs().sum(0).max())
+    # sampled tokens: dx
+    P = OB.params_of(inp)
+    idx = io["topk_idx"].cpu().numpy()
+    kept = io["row_of"].cpu().numpy().reshape(-1) >= 0
+    demand = io["demand"].cpu().numpy()
+    dy64 = oracle.decode(dy_h)
+    toks = np.linspace(0, T - 1, 6).astype(np.int64)
+    log("  oracle: sampled tokens")
+    ref = OB.backward_tokens(cfg, P, idx, kept, dy64, LAM, toks, demand)
+    got = f64(G1["dx"])[toks]
+    err = np.max(np.abs(got - ref))
+    log(f"  dx (sampled tokens) rel err {err / np.max(np.abs(ref)):.3g}")
+    assert err <= tol(cfg) * np.max(np.abs(ref))
+    # one expert, sampled hidden units
+    counts = io["counts"].cpu().numpy()
+    e = int(np.argmin(np.where(counts > 0, counts, np.iinfo(np.int64).max)))
+    hid = np.linspace(0, F - 1, 32).astype(np.int64)
+    log(f"  oracle: expert {e} ({counts[e]} rows), 32 hidden units")
+    r1, r3, r2 = OB.backward_expert(cfg, P, e, idx, kept, dy64, hidden=hid)
+    hid_t = torch.from_numpy(hid).cuda()
+    for name, got_t, want in (("dw1", G1["dw1"][e][hid_t], r1), ("dw2", G1["dw2"][e][:, hid_t], r2),
+                              ("dw3", G1["dw3"][e][hid_t] if r3 is not None else None, r3)):
+        if want is None:
+            continue
+        g = f64(got_t)
+        err = np.max(np.abs(g - want))
+        log(f"  {name} (expert {e}) rel err {err / np.max(np.abs(want)):.3g}")
+        assert err <= tol(cfg) * np.max(np.abs(want)), name
