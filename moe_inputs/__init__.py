@@ -22,7 +22,10 @@ regenerated alone.  Activations are N(0, 1); weights are N(0, 1/d_in)
 with d_in the contracted dimension; bf16 tensors are rounded to nearest
 even.  The per-expert router bias that models hot experts is computed,
 not drawn: b_e = -s * ln(e + 1) for the local expert index e within a
-head, so softmax(b) over one head is exactly the Zipf(s) pmf.
+head, so softmax(b) over one head is exactly the Zipf(s) pmf.  The
+selection-only balancing bias of the routing variants, when a workload asks
+for one, is 0.001 * n_e with n_e drawn uniformly from [-steps, steps] (stream
+tag 11): the state such a bias reaches after some updates of step 0.001.
 """
 from .configs import MoEConfig, CONFIGS, SMALL, config_by_name  # noqa: F401
 from .gen import generate, bf16_bits_from_f32, Inputs  # noqa: F401

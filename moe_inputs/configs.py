@@ -9,6 +9,7 @@ seconds, while still spanning several GEMM tiles and a ragged tail.
 from dataclasses import dataclass, replace, asdict
 
 DROP_NONE, DROP_CAPACITY, DROP_AFFINITY = 0, 1, 2
+ROUTE_TOKEN_CHOICE, ROUTE_EXPERT_CHOICE = 0, 1
 ACT_RELU, ACT_SWIGLU = 0, 1
 F32, BF16 = 0, 1
 
@@ -36,8 +37,12 @@ class MoEConfig:
     residual: int = 1       # 1: combine adds the layer input
     act_dtype: int = BF16
     router_dtype: int = BF16
+    route_mode: int = ROUTE_TOKEN_CHOICE  # expert choice: each expert keeps its top-`capacity` tokens
+    sel_bias_gate: int = 0  # with a selection bias: 1 the gate is p + b, 0 the gate is p
+    seq_len: int = 0        # > 0: per-sequence balance statistic over sequences of seq_len tokens
     # input recipe (not part of the C struct)
     zipf_s: float = 0.0     # > 0: router bias b_e = -s ln(e+1) per head
+    sel_bias_steps: int = 0  # > 0: selection bias b_e = 0.001 * n_e, n_e uniform in [-steps, steps]
     seed: int = 0
     tag: int = 0            # config tag mixed into every tensor's stream
 
@@ -47,7 +52,8 @@ class MoEConfig:
 
     @property
     def k_total(self):
-        return self.n_heads * self.top_k
+        """Assignment slots per token: H * top_k, or one per expert with expert choice."""
+        return self.n_experts if self.route_mode == ROUTE_EXPERT_CHOICE else self.n_heads * self.top_k
 
     @property
     def d_latent(self):
@@ -59,7 +65,7 @@ class MoEConfig:
 
     def c_fields(self):
         d = asdict(self)
-        for k in ("name", "zipf_s", "seed", "tag"):
+        for k in ("name", "zipf_s", "sel_bias_steps", "seed", "tag"):
             d.pop(k)
         return d
 

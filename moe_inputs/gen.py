@@ -32,6 +32,7 @@ class Inputs:
     ws2: np.ndarray = None              # [d_model, n_s*d_ff]
     w_in: np.ndarray = None             # [H*d_head, d_model]
     w_out: np.ndarray = None            # [d_model, H*d_head]
+    sel_bias: np.ndarray = None         # [E] float32 or None: selection-only expert bias
     meta: dict = field(default_factory=dict)
 
     def is_bf16(self, name):
@@ -111,5 +112,11 @@ def generate(cfg: MoEConfig, threads=None) -> Inputs:
         eh = E // H
         b = (-cfg.zipf_s * np.log(np.arange(1, eh + 1, dtype=np.float64))).astype(np.float32)
         bias = np.tile(b, H)
+    sel_bias = None
+    if cfg.sel_bias_steps > 0:
+        # a balancing bias as it stands after some +-0.001 updates
+        rng = np.random.default_rng([cfg.seed, cfg.tag, 11, 0])
+        n = rng.integers(-cfg.sel_bias_steps, cfg.sel_bias_steps + 1, size=E)
+        sel_bias = (n * 0.001).astype(np.float32)
     return Inputs(cfg=cfg, x=x, w_router=w_router, bias=bias, w1=w1, w3=w3, w2=w2,
-                  ws1=ws1, ws3=ws3, ws2=ws2, w_in=w_in, w_out=w_out)
+                  ws1=ws1, ws3=ws3, ws2=ws2, w_in=w_in, w_out=w_out, sel_bias=sel_bias)

@@ -20,7 +20,8 @@ Sources (page titles as published; sections as headed on each page):
   [LatentMoE] "多头 LatentMoE 与 Head Parallel" (euno.news summary of arXiv
               2602.04870) -- section "方法论" items 1-2.
   [LocMoE+]   jiqizhixin.com article on LocMoE+ -- router-taxonomy paragraph
-              (token-choice router with per-expert truncation at capacity C).
+              (token-choice router with per-expert truncation at capacity C;
+              expert-choice router: every expert picks its top-C tokens).
 
 Readings of points the pages leave open are listed in the design doc
 ("Readings"); the ones used here are restated at the function that uses them.
@@ -29,6 +30,7 @@ import numpy as np
 
 RELU, SWIGLU = 0, 1
 DROP_NONE, DROP_CAPACITY, DROP_AFFINITY = 0, 1, 2
+ROUTE_TOKEN_CHOICE, ROUTE_EXPERT_CHOICE = 0, 1
 
 
 # --------------------------------------------------------------------------- storage
@@ -125,6 +127,79 @@ def aux_loss(p, idx):
     return float(np.sum(m * c / S))
 
 
+def biased_keys(p, sel_bias):
+    """Selection keys s_{i,t} + b_i of the balancing bias, in float32.
+
+    ([MoE-evo] "DeepSeek-V3" item 1: a per-expert bias b_i is added to the
+    token-expert affinity s_{i,t} and the top-K of the sums is selected.)
+    The affinity is the softmax probability (the pages' gating score).  The
+    float64 probability is rounded to float32 once and the bias added in
+    float32: the precision the kernel takes this decision in.
+    """
+    return (np.asarray(p, np.float64).astype(np.float32) + np.asarray(sel_bias, np.float32)) + np.float32(0.0)
+
+
+def select_topk_keys(keys, k, n_groups=0, topk_groups=0):
+    """Top-k by an explicit float32 key (key descending, lower index first on ties).
+
+    The same selector as select_topk, taking its order from `keys` instead of
+    the logits; the group score is the largest key in the group.
+    """
+    return select_topk(keys, k, n_groups, topk_groups)
+
+
+def biased_gates(p, sel_bias, idx, renorm, bias_in_gate):
+    """Gates under the balancing bias ([MoE-evo] "DeepSeek-V3" item 1).
+
+    The printed formula gives a chosen expert the value s_{i,t} + b_i and
+    every other expert 0; with bias_in_gate == 0 the gate is s_{i,t} alone
+    (the bias only steers selection).  Renormalisation, when asked for,
+    divides by the chosen values' sum as for the plain gates.
+    """
+    w = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    if bias_in_gate:
+        w = w + np.asarray(sel_bias, np.float64)[idx]
+    if renorm:
+        w = w / w.sum(axis=1, keepdims=True)
+    return w
+
+
+def sel_bias_update(sel_bias, counts, gamma):
+    """One update of the balancing bias ([MoE-evo] "DeepSeek-V3" item 1).
+
+    An overloaded expert's bias falls by gamma, an underloaded one's rises by
+    gamma.  Reading: the load is the number of tokens that chose the expert
+    in this batch and "overloaded" means above the mean load over the
+    experts; an expert exactly at the mean keeps its bias.  The comparison
+    c_e * E versus sum(c) is done in integers.
+    """
+    c = np.asarray(counts, np.int64)
+    E = len(c)
+    tot = int(c.sum())
+    step = np.sign(tot - c * E).astype(np.float32)  # +1 underloaded, -1 overloaded
+    return (np.asarray(sel_bias, np.float32) + np.float32(gamma) * step).astype(np.float32)
+
+
+def seq_balance(p, idx, seq_len):
+    """Per-sequence balance statistic  sum_i f_i P_i  ([MoE-evo] "DeepSeek-V3" item 4).
+
+    For each run of seq_len consecutive tokens: f_i is expert i's load
+    frequency, the number of the sequence's (token, choice) pairs that chose
+    i divided by the sequence length (the same normalisation as GShard's
+    c_e / S, item 1), and P_i the mean probability of i over the sequence.
+    The complementary loss is alpha times this value (alpha = 0.0001 on the
+    page); the caller applies alpha.
+    """
+    T, E = p.shape
+    L = int(seq_len)
+    out = np.zeros(T // L, np.float64)
+    for s in range(T // L):
+        ps = p[s * L:(s + 1) * L]
+        c = np.bincount(idx[s * L:(s + 1) * L].reshape(-1), minlength=E).astype(np.float64)
+        out[s] = float(np.sum((c / L) * (ps.sum(axis=0) / L)))
+    return out
+
+
 # --------------------------------------------------------------------------- keep rules
 def keep_capacity(e_flat, n_experts, C):
     """Token-choice routing truncated at capacity C per expert.
@@ -157,6 +232,23 @@ def keep_affinity(e_flat, w32_flat, n_experts, num, den):
         keep = (num * n + den - 1) // den
         ranked = sorted(members, key=lambda a: (-float(w32_flat[a]), a))
         kept[ranked[:keep]] = True
+    return kept
+
+
+def keep_expert_choice(e_flat, w32_flat, n_experts, C):
+    """Expert-choice routing: every expert keeps its top-C tokens by gate.
+
+    ([LocMoE+] router-taxonomy paragraph: the expert-choice router lets each
+    expert select the top-C tokens that suit it.)  Every token offers one
+    assignment to every expert (flat index a = t*E + e, gate = p_{t,e}); per
+    expert the min(C, T) assignments with the largest float32 gate are kept,
+    ties to the smaller flat index (the earlier token).
+    """
+    kept = np.zeros(len(e_flat), bool)
+    for e in range(n_experts):
+        members = np.nonzero(e_flat == e)[0].tolist()
+        ranked = sorted(members, key=lambda a: (-float(w32_flat[a]), a))
+        kept[ranked[:min(C, len(members))]] = True
     return kept
 
 
@@ -211,7 +303,7 @@ def expert_ffn(v, w1, w3, w2, act):
 
 
 # --------------------------------------------------------------------------- layer
-def route(cfg, zr, w_router, bias=None, logits=None):
+def route(cfg, zr, w_router, bias=None, logits=None, sel_bias=None):
     """Routing of every token: logits, probabilities, top-k, gates (+ aux for one head).
 
     Per head h the router reads the head's slice of its input and softmaxes
@@ -231,22 +323,43 @@ def route(cfg, zr, w_router, bias=None, logits=None):
             l32[:, h * Eh:(h + 1) * Eh] = router_logits(
                 zr[:, h * dh:(h + 1) * dh], w_r[h * Eh:(h + 1) * Eh], b)
     p = np.empty((T, cfg.n_experts), np.float64)
-    idx = np.empty((T, H * k), np.int32)
     for h in range(H):
         sl = slice(h * Eh, (h + 1) * Eh)
         p[:, sl] = softmax(l32[:, sl])
-        idx[:, h * k:(h + 1) * k] = h * Eh + select_topk(l32[:, sl], k, cfg.n_groups, cfg.topk_groups)
-    w = np.empty((T, H * k), np.float64)
-    for h in range(H):
-        w[:, h * k:(h + 1) * k] = gates(p, idx[:, h * k:(h + 1) * k], cfg.renorm)
+    if getattr(cfg, "route_mode", ROUTE_TOKEN_CHOICE) == ROUTE_EXPERT_CHOICE:
+        # expert choice (one head): every token offers every expert; the
+        # experts' own top-C choice is the keep rule
+        E = cfg.n_experts
+        idx = np.tile(np.arange(E, dtype=np.int32), (T, 1))
+        w = p.copy()
+    else:
+        idx = np.empty((T, H * k), np.int32)
+        for h in range(H):
+            sl = slice(h * Eh, (h + 1) * Eh)
+            if sel_bias is None:
+                idx[:, h * k:(h + 1) * k] = h * Eh + select_topk(l32[:, sl], k, cfg.n_groups, cfg.topk_groups)
+            else:
+                keys = biased_keys(p[:, sl], sel_bias[sl])
+                idx[:, h * k:(h + 1) * k] = h * Eh + select_topk_keys(keys, k, cfg.n_groups, cfg.topk_groups)
+        w = np.empty((T, H * k), np.float64)
+        for h in range(H):
+            ih = idx[:, h * k:(h + 1) * k]
+            if sel_bias is None:
+                w[:, h * k:(h + 1) * k] = gates(p, ih, cfg.renorm)
+            else:
+                w[:, h * k:(h + 1) * k] = biased_gates(p, sel_bias, ih, cfg.renorm, cfg.sel_bias_gate)
     aux = aux_loss(p, idx) if H == 1 else None
-    return dict(logits=l32, p=p, topk_idx=idx, topk_w=w, topk_w32=w.astype(np.float32), aux=aux)
+    seq = seq_balance(p, idx, cfg.seq_len) if getattr(cfg, "seq_len", 0) else None
+    return dict(logits=l32, p=p, topk_idx=idx, topk_w=w, topk_w32=w.astype(np.float32), aux=aux, seq=seq)
 
 
 def keep(cfg, topk_idx, topk_w32):
     """Keep rule over the flat assignments a = t*(H*k) + j."""
     e_flat = np.asarray(topk_idx).reshape(-1).astype(np.int64)
-    if cfg.drop == DROP_NONE:
+    if getattr(cfg, "route_mode", ROUTE_TOKEN_CHOICE) == ROUTE_EXPERT_CHOICE:
+        kept = keep_expert_choice(e_flat, np.asarray(topk_w32, np.float32).reshape(-1), cfg.n_experts,
+                                  cfg.capacity)
+    elif cfg.drop == DROP_NONE:
         # no token dropping ([MoE-evo] "DeepSeek-V3" item 5)
         kept = np.ones(len(e_flat), bool)
     elif cfg.drop == DROP_CAPACITY:
@@ -277,11 +390,12 @@ def forward(cfg, inp, logits=None, tokens=None, want_xperm=False):
     affinity rule couple tokens); the expert outputs are evaluated for
     `tokens` only.
     """
-    T, H, dh, k, E = cfg.T, cfg.n_heads, cfg.d_head, cfg.top_k, cfg.n_experts
+    T, H, dh, E = cfg.T, cfg.n_heads, cfg.d_head, cfg.n_experts
+    k = E if getattr(cfg, "route_mode", ROUTE_TOKEN_CHOICE) == ROUTE_EXPERT_CHOICE else cfg.top_k
     K = H * k
     x = decode(inp.x)
     z = x @ decode(inp.w_in).T if cfg.latent_proj else x
-    r = route(cfg, z, inp.w_router, inp.bias, logits)
+    r = route(cfg, z, inp.w_router, inp.bias, logits, getattr(inp, "sel_bias", None))
     kp = keep(cfg, r["topk_idx"], r["topk_w32"])
     out = dict(r, **kp, z=z if cfg.latent_proj else None)
     toks = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)

@@ -123,11 +123,11 @@ def _ungated(cfg, inp, out):
     return out2
 
 
-def m_route_head0(cfg, zr, w_router, bias=None, logits=None):
+def m_route_head0(cfg, zr, w_router, bias=None, logits=None, sel_bias=None):
     if cfg.n_heads == 1 or zr is None:
-        return _orig["route"](cfg, zr, w_router, bias, logits)
+        return _orig["route"](cfg, zr, w_router, bias, logits, sel_bias)
     z0 = np.tile(zr[:, :cfg.d_head], (1, cfg.n_heads))
-    return _orig["route"](cfg, z0, w_router, bias, logits)
+    return _orig["route"](cfg, z0, w_router, bias, logits, sel_bias)
 
 
 MUTANTS = [
