@@ -1,6 +1,6 @@
 """Benchmark: MoE layer forward tokens/s on one MI355X, with roofline fractions.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1|c2|c3|c4|c0] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1|c2|c3|c4|c0|c2ec|c2v3] [--no-cpu]
 
 Prints ONE JSON line on stdout (progress goes to stderr).  A step is one
 moe_layer_fwd call (route -> dispatch -> expert FFN -> combine, plus the latent
@@ -167,10 +167,11 @@ def main():
         sys.exit(2)
     import torch
     import routing_dispatch_expert_router_amd as moe
-    from moe_inputs import CONFIGS, generate
+    from moe_inputs import CONFIGS, VARIANTS, generate
 
-    names = {"c0": 0, "c1": 1, "c2": 2, "c3": 3, "c4": 4}
-    cfg = CONFIGS[names[args.config]] if args.config in names else next(c for c in CONFIGS if c.name == args.config)
+    short = {"c0": CONFIGS[0], "c1": CONFIGS[1], "c2": CONFIGS[2], "c3": CONFIGS[3], "c4": CONFIGS[4],
+             "c2ec": VARIANTS[0], "c2v3": VARIANTS[1]}
+    cfg = short[args.config] if args.config in short else next(c for c in CONFIGS + VARIANTS if c.name == args.config)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev_name = torch.cuda.get_device_properties(0).name
     log(f"[bench] {cfg.name} on {dev_name}: generating inputs")
@@ -187,7 +188,7 @@ def main():
 
     W = dict(w_router=dev(inp.w_router), router_bias=dev(inp.bias), w1=dev(inp.w1), w3=dev(inp.w3),
              w2=dev(inp.w2), ws1=dev(inp.ws1), ws3=dev(inp.ws3), ws2=dev(inp.ws2), w_in=dev(inp.w_in),
-             w_out=dev(inp.w_out))
+             w_out=dev(inp.w_out), sel_bias=dev(inp.sel_bias))
     x = dev(inp.x)
     y = torch.empty_like(x)
     T, K, E, dh = cfg.T, cfg.k_total, cfg.n_experts, cfg.d_head
@@ -203,7 +204,8 @@ def main():
               y_perm=torch.empty(Rm, dh, dtype=adt, device="cuda"),
               shared_out=torch.empty(T, cfg.d_model, dtype=adt, device="cuda") if cfg.n_shared else None,
               z=torch.empty(T, cfg.d_latent, dtype=adt, device="cuda") if cfg.latent_proj else None,
-              o=torch.empty(T, cfg.d_latent, dtype=adt, device="cuda") if cfg.latent_proj else None)
+              o=torch.empty(T, cfg.d_latent, dtype=adt, device="cuda") if cfg.latent_proj else None,
+              seq_loss=torch.empty(T // cfg.seq_len, dtype=torch.float32, device="cuda") if cfg.seq_len else None)
     ws = moe.workspace(cfg)
     stream = torch.cuda.current_stream()
 
@@ -245,7 +247,8 @@ def main():
 
     st = {}
     st["route"] = timed(lambda: moe.moe_route(cfg, xin, W["w_router"], W["router_bias"], None,
-                                              moe.MOE_LOGITS_COMPUTE, io["topk_idx"], io["topk_w"], None, ws))
+                                              moe.MOE_LOGITS_COMPUTE, io["topk_idx"], io["topk_w"], None, ws,
+                                              sel_bias=W["sel_bias"], seq_loss=io["seq_loss"]))
     st["dispatch"] = timed(lambda: moe.moe_dispatch(cfg, io["topk_idx"], io["topk_w"], None, io["demand"],
                                                     io["counts"], io["offsets"], io["row_of"], io["src_of"],
                                                     None, ws))
@@ -256,6 +259,10 @@ def main():
     st["combine"] = timed(lambda: moe.moe_combine(cfg, io["y_perm"], io["row_of"], io["topk_w"],
                                                   x if (cfg.residual and not cfg.latent_proj) else None,
                                                   io["shared_out"], io["o"] if cfg.latent_proj else y))
+    if W["sel_bias"] is not None:
+        # one balancing-bias update from this batch's loads, on a scratch copy of the bias
+        b_tmp = W["sel_bias"].clone()
+        st["sel_bias_update"] = timed(lambda: moe.moe_sel_bias_update(cfg, io["demand"], b_tmp, 0.001))
     bwd = None
     if not args.no_backward and moe.moe_backward_workspace_bytes(cfg) > 0:
         bwd = time_backward(cfg, moe, W, x, inp, args, stream)
@@ -278,6 +285,8 @@ def main():
     }
     for k in ("route", "dispatch", "combine"):
         stages[k]["hbm_frac"] = stages[k]["GBs"] / PEAK_HBM_GBS
+    if "sel_bias_update" in st:
+        stages["sel_bias_update"] = {"us": st["sel_bias_update"] * 1e6}
     stages["expert_ffn"]["mfma_frac"] = ffn_tf / peak
     for k, v in stages.items():
         log(f"[bench]   {k:10s} " + "  ".join(f"{a}={b:.4g}" for a, b in v.items()))
@@ -290,7 +299,10 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d_model": cfg.d_model, "n_experts": E, "top_k": cfg.top_k,
                    "n_heads": cfg.n_heads, "d_ff": cfg.d_ff, "n_shared": cfg.n_shared, "kept_rows": R,
                    "act": "swiglu" if cfg.act == 1 else "relu",
-                   "drop": ["none", "capacity", "affinity"][cfg.drop], "parallelism": "single GPU"},
+                   "drop": "expert_choice" if cfg.route_mode == 1 else ["none", "capacity", "affinity"][cfg.drop],
+                   "capacity": cfg.capacity if cfg.drop == 1 else None,
+                   "selection_bias": inp.sel_bias is not None, "seq_len": cfg.seq_len or None,
+                   "parallelism": "single GPU"},
         "roofline": {"kernel": "grouped_gemm_kernel, expert FFN (gate/up and down launches, rows gathered from x)",
                      "bound": "mfma", "achieved": ffn_tf, "peak": peak, "unit": "TFLOP/s", "frac": ffn_tf / peak,
                      "traffic": measured_traffic(cfg), "traffic_unit": "HBM bytes per expert-FFN call (all its launches)",
@@ -302,7 +314,8 @@ def main():
     if bwd is not None:
         bwd["fwd_bwd_tokens_per_s"] = T / ((ms_step + bwd["ms_per_step"]) * 1e-3)
     if not args.no_cpu:
-        sample = args.cpu_tokens or {0: 256, 1: 384, 2: 1024, 3: 96, 4: 2048}[names.get(args.config, 1)]
+        sample = args.cpu_tokens or {"c0": 256, "c1": 384, "c2": 1024, "c3": 96, "c4": 2048, "c2ec": 1024,
+                                     "c2v3": 1024}.get(args.config, 384)
         log(f"[bench] oracle CPU baseline on {sample} tokens")
         line["cpu_baseline"] = cpu_baseline(cfg, inp, sample)
     s = json.dumps(line)

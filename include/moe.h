@@ -65,6 +65,17 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum { MOE_ACT_RELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
 typedef enum { MOE_DROP_NONE = 0, MOE_DROP_CAPACITY = 1, MOE_DROP_AFFINITY = 2 } moe_drop;
+/* Who chooses ["jiqizhixin.com article on LocMoE+", router-taxonomy paragraph]:
+ *   TOKEN_CHOICE   every token picks top_k experts (per head)
+ *   EXPERT_CHOICE  every expert picks its top-C tokens by gate, C = capacity.
+ *                  Each token then has K = E assignment slots, slot j being
+ *                  expert j (topk_idx[t][j] = j, topk_w[t][j] = p_{t,j}); the
+ *                  keep rule is the experts' choice: per expert the min(C, T)
+ *                  largest gates are kept, equal gates to the earlier token.
+ *                  Requires n_heads == 1, n_groups == 0, renorm == 0,
+ *                  latent_proj == 0 and drop == MOE_DROP_CAPACITY (the C);
+ *                  top_k is not used. */
+typedef enum { MOE_ROUTE_TOKEN_CHOICE = 0, MOE_ROUTE_EXPERT_CHOICE = 1 } moe_route_mode;
 typedef enum {
   MOE_LOGITS_COMPUTE = 0,        /* compute scores from x and W_r; logits buffer unused (may be NULL) */
   MOE_LOGITS_COMPUTE_STORE = 1,  /* compute, and also write them to `logits` */
@@ -95,6 +106,11 @@ typedef struct moe_config {
                            residual is added after the output projection) */
   int32_t act_dtype;    /* moe_dtype of activations and expert weights */
   int32_t router_dtype; /* moe_dtype of W_r; MOE_BF16 requires act_dtype == MOE_BF16 */
+  int32_t route_mode;   /* moe_route_mode */
+  int32_t sel_bias_gate;/* with a selection bias (moe_weights.sel_bias): 1 the gate of a chosen
+                           expert is p + b (the formula as the page prints it), 0 it is p */
+  int32_t seq_len;      /* > 0: report the per-sequence balance statistic over runs of seq_len
+                           consecutive tokens (T % seq_len == 0, n_heads == 1); 0: off */
 } moe_config;
 
 /* Weights of one layer (device pointers; [out, in] layout). */
@@ -109,6 +125,8 @@ typedef struct moe_weights {
   const void *ws2;          /* [d_model, n_shared*d_ff] */
   const void *w_in;         /* [H*d_head, d_model] latent in-projection, or NULL */
   const void *w_out;        /* [d_model, H*d_head] latent out-projection, or NULL */
+  const float *sel_bias;    /* [E] float32 or NULL: balancing bias added to the probabilities for
+                               the top-k choice only (token choice; see moe_route) */
 } moe_weights;
 
 /* Optional outputs and intermediates of moe_layer_fwd.  Every pointer may be
@@ -125,6 +143,7 @@ typedef struct moe_layer_io {
   int32_t *row_of;          /* [T, K] row of each assignment in x_perm, -1 if dropped */
   int32_t *src_of;          /* [R_max] flat assignment (t*K + j) held by each row */
   float *aux_loss;          /* [1] GShard auxiliary loss (H == 1 only) */
+  float *seq_loss;          /* [T / seq_len] per-sequence balance statistic (seq_len > 0), or NULL */
   void *z;                  /* [T, H*d_head] act: latent (latent_proj only) */
   void *x_perm;             /* [R_max, d_head] act: expert-contiguous expert inputs; if
                                NULL, none is written and the expert FFN reads its rows
@@ -139,7 +158,7 @@ size_t moe_workspace_bytes(const moe_config *cfg);
 
 /* [host] Upper bound on R, the number of kept assignments:
  * T*H*top_k for MOE_DROP_NONE / MOE_DROP_AFFINITY, min(T*top_k, E*C) for
- * MOE_DROP_CAPACITY.  -1 for an invalid cfg. */
+ * MOE_DROP_CAPACITY, E*min(C, T) for expert choice.  -1 for an invalid cfg. */
 int64_t moe_rows_upper_bound(const moe_config *cfg);
 
 /* [host] Static string naming a moe_status value. */
@@ -168,11 +187,35 @@ int moe_check_config(const moe_config *cfg);
  *   aux_loss  [1] float32 out or NULL: sum_e m_e * c_e / T with m_e the mean
  *             probability and c_e the number of choices of e; H == 1 only
  *             (MOE_ERR_UNSUPPORTED otherwise)
+ *   sel_bias  [E] float32 or NULL: balancing bias ["MoE技术演进", "DeepSeek-V3"
+ *             item 1].  The top-k (and group scores) are taken on the float32
+ *             keys p + b instead of the scores; the gate of a chosen expert is
+ *             p + b if cfg->sel_bias_gate, else p (then renormalised if
+ *             cfg->renorm).  Token choice only (MOE_ERR_UNSUPPORTED otherwise).
+ *   seq_loss  [T / seq_len] float32 out or NULL (requires cfg->seq_len > 0):
+ *             for each run of seq_len consecutive tokens, sum_e f_e P_e with
+ *             f_e = (choices of e in the run) / seq_len and P_e the mean
+ *             probability of e over the run ["MoE技术演进", "DeepSeek-V3"
+ *             item 4: the sequence-wise balance loss is alpha times this]
+ * Expert choice (cfg->route_mode): topk_idx/topk_w are [T, E] with slot j =
+ * expert j and the gate p_{t,j}; the experts choose in moe_dispatch.
  * Scores must be finite; non-finite scores give unspecified routing.
  */
 int moe_route(const moe_config *cfg, const void *x, const void *w_router, const float *bias,
-              float *logits, int mode, int32_t *topk_idx, float *topk_w, float *aux_loss,
-              void *ws, size_t ws_bytes, hipStream_t stream);
+              const float *sel_bias, float *logits, int mode, int32_t *topk_idx, float *topk_w,
+              float *aux_loss, float *seq_loss, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_sel_bias_update -- one step of the balancing-bias update
+ * ["MoE技术演进", "DeepSeek-V3" item 1: the bias of an overloaded expert falls
+ * by gamma, that of an underloaded one rises by gamma (gamma = 0.001 there)].
+ * Per head h: with n_e the load of expert e (e.g. moe_dispatch's demand) and
+ * N_h the head's total, b_e -= gamma if n_e * E_h > N_h, b_e += gamma if
+ * n_e * E_h < N_h, unchanged at the mean (integer comparison).
+ *   load      [E] int32 in;  sel_bias [E] float32 in/out
+ */
+int moe_sel_bias_update(const moe_config *cfg, const int32_t *load, float *sel_bias, float gamma,
+                        hipStream_t stream);
 
 /*
  * moe_dispatch -- keep rule and permutation of tokens into an expert-contiguous buffer.
@@ -186,6 +229,9 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router, const 
  *   CAPACITY  a kept iff fewer than C earlier assignments (smaller a) chose e(a)
  *   AFFINITY  per expert, the ceil(keep_num*n_e/keep_den) assignments with the
  *             largest topk_w are kept (equal gates: smaller a first)
+ *   expert choice (cfg->route_mode): per expert, the min(C, n_e) assignments
+ *             with the largest topk_w are kept (equal gates: smaller a first);
+ *             K = E and a = t*E + e
  *
  *   topk_idx  [T, K] in, values in [0, E) (out-of-range values: undefined behaviour)
  *   topk_w    [T, K] in; read only for AFFINITY (may be NULL otherwise)

@@ -27,5 +27,5 @@ selection-only balancing bias of the routing variants, when a workload asks
 for one, is 0.001 * n_e with n_e drawn uniformly from [-steps, steps] (stream
 tag 11): the state such a bias reaches after some updates of step 0.001.
 """
-from .configs import MoEConfig, CONFIGS, SMALL, config_by_name  # noqa: F401
+from .configs import MoEConfig, CONFIGS, SMALL, VARIANTS, SMALL_VARIANTS, config_by_name  # noqa: F401
 from .gen import generate, bf16_bits_from_f32, Inputs  # noqa: F401

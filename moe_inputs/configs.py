@@ -109,8 +109,30 @@ SMALL = [
 ]
 
 
+# Routing variants on the fine-grained workload's shapes.
+# Expert choice: every expert keeps its top-768 tokens (= T*6/64: as many rows as
+# top-6 token choice at capacity factor 1.0).
+C2EC = C2.with_(name="c2ec_expert_choice_t8192_d2048_e64", route_mode=ROUTE_EXPERT_CHOICE, capacity=768, tag=5)
+# Balancing bias (selection only) with no dropping, and the per-sequence balance
+# statistic over two 4096-token sequences.
+C2V3 = C2.with_(name="c2v3_balancing_bias_t8192_d2048_e64", drop=DROP_NONE, capacity=0, sel_bias_steps=8,
+                seq_len=4096, tag=6)
+VARIANTS = [C2EC, C2V3]
+
+SMALL_VARIANTS = [
+    C2EC.with_(name="c2ec_s", T=520, d_model=256, d_head=256, n_experts=16, d_ff=192,
+               capacity=(520 * 6 + 15) // 16, tag=15),
+    C2V3.with_(name="c2v3_s", T=520, d_model=256, d_head=256, n_experts=16, d_ff=192, seq_len=260, tag=16),
+    # group-limited selection on the biased keys, bias inside renormalised-free gates, fp32
+    C3.with_(name="c3v3_s", T=400, d_model=320, d_head=320, n_experts=40, n_groups=8, topk_groups=3, d_ff=192,
+             drop=DROP_NONE, sel_bias_steps=8, sel_bias_gate=1, seq_len=100, n_shared=0, tag=17),
+    # expert choice in float32 with a ragged T and C > T / E
+    C0.with_(name="c0ec_f32", T=199, route_mode=ROUTE_EXPERT_CHOICE, capacity=70, tag=18),
+]
+
+
 def config_by_name(name):
-    for c in CONFIGS + SMALL:
+    for c in CONFIGS + SMALL + VARIANTS + SMALL_VARIANTS:
         if c.name == name:
             return c
     raise KeyError(name)

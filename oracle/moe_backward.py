@@ -35,6 +35,12 @@ Router:
   dW_r += dl^T x,  db += sum_t dl_t,  dx_t += W_r^T dl_t
 Shared experts and the residual: the same MLP backward with gate 1, and dx_t += dy_t.
 
+Routing variants: with expert choice every token has one slot per expert
+(K = E) and the experts' top-C choice is the keep mask; with the balancing
+bias b the decisions used b but are held fixed, and a gate that includes b
+(g = p + b, optionally renormalised) has the same derivative in p as
+without it, up to the renormalising sum, which then runs over p + b.
+
 The backward is defined for one routing head without the latent projections
 (the configurations moe_layer_bwd supports).  The probabilities p are those
 of the float64 logits (the forward rounds logits to float32 only to take its
@@ -55,8 +61,22 @@ def _silu_grad(a):
 def params_of(inp):
     """The float64 parameters of a generated input set, by name."""
     d = lambda a: None if a is None else decode(a)
+    sb = getattr(inp, "sel_bias", None)
     return dict(x=d(inp.x), w_router=d(inp.w_router), bias=None if inp.bias is None else np.asarray(inp.bias, np.float64),
-                w1=d(inp.w1), w3=d(inp.w3), w2=d(inp.w2), ws1=d(inp.ws1), ws3=d(inp.ws3), ws2=d(inp.ws2))
+                w1=d(inp.w1), w3=d(inp.w3), w2=d(inp.w2), ws1=d(inp.ws1), ws3=d(inp.ws3), ws2=d(inp.ws2),
+                sel_bias=None if sb is None else np.asarray(sb, np.float64))
+
+
+def _gate_values(cfg, P, pc, idx):
+    """Gates from the chosen probabilities pc: p (+ b when the bias is in the gate),
+    renormalised if asked; also returns the renormalising sum (None without)."""
+    g = pc
+    if P.get("sel_bias") is not None and getattr(cfg, "sel_bias_gate", 0):
+        g = pc + P["sel_bias"][idx.astype(np.int64)]
+    if cfg.renorm:
+        S = g.sum(axis=-1, keepdims=True)
+        return g / S, S
+    return g, None
 
 
 def _check_cfg(cfg):
@@ -70,14 +90,12 @@ def forward_fixed(cfg, P, topk_idx, kept, lam=0.0, dy=None):
     topk_idx [T, k] and kept [T*k] are the forward's decisions.
     """
     _check_cfg(cfg)
-    x, T, k = P["x"], cfg.T, cfg.top_k
+    x, T, k = P["x"], cfg.T, cfg.k_total
     l = x @ P["w_router"].T
     if P["bias"] is not None:
         l = l + P["bias"]
     p = softmax(l)
-    g = np.take_along_axis(p, topk_idx.astype(np.int64), axis=1)
-    if cfg.renorm:
-        g = g / g.sum(axis=1, keepdims=True)
+    g, _ = _gate_values(cfg, P, np.take_along_axis(p, topk_idx.astype(np.int64), axis=1), topk_idx)
     y = x.copy() if cfg.residual else np.zeros_like(x)
     keep2 = kept.reshape(T, k)
     for t in range(T):
@@ -149,7 +167,7 @@ def backward(cfg, P, topk_idx, kept, dy, lam=0.0):
     plus the intermediates dg [T, k] (gate gradients) and dl [T, E] (logit gradients).
     """
     _check_cfg(cfg)
-    x, T, k, E = P["x"], cfg.T, cfg.top_k, cfg.n_experts
+    x, T, k, E = P["x"], cfg.T, cfg.k_total, cfg.n_experts
     dy = np.asarray(dy, np.float64)
     l = x @ P["w_router"].T
     if P["bias"] is not None:
@@ -157,7 +175,7 @@ def backward(cfg, P, topk_idx, kept, dy, lam=0.0):
     p = softmax(l)
     idx = topk_idx.astype(np.int64)
     pc = np.take_along_axis(p, idx, axis=1)
-    g = pc / pc.sum(axis=1, keepdims=True) if cfg.renorm else pc
+    g, Psum = _gate_values(cfg, P, pc, idx)
     keep2 = kept.reshape(T, k)
 
     dx = dy.copy() if cfg.residual else np.zeros_like(x)
@@ -184,7 +202,6 @@ def backward(cfg, P, topk_idx, kept, dy, lam=0.0):
     # router: gates -> probabilities -> logits
     dp = np.zeros_like(p)
     if cfg.renorm:
-        Psum = pc.sum(axis=1, keepdims=True)
         dpc = (dg - np.sum(dg * g, axis=1, keepdims=True)) / Psum
     else:
         dpc = dg
@@ -220,8 +237,8 @@ def _gates_and_p(cfg, P, xt, idx_t):
         l = l + P["bias"]
     p = softmax(l)
     pc = np.take_along_axis(p, idx_t.astype(np.int64), axis=-1)
-    g = pc / pc.sum(axis=-1, keepdims=True) if cfg.renorm else pc
-    return p, pc, g
+    g, S = _gate_values(cfg, P, pc, idx_t)
+    return p, (pc if S is None else S), g
 
 
 def backward_tokens(cfg, P, topk_idx, kept, dy, lam, tokens, demand):
@@ -229,13 +246,13 @@ def backward_tokens(cfg, P, topk_idx, kept, dy, lam, tokens, demand):
     token (a token's input gradient depends on its own choices, and on the other
     tokens only through the aux loss's demand counts `demand` [E])."""
     _check_cfg(cfg)
-    k, T = cfg.top_k, cfg.T
+    k, T = cfg.k_total, cfg.T
     keep2 = np.asarray(kept).reshape(T, k)
     out = []
     for t in np.asarray(tokens, np.int64):
         xt = P["x"][t:t + 1]
         idx_t = topk_idx[t:t + 1].astype(np.int64)
-        p, pc, g = _gates_and_p(cfg, P, xt, idx_t)
+        p, S, g = _gates_and_p(cfg, P, xt, idx_t)
         dyt = np.asarray(dy[t:t + 1], np.float64)
         dx = dyt.copy() if cfg.residual else np.zeros_like(dyt)
         dg = np.zeros((1, k))
@@ -248,7 +265,7 @@ def backward_tokens(cfg, P, topk_idx, kept, dy, lam, tokens, demand):
             dv, _, _, _ = _mlp_backward(cfg.act, xt, P["w1"][e], w3, P["w2"][e], g[0, j] * dyt)
             dx += dv
         dp = np.zeros_like(p)
-        dpc = (dg - np.sum(dg * g, axis=1, keepdims=True)) / pc.sum(axis=1, keepdims=True) if cfg.renorm else dg
+        dpc = (dg - np.sum(dg * g, axis=1, keepdims=True)) / S if cfg.renorm else dg
         np.add.at(dp, (np.zeros(k, np.int64), idx_t[0]), dpc[0])
         if lam:
             dp += lam * np.asarray(demand, np.float64)[None, :] / (T * T)
@@ -269,7 +286,7 @@ def backward_expert(cfg, P, e, topk_idx, kept, dy, hidden=None):
     and dW3, columns of dW2: F = sum_f W2[:, f] h_f, so a unit's weight
     gradients depend on that unit only (and the upstream dF)."""
     _check_cfg(cfg)
-    T, k = cfg.T, cfg.top_k
+    T, k = cfg.T, cfg.k_total
     idx = topk_idx.astype(np.int64)
     rows, cols = np.nonzero((idx == e) & np.asarray(kept).reshape(T, k))
     xv = P["x"][rows]

@@ -28,16 +28,20 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DROP_NONE, MOE_DROP_CAPACITY, MOE_DROP_AFFINITY = 0, 1, 2
+MOE_ROUTE_TOKEN_CHOICE, MOE_ROUTE_EXPERT_CHOICE = 0, 1
 MOE_LOGITS_COMPUTE, MOE_LOGITS_COMPUTE_STORE, MOE_LOGITS_LOAD = 0, 1, 2
 
 CONFIG_FIELDS = ["T", "d_model", "n_heads", "d_head", "n_experts", "top_k", "n_groups", "topk_groups",
                  "renorm", "drop", "capacity", "keep_num", "keep_den", "d_ff", "act", "n_shared",
-                 "latent_proj", "residual", "act_dtype", "router_dtype"]
+                 "latent_proj", "residual", "act_dtype", "router_dtype", "route_mode", "sel_bias_gate",
+                 "seq_len"]
+# fields an older config object may lack: they default to 0 (token choice, no bias in the gate, off)
+_OPTIONAL_FIELDS = {"route_mode", "sel_bias_gate", "seq_len"}
 
 # exported symbols, as declared in include/moe.h
 SYMBOLS = ["moe_workspace_bytes", "moe_rows_upper_bound", "moe_status_str", "moe_check_config",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd",
-           "moe_backward_workspace_bytes", "moe_transpose_weights", "moe_layer_bwd"]
+           "moe_sel_bias_update", "moe_backward_workspace_bytes", "moe_transpose_weights", "moe_layer_bwd"]
 
 
 class MoeConfig(ctypes.Structure):
@@ -46,14 +50,15 @@ class MoeConfig(ctypes.Structure):
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_router", "router_bias", "w1", "w3", "w2", "ws1", "ws3", "ws2", "w_in", "w_out")]
+                ("w_router", "router_bias", "w1", "w3", "w2", "ws1", "ws3", "ws2", "w_in", "w_out", "sel_bias")]
 
 
 class MoeLayerIO(ctypes.Structure):
     _fields_ = [("logits", ctypes.c_void_p), ("logits_mode", ctypes.c_int32),
                 ("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("demand", ctypes.c_void_p),
                 ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p), ("row_of", ctypes.c_void_p),
-                ("src_of", ctypes.c_void_p), ("aux_loss", ctypes.c_void_p), ("z", ctypes.c_void_p),
+                ("src_of", ctypes.c_void_p), ("aux_loss", ctypes.c_void_p), ("seq_loss", ctypes.c_void_p),
+                ("z", ctypes.c_void_p),
                 ("x_perm", ctypes.c_void_p), ("y_perm", ctypes.c_void_p), ("shared_out", ctypes.c_void_p),
                 ("o", ctypes.c_void_p)]
 
@@ -83,7 +88,8 @@ def _load():
         "moe_rows_upper_bound": (ctypes.c_int64, [Z]),
         "moe_status_str": (ctypes.c_char_p, [I]),
         "moe_check_config": (I, [Z]),
-        "moe_route": (I, [Z, P, P, P, P, I, P, P, P, P, S, P]),
+        "moe_route": (I, [Z, P, P, P, P, P, I, P, P, P, P, P, S, P]),
+        "moe_sel_bias_update": (I, [Z, P, P, ctypes.c_float, P]),
         "moe_dispatch": (I, [Z, P, P, P, P, P, P, P, P, P, P, S, P]),
         "moe_expert_ffn": (I, [Z, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
         "moe_expert_ffn_gather": (I, [Z, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
@@ -105,7 +111,10 @@ _lib = _load()
 
 def config_struct(cfg):
     """moe_config from any object (or dict) carrying the C field names."""
-    get = (lambda n: cfg[n]) if isinstance(cfg, dict) else (lambda n: getattr(cfg, n))
+    if isinstance(cfg, dict):
+        get = lambda n: cfg[n] if (n in cfg or n not in _OPTIONAL_FIELDS) else 0
+    else:
+        get = lambda n: getattr(cfg, n) if (hasattr(cfg, n) or n not in _OPTIONAL_FIELDS) else 0
     return MoeConfig(*[int(get(n)) for n in CONFIG_FIELDS])
 
 
@@ -161,11 +170,18 @@ def _nbytes(ws):
     return 0 if ws is None else ws.numel() * ws.element_size()
 
 
-def moe_route(cfg, x, w_router, bias, logits, mode, topk_idx, topk_w, aux_loss, ws, stream=None):
+def moe_route(cfg, x, w_router, bias, logits, mode, topk_idx, topk_w, aux_loss, ws, stream=None, sel_bias=None,
+              seq_loss=None):
     c = _c(cfg)
-    return _check(_lib.moe_route(ctypes.byref(c), _p(x), _p(w_router), _p(bias), _p(logits), int(mode),
-                                 _p(topk_idx), _p(topk_w), _p(aux_loss), _p(ws), _nbytes(ws), _stream(stream)),
-                  "moe_route")
+    return _check(_lib.moe_route(ctypes.byref(c), _p(x), _p(w_router), _p(bias), _p(sel_bias), _p(logits),
+                                 int(mode), _p(topk_idx), _p(topk_w), _p(aux_loss), _p(seq_loss), _p(ws),
+                                 _nbytes(ws), _stream(stream)), "moe_route")
+
+
+def moe_sel_bias_update(cfg, load, sel_bias, gamma, stream=None):
+    c = _c(cfg)
+    return _check(_lib.moe_sel_bias_update(ctypes.byref(c), _p(load), _p(sel_bias), float(gamma), _stream(stream)),
+                  "moe_sel_bias_update")
 
 
 def moe_dispatch(cfg, topk_idx, topk_w, x, demand, counts, offsets, row_of, src_of, x_perm, ws, stream=None):

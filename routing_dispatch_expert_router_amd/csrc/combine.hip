@@ -31,23 +31,26 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int q = (int)(i - t * cpr);
     const int c0 = q * EPC;
     const int h = c0 / dh;
-    int row[KH];
-    float w[KH];
+    constexpr int KA = KH > 0 ? KH : 1;  // KH == 0: a runtime loop over k (expert choice)
+    int row[KA];
+    float w[KA];
+    u32x4 v[KA];
+    if constexpr (KH > 0) {
 #pragma unroll
-    for (int j = 0; j < KH; ++j) {
-      row[j] = -1;
-      w[j] = 0.f;
-      if (j < k) {
-        const int r = row_of[t * K + h * k + j];
-        row[j] = (r >= 0 && r < r_max) ? r : -1;
-        w[j] = topk_w[t * K + h * k + j];
+      for (int j = 0; j < KH; ++j) {
+        row[j] = -1;
+        w[j] = 0.f;
+        if (j < k) {
+          const int r = row_of[t * K + h * k + j];
+          row[j] = (r >= 0 && r < r_max) ? r : -1;
+          w[j] = topk_w[t * K + h * k + j];
+        }
       }
-    }
-    u32x4 v[KH];
 #pragma unroll
-    for (int j = 0; j < KH; ++j)
-      v[j] = row[j] >= 0 ? reinterpret_cast<const u32x4 *>(y_perm + (size_t)row[j] * dh + (c0 - h * dh))[0]
-                         : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < KH; ++j)
+        v[j] = row[j] >= 0 ? reinterpret_cast<const u32x4 *>(y_perm + (size_t)row[j] * dh + (c0 - h * dh))[0]
+                           : u32x4{0u, 0u, 0u, 0u};
+    }
     u32x4 rv = res ? reinterpret_cast<const u32x4 *>(res + (size_t)t * width)[q] : u32x4{0u, 0u, 0u, 0u};
     u32x4 sv = sh ? reinterpret_cast<const u32x4 *>(sh + (size_t)t * width)[q] : u32x4{0u, 0u, 0u, 0u};
     float acc[EPC];
@@ -64,12 +67,38 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[e] += Elem<TA>::to_f32(p[e]);
     }
+    if constexpr (KH > 0) {
 #pragma unroll
-    for (int j = 0; j < KH; ++j) {
-      if (row[j] < 0) continue;
-      const TA *p = reinterpret_cast<const TA *>(&v[j]);
+      for (int j = 0; j < KH; ++j) {
+        if (row[j] < 0) continue;
+        const TA *p = reinterpret_cast<const TA *>(&v[j]);
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[e] += w[j] * Elem<TA>::to_f32(p[e]);
+        for (int e = 0; e < EPC; ++e) acc[e] += w[j] * Elem<TA>::to_f32(p[e]);
+      }
+    } else {
+      // slots scanned four at a time (16-byte loads) when the row allows it
+      const int32_t *ro = row_of + t * K + h * k;
+      const bool vec = (k & 3) == 0 && ((uintptr_t)ro & 15) == 0;
+      for (int j0 = 0; j0 < k; j0 += 4) {
+        int r4[4];
+        if (vec) {
+          const int4 q4 = *reinterpret_cast<const int4 *>(ro + j0);
+          r4[0] = q4.x; r4[1] = q4.y; r4[2] = q4.z; r4[3] = q4.w;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) r4[u] = j0 + u < k ? ro[j0 + u] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = r4[u];
+          if (r < 0 || r >= r_max) continue;
+          const float wj = topk_w[t * K + h * k + j0 + u];
+          const u32x4 vj = reinterpret_cast<const u32x4 *>(y_perm + (size_t)r * dh + (c0 - h * dh))[0];
+          const TA *p = reinterpret_cast<const TA *>(&vj);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[e] += wj * Elem<TA>::to_f32(p[e]);
+        }
+      }
     }
     u32x4 o;
     TA *ov = reinterpret_cast<TA *>(&o);
@@ -95,7 +124,8 @@ static void launch_typed(const Shape &s, const void *y_perm, const int32_t *row_
   if (s.k <= 1) launch_c<TA, 1>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
   else if (s.k <= 2) launch_c<TA, 2>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
   else if (s.k <= 4) launch_c<TA, 4>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
-  else launch_c<TA, 8>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
+  else if (s.k <= 8) launch_c<TA, 8>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
+  else launch_c<TA, 0>(s, y_perm, row_of, topk_w, residual, shared_out, y, st);
 }
 
 int launch_combine(const Shape &s, const void *y_perm, const int32_t *row_of, const float *topk_w,

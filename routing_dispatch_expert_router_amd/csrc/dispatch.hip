@@ -1,6 +1,8 @@
 // Dispatch: keep rule and the permutation into an expert-contiguous buffer.
 //
 // Capacity C with overflow through the residual: "MoE技术演进", "GShard" item 1.
+// Expert choice (each expert keeps its top-C tokens): the LocMoE+ article's
+// router-taxonomy paragraph; it runs as the affinity path with C as the count.
 // Keep the best 90 % of each expert's tokens by affinity: "MoE技术演进",
 // "DeepSeek-V2" item 5 (here per expert, affinity = gate).  No dropping:
 // "DeepSeek-V3" item 5.  Count tokens per expert first, then fill each
@@ -111,23 +113,23 @@ __global__ __launch_bounds__(256) void disp_rank_kernel(
     }
     base[e] = b;
     dem[e] = tot;
-    kept[e] = drop == 0 ? tot
-              : drop == 1 ? min(tot, C)
-                          : (int)(((long)keep_num * tot + keep_den - 1) / keep_den);
+    kept[e] = drop == DROP_NONE       ? tot
+              : drop == DROP_AFFINITY ? (int)(((long)keep_num * tot + keep_den - 1) / keep_den)
+                                      : min(tot, C);  // capacity, or the experts' top-C choice
   }
   __syncthreads();
   const int R = block_scan_experts(kept, off, E, tmp);
-  if (drop == 2) block_scan_experts(dem, aoff, E, tmp);
+  if (drop >= DROP_AFFINITY) block_scan_experts(dem, aoff, E, tmp);
   if (c == 0) {
     for (int e = tid; e < E; e += 256) {
       demand[e] = dem[e];
       counts[e] = kept[e];
       offsets[e] = off[e];
-      if (drop == 2) all_off_out[e] = aoff[e];
+      if (drop >= DROP_AFFINITY) all_off_out[e] = aoff[e];
     }
     if (tid == 0) {
       offsets[E] = R;
-      if (drop == 2) all_off_out[E] = (int)n;
+      if (drop >= DROP_AFFINITY) all_off_out[E] = (int)n;
     }
   }
   constexpr int SUB = CH / 4;
@@ -162,10 +164,10 @@ __global__ __launch_bounds__(256) void disp_rank_kernel(
     bool leader = act && ((m >> lane) >> 1) == 0ull;
     if (leader) cnt[w * E + e] = rank + 1;
     if (act) {
-      if (drop == 2) {
+      if (drop >= DROP_AFFINITY) {
         seg[aoff[e] + rank] = (int32_t)a;
       } else {
-        bool kp = (drop == 0) || rank < C;
+        bool kp = (drop == DROP_NONE) || rank < C;
         int row = kp ? off[e] + rank : -1;
         row_of[a] = row;
         if (kp) src_of[row] = (int32_t)a;
@@ -192,18 +194,20 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
   return incl - v;
 }
 
-// One block per expert.  The expert's gate keys (up to AFF_LDS of them) are
-// staged in LDS; a 4-pass radix select (8 bits per pass, digit found by a
-// suffix scan over the 256 bins) gives the keep-th largest key; two ordered
-// scans then pick the kept assignments and their rows.
-constexpr int AFF_LDS = 2048;
+// One block per expert.  The expert's gate keys and assignments (up to `cap`
+// of them, in dynamic LDS) are staged once; a 4-pass radix select (8 bits per
+// pass, digit found by a suffix scan over the 256 bins) gives the keep-th
+// largest key; two ordered scans then pick the kept assignments and their rows.
+// An expert with more than `cap` assignments reads them from global memory.
+constexpr int AFF_LDS_MAX = (160 * 1024 - 4096) / 8;  // keys + indices beside ~2 KiB of static LDS
 
 __global__ __launch_bounds__(256) void disp_affinity_kernel(
     const int32_t *__restrict__ seg, const int32_t *__restrict__ all_off, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, const float *__restrict__ topk_w, int32_t *__restrict__ row_of,
-    int32_t *__restrict__ src_of) {
-  __shared__ uint32_t skey[AFF_LDS];
-  __shared__ int sa[AFF_LDS];
+    int32_t *__restrict__ src_of, int cap) {
+  extern __shared__ uint32_t dyn_lds[];
+  uint32_t *skey = dyn_lds;
+  int *sa = (int *)(dyn_lds + cap);
   __shared__ int hist[256];
   __shared__ int tmp[256];
   __shared__ uint32_t s_prefix;
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(256) void disp_affinity_kernel(
   const int keep = counts[e];
   const int out0 = offsets[e];
   if (n == 0) return;
-  const bool staged = n <= AFF_LDS;
+  const bool staged = n <= cap;
   if (staged) {
     for (int i = tid; i < n; i += 256) {
       const int a = seg[beg + i];
@@ -297,14 +301,21 @@ __global__ __launch_bounds__(256) void disp_scatter_kernel(
     const int q = (int)(i - t * cpr);
     const int c0 = q * EPC;
     const int h = c0 / dh;
-    int row[KH];
-#pragma unroll
-    for (int j = 0; j < KH; ++j) row[j] = j < k ? row_of[t * K + h * k + j] : -1;
     const u32x4 v = reinterpret_cast<const u32x4 *>(x + (size_t)t * width)[q];
+    if constexpr (KH == 0) {  // many slots per token (expert choice): a plain loop
+      for (int j = 0; j < k; ++j) {
+        const int r = row_of[t * K + h * k + j];
+        if (r >= 0 && r < r_max) reinterpret_cast<u32x4 *>(x_perm + (size_t)r * dh + (c0 - h * dh))[0] = v;
+      }
+    } else {
+      int row[KH];
 #pragma unroll
-    for (int j = 0; j < KH; ++j)
-      if (row[j] >= 0 && row[j] < r_max)
-        reinterpret_cast<u32x4 *>(x_perm + (size_t)row[j] * dh + (c0 - h * dh))[0] = v;
+      for (int j = 0; j < KH; ++j) row[j] = j < k ? row_of[t * K + h * k + j] : -1;
+#pragma unroll
+      for (int j = 0; j < KH; ++j)
+        if (row[j] >= 0 && row[j] < r_max)
+          reinterpret_cast<u32x4 *>(x_perm + (size_t)row[j] * dh + (c0 - h * dh))[0] = v;
+    }
   }
 }
 
@@ -314,7 +325,7 @@ static long n_chunks(const Shape &s) { return ((long)s.T * s.K + CH - 1) / CH; }
 size_t dispatch_ws_bytes(const Shape &s) {
   size_t b = align_up((size_t)n_chunks(s) * s.E * 4, 256);  // chunk histograms
   b += align_up((size_t)(s.E + 1) * 4, 256);                  // all_off
-  if (s.drop == 2) b += align_up((size_t)s.T * s.K * 4, 256);  // expert-sorted segments
+  if (s.drop >= DROP_AFFINITY) b += align_up((size_t)s.T * s.K * 4, 256);  // expert-sorted segments
   return b;
 }
 
@@ -329,7 +340,8 @@ static void launch_scatter(const Shape &s, const void *x, const int32_t *row_of,
   if (s.k <= 1) SC(1);
   else if (s.k <= 2) SC(2);
   else if (s.k <= 4) SC(4);
-  else SC(8);
+  else if (s.k <= 8) SC(8);
+  else SC(0);
 #undef SC
 }
 
@@ -343,16 +355,18 @@ int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w
   p += align_up((size_t)nc * s.E * 4, 256);
   int32_t *all_off = (int32_t *)p;
   p += align_up((size_t)(s.E + 1) * 4, 256);
-  int32_t *seg = (s.drop == 2) ? (int32_t *)p : nullptr;
+  int32_t *seg = (s.drop >= DROP_AFFINITY) ? (int32_t *)p : nullptr;
 
   hipLaunchKernelGGL(disp_hist_kernel, dim3(nc), dim3(256), s.E * 4, st, topk_idx, n, s.E, hist);
   if (int rc = launch_status("dispatch histogram")) return rc;
   hipLaunchKernelGGL(disp_rank_kernel, dim3(nc), dim3(256), 9 * s.E * 4, st, topk_idx, n, s.E, (int)nc, hist,
                      s.drop, s.C, s.keep_num, s.keep_den, demand, counts, offsets, all_off, row_of, src_of, seg);
   if (int rc = launch_status("dispatch rank")) return rc;
-  if (s.drop == 2) {
-    hipLaunchKernelGGL(disp_affinity_kernel, dim3(s.E), dim3(256), 0, st, seg, all_off, counts, offsets,
-                       topk_w, row_of, src_of);
+  if (s.drop >= DROP_AFFINITY) {
+    // an expert holds at most T assignments (one per token of its head)
+    const int cap = (int)std::min<long>(std::max(s.T, 1), AFF_LDS_MAX);
+    hipLaunchKernelGGL(disp_affinity_kernel, dim3(s.E), dim3(256), (size_t)cap * 8, st, seg, all_off, counts,
+                       offsets, topk_w, row_of, src_of, cap);
     if (int rc = launch_status("dispatch affinity")) return rc;
   }
   if (x_perm) {

@@ -14,10 +14,15 @@ namespace moe {
 int launch_status(const char *what);
 
 // Validated, normalised layer shape.
+// keep rules as the kernels see them: the public moe_drop values, and the
+// experts' own top-C choice of expert-choice routing
+enum { DROP_NONE = 0, DROP_CAPACITY = 1, DROP_AFFINITY = 2, DROP_TOPC = 3 };
+
 struct Shape {
-  int T, d, H, dh, E, Eh, k, K;  // K = H * k assignments per token
+  int T, d, H, dh, E, Eh, k, K;  // K = H * k assignments per token (expert choice: k = K = E)
   int n_groups, topk_groups, renorm;
   int drop, C, keep_num, keep_den;
+  int expert_choice, sel_gate, seq_len;
   int dff, act, n_shared, latent, residual;
   bool act_f32, router_f32;
   long R_max;                     // upper bound on kept rows
@@ -31,8 +36,10 @@ struct RouteGeom {
 RouteGeom route_geometry(const Shape &s);
 bool route_supported(const Shape &s);
 size_t route_ws_bytes(const Shape &s);
-int launch_route(const Shape &s, const void *x, const void *w_router, const float *bias, float *logits,
-                 int mode, int32_t *topk_idx, float *topk_w, float *aux_loss, void *ws, hipStream_t st);
+int launch_route(const Shape &s, const void *x, const void *w_router, const float *bias, const float *sel_bias,
+                 float *logits, int mode, int32_t *topk_idx, float *topk_w, float *aux_loss, float *seq_loss,
+                 void *ws, hipStream_t st);
+int launch_sel_bias_update(const Shape &s, const int32_t *load, float *sel_bias, float gamma, hipStream_t st);
 
 // ---------------------------------------------------------------- dispatch
 size_t dispatch_ws_bytes(const Shape &s);

@@ -37,6 +37,12 @@ int make_shape(const moe_config *c, Shape *s) {
     if ((long)c->top_k > (long)c->topk_groups * (Eh / c->n_groups)) return MOE_ERR_ARG;
   }
   if ((c->renorm != 0 && c->renorm != 1) || c->drop < 0 || c->drop > 2) return MOE_ERR_ARG;
+  if ((c->route_mode != MOE_ROUTE_TOKEN_CHOICE && c->route_mode != MOE_ROUTE_EXPERT_CHOICE) ||
+      (c->sel_bias_gate != 0 && c->sel_bias_gate != 1) || c->seq_len < 0)
+    return MOE_ERR_ARG;
+  if (c->seq_len > 0 && c->T % c->seq_len) return MOE_ERR_ARG;
+  const bool ec = c->route_mode == MOE_ROUTE_EXPERT_CHOICE;
+  if (ec && (c->drop != MOE_DROP_CAPACITY || c->renorm)) return MOE_ERR_ARG;
   if (c->drop == MOE_DROP_CAPACITY && c->capacity < 0) return MOE_ERR_ARG;
   if (c->drop == MOE_DROP_AFFINITY && (c->keep_num <= 0 || c->keep_den <= 0 || c->keep_num > c->keep_den))
     return MOE_ERR_ARG;
@@ -50,17 +56,23 @@ int make_shape(const moe_config *c, Shape *s) {
   if (c->top_k > 8 || Eh > 256 || c->n_experts > 1024 || c->n_groups > 32) return MOE_ERR_UNSUPPORTED;
   if (c->act_dtype == MOE_F32 && c->router_dtype == MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 0 && (c->n_heads != 1 || c->latent_proj)) return MOE_ERR_UNSUPPORTED;
-  if ((long)c->T * c->n_heads * c->top_k > 0x7FFFFFFFL) return MOE_ERR_UNSUPPORTED;
+  if (ec && (c->n_heads != 1 || c->n_groups || c->latent_proj)) return MOE_ERR_UNSUPPORTED;
+  if (c->seq_len > 0 && c->n_heads != 1) return MOE_ERR_UNSUPPORTED;
+  const long kslots = ec ? c->n_experts : (long)c->n_heads * c->top_k;
+  if ((long)c->T * kslots > 0x7FFFFFFFL) return MOE_ERR_UNSUPPORTED;
   s->T = c->T; s->d = c->d_model; s->H = c->n_heads; s->dh = c->d_head; s->E = c->n_experts; s->Eh = Eh;
-  s->k = c->top_k; s->K = c->n_heads * c->top_k;
+  s->k = ec ? Eh : c->top_k; s->K = (int)kslots;
   s->n_groups = c->n_groups; s->topk_groups = c->topk_groups; s->renorm = c->renorm;
-  s->drop = c->drop; s->C = c->capacity; s->keep_num = c->keep_num; s->keep_den = c->keep_den;
+  s->drop = ec ? moe::DROP_TOPC : c->drop; s->C = c->capacity; s->keep_num = c->keep_num;
+  s->keep_den = c->keep_den;
+  s->expert_choice = ec; s->sel_gate = c->sel_bias_gate; s->seq_len = c->seq_len;
   s->dff = c->d_ff; s->act = c->act; s->n_shared = c->n_shared; s->latent = c->latent_proj;
   s->residual = c->residual;
   s->act_f32 = c->act_dtype == MOE_F32;
   s->router_f32 = c->router_dtype == MOE_F32;
   long tk = (long)s->T * s->K;
-  s->R_max = (s->drop == MOE_DROP_CAPACITY) ? (tk < (long)s->E * s->C ? tk : (long)s->E * s->C) : tk;
+  if (ec) s->R_max = (long)s->E * std::min<long>(s->C, s->T);
+  else s->R_max = (s->drop == MOE_DROP_CAPACITY) ? std::min<long>(tk, (long)s->E * s->C) : tk;
   if (!moe::route_supported(*s)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -205,9 +217,9 @@ int moe_check_config(const moe_config *cfg) {
   return make_shape(cfg, &s);
 }
 
-int moe_route(const moe_config *cfg, const void *x, const void *w_router, const float *bias, float *logits,
-              int mode, int32_t *topk_idx, float *topk_w, float *aux_loss, void *ws, size_t ws_bytes,
-              hipStream_t stream) {
+int moe_route(const moe_config *cfg, const void *x, const void *w_router, const float *bias,
+              const float *sel_bias, float *logits, int mode, int32_t *topk_idx, float *topk_w,
+              float *aux_loss, float *seq_loss, void *ws, size_t ws_bytes, hipStream_t stream) {
   Shape s;
   int rc = make_shape(cfg, &s);
   if (rc) return rc;
@@ -216,10 +228,23 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router, const 
   if (mode != MOE_LOGITS_LOAD && (!x || !w_router)) return MOE_ERR_ARG;
   if (mode != MOE_LOGITS_COMPUTE && !logits) return MOE_ERR_ARG;
   if (aux_loss && s.H != 1) return MOE_ERR_UNSUPPORTED;
+  if (seq_loss && s.seq_len == 0) return MOE_ERR_ARG;
+  if (sel_bias && s.expert_choice) return MOE_ERR_UNSUPPORTED;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   if (s.T == 0) return MOE_OK;
   clear_stale_error();
-  return rc_of(moe::launch_route(s, x, w_router, bias, logits, mode, topk_idx, topk_w, aux_loss, ws, stream));
+  return rc_of(moe::launch_route(s, x, w_router, bias, sel_bias, logits, mode, topk_idx, topk_w, aux_loss,
+                                 seq_loss, ws, stream));
+}
+
+int moe_sel_bias_update(const moe_config *cfg, const int32_t *load, float *sel_bias, float gamma,
+                        hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, &s);
+  if (rc) return rc;
+  if (!load || !sel_bias) return MOE_ERR_ARG;
+  clear_stale_error();
+  return rc_of(moe::launch_sel_bias_update(s, load, sel_bias, gamma, stream));
 }
 
 int moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, const float *topk_w, const void *x,
@@ -306,6 +331,8 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
   if (s.n_shared && (!w->ws1 || !w->ws2 || ((s.act == MOE_ACT_SWIGLU) != (w->ws3 != nullptr)))) return MOE_ERR_ARG;
   if (s.latent && (!w->w_in || !w->w_out)) return MOE_ERR_ARG;
   if (io->aux_loss && s.H != 1) return MOE_ERR_UNSUPPORTED;
+  if (io->seq_loss && s.seq_len == 0) return MOE_ERR_ARG;
+  if (w->sel_bias && s.expert_choice) return MOE_ERR_UNSUPPORTED;
   if (!io->x_perm && !gather_supported(s)) return MOE_ERR_UNSUPPORTED;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   if (s.T == 0) return MOE_OK;
@@ -334,8 +361,8 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
       return rc;
     xin = z;
   }
-  if ((rc = rc_of(moe::launch_route(s, xin, w->w_router, w->router_bias, io->logits, mode, topk_idx, topk_w,
-                                    io->aux_loss, scratch, stream))))
+  if ((rc = rc_of(moe::launch_route(s, xin, w->w_router, w->router_bias, w->sel_bias, io->logits, mode, topk_idx,
+                                    topk_w, io->aux_loss, io->seq_loss, scratch, stream))))
     return rc;
   if ((rc = rc_of(moe::launch_dispatch(s, topk_idx, topk_w, xin, demand, counts, offsets, row_of, src_of, x_perm,
                                        scratch, stream))))
@@ -403,6 +430,8 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
   if (rc) return rc;
   if (!w || !wt || !x || !dy || !io || !g) return MOE_ERR_ARG;
   if (!bwd_supported(s)) return MOE_ERR_UNSUPPORTED;
+  // a bias inside renormalised gates changes the renormalisation's derivative
+  if (w->sel_bias && s.sel_gate && s.renorm) return MOE_ERR_UNSUPPORTED;
   const bool glu = s.act == MOE_ACT_SWIGLU;
   if (!w->w_router || !w->w1 || !w->w2 || (glu && !w->w3) || !wt->w13t || !wt->w2t) return MOE_ERR_ARG;
   if (!io->logits || !io->topk_idx || !io->topk_w || !io->demand || !io->offsets || !io->row_of ||

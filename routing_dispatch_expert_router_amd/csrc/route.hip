@@ -5,7 +5,11 @@
 // "MoE技术演进", "DeepSeek-V2" item 3 (pick the best M devices, then top-K inside;
 // devices are groups of consecutive experts here).  Per-head selection inside
 // a fixed expert partition: "多头 LatentMoE 与 Head Parallel", 方法论 item 2.
-// Aux loss: "MoE技术演进", "GShard" item 1.
+// Aux loss: "MoE技术演进", "GShard" item 1.  Balancing bias added to the
+// probabilities for selection, its update, and the sequence-wise balance term:
+// "MoE技术演进", "DeepSeek-V3" items 1 and 4.  Expert-choice routing (every
+// token offers every expert; the experts choose in dispatch): the LocMoE+
+// article's router-taxonomy paragraph.
 //
 // Two kernels.  route_logits: a split-K MFMA product of a token tile with the
 // head's router weights (staged in LDS, shared by the block's 4 waves), writing
@@ -151,12 +155,17 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
 // ------------------------------------------------------------------ selection
 // L lanes (a power of two <= 16) per (token, head) pair; lane j of a pair owns
 // local experts j, j+L, j+2L, ...  (at most EPL of them).
+// sel_bias != NULL: selection (and group scores) on the float32 keys p + b
+// instead of the scores; the gate is p, plus b when sel_gate.  all_experts:
+// the token lists every expert of its head in index order with gate p (expert
+// choice; no top-k).  probs != NULL: p of every expert is written out.
 template <int EPL, int KMAX>
 __global__ __launch_bounds__(256) void route_select_kernel(
     const float *__restrict__ part, int nsplit, const float *__restrict__ bias,
     float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
     float *__restrict__ aux_p, int32_t *__restrict__ aux_c,
-    int T, int H, int E, int Eh, int k, int L, int n_groups, int topk_groups, int renorm) {
+    int T, int H, int E, int Eh, int k, int L, int n_groups, int topk_groups, int renorm,
+    const float *__restrict__ sel_bias, int sel_gate, int all_experts, float *__restrict__ probs) {
   extern __shared__ float sh[];  // [pairs_per_block][Eh] probabilities for the aux partials
   const int tid = threadIdx.x;
   const int ppb = 256 / L;
@@ -191,6 +200,50 @@ __global__ __launch_bounds__(256) void route_select_kernel(
 #pragma unroll
   for (int i = 0; i < EPL; ++i) s += (j + L * i < Eh) ? __expf(lv[i] - m) : 0.f;
   s = group_sum_fixed(s, L);
+  if (probs && valid) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = j + L * i;
+      if (e < Eh) probs[(size_t)t * E + h * Eh + e] = __expf(lv[i] - m) / s;
+    }
+  }
+  if (all_experts) {  // expert choice: slot e = expert e, gate p (one head)
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = j + L * i;
+        if (e < Eh) {
+          topk_idx[(size_t)t * Eh + e] = e;
+          topk_w[(size_t)t * Eh + e] = __expf(lv[i] - m) / s;
+        }
+      }
+    }
+    if (aux_p) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = j + L * i;
+        if (e < Eh) sh[pr * Eh + e] = valid ? __expf(lv[i] - m) / s : 0.f;
+      }
+      __syncthreads();
+      const long first = (long)blockIdx.x * ppb;
+      const int nvalid = (int)min((long)ppb, (long)T * H - first);
+      for (int e = tid; e < Eh; e += 256) {
+        float acc = 0.f;
+        for (int q = 0; q < ppb; ++q) acc += sh[q * Eh + e];
+        aux_p[(size_t)blockIdx.x * Eh + e] = acc;
+        atomicAdd(&aux_c[e], nvalid);  // every token offers every expert
+      }
+    }
+    return;
+  }
+  // selection keys: the scores, or p + b under the balancing bias
+  float kv[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = j + L * i;
+    kv[i] = lv[i];
+    if (sel_bias && valid && e < Eh) kv[i] = (__expf(lv[i] - m) / s + sel_bias[h * Eh + e]) + 0.0f;
+  }
 
   // group-limited: allowed-group bitmask (groups of consecutive experts)
   uint32_t allowed = 0xFFFFFFFFu;
@@ -208,7 +261,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
       if (g < n_groups) {
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
-          if (j + L * i < Eh && grp[i] == g) v = fmaxf(v, lv[i]);
+          if (j + L * i < Eh && grp[i] == g) v = fmaxf(v, kv[i]);
         v = wave_max(v, L);
       }
       gkey[g] = score_key(v);
@@ -231,7 +284,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     int e = j + L * i;
     bool ok = e < Eh;
     if (ok && n_groups > 0) ok = (allowed >> grp[i]) & 1u;
-    kk[i] = ok ? (((uint64_t)score_key(lv[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)) : 0ull;
+    kk[i] = ok ? (((uint64_t)score_key(kv[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)) : 0ull;
   }
   int sel_e[KMAX];
   float sel_l[KMAX];
@@ -264,6 +317,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     for (int r = 0; r < KMAX; ++r) {
       if (r >= k) break;
       wr[r] = __expf(sel_l[r] - m) / s;
+      if (sel_bias && sel_gate) wr[r] += sel_bias[h * Eh + sel_e[r]];
       wsum += wr[r];
     }
 #pragma unroll
@@ -310,6 +364,81 @@ __global__ void route_aux_kernel(const float *__restrict__ aux_p, const int32_t 
   if (threadIdx.x == 0) *aux = red[0];
 }
 
+// Per-sequence balance statistic, two passes.  Pass 1: one block per chunk of
+// SEQ_CH tokens inside one sequence: column sums of p over the chunk (tokens in
+// order) and the chunk's choice counts (integer LDS atomics, order-free).
+// Pass 2: one block per sequence adds its chunks in order and reduces
+// sum_e (c_e / L) (P_e / L) by a fixed tree.
+constexpr int SEQ_CH = 32;
+
+__global__ __launch_bounds__(256) void route_seq_part_kernel(const float *__restrict__ probs,
+                                                             const int32_t *__restrict__ topk_idx, int E, int K,
+                                                             int L, int nch, float *__restrict__ psum,
+                                                             int32_t *__restrict__ pcnt) {
+  extern __shared__ int cnt[];  // [E]
+  const int tid = threadIdx.x;
+  const int sq = blockIdx.x / nch, ch = blockIdx.x % nch;
+  const long t0 = (long)sq * L + (long)ch * SEQ_CH;
+  const int nt = min(SEQ_CH, L - ch * SEQ_CH);
+  for (int e = tid; e < E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  for (int i = tid; i < nt * K; i += 256) atomicAdd(&cnt[topk_idx[t0 * K + i]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    float P = 0.f;
+    for (int t = 0; t < nt; ++t) P += probs[(size_t)(t0 + t) * E + e];
+    psum[(size_t)blockIdx.x * E + e] = P;
+    pcnt[(size_t)blockIdx.x * E + e] = cnt[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void route_seq_kernel(const float *__restrict__ psum,
+                                                        const int32_t *__restrict__ pcnt, int E, int L, int nch,
+                                                        float *__restrict__ seq_loss) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  const size_t b0 = (size_t)blockIdx.x * nch;
+  float v = 0.f;
+  for (int e = tid; e < E; e += 256) {
+    float P = 0.f;
+    long c = 0;
+    for (int ch = 0; ch < nch; ++ch) {
+      P += psum[(b0 + ch) * E + e];
+      c += pcnt[(b0 + ch) * E + e];
+    }
+    v += ((float)c / (float)L) * (P / (float)L);
+  }
+  red[tid] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) seq_loss[blockIdx.x] = red[0];
+}
+
+// Balancing-bias update, one block per head: b_e += gamma * sign(N_h - n_e E_h)
+// with N_h the head's total load (integer comparison).
+__global__ __launch_bounds__(256) void sel_bias_update_kernel(const int32_t *__restrict__ load, float *sel_bias,
+                                                              int Eh, float gamma) {
+  __shared__ long long red[256];
+  const int tid = threadIdx.x, h = blockIdx.x;
+  long long v = 0;
+  for (int e = tid; e < Eh; e += 256) v += load[(size_t)h * Eh + e];
+  red[tid] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  const long long tot = red[0];
+  for (int e = tid; e < Eh; e += 256) {
+    const long long n = (long long)load[(size_t)h * Eh + e] * Eh;
+    const float step = n > tot ? -1.f : (n < tot ? 1.f : 0.f);
+    sel_bias[(size_t)h * Eh + e] = sel_bias[(size_t)h * Eh + e] + gamma * step;
+  }
+}
+
 __global__ void zero_i32_kernel(int32_t *p, long n) {
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) p[i] = 0;
 }
@@ -353,6 +482,11 @@ size_t route_ws_bytes(const Shape &s) {
   if (g.nplanes == 3) b += align_up((size_t)s.H * 3 * g.Epad * s.dh * 2, 256);
   b += align_up((size_t)g.sel_blocks * s.Eh * 4, 256);                   // aux partials
   b += align_up((size_t)s.E * 4, 256);                                    // aux counts
+  if (s.seq_len > 0) {
+    const size_t nb = (size_t)(s.T / s.seq_len) * ((s.seq_len + SEQ_CH - 1) / SEQ_CH);
+    b += align_up((size_t)s.T * s.E * 4, 256);                            // probabilities
+    b += 2 * align_up(nb * s.E * 4, 256);                                  // chunk sums and counts
+  }
   return b;
 }
 
@@ -402,8 +536,9 @@ bool route_supported(const Shape &s) {
   return g.nf > 0 && g.epl <= 16;
 }
 
-int launch_route(const Shape &s, const void *x, const void *w_router, const float *bias, float *logits,
-                 int mode, int32_t *topk_idx, float *topk_w, float *aux_loss, void *ws, hipStream_t st) {
+int launch_route(const Shape &s, const void *x, const void *w_router, const float *bias, const float *sel_bias,
+                 float *logits, int mode, int32_t *topk_idx, float *topk_w, float *aux_loss, float *seq_loss,
+                 void *ws, hipStream_t st) {
   RouteGeom g = route_geometry(s);
   char *p = (char *)ws;
   float *part = (float *)p;
@@ -416,6 +551,17 @@ int launch_route(const Shape &s, const void *x, const void *w_router, const floa
   float *aux_p = (float *)p;
   p += align_up((size_t)g.sel_blocks * s.Eh * 4, 256);
   int32_t *aux_c = (int32_t *)p;
+  p += align_up((size_t)s.E * 4, 256);
+  float *probs = nullptr, *psum = nullptr;
+  int32_t *pcnt = nullptr;
+  const int nseq = s.seq_len > 0 ? s.T / s.seq_len : 0, nch = s.seq_len > 0 ? (s.seq_len + SEQ_CH - 1) / SEQ_CH : 0;
+  if (seq_loss) {
+    probs = (float *)p;
+    p += align_up((size_t)s.T * s.E * 4, 256);
+    psum = (float *)p;
+    p += align_up((size_t)nseq * nch * s.E * 4, 256);
+    pcnt = (int32_t *)p;
+  }
 
   const float *src = part;
   int nsplit = g.ksplit;
@@ -450,7 +596,8 @@ int launch_route(const Shape &s, const void *x, const void *w_router, const floa
 #define SEL(EPL_)                                                                                   \
   hipLaunchKernelGGL((route_select_kernel<EPL_, 8>), dim3(g.sel_blocks), dim3(256), shm, st, src, nsplit, \
                      bias, lout, topk_idx, topk_w, aux ? aux_p : nullptr, aux_c, s.T, s.H, s.E, s.Eh, s.k,   \
-                     g.L, s.n_groups, s.topk_groups, s.renorm)
+                     g.L, s.n_groups, s.topk_groups, s.renorm, s.expert_choice ? nullptr : sel_bias, s.sel_gate, \
+                     s.expert_choice, probs)
   if (g.epl <= 4) SEL(4);
   else if (g.epl <= 8) SEL(8);
   else SEL(16);
@@ -461,7 +608,20 @@ int launch_route(const Shape &s, const void *x, const void *w_router, const floa
                        aux_loss);
     LAUNCH_CHECK();
   }
+  if (seq_loss) {
+    hipLaunchKernelGGL(route_seq_part_kernel, dim3((unsigned)(nseq * nch)), dim3(256), (size_t)s.E * 4, st, probs,
+                       topk_idx, s.E, s.K, s.seq_len, nch, psum, pcnt);
+    LAUNCH_CHECK();
+    hipLaunchKernelGGL(route_seq_kernel, dim3((unsigned)nseq), dim3(256), 0, st, psum, pcnt, s.E, s.seq_len, nch,
+                       seq_loss);
+    LAUNCH_CHECK();
+  }
   return 0;
+}
+
+int launch_sel_bias_update(const Shape &s, const int32_t *load, float *sel_bias, float gamma, hipStream_t st) {
+  hipLaunchKernelGGL(sel_bias_update_kernel, dim3((unsigned)s.H), dim3(256), 0, st, load, sel_bias, s.Eh, gamma);
+  return launch_status("selection bias update");
 }
 
 }  // namespace moe

@@ -64,7 +64,7 @@ def tol(cfg):
 def weights_dev(cfg, inp):
     return dict(w_router=dev(inp.w_router), router_bias=dev(inp.bias), w1=dev(inp.w1), w3=dev(inp.w3),
                 w2=dev(inp.w2), ws1=dev(inp.ws1), ws3=dev(inp.ws3), ws2=dev(inp.ws2), w_in=dev(inp.w_in),
-                w_out=dev(inp.w_out))
+                w_out=dev(inp.w_out), sel_bias=dev(getattr(inp, "sel_bias", None)))
 
 
 def routing_margin(cfg, l32):

@@ -6,7 +6,8 @@ What pins what:
                    every parameter, on tiny configurations covering ReLU /
                    SwiGLU, renormalised gates, capacity and affinity drops,
                    group-limited routing, shared experts, the residual
-                   switch, and the aux-loss term alone
+                   switch, expert-choice routing, the balancing bias in and
+                   out of the (renormalised) gate, and the aux-loss term alone
   forward_fixed    equals the main oracle's layer output (which takes its
                    probabilities from float32-rounded logits) to 1e-5
   special cases    one expert with top-1: p = g = 1, so no gradient reaches
@@ -38,6 +39,10 @@ def tiny_cfgs():
         base.with_(name="bwd_affinity_groups", drop=2, keep_num=2, keep_den=3, n_groups=2, topk_groups=1,
                    n_experts=6, top_k=2),
         base.with_(name="bwd_no_residual_zipf", residual=0, zipf_s=1.0, top_k=3),
+        base.with_(name="bwd_expert_choice", route_mode=1, drop=1, capacity=5),
+        base.with_(name="bwd_selbias_in_gate", sel_bias_steps=40, sel_bias_gate=1, n_shared=1),
+        base.with_(name="bwd_selbias_renorm", sel_bias_steps=40, renorm=1),
+        base.with_(name="bwd_selbias_in_gate_renorm", sel_bias_steps=40, sel_bias_gate=1, renorm=1),
         base.with_(name="bwd_one_expert", n_experts=1, top_k=1),
     ]
 

@@ -102,24 +102,23 @@ def test_calls_reject_bad_arguments_before_launching():
     c = moe.config_struct(CONFIGS[2])
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
     # null config
-    assert lib.moe_route(None, fake, fake, None, None, 0, fake, fake, None, fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    assert lib.moe_route(None, fake, fake, None, None, None, 0, fake, fake, None, None, fake, 1 << 40, None) == moe.MOE_ERR_ARG
     # missing outputs
-    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 0, None, fake, None, fake, 1 << 40, None) \
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, 0, None, fake, None, None, fake, 1 << 40, None) \
         == moe.MOE_ERR_ARG
     # LOAD mode needs logits
-    assert lib.moe_route(ctypes.byref(c), None, None, None, None, 2, fake, fake, None, fake, 1 << 40, None) \
+    assert lib.moe_route(ctypes.byref(c), None, None, None, None, None, 2, fake, fake, None, None, fake, 1 << 40, None) \
         == moe.MOE_ERR_ARG
     # bad mode
-    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 5, fake, fake, None, fake, 1 << 40, None) \
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, 5, fake, fake, None, None, fake, 1 << 40, None) \
         == moe.MOE_ERR_ARG
     # workspace too small / misaligned
-    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 0, fake, fake, None, fake, 16, None) \
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, 0, fake, fake, None, None, fake, 16, None) \
         == moe.MOE_ERR_WORKSPACE
-    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 0, fake, fake, None, ctypes.c_void_p(0x1001),
-                         1 << 40, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, 0, fake, fake, None, None, ctypes.c_void_p(0x1001), 1 << 40, None) == moe.MOE_ERR_WORKSPACE
     # aux loss is defined for one head only
     c4 = moe.config_struct(CONFIGS[4])
-    assert lib.moe_route(ctypes.byref(c4), fake, fake, None, None, 0, fake, fake, fake, fake, 1 << 40, None) \
+    assert lib.moe_route(ctypes.byref(c4), fake, fake, None, None, None, 0, fake, fake, fake, None, fake, 1 << 40, None) \
         == moe.MOE_ERR_UNSUPPORTED
     # affinity keep needs the gates
     c3 = moe.config_struct(CONFIGS[3])
@@ -149,8 +148,8 @@ def test_calls_reject_bad_arguments_before_launching():
 
 
 def test_config_struct_layout_matches_header():
-    # 20 int32 fields, in header order
-    assert ctypes.sizeof(moe.MoeConfig) == 20 * 4
+    # 23 int32 fields, in header order
+    assert ctypes.sizeof(moe.MoeConfig) == 23 * 4
     src = open(HEADER).read()
     body = src[src.index("typedef struct moe_config {"):src.index("} moe_config;")]
     fields = re.findall(r"int32_t\s+([^;]+);", body)
@@ -187,3 +186,35 @@ def test_backward_rejects_bad_arguments_before_launching():
     assert lib.moe_layer_bwd(ctypes.byref(c4), ctypes.byref(w), ctypes.byref(wt), fake, fake, 0.0, ctypes.byref(io),
                              ctypes.byref(g), fake, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_transpose_weights(ctypes.byref(c), ctypes.byref(w), ctypes.byref(wt), None) == moe.MOE_ERR_ARG
+
+
+def test_routing_variant_checks():
+    """Expert choice, the balancing bias and the sequence statistic: argument rules (no launches)."""
+    lib = moe._lib
+    fake = ctypes.c_void_p(0x1000)
+    base = CONFIGS[2]
+    ec = base.with_(route_mode=1)
+    assert moe.moe_check_config(ec) == moe.MOE_OK
+    # K = E slots per token, R bounded by E * min(C, T)
+    assert moe.moe_rows_upper_bound(ec) == ec.n_experts * min(ec.capacity, ec.T)
+    # expert choice needs the capacity rule and no renormalisation
+    assert moe.moe_check_config(ec.with_(drop=0)) == moe.MOE_ERR_ARG
+    assert moe.moe_check_config(ec.with_(renorm=1)) == moe.MOE_ERR_ARG
+    assert moe.moe_check_config(CONFIGS[4].with_(route_mode=1, drop=1, capacity=8)) == moe.MOE_ERR_UNSUPPORTED
+    assert moe.moe_check_config(CONFIGS[3].with_(route_mode=1, drop=1, capacity=8)) == moe.MOE_ERR_UNSUPPORTED
+    assert moe.moe_check_config(base.with_(route_mode=2)) == moe.MOE_ERR_ARG
+    assert moe.moe_check_config(base.with_(sel_bias_gate=2)) == moe.MOE_ERR_ARG
+    # the sequence length divides T; one head only
+    assert moe.moe_check_config(base.with_(seq_len=4096)) == moe.MOE_OK
+    assert moe.moe_check_config(base.with_(seq_len=3000)) == moe.MOE_ERR_ARG
+    assert moe.moe_check_config(CONFIGS[4].with_(seq_len=4096)) == moe.MOE_ERR_UNSUPPORTED
+    c = moe.config_struct(base)
+    # a sequence statistic needs seq_len; a selection bias is for token choice only
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, 0, fake, fake, None, fake, fake, 1 << 40,
+                         None) == moe.MOE_ERR_ARG
+    ce = moe.config_struct(ec)
+    assert lib.moe_route(ctypes.byref(ce), fake, fake, None, fake, None, 0, fake, fake, None, None, fake, 1 << 40,
+                         None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_sel_bias_update(ctypes.byref(c), None, fake, 0.001, None) == moe.MOE_ERR_ARG
+    assert lib.moe_sel_bias_update(ctypes.byref(c), fake, None, 0.001, None) == moe.MOE_ERR_ARG
+    assert lib.moe_sel_bias_update(None, fake, fake, 0.001, None) == moe.MOE_ERR_ARG
