@@ -194,6 +194,26 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
   return incl - v;
 }
 
+// Exclusive count of set flags over a 256-thread block (thread order) and the
+// total: in-wave ballot prefix plus the earlier waves' counts.
+__device__ __forceinline__ int block_excl_count(bool f, int *wsum, int *total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t b = __ballot(f);
+  const int in_wave = __popcll(b & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[w] = __popcll(b);
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int v = wsum[q];
+    before += q < w ? v : 0;
+    tot += v;
+  }
+  __syncthreads();  // wsum is rewritten by the next call
+  *total = tot;
+  return before + in_wave;
+}
+
 // One block per expert.  The expert's gate keys and assignments (up to `cap`
 // of them, in dynamic LDS) are staged once; a 4-pass radix select (8 bits per
 // pass, digit found by a suffix scan over the 256 bins) gives the keep-th
@@ -268,11 +288,11 @@ __global__ __launch_bounds__(256) void disp_affinity_kernel(
       kept = act;
     } else {
       const bool eq = act && key == prefix;
-      const int eq_before = block_excl_scan(eq ? 1 : 0, tmp, &tot);
+      const int eq_before = block_excl_count(eq, tmp, &tot);
       kept = act && (key > prefix || (eq && eq_seen + eq_before < need));
       eq_seen += tot;
     }
-    const int kb = block_excl_scan(kept ? 1 : 0, tmp, &tot);
+    const int kb = block_excl_count(kept, tmp, &tot);
     if (act) {
       // never past this expert's `keep` rows, even if the selection were off
       kept = kept && (kept_seen + kb < keep);

@@ -396,17 +396,45 @@ __global__ __launch_bounds__(256) void route_seq_kernel(const float *__restrict_
                                                         const int32_t *__restrict__ pcnt, int E, int L, int nch,
                                                         float *__restrict__ seq_loss) {
   __shared__ float red[256];
+  __shared__ float gp[256];
+  __shared__ int gc[256];
   const int tid = threadIdx.x;
   const size_t b0 = (size_t)blockIdx.x * nch;
   float v = 0.f;
-  for (int e = tid; e < E; e += 256) {
-    float P = 0.f;
-    long c = 0;
-    for (int ch = 0; ch < nch; ++ch) {
-      P += psum[(b0 + ch) * E + e];
-      c += pcnt[(b0 + ch) * E + e];
+  if (E <= 128) {
+    // G groups of E threads split the chunks; the groups' sums are added in order
+    const int G = 256 / E, g = tid / E, e = tid % E;
+    if (g < G) {
+      const int c0 = (int)((long)nch * g / G), c1 = (int)((long)nch * (g + 1) / G);
+      float P = 0.f;
+      int c = 0;
+      for (int ch = c0; ch < c1; ++ch) {
+        P += psum[(b0 + ch) * E + e];
+        c += pcnt[(b0 + ch) * E + e];
+      }
+      gp[g * E + e] = P;
+      gc[g * E + e] = c;
     }
-    v += ((float)c / (float)L) * (P / (float)L);
+    __syncthreads();
+    if (tid < E) {
+      float P = 0.f;
+      long c = 0;
+      for (int q = 0; q < G; ++q) {
+        P += gp[q * E + tid];
+        c += gc[q * E + tid];
+      }
+      v = ((float)c / (float)L) * (P / (float)L);
+    }
+  } else {
+    for (int e = tid; e < E; e += 256) {
+      float P = 0.f;
+      long c = 0;
+      for (int ch = 0; ch < nch; ++ch) {
+        P += psum[(b0 + ch) * E + e];
+        c += pcnt[(b0 + ch) * E + e];
+      }
+      v += ((float)c / (float)L) * (P / (float)L);
+    }
   }
   red[tid] = v;
   __syncthreads();
