@@ -576,6 +576,18 @@ static int pick_tile(long rows, int groups) {
   return avg >= 1024 ? TILE_256x256_W8 : TILE_128x128_W8;
 }
 
+// Routed products.  With expert choice every expert holds exactly min(C, T)
+// rows (known here): the big tile unless its last row tile would be mostly
+// padding.  Otherwise only the average is known.
+static int pick_tile_routed(const Shape &s) {
+  if (s.expert_choice) {
+    const long n = std::min<long>(s.C, s.T);
+    const long waste = (n + 255) / 256 * 256 - n;
+    return (n >= 256 && waste * 8 <= n) ? TILE_256x256_W8 : TILE_128x128_W8;
+  }
+  return pick_tile(s.R_max, s.E);
+}
+
 // A plain product (one group, no routed rows: a.E == 0, a.has_x == 1): the
 // tile count of each launch is known on the host; launches with no tiles are
 // skipped.
@@ -616,7 +628,7 @@ int gemm_routed(const Shape &s, int epi, const void *A, long lda, const int32_t 
   a.B = B; a.B2 = B2; a.ldb = ldb; a.bstride = bstride; a.C = C; a.ldc = ldc;
   a.offsets = offsets; a.E = s.E; a.N = N; a.K = K; a.Mr_bound = s.R_max; a.G = s.E;
   a.dh = dh; a.lddh = lddh; a.hout = hout; a.ldh = ldh;
-  const int tile = s.act_f32 ? TILE_128x128 : pick_tile(s.R_max, s.E);
+  const int tile = s.act_f32 ? TILE_128x128 : pick_tile_routed(s);
   Launch l[2];
   const int nl = plan_launches(tile, l);
   PrepArgs pa{};
@@ -696,7 +708,7 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
   const bool glu = s.act == 1;
   const int has_x = s.n_shared ? 1 : 0;
   // f32 layers are parity-sized: the small tile is plenty
-  const int tile = sizeof(TE) == 4 ? TILE_128x128 : pick_tile(s.R_max, s.E);
+  const int tile = sizeof(TE) == 4 ? TILE_128x128 : pick_tile_routed(s);
   const int epi1 = glu ? EPI_SWIGLU : EPI_RELU;
   Launch l[2];
   const int nl = plan_launches(tile, l);
