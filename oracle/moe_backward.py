@@ -41,8 +41,15 @@ bias b the decisions used b but are held fixed, and a gate that includes b
 (g = p + b, optionally renormalised) has the same derivative in p as
 without it, up to the renormalising sum, which then runs over p + b.
 
-The backward is defined for one routing head without the latent projections
-(the configurations moe_layer_bwd supports).  The probabilities p are those
+Several routing heads and the latent projections ([LatentMoE] 方法论 items
+1-2): u = x W_in^T (or u = x), head h routes on u's h-th slice within its own
+E_h experts (softmax and renormalisation per head) and its experts run on that
+slice, o_{t,h} = sum_{j in head h} g_{t,j} F_e(u_{t,h}); y = o W_out^T + x.
+Then do = dy W_out, dW_out = dy^T o, the per-head backward above runs with do
+in place of dy and u in place of x (giving du), dW_in = du^T x and
+dx = dy + du W_in.  The aux loss is defined for one head only.
+
+The probabilities p are those
 of the float64 logits (the forward rounds logits to float32 only to take its
 decisions); forward_fixed below is that smooth function, which the
 finite-difference pins differentiate.
@@ -64,7 +71,33 @@ def params_of(inp):
     sb = getattr(inp, "sel_bias", None)
     return dict(x=d(inp.x), w_router=d(inp.w_router), bias=None if inp.bias is None else np.asarray(inp.bias, np.float64),
                 w1=d(inp.w1), w3=d(inp.w3), w2=d(inp.w2), ws1=d(inp.ws1), ws3=d(inp.ws3), ws2=d(inp.ws2),
-                sel_bias=None if sb is None else np.asarray(sb, np.float64))
+                sel_bias=None if sb is None else np.asarray(sb, np.float64),
+                w_in=d(getattr(inp, "w_in", None)), w_out=d(getattr(inp, "w_out", None)))
+
+
+def _u(cfg, P, x=None):
+    """Expert and router input: the latent u = x W_in^T, or x itself."""
+    x = P["x"] if x is None else x
+    return x @ P["w_in"].T if cfg.latent_proj else x
+
+
+def _probs(cfg, P, u):
+    """p [n, E]: per head h, softmax over its E_h experts of u_h W_r[h]^T (+ b_h)."""
+    H, Eh, dh = cfg.n_heads, cfg.e_per_head, cfg.d_head
+    p = np.empty((u.shape[0], cfg.n_experts))
+    for h in range(H):
+        rows = slice(h * Eh, (h + 1) * Eh)
+        l = u[:, h * dh:(h + 1) * dh] @ P["w_router"][rows].T
+        if P["bias"] is not None:
+            l = l + P["bias"][rows]
+        p[:, rows] = softmax(l)
+    return p
+
+
+def _kh(cfg):
+    """Slots per head (k) and per token (K = H k)."""
+    K = cfg.k_total
+    return K // cfg.n_heads, K
 
 
 def _gate_values(cfg, P, pc, idx):
@@ -74,14 +107,35 @@ def _gate_values(cfg, P, pc, idx):
     if P.get("sel_bias") is not None and getattr(cfg, "sel_bias_gate", 0):
         g = pc + P["sel_bias"][idx.astype(np.int64)]
     if cfg.renorm:
-        S = g.sum(axis=-1, keepdims=True)
+        # per head: the sum over the head's own k slots
+        k, K = _kh(cfg)
+        n = g.shape[0]
+        S = np.repeat(g.reshape(n, K // k, k).sum(axis=2), k, axis=1)
         return g / S, S
     return g, None
 
 
-def _check_cfg(cfg):
-    if cfg.n_heads != 1 or cfg.latent_proj:
-        raise NotImplementedError("the backward oracle covers one routing head without latent projections")
+def _check_cfg(cfg, lam=0.0):
+    if lam and cfg.n_heads != 1:
+        raise ValueError("the aux loss is defined for one routing head")
+
+
+def routed_o(cfg, P, topk_idx, kept, u=None):
+    """o [T, H*d_head]: each head's gate-weighted sum of its kept experts on its slice of u."""
+    u = _u(cfg, P) if u is None else u
+    T, dh, Eh = cfg.T, cfg.d_head, cfg.e_per_head
+    k, K = _kh(cfg)
+    idx = topk_idx.astype(np.int64)
+    g, _ = _gate_values(cfg, P, np.take_along_axis(_probs(cfg, P, u), idx, axis=1), idx)
+    keep2 = np.asarray(kept).reshape(T, K)
+    o = np.zeros((T, cfg.n_heads * dh))
+    for e in range(cfg.n_experts):
+        h = e // Eh
+        rows, cols = np.nonzero((idx == e) & keep2)
+        if len(rows):
+            hs = slice(h * dh, (h + 1) * dh)
+            o[rows, hs] += g[rows, cols][:, None] * _ffn(cfg, P, e, u[rows, hs])
+    return o
 
 
 def forward_fixed(cfg, P, topk_idx, kept, lam=0.0, dy=None):
@@ -89,22 +143,15 @@ def forward_fixed(cfg, P, topk_idx, kept, lam=0.0, dy=None):
 
     topk_idx [T, k] and kept [T*k] are the forward's decisions.
     """
-    _check_cfg(cfg)
-    x, T, k = P["x"], cfg.T, cfg.k_total
-    l = x @ P["w_router"].T
-    if P["bias"] is not None:
-        l = l + P["bias"]
-    p = softmax(l)
-    g, _ = _gate_values(cfg, P, np.take_along_axis(p, topk_idx.astype(np.int64), axis=1), topk_idx)
-    y = x.copy() if cfg.residual else np.zeros_like(x)
-    keep2 = kept.reshape(T, k)
-    for t in range(T):
-        for j in range(k):
-            if not keep2[t, j]:
-                continue
-            e = int(topk_idx[t, j])
-            y[t] += g[t, j] * _ffn(cfg, P, e, x[t:t + 1])[0]
-    if cfg.n_shared:
+    _check_cfg(cfg, lam)
+    x, T = P["x"], cfg.T
+    u = _u(cfg, P)
+    p = _probs(cfg, P, u)
+    o = routed_o(cfg, P, topk_idx, kept, u)
+    if cfg.latent_proj:
+        y = o @ P["w_out"].T + x
+    else:
+        y = (x.copy() if cfg.residual else np.zeros_like(x)) + o
         for i in range(cfg.n_shared):
             y += _shared_ffn(cfg, P, i, x)
     L = None
@@ -160,61 +207,95 @@ def _mlp_backward(act, v, w1, w3, w2, dF):
     return dv, dW1, dW3, dW2
 
 
+def _head_softmax_backward(cfg, p, dp):
+    """dl = p (dp - <p, dp>) within each head's experts (softmax Jacobian per head)."""
+    Eh = cfg.e_per_head
+    dl = np.empty_like(p)
+    for h in range(cfg.n_heads):
+        rows = slice(h * Eh, (h + 1) * Eh)
+        ph, dph = p[:, rows], dp[:, rows]
+        dl[:, rows] = ph * (dph - np.sum(ph * dph, axis=1, keepdims=True))
+    return dl
+
+
+def _gate_to_prob_grad(cfg, g, S, dg):
+    """dp at the chosen slots from the gate gradients (per-head renormalisation)."""
+    if not cfg.renorm:
+        return dg
+    k, K = _kh(cfg)
+    n = dg.shape[0]
+    sdg = np.repeat((dg * g).reshape(n, K // k, k).sum(axis=2), k, axis=1)
+    return (dg - sdg) / S
+
+
 def backward(cfg, P, topk_idx, kept, dy, lam=0.0):
     """Gradients of L = <dy, y> + lam * l_aux (see the module docstring), float64.
 
-    Returns dict: dx, dw_router, dbias, dw1, dw3, dw2, dws1, dws3, dws2 (None where absent),
-    plus the intermediates dg [T, k] (gate gradients) and dl [T, E] (logit gradients).
+    Returns dict: dx, dw_router, dbias, dw1, dw3, dw2, dws1, dws3, dws2, dw_in, dw_out
+    (None where absent), plus the intermediates dg [T, K] (gate gradients), dl [T, E]
+    (logit gradients) and du [T, H*d_head] (gradient of the expert input u).
     """
-    _check_cfg(cfg)
-    x, T, k, E = P["x"], cfg.T, cfg.k_total, cfg.n_experts
+    _check_cfg(cfg, lam)
+    x, T, E, Eh, dh = P["x"], cfg.T, cfg.n_experts, cfg.e_per_head, cfg.d_head
+    k, K = _kh(cfg)
     dy = np.asarray(dy, np.float64)
-    l = x @ P["w_router"].T
-    if P["bias"] is not None:
-        l = l + P["bias"]
-    p = softmax(l)
+    u = _u(cfg, P)
+    p = _probs(cfg, P, u)
     idx = topk_idx.astype(np.int64)
     pc = np.take_along_axis(p, idx, axis=1)
-    g, Psum = _gate_values(cfg, P, pc, idx)
-    keep2 = kept.reshape(T, k)
+    g, S = _gate_values(cfg, P, pc, idx)
+    keep2 = np.asarray(kept).reshape(T, K)
 
-    dx = dy.copy() if cfg.residual else np.zeros_like(x)
+    dw_in = dw_out = None
+    if cfg.latent_proj:
+        o = routed_o(cfg, P, topk_idx, kept, u)
+        dw_out = dy.T @ o
+        do = dy @ P["w_out"]
+    else:
+        do = dy
+    du = np.zeros((T, cfg.n_heads * dh))
     dw1 = np.zeros_like(P["w1"])
     dw2 = np.zeros_like(P["w2"])
     dw3 = np.zeros_like(P["w3"]) if P["w3"] is not None else None
-    dg = np.zeros((T, k))
+    dg = np.zeros((T, K))
     for e in range(E):
         rows, cols = np.nonzero((idx == e) & keep2)
         if len(rows) == 0:
             continue
-        v = x[rows]
+        hs = slice((e // Eh) * dh, (e // Eh + 1) * dh)
+        v = u[rows, hs]
         w3 = P["w3"][e] if P["w3"] is not None else None
         F = _ffn(cfg, P, e, v)
-        dg[rows, cols] = np.sum(dy[rows] * F, axis=1)
-        dF = g[rows, cols][:, None] * dy[rows]
+        dg[rows, cols] = np.sum(do[rows, hs] * F, axis=1)
+        dF = g[rows, cols][:, None] * do[rows, hs]
         dv, a, b, c = _mlp_backward(cfg.act, v, P["w1"][e], w3, P["w2"][e], dF)
-        np.add.at(dx, rows, dv)
+        np.add.at(du, (rows[:, None], np.arange(hs.start, hs.stop)[None, :]), dv)
         dw1[e] += a
         dw2[e] += c
         if b is not None:
             dw3[e] += b
 
-    # router: gates -> probabilities -> logits
+    # router: gates -> probabilities -> logits, per head
     dp = np.zeros_like(p)
-    if cfg.renorm:
-        dpc = (dg - np.sum(dg * g, axis=1, keepdims=True)) / Psum
-    else:
-        dpc = dg
-    np.add.at(dp, (np.arange(T)[:, None].repeat(k, 1), idx), dpc)
+    np.add.at(dp, (np.arange(T)[:, None].repeat(K, 1), idx), _gate_to_prob_grad(cfg, g, S, dg))
     if lam:
         c = np.bincount(idx.reshape(-1), minlength=E).astype(np.float64)
         dp += lam * c[None, :] / (T * T)
-    dl = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
-    dw_router = dl.T @ x
+    dl = _head_softmax_backward(cfg, p, dp)
+    dw_router = np.empty_like(P["w_router"])
+    for h in range(cfg.n_heads):
+        rows = slice(h * Eh, (h + 1) * Eh)
+        hs = slice(h * dh, (h + 1) * dh)
+        dw_router[rows] = dl[:, rows].T @ u[:, hs]
+        du[:, hs] += dl[:, rows] @ P["w_router"][rows]
     dbias = dl.sum(axis=0)
-    dx += dl @ P["w_router"]
 
     dws1 = dws2 = dws3 = None
+    if cfg.latent_proj:
+        dw_in = du.T @ x
+        dx = dy + du @ P["w_in"]
+    else:
+        dx = (dy.copy() if cfg.residual else np.zeros_like(x)) + du
     if cfg.n_shared:
         dws1, dws2 = np.zeros_like(P["ws1"]), np.zeros_like(P["ws2"])
         dws3 = np.zeros_like(P["ws3"]) if P["ws3"] is not None else None
@@ -228,49 +309,49 @@ def backward(cfg, P, topk_idx, kept, dy, lam=0.0):
             if b is not None:
                 dws3[i * f:(i + 1) * f] += b
     return dict(dx=dx, dw_router=dw_router, dbias=dbias, dw1=dw1, dw3=dw3, dw2=dw2,
-                dws1=dws1, dws3=dws3, dws2=dws2, dg=dg, dl=dl)
-
-
-def _gates_and_p(cfg, P, xt, idx_t):
-    l = xt @ P["w_router"].T
-    if P["bias"] is not None:
-        l = l + P["bias"]
-    p = softmax(l)
-    pc = np.take_along_axis(p, idx_t.astype(np.int64), axis=-1)
-    g, S = _gate_values(cfg, P, pc, idx_t)
-    return p, (pc if S is None else S), g
+                dws1=dws1, dws3=dws3, dws2=dws2, dw_in=dw_in, dw_out=dw_out, dg=dg, dl=dl, du=du)
 
 
 def backward_tokens(cfg, P, topk_idx, kept, dy, lam, tokens, demand):
     """dx of the given tokens only: the same chain rule as `backward`, evaluated per
     token (a token's input gradient depends on its own choices, and on the other
     tokens only through the aux loss's demand counts `demand` [E])."""
-    _check_cfg(cfg)
-    k, T = cfg.k_total, cfg.T
-    keep2 = np.asarray(kept).reshape(T, k)
+    _check_cfg(cfg, lam)
+    T, E, Eh, dh = cfg.T, cfg.n_experts, cfg.e_per_head, cfg.d_head
+    k, K = _kh(cfg)
+    keep2 = np.asarray(kept).reshape(T, K)
     out = []
     for t in np.asarray(tokens, np.int64):
         xt = P["x"][t:t + 1]
+        ut = _u(cfg, P, xt)
         idx_t = topk_idx[t:t + 1].astype(np.int64)
-        p, S, g = _gates_and_p(cfg, P, xt, idx_t)
+        p = _probs(cfg, P, ut)
+        g, S = _gate_values(cfg, P, np.take_along_axis(p, idx_t, axis=1), idx_t)
         dyt = np.asarray(dy[t:t + 1], np.float64)
-        dx = dyt.copy() if cfg.residual else np.zeros_like(dyt)
-        dg = np.zeros((1, k))
-        for j in range(k):
+        dot = dyt @ P["w_out"] if cfg.latent_proj else dyt
+        du = np.zeros((1, cfg.n_heads * dh))
+        dg = np.zeros((1, K))
+        for j in range(K):
             if not keep2[t, j]:
                 continue
             e = int(idx_t[0, j])
+            hs = slice((e // Eh) * dh, (e // Eh + 1) * dh)
             w3 = P["w3"][e] if P["w3"] is not None else None
-            dg[0, j] = float(np.sum(dyt * _ffn(cfg, P, e, xt)))
-            dv, _, _, _ = _mlp_backward(cfg.act, xt, P["w1"][e], w3, P["w2"][e], g[0, j] * dyt)
-            dx += dv
+            dg[0, j] = float(np.sum(dot[:, hs] * _ffn(cfg, P, e, ut[:, hs])))
+            dv, _, _, _ = _mlp_backward(cfg.act, ut[:, hs], P["w1"][e], w3, P["w2"][e], g[0, j] * dot[:, hs])
+            du[:, hs] += dv
         dp = np.zeros_like(p)
-        dpc = (dg - np.sum(dg * g, axis=1, keepdims=True)) / S if cfg.renorm else dg
-        np.add.at(dp, (np.zeros(k, np.int64), idx_t[0]), dpc[0])
+        np.add.at(dp, (np.zeros(K, np.int64), idx_t[0]), _gate_to_prob_grad(cfg, g, S, dg)[0])
         if lam:
             dp += lam * np.asarray(demand, np.float64)[None, :] / (T * T)
-        dl = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
-        dx += dl @ P["w_router"]
+        dl = _head_softmax_backward(cfg, p, dp)
+        for h in range(cfg.n_heads):
+            rows = slice(h * Eh, (h + 1) * Eh)
+            du[:, h * dh:(h + 1) * dh] += dl[:, rows] @ P["w_router"][rows]
+        if cfg.latent_proj:
+            dx = dyt + du @ P["w_in"]
+        else:
+            dx = (dyt.copy() if cfg.residual else np.zeros_like(dyt)) + du
         for i in range(cfg.n_shared):
             w1, w3, w2 = _shared_slices(cfg, P, i)
             dv, _, _, _ = _mlp_backward(cfg.act, xt, w1, w3, w2, dyt)
@@ -285,14 +366,19 @@ def backward_expert(cfg, P, e, topk_idx, kept, dy, hidden=None):
     `hidden` (index array) restricts them to those hidden units -- rows of dW1
     and dW3, columns of dW2: F = sum_f W2[:, f] h_f, so a unit's weight
     gradients depend on that unit only (and the upstream dF)."""
-    _check_cfg(cfg)
-    T, k = cfg.T, cfg.k_total
+    T, Eh, dh = cfg.T, cfg.e_per_head, cfg.d_head
+    k, K = _kh(cfg)
     idx = topk_idx.astype(np.int64)
-    rows, cols = np.nonzero((idx == e) & np.asarray(kept).reshape(T, k))
-    xv = P["x"][rows]
-    _, _, g = _gates_and_p(cfg, P, xv, idx[rows])
-    dF = g[np.arange(len(rows)), cols][:, None] * np.asarray(dy, np.float64)[rows]
-    hs = slice(None) if hidden is None else np.asarray(hidden, np.int64)
-    w3 = P["w3"][e][hs] if P["w3"] is not None else None
-    _, dW1, dW3, dW2 = _mlp_backward(cfg.act, xv, P["w1"][e][hs], w3, P["w2"][e][:, hs], dF)
+    rows, cols = np.nonzero((idx == e) & np.asarray(kept).reshape(T, K))
+    hs = slice((e // Eh) * dh, (e // Eh + 1) * dh)
+    xr = P["x"][rows]
+    ur = _u(cfg, P, xr)
+    p = _probs(cfg, P, ur)
+    g, _ = _gate_values(cfg, P, np.take_along_axis(p, idx[rows], axis=1), idx[rows])
+    dyr = np.asarray(dy, np.float64)[rows]
+    dor = dyr @ P["w_out"] if cfg.latent_proj else dyr
+    dF = g[np.arange(len(rows)), cols][:, None] * dor[:, hs]
+    hu = slice(None) if hidden is None else np.asarray(hidden, np.int64)
+    w3 = P["w3"][e][hu] if P["w3"] is not None else None
+    _, dW1, dW3, dW2 = _mlp_backward(cfg.act, ur[:, hs], P["w1"][e][hu], w3, P["w2"][e][:, hu], dF)
     return dW1, dW3, dW2

@@ -7,7 +7,9 @@ What pins what:
                    SwiGLU, renormalised gates, capacity and affinity drops,
                    group-limited routing, shared experts, the residual
                    switch, expert-choice routing, the balancing bias in and
-                   out of the (renormalised) gate, and the aux-loss term alone
+                   out of the (renormalised) gate, several routing heads with
+                   and without the latent projections (W_in and W_out
+                   perturbed too), and the aux-loss term alone
   forward_fixed    equals the main oracle's layer output (which takes its
                    probabilities from float32-rounded logits) to 1e-5
   special cases    one expert with top-1: p = g = 1, so no gradient reaches
@@ -43,6 +45,10 @@ def tiny_cfgs():
         base.with_(name="bwd_selbias_in_gate", sel_bias_steps=40, sel_bias_gate=1, n_shared=1),
         base.with_(name="bwd_selbias_renorm", sel_bias_steps=40, renorm=1),
         base.with_(name="bwd_selbias_in_gate_renorm", sel_bias_steps=40, sel_bias_gate=1, renorm=1),
+        MoEConfig("bwd_multihead_latent", T=10, d_model=24, n_heads=2, d_head=8, n_experts=6, top_k=1, d_ff=8,
+                  latent_proj=1, zipf_s=1.0, act_dtype=0, router_dtype=0, tag=61),
+        MoEConfig("bwd_multihead_renorm_relu", T=11, d_model=16, n_heads=2, d_head=8, n_experts=4, top_k=2,
+                  renorm=1, d_ff=8, act=RELU, act_dtype=0, router_dtype=0, tag=62),
         base.with_(name="bwd_one_expert", n_experts=1, top_k=1),
     ]
 
@@ -65,11 +71,13 @@ def _names(cfg, P):
         n.append("w3")
     if cfg.n_shared:
         n += ["ws1", "ws2"] + (["ws3"] if P["ws3"] is not None else [])
+    if cfg.latent_proj:
+        n += ["w_in", "w_out"]
     return n
 
 
 _GRAD = dict(x="dx", w_router="dw_router", bias="dbias", w1="dw1", w3="dw3", w2="dw2",
-             ws1="dws1", ws3="dws3", ws2="dws2")
+             ws1="dws1", ws3="dws3", ws2="dws2", w_in="dw_in", w_out="dw_out")
 
 
 def _fd_check(cfg, lam, dy_scale=1.0, eps=1e-6, tol=1e-6):
@@ -90,10 +98,16 @@ def _fd_check(cfg, lam, dy_scale=1.0, eps=1e-6, tol=1e-6):
         assert abs(fd - an) <= tol * max(1.0, abs(an)), f"{cfg.name} lam={lam} d{name}: fd {fd} vs {an}"
 
 
+def _lam(cfg, lam):
+    """The aux loss exists for one routing head only."""
+    return lam if cfg.n_heads == 1 else 0.0
+
+
 def check_fd_all():
     for cfg in tiny_cfgs():
         _fd_check(cfg, 0.0)
-        _fd_check(cfg, 0.37)
+        if cfg.n_heads == 1:
+            _fd_check(cfg, 0.37)
 
 
 def check_fd_aux_only():
@@ -137,9 +151,10 @@ def check_restricted_forms():
     for cfg in tiny_cfgs():
         inp, out, P, dy = _setup(cfg)
         idx, kept = out["topk_idx"], out["kept"]
-        G = B.backward(cfg, P, idx, kept, dy, 0.37)
+        lam = _lam(cfg, 0.37)
+        G = B.backward(cfg, P, idx, kept, dy, lam)
         toks = np.arange(0, cfg.T, 3)
-        dx = B.backward_tokens(cfg, P, idx, kept, dy, 0.37, toks, out["demand"])
+        dx = B.backward_tokens(cfg, P, idx, kept, dy, lam, toks, out["demand"])
         assert np.allclose(dx, G["dx"][toks], rtol=1e-10, atol=1e-12), cfg.name
         for e in range(cfg.n_experts):
             dW1, dW3, dW2 = B.backward_expert(cfg, P, e, idx, kept, dy)

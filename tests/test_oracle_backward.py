@@ -42,11 +42,17 @@ def m_mlp_transposed(act, v, w1, w3, w2, dF):
 _orig_mlp = B._mlp_backward
 
 
+def m_global_softmax_jacobian(cfg, p, dp):
+    # the Jacobian taken over all experts instead of each head's own
+    return p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+
+
 @pytest.mark.parametrize("name,target,repl", [
     ("silu_grad", "_silu_grad", m_silu_grad_is_sigmoid),
     ("renorm", "backward", m_no_renorm_correction),
     ("aux_scale", "backward", m_aux_over_S),
     ("dw2_mixed", "_mlp_backward", m_mlp_transposed),
+    ("global_softmax", "_head_softmax_backward", m_global_softmax_jacobian),
 ])
 def test_backward_mutant_caught(monkeypatch, name, target, repl):
     monkeypatch.setattr(B, target, repl)
