@@ -91,10 +91,10 @@ def measured_traffic(cfg):
 
 
 def time_backward(cfg, moe, W, x, inp, args, stream):
-    """moe_layer_bwd on the same batch (dy synthetic, aux weight 0.01): ms per step, and the
-    forward + backward step as tokens/s.  Algorithmic FLOPs of the backward: twice the
-    forward's expert FLOPs (input and weight gradients); the gate/up recompute the
-    backward does on top is not counted."""
+    """moe_layer_bwd on the same batch (dy synthetic, aux weight 0.01 for one head): ms per
+    step, and the forward + backward step as tokens/s.  Algorithmic FLOPs of the backward:
+    twice the forward's expert and projection FLOPs (input and weight gradients); the
+    gate/up recompute the backward does on top is not counted."""
     import torch
     T, K, E, dh, F, d = cfg.T, cfg.k_total, cfg.n_experts, cfg.d_head, cfg.d_ff, cfg.d_model
     Rm = moe.moe_rows_upper_bound(cfg)
@@ -106,19 +106,24 @@ def time_backward(cfg, moe, W, x, inp, args, stream):
               topk_idx=e(T, K, dt=torch.int32), topk_w=e(T, K, dt=torch.float32), demand=e(E, dt=torch.int32),
               counts=e(E, dt=torch.int32), offsets=e(E + 1, dt=torch.int32), row_of=e(T, K, dt=torch.int32),
               src_of=e(max(Rm, 1), dt=torch.int32), y_perm=e(max(Rm, 1), dh),
-              shared_out=e(T, d) if fs else None)
+              shared_out=e(T, d) if fs else None,
+              z=e(T, cfg.d_latent) if cfg.latent_proj else None, o=e(T, cfg.d_latent) if cfg.latent_proj else None)
     y = torch.empty_like(x)
     moe.moe_layer_fwd(cfg, W, x, y, io, moe.workspace(cfg))
+    D = cfg.d_latent
     wt = dict(w13t=e(E, dh, m * F), w2t=e(E, F, dh), ws13t=e(d, m * fs) if fs else None,
-              ws2t=e(fs, d) if fs else None)
+              ws2t=e(fs, d) if fs else None, w_in_t=e(d, D) if cfg.latent_proj else None,
+              w_out_t=e(D, d) if cfg.latent_proj else None)
     moe.moe_transpose_weights(cfg, W, wt)
     g = dict(dx=e(T, d), dw_router=e(E, dh, dt=torch.float32), dbias=e(E, dt=torch.float32), dw1=e(E, F, dh),
              dw3=e(E, F, dh) if cfg.act == 1 else None, dw2=e(E, dh, F), dws1=e(fs, d) if fs else None,
-             dws3=e(fs, d) if (fs and cfg.act == 1) else None, dws2=e(d, fs) if fs else None)
+             dws3=e(fs, d) if (fs and cfg.act == 1) else None, dws2=e(d, fs) if fs else None,
+             dw_in=e(D, d) if cfg.latent_proj else None, dw_out=e(d, D) if cfg.latent_proj else None)
     gen = torch.Generator(device="cuda").manual_seed(1234)
     dy = torch.randn(T, d, device="cuda", generator=gen).to(adt)
     ws = moe.backward_workspace(cfg)
-    step = lambda: moe.moe_layer_bwd(cfg, W, wt, x, dy, 0.01, io, g, ws)
+    aux_w = 0.01 if cfg.n_heads == 1 else 0.0  # the aux loss is defined for one routing head
+    step = lambda: moe.moe_layer_bwd(cfg, W, wt, x, dy, aux_w, io, g, ws)
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
@@ -131,12 +136,13 @@ def time_backward(cfg, moe, W, x, inp, args, stream):
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / n
     R = int(io["offsets"][E].item())
-    flops = 2 * algorithmic(cfg, R)["ffn_flops"]
+    alg = algorithmic(cfg, R)
+    flops = 2 * (alg["ffn_flops"] + alg["proj_flops"])
     tf = flops / (ms * 1e-3) / 1e12
     peak = PEAK_F32_TFLOPS if cfg.act_dtype == 0 else PEAK_BF16_TFLOPS
     log(f"[bench] backward {ms:.3f} ms/step, {tf:.4g} TFLOP/s ({tf / peak:.1%} of peak)")
     return {"ms_per_step": ms, "steps": n, "algorithmic_flops": flops, "TFLOPs": tf, "mfma_frac": tf / peak,
-            "aux_weight": 0.01}
+            "aux_weight": aux_w}
 
 
 def cpu_threads():

@@ -319,15 +319,17 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
                   moe_layer_io *io, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ============================================================ backward
- * Gradients of  L = sum_t <dy_t, y_t> + aux_weight * l_aux  for one routing
- * head without latent projections (n_heads == 1, latent_proj == 0), with the
+ * Gradients of  L = sum_t <dy_t, y_t> + aux_weight * l_aux  with the
  * forward's discrete decisions (top-k choice, keep rule) held fixed: those are
  * piecewise constant, so the gradient flows through the gate values, the
- * experts, the router probabilities, the shared experts and the residual.
+ * experts, the router probabilities, the shared experts, the residual and,
+ * for the multi-head latent layer, the two projections (per head: softmax,
+ * renormalisation and router over the head's own experts and slice).
  * ["MoE技术演进", "GShard" item 3 (FFN_e and the gate-weighted sum), item 1
  * (aux loss); "DeepSeekMoE" items 1-2 (gates, shared experts, residual);
  * "Adaptive Mixtures of Local Experts" (softmax gating equation);
- * "大语言模型并行策略（七）：专家并行", "MoE 模型的参数量分析" (SwiGLU experts)]
+ * "大语言模型并行策略（七）：专家并行", "MoE 模型的参数量分析" (SwiGLU experts);
+ * "多头 LatentMoE 与 Head Parallel", 方法论 items 1-2 (latent space, heads)]
  */
 
 /* Transposed weights for the backward products (caller-allocated, act dtype;
@@ -335,9 +337,11 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
  *   w13t  [E, d_head, m*d_ff]        row c of expert e = (W1[e][:, c], W3[e][:, c])
  *   w2t   [E, d_ff, d_head]          W2[e]^T
  *   ws13t [d_model, m*n_s*d_ff]      (Ws1[:, c], Ws3[:, c]); NULL when n_shared == 0
- *   ws2t  [n_s*d_ff, d_model]        Ws2^T;                 NULL when n_shared == 0 */
+ *   ws2t  [n_s*d_ff, d_model]        Ws2^T;                 NULL when n_shared == 0
+ *   w_in_t  [d_model, H*d_head]      W_in^T;                NULL without latent_proj
+ *   w_out_t [H*d_head, d_model]      W_out^T;               NULL without latent_proj */
 typedef struct moe_weights_t {
-  void *w13t, *w2t, *ws13t, *ws2t;
+  void *w13t, *w2t, *ws13t, *ws2t, *w_in_t, *w_out_t;
 } moe_weights_t;
 
 /* Gradient outputs.  Weight gradients have the weights' shapes; expert and
@@ -348,6 +352,7 @@ typedef struct moe_grads {
   float *dbias;      /* [E] float32, or NULL */
   void *dw1, *dw3, *dw2;     /* [E, d_ff, d_head], [E, d_ff, d_head] (SwiGLU), [E, d_head, d_ff] */
   void *dws1, *dws3, *dws2;  /* shared experts (n_shared > 0) */
+  void *dw_in, *dw_out;      /* [H*d_head, d_model], [d_model, H*d_head] (latent_proj) */
 } moe_grads;
 
 /* [host] Workspace bytes moe_layer_bwd needs (0 when cfg is invalid or the
@@ -366,13 +371,17 @@ int moe_transpose_weights(const moe_config *cfg, const moe_weights *w, const moe
  *   aux_weight coefficient of l_aux in L (0: no aux term)
  *   io         the forward's state: logits (the forward's scores, bias
  *              included: run it with MOE_LOGITS_COMPUTE_STORE), topk_idx,
- *              topk_w, demand, offsets, row_of, src_of, y_perm -- all required
+ *              topk_w, demand, offsets, row_of, src_of, y_perm -- all
+ *              required; with latent_proj also z and o
  *   g          gradient outputs (dbias may be NULL; shared ones required when
- *              n_shared > 0; dw3 required for SwiGLU)
+ *              n_shared > 0; dw3 required for SwiGLU; dw_in and dw_out with
+ *              latent_proj)
  * Products accumulate in float32 and round once to act_dtype (weight
  * gradients per expert over all its rows); the router gradients stay float32.
  * Per-row and per-token sums run in a fixed order: results are bitwise
- * reproducible.  MOE_ERR_UNSUPPORTED for n_heads > 1 or latent_proj.
+ * reproducible.  aux_weight must be 0 when n_heads > 1 (the aux loss is
+ * defined for one head); a selection bias inside renormalised gates
+ * (sel_bias_gate with renorm) is MOE_ERR_UNSUPPORTED.
  */
 int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights_t *wt, const void *x,
                   const void *dy, float aux_weight, const moe_layer_io *io, moe_grads *g, void *ws,

@@ -64,11 +64,12 @@ class MoeLayerIO(ctypes.Structure):
 
 
 class MoeWeightsT(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w13t", "w2t", "ws13t", "ws2t")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w13t", "w2t", "ws13t", "ws2t", "w_in_t", "w_out_t")]
 
 
 class MoeGrads(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("dx", "dw_router", "dbias", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dx", "dw_router", "dbias", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2",
+                                                "dw_in", "dw_out")]
 
 
 class MoeError(RuntimeError):

@@ -21,20 +21,24 @@ __global__ void zero_f32_kernel(float *p, long n) {
 }
 
 // ---------------------------------------------------------------- per kept row
-// dg[a] = <dy_t, y_perm_r> and dY_r = g_a * dy_t for row r holding assignment
-// a = t*K + j.  One wave per row; dg of dropped assignments stays 0.
+// dg[a] = <dy_{t,h}, y_perm_r> and dY_r = g_a * dy_{t,h} for row r holding
+// assignment a = t*K + j on expert e of head h = e / E_h (dy_{t,h}: columns
+// [h*dh, (h+1)*dh) of row t).  One wave per row; dg of dropped assignments
+// stays 0.
 template <typename TA>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(const TA *__restrict__ dy, const TA *__restrict__ y_perm,
                                                        const float *__restrict__ gates,
                                                        const int32_t *__restrict__ src_of,
-                                                       const int32_t *__restrict__ offsets, int E, int K, int dh,
-                                                       long ld_dy, TA *__restrict__ dY, float *__restrict__ dg) {
+                                                       const int32_t *__restrict__ topk_idx,
+                                                       const int32_t *__restrict__ offsets, int E, int Eh, int K,
+                                                       int dh, long ld_dy, TA *__restrict__ dY,
+                                                       float *__restrict__ dg) {
   constexpr int EPC = 16 / sizeof(TA);
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= offsets[E]) return;
-  const int a = src_of[r], t = a / K;
+  const int a = src_of[r], t = a / K, h = topk_idx[a] / Eh;
   const float g = gates[a];
-  const u32x4 *s = (const u32x4 *)(dy + (size_t)t * ld_dy);
+  const u32x4 *s = (const u32x4 *)(dy + (size_t)t * ld_dy + (size_t)h * dh);
   const u32x4 *yp = (const u32x4 *)(y_perm + (size_t)r * dh);
   u32x4 *o = (u32x4 *)(dY + (size_t)r * dh);
   float dot = 0.f;
@@ -96,12 +100,13 @@ __global__ __launch_bounds__(1024) void bwd_poff_kernel(const int32_t *__restric
   if (tid == 1023) poff[E] = s[1023];
 }
 
-// pmap_r[j] = row r held by padded column j (or -1); pmap_x[j] = its token
+// pmap_r[j] = row r held by padded column j (or -1); pmap_x[j] = t*H + h for
+// its token t and head h: the row of the expert input viewed as [T*H, dh]
 __global__ void bwd_pmap_kernel(const int32_t *__restrict__ offsets, const int32_t *__restrict__ poff,
-                                const int32_t *__restrict__ src_of, int E, int K, long npad,
+                                const int32_t *__restrict__ src_of, int E, int Eh, int H, int K, long npad,
                                 int32_t *__restrict__ pmap_r, int32_t *__restrict__ pmap_x) {
   for (long j = blockIdx.x * (long)blockDim.x + threadIdx.x; j < npad; j += (long)gridDim.x * blockDim.x) {
-    int r = -1;
+    int r = -1, e = 0;
     if (j < poff[E]) {
       int lo = 0, hi = E - 1;
       while (lo < hi) {
@@ -110,9 +115,10 @@ __global__ void bwd_pmap_kernel(const int32_t *__restrict__ offsets, const int32
       }
       const int rr = offsets[lo] + (int)(j - poff[lo]);
       if (rr < offsets[lo + 1]) r = rr;
+      e = lo;
     }
     pmap_r[j] = r;
-    pmap_x[j] = r >= 0 ? src_of[r] / K : -1;
+    pmap_x[j] = r >= 0 ? (src_of[r] / K) * H + e / Eh : -1;
   }
 }
 
@@ -155,49 +161,50 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TA *__restrict__ s
 }
 
 // ---------------------------------------------------------------- router
-// dl[t][e] = p_e (dp_e - sum_e' p_e' dp_e'), p = softmax(logits_t); dp from the
-// gate gradients (renormalised: (dg_j - sum dg g) / P at the chosen experts)
-// plus lam * demand_e / T^2 (aux loss).  One wave per token.
+// dl[t][e] = p_e (dp_e - sum_e' p_e' dp_e') over the head's E_h experts,
+// p = the head's softmax of the logits; dp from the gate gradients of the
+// head's k slots (renormalised: (dg_j - sum dg g) / P at the chosen experts)
+// plus lam * demand_e / T^2 (aux loss, one head).  One wave per (token, head).
 __global__ __launch_bounds__(256) void router_bwd_kernel(const float *__restrict__ logits,
                                                          const int32_t *__restrict__ topk_idx,
                                                          const float *__restrict__ gates,
                                                          const float *__restrict__ dg,
-                                                         const int32_t *__restrict__ demand, int T, int E, int k,
-                                                         int renorm, float lam, float *__restrict__ dl) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (t >= T) return;
-  const float *l = logits + (size_t)t * E;
+                                                         const int32_t *__restrict__ demand, int T, int H, int E,
+                                                         int Eh, int K, int k, int renorm, float lam,
+                                                         float *__restrict__ dl) {
+  const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (pair >= (long)T * H) return;
+  const int t = (int)(pair / H), h = (int)(pair % H);
+  const float *l = logits + (size_t)t * E + (size_t)h * Eh;
+  const int32_t *ti = topk_idx + (size_t)t * K + (size_t)h * k;
+  const float *tg = gates + (size_t)t * K + (size_t)h * k;
+  const float *tdg = dg + (size_t)t * K + (size_t)h * k;
   float m = -INFINITY;
-  for (int e = lane; e < E; e += 64) m = fmaxf(m, l[e]);
+  for (int e = lane; e < Eh; e += 64) m = fmaxf(m, l[e]);
   m = wave_max(m, WAVE);
   float z = 0.f;
-  for (int e = lane; e < E; e += 64) z += __expf(l[e] - m);
+  for (int e = lane; e < Eh; e += 64) z += __expf(l[e] - m);
   z = group_sum_fixed(z, WAVE);
   // chosen experts: P = sum p, S = sum dg * g
   float P = 0.f, sdg = 0.f;
   for (int j = 0; j < k; ++j) {
-    const int e = topk_idx[(size_t)t * k + j];
+    const int e = ti[j] - h * Eh;
     P += __expf(l[e] - m) / z;
-    sdg += dg[(size_t)t * k + j] * gates[(size_t)t * k + j];
+    sdg += tdg[j] * tg[j];
   }
   const float invT2 = 1.0f / ((float)T * (float)T);
+  auto dp_of = [&](int e) {
+    float dp = lam * (float)demand[h * Eh + e] * invT2;
+    for (int j = 0; j < k; ++j)
+      if (ti[j] - h * Eh == e) dp += renorm ? (tdg[j] - sdg) / P : tdg[j];
+    return dp;
+  };
   // dp_e for this lane's experts, then sum p * dp
   float spdp = 0.f;
-  for (int e = lane; e < E; e += 64) {
-    const float p = __expf(l[e] - m) / z;
-    float dp = lam * (float)demand[e] * invT2;
-    for (int j = 0; j < k; ++j)
-      if (topk_idx[(size_t)t * k + j] == e) dp += renorm ? (dg[(size_t)t * k + j] - sdg) / P : dg[(size_t)t * k + j];
-    spdp += p * dp;
-  }
+  for (int e = lane; e < Eh; e += 64) spdp += __expf(l[e] - m) / z * dp_of(e);
   spdp = group_sum_fixed(spdp, WAVE);
-  for (int e = lane; e < E; e += 64) {
-    const float p = __expf(l[e] - m) / z;
-    float dp = lam * (float)demand[e] * invT2;
-    for (int j = 0; j < k; ++j)
-      if (topk_idx[(size_t)t * k + j] == e) dp += renorm ? (dg[(size_t)t * k + j] - sdg) / P : dg[(size_t)t * k + j];
-    dl[(size_t)t * E + e] = p * (dp - spdp);
-  }
+  for (int e = lane; e < Eh; e += 64) dl[(size_t)t * E + (size_t)h * Eh + e] = __expf(l[e] - m) / z * (dp_of(e) - spdp);
 }
 
 // ---------------------------------------------------------------- float32 tile
@@ -249,18 +256,22 @@ __device__ __forceinline__ void tile_outer(float (&acc)[4][4], TileSmem &sm, con
   }
 }
 
-// dW_r = dl^T x in float32: m = expert, n = column, k = token.  Block (eb, cb,
-// ts) covers token range ts of gridDim.z and writes part[ts][e][c]; a second
-// pass adds the ranges in ascending order (fixed order: reproducible).
+// dW_r = dl^T u in float32, per head h: rows [h*E_h, (h+1)*E_h) of dW_r from
+// the head's dl columns and u's h-th slice (m = expert, n = column, k = token).
+// Block (eb, cb, h*nsplit + ts) covers token range ts and writes
+// part[ts][e][c]; a second pass adds the ranges in ascending order (fixed
+// order: reproducible).
 template <typename TX>
 __global__ __launch_bounds__(256) void router_wgrad_kernel(const float *__restrict__ dl, const TX *__restrict__ x,
-                                                           long ldx, int T, int E, int d, float *__restrict__ part) {
+                                                           long ldx, int T, int E, int Eh, int dh, int nsplit,
+                                                           float *__restrict__ part) {
   __shared__ TileSmem sm;
-  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64, ts = blockIdx.z;
-  const int per = (T + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  const int h = blockIdx.z / nsplit, ts = blockIdx.z % nsplit;
+  const int per = (T + nsplit - 1) / nsplit;
   const int t_beg = min(T, ts * per), t_end = min(T, t_beg + per);
   float acc[4][4] = {};
-  tile_outer<false>(acc, sm, dl, E, E, x, ldx, d, m0, n0, t_beg, t_end);
+  tile_outer<false>(acc, sm, dl + (size_t)h * Eh, E, Eh, x + (size_t)h * dh, ldx, dh, m0, n0, t_beg, t_end);
   const int tm = threadIdx.x >> 4, tn = threadIdx.x & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -268,7 +279,7 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float *__restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = n0 + 4 * tn + j;
-      if (e < E && c < d) part[((size_t)ts * E + e) * d + c] = acc[i][j];
+      if (e < Eh && c < dh) part[((size_t)ts * E + (size_t)h * Eh + e) * dh + c] = acc[i][j];
     }
   }
 }
@@ -299,19 +310,26 @@ __global__ __launch_bounds__(256) void router_dbias_kernel(const float *__restri
 }
 
 // ---------------------------------------------------------------- input gradient
-// dx[t][c] = [dy[t][c]] + [dxs[t][c]] + sum_j dXr[row_of[t][j]][c] + sum_e dl[t][e] W_r[e][c],
+// For column c of head h (c = h*dh + cl):
+//   out[t][c] = [dy[t][c]] + [dxs[t][c]] + sum_{j in head h} dXr[row_of[t][j]][cl]
+//               + sum_{e in head h} dl[t][e] W_r[e][cl],
 // float32 in that order (the router term over experts ascending), rounded
-// once.  A thread owns one column of DX_TOK consecutive tokens: every global
-// access of a wave covers 64 consecutive columns, and the dl reads have
-// block-uniform addresses (scalar loads).
+// once: the layer's dx (one head or no latent projection), or the gradient of
+// the latent u.  A thread owns one column of DX_TOK consecutive tokens; a
+// block's 256 columns lie in one head, so the dl reads have block-uniform
+// addresses (scalar loads).
 constexpr int DX_TOK = 8;
 template <typename TA, typename TR>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const TA *__restrict__ dy, const TA *__restrict__ dxs,
                                                      const TA *__restrict__ dXr, const int32_t *__restrict__ row_of,
                                                      const float *__restrict__ dl, const TR *__restrict__ w_r, int T,
-                                                     int d, int K, int E, int residual, TA *__restrict__ dx) {
-  const int t0 = blockIdx.x * DX_TOK, c = blockIdx.y * 256 + threadIdx.x;
-  if (c >= d) return;
+                                                     int D, int dh, int H, int K, int k, int E, int Eh, int residual,
+                                                     TA *__restrict__ dx) {
+  const int cpb = (dh + 255) / 256;  // column blocks per head
+  const int h = blockIdx.y / cpb, cl = (blockIdx.y % cpb) * 256 + threadIdx.x;
+  const int t0 = blockIdx.x * DX_TOK;
+  if (cl >= dh) return;
+  const int c = h * dh + cl;
   const int nt = min(DX_TOK, T - t0);
   float acc[DX_TOK];
 #pragma unroll
@@ -319,23 +337,24 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const TA *__restrict__ dy, 
     float v = 0.f;
     if (i < nt) {
       const int t = t0 + i;
-      const size_t o = (size_t)t * d + c;
+      const size_t o = (size_t)t * D + c;
       if (residual) v = Elem<TA>::to_f32(dy[o]);
       if (dxs) v += Elem<TA>::to_f32(dxs[o]);
-      for (int q = 0; q < K; ++q) {
-        const int r = row_of[(size_t)t * K + q];
-        if (r >= 0) v += Elem<TA>::to_f32(dXr[(size_t)r * d + c]);
+      for (int q = 0; q < k; ++q) {
+        const int r = row_of[(size_t)t * K + h * k + q];
+        if (r >= 0) v += Elem<TA>::to_f32(dXr[(size_t)r * dh + cl]);
       }
     }
     acc[i] = v;
   }
-  const float *dlb = dl + (size_t)t0 * E;
-  if (nt == DX_TOK && (E & 3) == 0) {
-    // dl rows are 16-byte aligned (the buffer is, and E % 4 == 0)
-    for (int e = 0; e < E; e += 4) {
+  const float *dlb = dl + (size_t)t0 * E + (size_t)h * Eh;
+  const TR *wr = w_r + (size_t)h * Eh * dh;
+  if (nt == DX_TOK && (E & 3) == 0 && (Eh & 3) == 0) {
+    // dl rows are 16-byte aligned (the buffer is, and E, E_h are multiples of 4)
+    for (int e = 0; e < Eh; e += 4) {
       float w[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = Elem<TR>::to_f32(w_r[(size_t)(e + u) * d + c]);
+      for (int u = 0; u < 4; ++u) w[u] = Elem<TR>::to_f32(wr[(size_t)(e + u) * dh + cl]);
 #pragma unroll
       for (int i = 0; i < DX_TOK; ++i) {
         const float4 l = *(const float4 *)(dlb + (size_t)i * E + e);
@@ -346,8 +365,8 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const TA *__restrict__ dy, 
       }
     }
   } else {
-    for (int e = 0; e < E; ++e) {
-      const float w = Elem<TR>::to_f32(w_r[(size_t)e * d + c]);
+    for (int e = 0; e < Eh; ++e) {
+      const float w = Elem<TR>::to_f32(wr[(size_t)e * dh + cl]);
 #pragma unroll
       for (int i = 0; i < DX_TOK; ++i)
         if (i < nt) acc[i] += dlb[(size_t)i * E + e] * w;
@@ -355,7 +374,7 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const TA *__restrict__ dy, 
   }
 #pragma unroll
   for (int i = 0; i < DX_TOK; ++i)
-    if (i < nt) dx[(size_t)(t0 + i) * d + c] = Elem<TA>::from_f32(acc[i]);
+    if (i < nt) dx[(size_t)(t0 + i) * D + c] = Elem<TA>::from_f32(acc[i]);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -378,8 +397,9 @@ int launch_transpose(bool f32, const void *src, long ld_src, long bs_src, const 
                                      batches, st);
 }
 
-int launch_bwd_rows(const Shape &s, const void *dy, const void *y_perm, const float *gates, const int32_t *src_of,
-                    const int32_t *offsets, void *dY, float *dg, hipStream_t st) {
+int launch_bwd_rows(const Shape &s, const void *dy, long ld_dy, const void *y_perm, const float *gates,
+                    const int32_t *src_of, const int32_t *topk_idx, const int32_t *offsets, void *dY, float *dg,
+                    hipStream_t st) {
   const long tk = (long)s.T * s.K;
   hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)std::min<long>((tk + 255) / 256, 4096)), dim3(256), 0, st, dg,
                      tk);
@@ -388,11 +408,12 @@ int launch_bwd_rows(const Shape &s, const void *dy, const void *y_perm, const fl
   const unsigned grid = (unsigned)((s.R_max + 3) / 4);
   if (s.act_f32)
     hipLaunchKernelGGL((bwd_rows_kernel<float>), dim3(grid), dim3(256), 0, st, (const float *)dy,
-                       (const float *)y_perm, gates, src_of, offsets, s.E, s.K, s.dh, (long)s.d, (float *)dY, dg);
+                       (const float *)y_perm, gates, src_of, topk_idx, offsets, s.E, s.Eh, s.K, s.dh, ld_dy,
+                       (float *)dY, dg);
   else
     hipLaunchKernelGGL((bwd_rows_kernel<uint16_t>), dim3(grid), dim3(256), 0, st, (const uint16_t *)dy,
-                       (const uint16_t *)y_perm, gates, src_of, offsets, s.E, s.K, s.dh, (long)s.d, (uint16_t *)dY,
-                       dg);
+                       (const uint16_t *)y_perm, gates, src_of, topk_idx, offsets, s.E, s.Eh, s.K, s.dh, ld_dy,
+                       (uint16_t *)dY, dg);
   return launch_status("backward rows");
 }
 
@@ -402,30 +423,32 @@ int launch_bwd_pad(const Shape &s, const int32_t *offsets, const int32_t *src_of
   if (int rc = launch_status("expert padding")) return rc;
   if (npad <= 0) return 0;
   hipLaunchKernelGGL(bwd_pmap_kernel, dim3((unsigned)std::min<long>((npad + 255) / 256, 8192)), dim3(256), 0, st,
-                     offsets, poff, src_of, s.E, s.K, npad, pmap_r, pmap_x);
+                     offsets, poff, src_of, s.E, s.Eh, s.H, s.K, npad, pmap_r, pmap_x);
   return launch_status("padding map");
 }
 
 int launch_router_bwd(const Shape &s, const float *logits, const int32_t *topk_idx, const float *gates,
                       const float *dg, const int32_t *demand, float lam, const void *x, float *dl, float *part,
                       float *dw_router, float *dbias, hipStream_t st) {
-  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((s.T + 3) / 4)), dim3(256), 0, st, logits, topk_idx, gates,
-                     dg, demand, s.T, s.E, s.K, s.renorm, lam, dl);
+  const long pairs = (long)s.T * s.H;
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, logits, topk_idx,
+                     gates, dg, demand, s.T, s.H, s.E, s.Eh, s.K, s.k, s.renorm, lam, dl);
   if (int rc = launch_status("router backward")) return rc;
   if (dbias) {
     hipLaunchKernelGGL(router_dbias_kernel, dim3((unsigned)s.E), dim3(256), 0, st, dl, s.T, s.E, dbias);
     if (int rc = launch_status("router bias gradient")) return rc;
   }
-  const int nsplit = router_wgrad_split(s.E, s.d);
-  const dim3 grid((unsigned)((s.E + 63) / 64), (unsigned)((s.d + 63) / 64), (unsigned)nsplit);
+  const int nsplit = router_wgrad_split(s);
+  const long ldx = (long)s.H * s.dh;
+  const dim3 grid((unsigned)((s.Eh + 63) / 64), (unsigned)((s.dh + 63) / 64), (unsigned)(nsplit * s.H));
   if (s.act_f32)
-    hipLaunchKernelGGL((router_wgrad_kernel<float>), grid, dim3(256), 0, st, dl, (const float *)x, (long)s.d, s.T,
-                       s.E, s.d, part);
+    hipLaunchKernelGGL((router_wgrad_kernel<float>), grid, dim3(256), 0, st, dl, (const float *)x, ldx, s.T, s.E,
+                       s.Eh, s.dh, nsplit, part);
   else
-    hipLaunchKernelGGL((router_wgrad_kernel<uint16_t>), grid, dim3(256), 0, st, dl, (const uint16_t *)x, (long)s.d,
-                       s.T, s.E, s.d, part);
+    hipLaunchKernelGGL((router_wgrad_kernel<uint16_t>), grid, dim3(256), 0, st, dl, (const uint16_t *)x, ldx, s.T,
+                       s.E, s.Eh, s.dh, nsplit, part);
   if (int rc = launch_status("router weight gradient")) return rc;
-  const long n = (long)s.E * s.d;
+  const long n = (long)s.E * s.dh;
   hipLaunchKernelGGL(router_wgrad_sum_kernel, dim3((unsigned)std::min<long>((n + 255) / 256, 4096)), dim3(256), 0,
                      st, part, n, nsplit, dw_router);
   return launch_status("router weight gradient");
@@ -444,21 +467,22 @@ int launch_set_kwin(int32_t *kwin, int tpad, hipStream_t st) {
 }
 
 int launch_bwd_dx(const Shape &s, const void *dy, const void *dxs, const void *dXr, const int32_t *row_of,
-                  const float *dl, const void *w_router, void *dx, hipStream_t st) {
-  if (s.T == 0 || s.d == 0) return 0;
-  const dim3 grid((unsigned)((s.T + DX_TOK - 1) / DX_TOK), (unsigned)((s.d + 255) / 256));
+                  const float *dl, const void *w_router, int residual, void *dx, hipStream_t st) {
+  if (s.T == 0) return 0;
+  const int D = s.H * s.dh;
+  const dim3 grid((unsigned)((s.T + DX_TOK - 1) / DX_TOK), (unsigned)(s.H * ((s.dh + 255) / 256)));
   if (s.act_f32) {
     hipLaunchKernelGGL((bwd_dx_kernel<float, float>), dim3(grid), dim3(256), 0, st, (const float *)dy,
-                       (const float *)dxs, (const float *)dXr, row_of, dl, (const float *)w_router, s.T, s.d, s.K,
-                       s.E, s.residual, (float *)dx);
+                       (const float *)dxs, (const float *)dXr, row_of, dl, (const float *)w_router, s.T, D, s.dh,
+                       s.H, s.K, s.k, s.E, s.Eh, residual, (float *)dx);
   } else if (s.router_f32) {
     hipLaunchKernelGGL((bwd_dx_kernel<uint16_t, float>), dim3(grid), dim3(256), 0, st, (const uint16_t *)dy,
-                       (const uint16_t *)dxs, (const uint16_t *)dXr, row_of, dl, (const float *)w_router, s.T, s.d,
-                       s.K, s.E, s.residual, (uint16_t *)dx);
+                       (const uint16_t *)dxs, (const uint16_t *)dXr, row_of, dl, (const float *)w_router, s.T, D,
+                       s.dh, s.H, s.K, s.k, s.E, s.Eh, residual, (uint16_t *)dx);
   } else {
     hipLaunchKernelGGL((bwd_dx_kernel<uint16_t, uint16_t>), dim3(grid), dim3(256), 0, st, (const uint16_t *)dy,
                        (const uint16_t *)dxs, (const uint16_t *)dXr, row_of, dl, (const uint16_t *)w_router, s.T,
-                       s.d, s.K, s.E, s.residual, (uint16_t *)dx);
+                       D, s.dh, s.H, s.K, s.k, s.E, s.Eh, residual, (uint16_t *)dx);
   }
   return launch_status("input gradient");
 }

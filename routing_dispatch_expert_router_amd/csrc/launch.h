@@ -60,22 +60,23 @@ int gemm_kgrouped(bool f32, const void *A, long lda, const void *B, long ldb, vo
 int launch_transpose(bool f32, const void *src, long ld_src, long bs_src, const int32_t *rmap, long nvalid,
                      long njcols, int ncols, int coff, void *dst, long ld_dst, long bs_dst, int batches,
                      hipStream_t st);
-int launch_bwd_rows(const Shape &s, const void *dy, const void *y_perm, const float *gates, const int32_t *src_of,
-                    const int32_t *offsets, void *dY, float *dg, hipStream_t st);
+int launch_bwd_rows(const Shape &s, const void *dy, long ld_dy, const void *y_perm, const float *gates,
+                    const int32_t *src_of, const int32_t *topk_idx, const int32_t *offsets, void *dY, float *dg,
+                    hipStream_t st);
 int launch_bwd_pad(const Shape &s, const int32_t *offsets, const int32_t *src_of, int32_t *poff, int32_t *pmap_r,
                    int32_t *pmap_x, long npad, hipStream_t st);
-// the router weight gradient sums router_wgrad_split(E, d) token ranges
+// the router weight gradient sums router_wgrad_split(s) token ranges
 // separately (enough 64 x 64 tiles to fill the chip), then adds them in order;
-// `part` holds router_wgrad_split(E, d) * E * d floats
-inline int router_wgrad_split(int E, int d) {
-  const long tiles = (long)((E + 63) / 64) * ((d + 63) / 64);
+// `part` holds router_wgrad_split(s) * E * d_head floats
+inline int router_wgrad_split(const Shape &s) {
+  const long tiles = (long)s.H * ((s.Eh + 63) / 64) * ((s.dh + 63) / 64);
   return (int)std::min<long>(64, std::max<long>(1, (4096 + tiles - 1) / std::max<long>(tiles, 1)));
 }
 int launch_router_bwd(const Shape &s, const float *logits, const int32_t *topk_idx, const float *gates,
                       const float *dg, const int32_t *demand, float lam, const void *x, float *dl, float *part,
                       float *dw_router, float *dbias, hipStream_t st);
 int launch_bwd_dx(const Shape &s, const void *dy, const void *dxs, const void *dXr, const int32_t *row_of,
-                  const float *dl, const void *w_router, void *dx, hipStream_t st);
+                  const float *dl, const void *w_router, int residual, void *dx, hipStream_t st);
 int launch_set_kwin(int32_t *kwin, int tpad, hipStream_t st);
 
 // ---------------------------------------------------------------- grouped GEMM / expert FFN

@@ -136,7 +136,7 @@ int rc_of(int launcher_rc) {
 }
 
 // ---------------------------------------------------------------- backward
-bool bwd_supported(const Shape &s) { return s.H == 1 && !s.latent && gather_supported(s); }
+bool bwd_supported(const Shape &s) { return gather_supported(s); }
 
 // columns of the per-expert padded, transposed activations: every expert's
 // rows rounded up to 64 (the GEMM k-chunk), and a multiple of 64 overall so
@@ -146,7 +146,7 @@ long tpad(const Shape &s) { return (s.T + 63) / 64 * 64; }
 
 struct BwdBufs {
   size_t dg, dl, rpart, dY, dH, dAB, Hr, dXr, poff, pmap_r, pmap_x, Xt, dYt, dABt, Ht, prefix, kwin;
-  size_t dHs, dABs, Hs, dxs, dyt, xt, dABst, Hst, total;
+  size_t dHs, dABs, Hs, dxs, dyt, xt, dABst, Hst, dout, du, ot, dut, total;
 };
 
 BwdBufs bwd_layout(const Shape &s) {
@@ -156,7 +156,7 @@ BwdBufs bwd_layout(const Shape &s) {
   size_t o = 0;
   b.dg = o; o += al((size_t)s.T * s.K * 4);
   b.dl = o; o += al((size_t)s.T * s.E * 4);
-  b.rpart = o; o += al((size_t)moe::router_wgrad_split(s.E, s.d) * s.E * s.d * 4);
+  b.rpart = o; o += al((size_t)moe::router_wgrad_split(s) * s.E * s.dh * 4);
   b.dY = o; o += al(R * s.dh * esz);
   b.dH = o; o += al(R * s.dff * esz);
   b.dAB = o; o += al(R * m * s.dff * esz);
@@ -180,6 +180,15 @@ BwdBufs bwd_layout(const Shape &s) {
     b.xt = o; o += al((size_t)s.d * Tp * esz);
     b.dABst = o; o += al(m * fs * Tp * esz);
     b.Hst = o; o += al(fs * Tp * esz);
+  }
+  if (s.latent) {  // the projections: do, du and the transposes of dy, x, o, du
+    const size_t D = (size_t)s.H * s.dh;
+    b.dout = o; o += al((size_t)s.T * D * esz);
+    b.du = o; o += al((size_t)s.T * D * esz);
+    b.dyt = o; o += al((size_t)s.d * Tp * esz);
+    b.xt = o; o += al((size_t)s.d * Tp * esz);
+    b.ot = o; o += al(D * Tp * esz);
+    b.dut = o; o += al(D * Tp * esz);
   }
   b.total = o;
   return b;
@@ -395,8 +404,19 @@ int moe_transpose_weights(const moe_config *cfg, const moe_weights *w, const moe
   const bool glu = s.act == MOE_ACT_SWIGLU;
   if (glu && !w->w3) return MOE_ERR_ARG;
   if (s.n_shared && (!w->ws1 || !w->ws2 || (glu && !w->ws3) || !wt->ws13t || !wt->ws2t)) return MOE_ERR_ARG;
+  if (s.latent && (!w->w_in || !w->w_out || !wt->w_in_t || !wt->w_out_t)) return MOE_ERR_ARG;
   const long m = glu ? 2 : 1, esz = s.act_f32 ? 4 : 2, dff = s.dff, dh = s.dh;
   clear_stale_error();
+  if (s.latent) {
+    const long D = (long)s.H * dh, d = s.d;
+    // w_in_t [d][D] = W_in^T, w_out_t [D][d] = W_out^T
+    if ((rc = rc_of(moe::launch_transpose(s.act_f32, w->w_in, d, 0, nullptr, D, D, (int)d, 0, wt->w_in_t, D, 0, 1,
+                                          stream))))
+      return rc;
+    if ((rc = rc_of(moe::launch_transpose(s.act_f32, w->w_out, D, 0, nullptr, d, d, (int)D, 0, wt->w_out_t, d, 0, 1,
+                                          stream))))
+      return rc;
+  }
   // w13t[e][c][0..dff) = W1[e][..][c], [dff..2dff) = W3[e][..][c]
   if ((rc = rc_of(moe::launch_transpose(s.act_f32, w->w1, dh, dff * dh, nullptr, dff, dff, (int)dh, 0, wt->w13t,
                                         m * dff, dh * m * dff, s.E, stream))))
@@ -441,6 +461,11 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
   if (s.n_shared && (!w->ws1 || !w->ws2 || (glu && !w->ws3) || !wt->ws13t || !wt->ws2t || !g->dws1 || !g->dws2 ||
                      (glu && !g->dws3)))
     return MOE_ERR_ARG;
+  if (s.latent && (!w->w_in || !w->w_out || !wt->w_in_t || !wt->w_out_t || !io->z || !io->o || !g->dw_in ||
+                   !g->dw_out))
+    return MOE_ERR_ARG;
+  // the aux loss is defined for one routing head
+  if (s.H > 1 && aux_weight != 0.0f) return MOE_ERR_UNSUPPORTED;
   const BwdBufs L = bwd_layout(s);
   if (!ws || ((uintptr_t)ws & 255) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (s.T == 0) return MOE_OK;
@@ -454,19 +479,31 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
   int32_t *prefix = (int32_t *)at(L.prefix), *kwin = (int32_t *)at(L.kwin);
   const bool f32 = s.act_f32;
   const long m = glu ? 2 : 1, esz = f32 ? 4 : 2, dh = s.dh, dff = s.dff, d = s.d, Rp = rpad_bound(s), Tp = tpad(s);
+  const long D = (long)s.H * dh;                 // width of the expert input u (x, or the latent z)
+  const void *u = s.latent ? io->z : x;
   const int epi_bwd = glu ? moe::GEMM_EPI_SWIGLU_BWD : moe::GEMM_EPI_RELU_BWD;
   const int32_t *offsets = io->offsets, *src_of = io->src_of;
 
   clear_stale_error();
-  // gate gradients dg = <dy, y_perm>, scaled row gradients dY = g * dy
-  if ((rc = rc_of(moe::launch_bwd_rows(s, dy, io->y_perm, io->topk_w, src_of, offsets, dY, dg, stream)))) return rc;
+  // latent layer: the gradient of o is do = dy W_out
+  const void *dyo = dy;
+  if (s.latent) {
+    dyo = at(L.dout);
+    if ((rc = rc_of(moe::launch_dense(f32, dy, wt->w_out_t, at(L.dout), nullptr, s.T, (int)D, (int)d, nullptr,
+                                      stream))))
+      return rc;
+  }
+  // gate gradients dg = <do_h, y_perm>, scaled row gradients dY = g * do_h
+  if ((rc = rc_of(moe::launch_bwd_rows(s, dyo, D, io->y_perm, io->topk_w, src_of, io->topk_idx, offsets, dY, dg,
+                                       stream))))
+    return rc;
   if ((rc = rc_of(moe::launch_bwd_pad(s, offsets, src_of, poff, pmap_r, pmap_x, Rp, stream)))) return rc;
   // dH = dY W2  (B = W2^T rows)
   if ((rc = rc_of(moe::gemm_routed(s, moe::GEMM_EPI_PLAIN, dY, dh, nullptr, wt->w2t, nullptr, dh, dff * dh, dH, dff,
                                    (int)dff, (int)dh, offsets, nullptr, 0, nullptr, 0, prefix, stream))))
     return rc;
-  // recompute the gate/up products from x, with the backward epilogue: dA|dB, H
-  if ((rc = rc_of(moe::gemm_routed(s, epi_bwd, x, d, src_of, w->w1, glu ? w->w3 : nullptr, dh, dff * dh, dAB,
+  // recompute the gate/up products from u, with the backward epilogue: dA|dB, H
+  if ((rc = rc_of(moe::gemm_routed(s, epi_bwd, u, D, src_of, w->w1, glu ? w->w3 : nullptr, dh, dff * dh, dAB,
                                    m * dff, (int)dff, (int)dh, offsets, dH, dff, Hr, dff, prefix, stream))))
     return rc;
   // dX rows = [dA dB] [W1; W3]
@@ -475,7 +512,8 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
                                    prefix, stream))))
     return rc;
   // transposed, per-expert padded activations for the weight gradients
-  if ((rc = rc_of(moe::launch_transpose(f32, x, d, 0, pmap_x, 0, Rp, (int)dh, 0, Xt, Rp, 0, 1, stream)))) return rc;
+  // (u viewed as [T*H, dh]: pmap_x holds t*H + h)
+  if ((rc = rc_of(moe::launch_transpose(f32, u, dh, 0, pmap_x, 0, Rp, (int)dh, 0, Xt, Rp, 0, 1, stream)))) return rc;
   if ((rc = rc_of(moe::launch_transpose(f32, dY, dh, 0, pmap_r, 0, Rp, (int)dh, 0, dYt, Rp, 0, 1, stream)))) return rc;
   if ((rc = rc_of(moe::launch_transpose(f32, dAB, m * dff, 0, pmap_r, 0, Rp, (int)(m * dff), 0, dABt, Rp, 0, 1,
                                         stream))))
@@ -492,7 +530,7 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
                                             s.E, (int)dff, (int)dh, poff, stream))))
     return rc;
   // router: dl, dW_r, dbias
-  if ((rc = rc_of(moe::launch_router_bwd(s, io->logits, io->topk_idx, io->topk_w, dg, io->demand, aux_weight, x, dl,
+  if ((rc = rc_of(moe::launch_router_bwd(s, io->logits, io->topk_idx, io->topk_w, dg, io->demand, aux_weight, u, dl,
                                          (float *)at(L.rpart), g->dw_router, g->dbias, stream))))
     return rc;
   // shared experts: the same MLP backward over all T tokens with gate 1
@@ -529,8 +567,27 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
                                               (int)fs, (int)d, kwin, stream))))
       return rc;
   }
-  // dx = [dy] + [dxs] + sum_j dX rows + dl W_r
-  return rc_of(moe::launch_bwd_dx(s, dy, dxs, dXr, io->row_of, dl, w->w_router, g->dx, stream));
+  if (!s.latent) {
+    // dx = [dy] + [dxs] + sum_j dX rows + dl W_r (per head)
+    return rc_of(moe::launch_bwd_dx(s, dy, dxs, dXr, io->row_of, dl, w->w_router, s.residual, g->dx, stream));
+  }
+  // latent layer: du as above, then dx = dy + du W_in, dW_in = du^T x, dW_out = dy^T o
+  void *du = at(L.du), *dyt = at(L.dyt), *xt = at(L.xt), *ot = at(L.ot), *dut = at(L.dut);
+  if ((rc = rc_of(moe::launch_bwd_dx(s, nullptr, nullptr, dXr, io->row_of, dl, w->w_router, 0, du, stream))))
+    return rc;
+  if ((rc = rc_of(moe::launch_dense(f32, du, wt->w_in_t, g->dx, dy, s.T, (int)d, (int)D, nullptr, stream))))
+    return rc;
+  if ((rc = rc_of(moe::launch_transpose(f32, dy, d, 0, nullptr, s.T, Tp, (int)d, 0, dyt, Tp, 0, 1, stream))))
+    return rc;
+  if ((rc = rc_of(moe::launch_transpose(f32, x, d, 0, nullptr, s.T, Tp, (int)d, 0, xt, Tp, 0, 1, stream)))) return rc;
+  if ((rc = rc_of(moe::launch_transpose(f32, io->o, D, 0, nullptr, s.T, Tp, (int)D, 0, ot, Tp, 0, 1, stream))))
+    return rc;
+  if ((rc = rc_of(moe::launch_transpose(f32, du, D, 0, nullptr, s.T, Tp, (int)D, 0, dut, Tp, 0, 1, stream))))
+    return rc;
+  if ((rc = rc_of(moe::launch_set_kwin(kwin, (int)Tp, stream)))) return rc;
+  if ((rc = rc_of(moe::gemm_kgrouped(f32, dyt, Tp, ot, Tp, g->dw_out, D, 0, 1, (int)d, (int)D, kwin, stream))))
+    return rc;
+  return rc_of(moe::gemm_kgrouped(f32, dut, Tp, xt, Tp, g->dw_in, d, 0, 1, (int)D, (int)d, kwin, stream));
 }
 
 }  // extern "C"

@@ -166,10 +166,8 @@ def test_one_hip_runtime_in_process():
 
 
 def test_backward_workspace_and_support():
-    for cfg in CONFIGS[:4] + SMALL[:4]:
+    for cfg in CONFIGS + SMALL:
         assert moe.moe_backward_workspace_bytes(cfg) > 0, cfg.name
-    assert moe.moe_backward_workspace_bytes(CONFIGS[4]) == 0   # multi-head latent: no backward
-    assert moe.moe_backward_workspace_bytes(SMALL[4]) == 0
 
 
 def test_backward_rejects_bad_arguments_before_launching():
@@ -182,9 +180,19 @@ def test_backward_rejects_bad_arguments_before_launching():
                              ctypes.byref(g), fake, 1 << 40, None) == moe.MOE_ERR_ARG
     assert lib.moe_layer_bwd(ctypes.byref(c), None, ctypes.byref(wt), fake, fake, 0.0, ctypes.byref(io),
                              ctypes.byref(g), fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    # latent layer: the projections' weights, transposes, z, o and their gradients are required
     c4 = moe.config_struct(CONFIGS[4])
-    assert lib.moe_layer_bwd(ctypes.byref(c4), ctypes.byref(w), ctypes.byref(wt), fake, fake, 0.0, ctypes.byref(io),
-                             ctypes.byref(g), fake, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    wf = moe.MoeWeights(**{n: 0x1000 for n, _ in moe.MoeWeights._fields_ if n not in ("w_in", "router_bias",
+                                                                                        "sel_bias")})
+    wtf = moe.MoeWeightsT(**{n: 0x1000 for n, _ in moe.MoeWeightsT._fields_})
+    iof = moe.MoeLayerIO(**{n: 0x1000 for n, _ in moe.MoeLayerIO._fields_ if n not in ("logits_mode",)})
+    gf = moe.MoeGrads(**{n: 0x1000 for n, _ in moe.MoeGrads._fields_})
+    assert lib.moe_layer_bwd(ctypes.byref(c4), ctypes.byref(wf), ctypes.byref(wtf), fake, fake, 0.0,
+                             ctypes.byref(iof), ctypes.byref(gf), fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    # several heads: no aux term
+    wf.w_in = 0x1000
+    assert lib.moe_layer_bwd(ctypes.byref(c4), ctypes.byref(wf), ctypes.byref(wtf), fake, fake, 0.5,
+                             ctypes.byref(iof), ctypes.byref(gf), fake, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_transpose_weights(ctypes.byref(c), ctypes.byref(w), ctypes.byref(wt), None) == moe.MOE_ERR_ARG
 
 

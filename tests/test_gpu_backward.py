@@ -1,5 +1,6 @@
 """GPU parity of the layer backward (moe_layer_bwd) against the float64 backward oracle.
 
+One-head layers, several routing heads with and without the latent projections.
 The forward runs on the GPU with the oracle's float32 scores loaded (routing
 identical); the oracle backward then takes the GPU's own keep decisions, so
 both sides differentiate the same function.  Bars: every gradient within
@@ -19,15 +20,27 @@ from tests.gpu_util import log, dev, f64, empty_act, i32, f32, tol, weights_dev
 pytestmark = pytest.mark.gpu
 
 ONE_HEAD = [c for c in SMALL if c.n_heads == 1 and not c.latent_proj]
+MULTI_HEAD = [c for c in SMALL if c.n_heads > 1]
 EDGE = [
     MoEConfig("bwd_edge_relu_bf16", T=70, d_model=128, n_heads=1, d_head=128, n_experts=5, top_k=2, d_ff=192,
               act=0, drop=1, capacity=20, n_shared=1, tag=70),
     MoEConfig("bwd_edge_k1_noresid", T=33, d_model=64, n_heads=1, d_head=64, n_experts=3, top_k=1, d_ff=64,
               residual=0, renorm=1, tag=71),
+    # two heads without projections (d_model = 2 * d_head), renormalised top-2 per head, ragged T
+    MoEConfig("bwd_edge_two_heads", T=45, d_model=256, n_heads=2, d_head=128, n_experts=10, top_k=2, d_ff=128,
+              renorm=1, drop=1, capacity=12, tag=72),
+    # latent heads with a d_head that is not a multiple of 256, float32
+    MoEConfig("bwd_edge_latent_f32", T=29, d_model=128, n_heads=3, d_head=64, n_experts=12, top_k=1, d_ff=64,
+              latent_proj=1, act=0, act_dtype=0, router_dtype=0, tag=73),
 ]
-CFGS = ONE_HEAD + EDGE
+CFGS = ONE_HEAD + MULTI_HEAD + EDGE
 IDS = [c.name for c in CFGS]
 LAM = 0.5
+
+
+def _lam(cfg):
+    """The aux loss exists for one routing head only."""
+    return LAM if cfg.n_heads == 1 else 0.0
 
 
 def _bits(t):
@@ -39,7 +52,9 @@ def _forward(cfg, inp, logits):
     Rm = moe.moe_rows_upper_bound(cfg)
     io = dict(logits=dev(logits), logits_mode=moe.MOE_LOGITS_LOAD, topk_idx=i32(T, K), topk_w=f32(T, K),
               demand=i32(E), counts=i32(E), offsets=i32(E + 1), row_of=i32(T, K), src_of=i32(max(Rm, 1)),
-              y_perm=empty_act(cfg, max(Rm, 1), cfg.d_head))
+              y_perm=empty_act(cfg, max(Rm, 1), cfg.d_head),
+              z=empty_act(cfg, T, cfg.d_latent) if cfg.latent_proj else None,
+              o=empty_act(cfg, T, cfg.d_latent) if cfg.latent_proj else None)
     W = weights_dev(cfg, inp)
     x = dev(inp.x)
     y = torch.empty_like(x)
@@ -53,10 +68,13 @@ def _transposed(cfg, W):
     adt = torch.bfloat16 if cfg.act_dtype == 1 else torch.float32
     E, dh, F, d = cfg.n_experts, cfg.d_head, cfg.d_ff, cfg.d_model
     fs = cfg.n_shared * F
+    D = cfg.d_latent
     wt = dict(w13t=torch.empty(E, dh, m * F, dtype=adt, device="cuda"),
               w2t=torch.empty(E, F, dh, dtype=adt, device="cuda"),
               ws13t=torch.empty(d, m * fs, dtype=adt, device="cuda") if fs else None,
-              ws2t=torch.empty(fs, d, dtype=adt, device="cuda") if fs else None)
+              ws2t=torch.empty(fs, d, dtype=adt, device="cuda") if fs else None,
+              w_in_t=torch.empty(d, D, dtype=adt, device="cuda") if cfg.latent_proj else None,
+              w_out_t=torch.empty(D, d, dtype=adt, device="cuda") if cfg.latent_proj else None)
     moe.moe_transpose_weights(cfg, W, wt)
     return wt
 
@@ -66,10 +84,12 @@ def _grads(cfg):
     E, dh, F, d = cfg.n_experts, cfg.d_head, cfg.d_ff, cfg.d_model
     fs = cfg.n_shared * F
     z = lambda *s: torch.full(s, float("nan"), dtype=adt, device="cuda")
+    D = cfg.d_latent
     return dict(dx=z(cfg.T, d), dw_router=f32(E, dh), dbias=f32(E), dw1=z(E, F, dh),
                 dw3=z(E, F, dh) if cfg.act == 1 else None, dw2=z(E, dh, F),
                 dws1=z(fs, d) if fs else None, dws3=z(fs, d) if (fs and cfg.act == 1) else None,
-                dws2=z(d, fs) if fs else None)
+                dws2=z(d, fs) if fs else None,
+                dw_in=z(D, d) if cfg.latent_proj else None, dw_out=z(d, D) if cfg.latent_proj else None)
 
 
 def _dy(cfg):
@@ -94,17 +114,21 @@ def test_backward_matches_oracle(cfg):
     dy = dev(dy_h)
     G = _grads(cfg)
     ws = moe.backward_workspace(cfg)
-    moe.moe_layer_bwd(cfg, W, wt, x, dy, LAM, io, G, ws)
+    lam = _lam(cfg)
+    moe.moe_layer_bwd(cfg, W, wt, x, dy, lam, io, G, ws)
     torch.cuda.synchronize()
     # the oracle differentiates the same decisions: the GPU's top-k and keep mask
     kept = io["row_of"].cpu().numpy().reshape(-1) >= 0
     P = OB.params_of(inp)
-    ref = OB.backward(cfg, P, io["topk_idx"].cpu().numpy(), kept, oracle.decode(dy_h), LAM)
+    # (with latent_proj the GPU's experts read its own stored z, the oracle float64 z: a rounding the bars cover)
+    ref = OB.backward(cfg, P, io["topk_idx"].cpu().numpy(), kept, oracle.decode(dy_h), lam)
     pairs = [("dx", "dx"), ("dw_router", "dw_router"), ("dbias", "dbias"), ("dw1", "dw1"), ("dw2", "dw2")]
     if cfg.act == 1:
         pairs.append(("dw3", "dw3"))
     if cfg.n_shared:
         pairs += [("dws1", "dws1"), ("dws2", "dws2")] + ([("dws3", "dws3")] if cfg.act == 1 else [])
+    if cfg.latent_proj:
+        pairs += [("dw_in", "dw_in"), ("dw_out", "dw_out")]
     for gk, rk in pairs:
         got, want = f64(G[gk]), ref[rk]
         scale = max(np.max(np.abs(want)), 1e-30)
@@ -114,7 +138,7 @@ def test_backward_matches_oracle(cfg):
         assert err <= tol(cfg) * scale, gk
 
 
-@pytest.mark.parametrize("cfg", [ONE_HEAD[1], EDGE[0]], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [ONE_HEAD[1], EDGE[0], MULTI_HEAD[0]], ids=lambda c: c.name)
 def test_backward_deterministic(cfg):
     inp = _inputs(cfg)
     out = oracle.forward(cfg, inp)
@@ -123,14 +147,21 @@ def test_backward_deterministic(cfg):
     dy = dev(_dy(cfg))
     ws = moe.backward_workspace(cfg)
     G1, G2 = _grads(cfg), _grads(cfg)
-    moe.moe_layer_bwd(cfg, W, wt, x, dy, LAM, io, G1, ws)
-    moe.moe_layer_bwd(cfg, W, wt, x, dy, LAM, io, G2, ws)
+    moe.moe_layer_bwd(cfg, W, wt, x, dy, _lam(cfg), io, G1, ws)
+    moe.moe_layer_bwd(cfg, W, wt, x, dy, _lam(cfg), io, G2, ws)
     torch.cuda.synchronize()
     for k in G1:
         if G1[k] is not None:
             assert torch.equal(_bits(G1[k]), _bits(G2[k])), k
 
 
-def test_backward_rejects_multihead():
+def test_backward_rejects_aux_with_several_heads():
+    """The aux loss is defined for one head: a nonzero weight with several heads is refused before launching."""
     cfg = SMALL[4]
-    assert moe.moe_backward_workspace_bytes(cfg) == 0
+    inp = _inputs(cfg)
+    out = oracle.forward(cfg, inp)
+    W, x, io = _forward(cfg, inp, out["logits"])
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_layer_bwd(cfg, W, _transposed(cfg, W), x, dev(_dy(cfg)), 0.5, io, _grads(cfg),
+                          moe.backward_workspace(cfg))
+    assert e.value.status == moe.MOE_ERR_UNSUPPORTED

@@ -1,10 +1,12 @@
-"""Backward at the full workload sizes (one routing head), in the launch configuration the
-benchmark times, against the float64 backward oracle on samples it evaluates cheaply:
+"""Backward at the full workload sizes, in the launch configuration the benchmark times,
+against the float64 backward oracle.  One-head workloads on samples it evaluates cheaply:
 dx of sampled tokens (a token's input gradient needs only its own experts and the
 demand counts), and the weight gradients of one expert restricted to sampled hidden
 units (they decompose over hidden units).  Router gradients: every token's logit
 gradient sums to zero over the experts (softmax Jacobian), so sum_e dbias_e and
-every column sum of dW_router vanish.  Plus finiteness and bitwise reproducibility.
+every column sum of dW_router vanish.  The multi-head latent workload's experts are
+small, so the oracle's whole backward runs and every gradient is compared.  Plus
+finiteness and bitwise reproducibility.
 """
 import numpy as np
 import pytest
@@ -18,8 +20,12 @@ from tests.gpu_util import log, dev, f64, tol, weights_dev, cached_inputs
 
 pytestmark = pytest.mark.gpu
 
-FULL = [c for c in CONFIGS[1:] if c.n_heads == 1 and not c.latent_proj]
-LAM = 0.01
+FULL = CONFIGS[1:]
+
+
+def _lam(cfg):
+    """Aux weight: the aux loss is defined for one routing head."""
+    return 0.01 if cfg.n_heads == 1 else 0.0
 
 
 def _bits(t):
@@ -39,13 +45,16 @@ def test_fullsize_backward(cfg):
     io = dict(logits=e_(T, E, dt=torch.float32), logits_mode=moe.MOE_LOGITS_COMPUTE_STORE,
               topk_idx=e_(T, K, dt=torch.int32), topk_w=e_(T, K, dt=torch.float32), demand=e_(E, dt=torch.int32),
               counts=e_(E, dt=torch.int32), offsets=e_(E + 1, dt=torch.int32), row_of=e_(T, K, dt=torch.int32),
-              src_of=e_(Rm, dt=torch.int32), y_perm=e_(Rm, dh))
+              src_of=e_(Rm, dt=torch.int32), y_perm=e_(Rm, dh),
+              z=e_(T, cfg.d_latent) if cfg.latent_proj else None, o=e_(T, cfg.d_latent) if cfg.latent_proj else None)
     W = weights_dev(cfg, inp)
     x = dev(inp.x)
     y = torch.empty_like(x)
     moe.moe_layer_fwd(cfg, W, x, y, io, moe.workspace(cfg))
+    D = cfg.d_latent
     wt = dict(w13t=e_(E, dh, m * F), w2t=e_(E, F, dh), ws13t=e_(d, m * fs) if fs else None,
-              ws2t=e_(fs, d) if fs else None)
+              ws2t=e_(fs, d) if fs else None, w_in_t=e_(d, D) if cfg.latent_proj else None,
+              w_out_t=e_(D, d) if cfg.latent_proj else None)
     moe.moe_transpose_weights(cfg, W, wt)
     rng = np.random.default_rng([5, cfg.tag])
     dy_h = bf16_bits_from_f32(rng.standard_normal((T, d)).astype(np.float32))
@@ -55,11 +64,13 @@ def test_fullsize_backward(cfg):
         return dict(dx=e_(T, d), dw_router=e_(E, dh, dt=torch.float32), dbias=e_(E, dt=torch.float32),
                     dw1=e_(E, F, dh), dw3=e_(E, F, dh) if cfg.act == 1 else None, dw2=e_(E, dh, F),
                     dws1=e_(fs, d) if fs else None, dws3=e_(fs, d) if (fs and cfg.act == 1) else None,
-                    dws2=e_(d, fs) if fs else None)
+                    dws2=e_(d, fs) if fs else None, dw_in=e_(D, d) if cfg.latent_proj else None,
+                    dw_out=e_(d, D) if cfg.latent_proj else None)
 
     ws = moe.backward_workspace(cfg)
     G1, G2 = grads(), grads()
     log("  GPU backward x2")
+    LAM = _lam(cfg)
     moe.moe_layer_bwd(cfg, W, wt, x, dy, LAM, io, G1, ws)
     moe.moe_layer_bwd(cfg, W, wt, x, dy, LAM, io, G2, ws)
     torch.cuda.synchronize()
@@ -78,6 +89,17 @@ def test_fullsize_backward(cfg):
     kept = io["row_of"].cpu().numpy().reshape(-1) >= 0
     demand = io["demand"].cpu().numpy()
     dy64 = oracle.decode(dy_h)
+    if cfg.latent_proj:
+        log("  oracle: the whole backward")
+        ref = OB.backward(cfg, P, idx, kept, dy64, LAM)
+        names = ["dx", "dw_router", "dbias", "dw1", "dw2", "dw_in", "dw_out"] + (["dw3"] if cfg.act == 1 else [])
+        for k in names:
+            got, want = f64(G1[k]), ref[k]
+            scale = np.max(np.abs(want))
+            err = np.max(np.abs(got - want))
+            log(f"  {k:10s} rel err {err / scale:.3g}")
+            assert err <= tol(cfg) * scale, k
+        return
     toks = np.linspace(0, T - 1, 6).astype(np.int64)
     log("  oracle: sampled tokens")
     ref = OB.backward_tokens(cfg, P, idx, kept, dy64, LAM, toks, demand)
