@@ -237,6 +237,10 @@ __global__ __launch_bounds__(256) void disp_affinity_kernel(
   const int keep = counts[e];
   const int out0 = offsets[e];
   if (n == 0) return;
+  if (keep == 0) {  // nothing kept (capacity 0): every assignment of e is dropped
+    for (int i = tid; i < n; i += 256) row_of[seg[beg + i]] = -1;
+    return;
+  }
   const bool staged = n <= cap;
   if (staged) {
     for (int i = tid; i < n; i += 256) {

@@ -257,3 +257,55 @@ def test_variant_backward(cfg):
         err = np.max(np.abs(got - want))
         log(f"  {k:10s} rel err {err / scale:.3g}")
         assert err <= tol(cfg) * scale, k
+
+
+# ------------------------------------------------------------------ edge cases
+def _edge_variants():
+    from moe_inputs import MoEConfig
+    base = MoEConfig("edge_var", T=37, d_model=128, n_heads=1, d_head=128, n_experts=4, top_k=2, d_ff=128,
+                     drop=1, capacity=9, route_mode=1, tag=80)
+    return [
+        base.with_(name="edge_ec_capacity0_shared", capacity=0, n_shared=1),
+        base.with_(name="edge_ec_capacity_over_T", capacity=50),
+        base.with_(name="edge_ec_T1", T=1, capacity=1),
+        base.with_(name="edge_ec_E1_relu_f32", n_experts=1, top_k=1, capacity=20, act=0, act_dtype=0,
+                   router_dtype=0),
+        base.with_(name="edge_bias_seq_T1", T=1, route_mode=0, drop=0, capacity=0, sel_bias_steps=5, seq_len=1),
+        base.with_(name="edge_bias_seq_whole", route_mode=0, drop=0, capacity=0, sel_bias_steps=5,
+                   sel_bias_gate=1, seq_len=37, top_k=4),
+    ]
+
+
+@pytest.mark.parametrize("cfg", _edge_variants(), ids=lambda c: c.name)
+def test_variant_edges(cfg):
+    log(f"variant edge {cfg.name}")
+    inp = generate(cfg)
+    out = oracle.forward(cfg, inp, want_xperm=True)
+    y, io, _, _ = _layer(cfg, inp, out["logits"])
+    assert np.array_equal(io["counts"].cpu().numpy(), out["counts"])
+    assert np.array_equal(io["row_of"].cpu().numpy(), out["row_of"])
+    got, ref = f64(y), out["y"]
+    err = np.max(np.abs(got - ref))
+    log(f"  max err {err:.3g}")
+    assert err <= tol(cfg) * max(np.max(np.abs(ref)), 1e-30)
+    if cfg.seq_len:
+        seq = f64(io["seq_loss"])
+        assert np.all(np.abs(seq - out["seq"]) <= 1e-5 * np.maximum(1.0, np.abs(out["seq"])))
+    # the backward on the same decisions
+    from tests.test_gpu_backward import _transposed, _grads, _dy
+    W = weights_dev(cfg, inp)
+    x = dev(inp.x)
+    G = _grads(cfg)
+    dy_h = _dy(cfg)
+    moe.moe_layer_bwd(cfg, W, _transposed(cfg, W), x, dev(dy_h), 0.5, io, G, moe.backward_workspace(cfg))
+    torch.cuda.synchronize()
+    kept = io["row_of"].cpu().numpy().reshape(-1) >= 0
+    ref = OB.backward(cfg, OB.params_of(inp), io["topk_idx"].cpu().numpy(), kept, oracle.decode(dy_h), 0.5)
+    for k in ["dx", "dw_router", "dbias", "dw1", "dw2"] + (["dws1", "dws2"] if cfg.n_shared else []):
+        got, want = f64(G[k]), ref[k]
+        # floor 1e-6: with expert choice every expert's aux load is T, so when no gate
+        # gradient reaches the router its dp is constant and the softmax Jacobian cancels
+        # it exactly; both sides then hold only rounding (float64 ~1e-18, float32 ~1e-9)
+        scale = max(np.max(np.abs(want)), 1e-6)
+        assert np.all(np.isfinite(got)), k
+        assert np.max(np.abs(got - want)) <= tol(cfg) * scale, k
