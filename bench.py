@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: automatic)")
     ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-graph", action="store_true", help="skip timing the step as a captured HIP graph")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB (a known-size "
                          "reference for the HBM byte counters of a profiler run)")
@@ -236,6 +237,31 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] {ms_step:.3f} ms/step (events), {wall / args.steps * 1e3:.3f} ms/step (wall)")
 
+    # ---- the same step captured once in a HIP graph and replayed (no per-launch host work)
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        gb.record(stream)
+        torch.cuda.synchronize()
+        gms = ga.elapsed_time(gb) / args.steps
+        graph = {"ms_per_step": gms, "tokens_per_s": T / (gms * 1e-3), "steps": args.steps}
+        log(f"[bench] graph replay {gms:.3f} ms/step")
+        del g
+
     # ---- per-stage times: the four C-ABI calls on the same data, HIP events on this stream
     xin = io["z"] if cfg.latent_proj else x
     reps = max(5, min(50, args.steps))
@@ -315,6 +341,7 @@ def main():
                      "algorithmic_flops": alg["ffn_flops"]},
         "stages": stages,
         "backward": bwd,
+        "graph": graph,
         "device": dev_name,
     }
     if bwd is not None:
