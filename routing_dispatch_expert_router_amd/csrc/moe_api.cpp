@@ -136,13 +136,21 @@ int rc_of(int launcher_rc) {
 }
 
 // ---------------------------------------------------------------- backward
-bool bwd_supported(const Shape &s) { return gather_supported(s); }
-
 // columns of the per-expert padded, transposed activations: every expert's
 // rows rounded up to 64 (the GEMM k-chunk), and a multiple of 64 overall so
 // rows of the transposed buffers stay 16-byte aligned
 long rpad_bound(const Shape &s) { return (s.R_max + 63) / 64 * 64 + 64L * s.E; }
 long tpad(const Shape &s) { return (s.T + 63) / 64 * 64; }
+
+// The weight-gradient products address their transposed operands with 32-bit
+// element offsets: every transposed buffer must stay below 2^31 elements.
+bool bwd_supported(const Shape &s) {
+  const long m = s.act == MOE_ACT_SWIGLU ? 2 : 1, lim = 1L << 31;
+  const long rows = std::max<long>(s.dh, m * s.dff);
+  if (!gather_supported(s) || rows * rpad_bound(s) >= lim) return false;
+  const long wide = std::max<long>({(long)s.d, (long)s.H * s.dh, m * s.n_shared * (long)s.dff});
+  return wide * tpad(s) < lim;
+}
 
 struct BwdBufs {
   size_t dg, dl, rpart, dY, dH, dAB, Hr, dXr, poff, pmap_r, pmap_x, Xt, dYt, dABt, Ht, prefix, kwin;

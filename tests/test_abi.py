@@ -168,6 +168,10 @@ def test_one_hip_runtime_in_process():
 def test_backward_workspace_and_support():
     for cfg in CONFIGS + SMALL:
         assert moe.moe_backward_workspace_bytes(cfg) > 0, cfg.name
+    # transposed weight-gradient operands past 2^31 elements (32-bit offsets): not supported
+    huge = CONFIGS[3].with_(T=131072)
+    assert moe.moe_check_config(huge) == moe.MOE_OK
+    assert moe.moe_backward_workspace_bytes(huge) == 0
 
 
 def test_backward_rejects_bad_arguments_before_launching():
