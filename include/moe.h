@@ -164,7 +164,11 @@ int64_t moe_rows_upper_bound(const moe_config *cfg);
 /* [host] Static string naming a moe_status value. */
 const char *moe_status_str(int status);
 
-/* [host] MOE_OK if `cfg` is valid and supported, else the error moe_* calls would return. */
+/* [host] MOE_OK if `cfg` is valid and supported, else the error moe_* calls would return.
+ * Supported sizes: T*K, T*max(d_model, H*d_head, m*d_ff, m*n_shared*d_ff),
+ * d_ff*d_head, n_shared*d_ff*d_model and H*d_head*d_model below 2^31
+ * (m = 2 for SwiGLU, else 1; the GEMM addresses one group's operands with
+ * 32-bit element offsets); MOE_ERR_UNSUPPORTED otherwise. */
 int moe_check_config(const moe_config *cfg);
 
 /*

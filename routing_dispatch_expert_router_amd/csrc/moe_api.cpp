@@ -60,6 +60,14 @@ int make_shape(const moe_config *c, Shape *s) {
   if (c->seq_len > 0 && c->n_heads != 1) return MOE_ERR_UNSUPPORTED;
   const long kslots = ec ? c->n_experts : (long)c->n_heads * c->top_k;
   if ((long)c->T * kslots > 0x7FFFFFFFL) return MOE_ERR_UNSUPPORTED;
+  {
+    // the GEMM addresses one group's operands with 32-bit element offsets
+    const long lim = 1L << 31, T = c->T, D = (long)c->n_heads * c->d_head, fs = (long)c->n_shared * c->d_ff;
+    const long m = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+    if (T * std::max<long>({(long)c->d_model, D, m * c->d_ff, m * fs}) >= lim) return MOE_ERR_UNSUPPORTED;
+    if ((long)c->d_ff * c->d_head >= lim || fs * c->d_model >= lim || D * c->d_model >= lim)
+      return MOE_ERR_UNSUPPORTED;
+  }
   s->T = c->T; s->d = c->d_model; s->H = c->n_heads; s->dh = c->d_head; s->E = c->n_experts; s->Eh = Eh;
   s->k = ec ? Eh : c->top_k; s->K = (int)kslots;
   s->n_groups = c->n_groups; s->topk_groups = c->topk_groups; s->renorm = c->renorm;
