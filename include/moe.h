@@ -323,7 +323,8 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
                   moe_layer_io *io, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ============================================================ backward
- * Gradients of  L = sum_t <dy_t, y_t> + aux_weight * l_aux  with the
+ * Gradients of  L = sum_t <dy_t, y_t> + aux_weight * l_aux
+ *                  + seq_weight * sum_s sum_e f_{s,e} P_{s,e}  with the
  * forward's discrete decisions (top-k choice, keep rule) held fixed: those are
  * piecewise constant, so the gradient flows through the gate values, the
  * experts, the router probabilities, the shared experts, the residual and,
@@ -373,6 +374,10 @@ int moe_transpose_weights(const moe_config *cfg, const moe_weights *w, const moe
  *   x          [T, d_model] act: the forward input
  *   dy         [T, d_model] act: upstream gradient of y
  *   aux_weight coefficient of l_aux in L (0: no aux term)
+ *   seq_weight coefficient of the summed per-sequence balance terms in L
+ *              (the statistic moe_route reports; alpha on the page,
+ *              "MoE技术演进", "DeepSeek-V3" item 4); requires cfg->seq_len
+ *              when nonzero (0: no such term)
  *   io         the forward's state: logits (the forward's scores, bias
  *              included: run it with MOE_LOGITS_COMPUTE_STORE), topk_idx,
  *              topk_w, demand, offsets, row_of, src_of, y_perm -- all
@@ -388,8 +393,8 @@ int moe_transpose_weights(const moe_config *cfg, const moe_weights *w, const moe
  * (sel_bias_gate with renorm) is MOE_ERR_UNSUPPORTED.
  */
 int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights_t *wt, const void *x,
-                  const void *dy, float aux_weight, const moe_layer_io *io, moe_grads *g, void *ws,
-                  size_t ws_bytes, hipStream_t stream);
+                  const void *dy, float aux_weight, float seq_weight, const moe_layer_io *io, moe_grads *g,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

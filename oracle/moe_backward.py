@@ -33,6 +33,7 @@ Router:
   dp_{t,e} += lam * c_e / S^2               (aux loss, every e)
   dl_{t,e} = p_{t,e} (dp_{t,e} - sum_e' p_{t,e'} dp_{t,e'})         (softmax Jacobian)
   dW_r += dl^T x,  db += sum_t dl_t,  dx_t += W_r^T dl_t
+  dp_{t,e} += alpha * c_{s,e} / L^2         (sequence-wise balance term, t in sequence s)
 Shared experts and the residual: the same MLP backward with gate 1, and dx_t += dy_t.
 
 Routing variants: with expert choice every token has one slot per expert
@@ -138,7 +139,15 @@ def routed_o(cfg, P, topk_idx, kept, u=None):
     return o
 
 
-def forward_fixed(cfg, P, topk_idx, kept, lam=0.0, dy=None):
+def _seq_counts(cfg, topk_idx):
+    """c[s][e]: choices of expert e within sequence s (runs of seq_len tokens)."""
+    L, E = cfg.seq_len, cfg.n_experts
+    idx = np.asarray(topk_idx).astype(np.int64)
+    return np.stack([np.bincount(idx[s * L:(s + 1) * L].reshape(-1), minlength=E)
+                     for s in range(cfg.T // L)]).astype(np.float64)
+
+
+def forward_fixed(cfg, P, topk_idx, kept, lam=0.0, dy=None, seq_w=0.0):
     """The layer output y (float64) with the decisions held fixed, and L = <dy, y> + lam * l_aux.
 
     topk_idx [T, k] and kept [T*k] are the forward's decisions.
@@ -160,6 +169,12 @@ def forward_fixed(cfg, P, topk_idx, kept, lam=0.0, dy=None):
         c = np.bincount(topk_idx.reshape(-1), minlength=cfg.n_experts).astype(np.float64)
         aux = float(np.sum(p.sum(axis=0) / S * c / S))
         L = float(np.sum(dy * y)) + lam * aux
+        if seq_w:
+            # sequence-wise balance term: sum over sequences of sum_e (c_se / Ls) P_se
+            Ls = cfg.seq_len
+            cs = _seq_counts(cfg, topk_idx)
+            Ps = p.reshape(T // Ls, Ls, -1).sum(axis=1) / Ls
+            L += seq_w * float(np.sum(cs / Ls * Ps))
     return y, L
 
 
@@ -228,8 +243,9 @@ def _gate_to_prob_grad(cfg, g, S, dg):
     return (dg - sdg) / S
 
 
-def backward(cfg, P, topk_idx, kept, dy, lam=0.0):
-    """Gradients of L = <dy, y> + lam * l_aux (see the module docstring), float64.
+def backward(cfg, P, topk_idx, kept, dy, lam=0.0, seq_w=0.0):
+    """Gradients of L = <dy, y> + lam * l_aux [+ seq_w * sum of the per-sequence balance
+    terms] (see the module docstring), float64.
 
     Returns dict: dx, dw_router, dbias, dw1, dw3, dw2, dws1, dws3, dws2, dw_in, dw_out
     (None where absent), plus the intermediates dg [T, K] (gate gradients), dl [T, E]
@@ -281,6 +297,10 @@ def backward(cfg, P, topk_idx, kept, dy, lam=0.0):
     if lam:
         c = np.bincount(idx.reshape(-1), minlength=E).astype(np.float64)
         dp += lam * c[None, :] / (T * T)
+    if seq_w:
+        # d/dp_{t,e} of sum_e (c_se / L) (1/L) sum_{t in s} p_{t,e} = c_se / L^2 for t in s
+        Ls = cfg.seq_len
+        dp += seq_w * np.repeat(_seq_counts(cfg, topk_idx), Ls, axis=0) / (Ls * Ls)
     dl = _head_softmax_backward(cfg, p, dp)
     dw_router = np.empty_like(P["w_router"])
     for h in range(cfg.n_heads):
@@ -312,7 +332,7 @@ def backward(cfg, P, topk_idx, kept, dy, lam=0.0):
                 dws1=dws1, dws3=dws3, dws2=dws2, dw_in=dw_in, dw_out=dw_out, dg=dg, dl=dl, du=du)
 
 
-def backward_tokens(cfg, P, topk_idx, kept, dy, lam, tokens, demand):
+def backward_tokens(cfg, P, topk_idx, kept, dy, lam, tokens, demand, seq_w=0.0):
     """dx of the given tokens only: the same chain rule as `backward`, evaluated per
     token (a token's input gradient depends on its own choices, and on the other
     tokens only through the aux loss's demand counts `demand` [E])."""
@@ -344,6 +364,9 @@ def backward_tokens(cfg, P, topk_idx, kept, dy, lam, tokens, demand):
         np.add.at(dp, (np.zeros(K, np.int64), idx_t[0]), _gate_to_prob_grad(cfg, g, S, dg)[0])
         if lam:
             dp += lam * np.asarray(demand, np.float64)[None, :] / (T * T)
+        if seq_w:
+            Ls = cfg.seq_len
+            dp += seq_w * _seq_counts(cfg, topk_idx)[t // Ls][None, :] / (Ls * Ls)
         dl = _head_softmax_backward(cfg, p, dp)
         for h in range(cfg.n_heads):
             rows = slice(h * Eh, (h + 1) * Eh)

@@ -99,7 +99,7 @@ def _load():
         "moe_backward_workspace_bytes": (S, [Z]),
         "moe_transpose_weights": (I, [Z, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeightsT), P]),
         "moe_layer_bwd": (I, [Z, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeightsT), P, P, ctypes.c_float,
-                              ctypes.POINTER(MoeLayerIO), ctypes.POINTER(MoeGrads), P, S, P]),
+                              ctypes.c_float, ctypes.POINTER(MoeLayerIO), ctypes.POINTER(MoeGrads), P, S, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -258,7 +258,7 @@ def moe_transpose_weights(cfg, weights, wt, stream=None):
                   "moe_transpose_weights")
 
 
-def moe_layer_bwd(cfg, weights, wt, x, dy, aux_weight, io, grads, ws, stream=None):
+def moe_layer_bwd(cfg, weights, wt, x, dy, aux_weight, io, grads, ws, stream=None, seq_weight=0.0):
     """io: the forward's moe_layer_io tensors (dict); grads: moe_grads field names -> tensors."""
     c = _c(cfg)
     w = _weights(weights)
@@ -267,5 +267,6 @@ def moe_layer_bwd(cfg, weights, wt, x, dy, aux_weight, io, grads, ws, stream=Non
     iob = MoeLayerIO(logits_mode=int(io.get("logits_mode", MOE_LOGITS_COMPUTE)), **kw)
     g = MoeGrads(**{k: (v.data_ptr() if v is not None else None) for k, v in grads.items()})
     return _check(_lib.moe_layer_bwd(ctypes.byref(c), ctypes.byref(w), ctypes.byref(t), _p(x), _p(dy),
-                                     float(aux_weight), ctypes.byref(iob), ctypes.byref(g), _p(ws), _nbytes(ws),
+                                     float(aux_weight), float(seq_weight), ctypes.byref(iob), ctypes.byref(g),
+                                     _p(ws), _nbytes(ws),
                                      _stream(stream)), "moe_layer_bwd")

@@ -164,13 +164,16 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TA *__restrict__ s
 // dl[t][e] = p_e (dp_e - sum_e' p_e' dp_e') over the head's E_h experts,
 // p = the head's softmax of the logits; dp from the gate gradients of the
 // head's k slots (renormalised: (dg_j - sum dg g) / P at the chosen experts)
-// plus lam * demand_e / T^2 (aux loss, one head).  One wave per (token, head).
+// plus lam * demand_e / T^2 (aux loss, one head) plus seq_w * c_{s,e} / L^2 for
+// the token's sequence s (sequence-wise balance term, one head).  One wave per
+// (token, head).
 __global__ __launch_bounds__(256) void router_bwd_kernel(const float *__restrict__ logits,
                                                          const int32_t *__restrict__ topk_idx,
                                                          const float *__restrict__ gates,
                                                          const float *__restrict__ dg,
                                                          const int32_t *__restrict__ demand, int T, int H, int E,
                                                          int Eh, int K, int k, int renorm, float lam,
+                                                         const int32_t *__restrict__ seq_cnt, int L, float seq_w,
                                                          float *__restrict__ dl) {
   const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -194,8 +197,11 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float *__restrict
     sdg += tdg[j] * tg[j];
   }
   const float invT2 = 1.0f / ((float)T * (float)T);
+  const float invL2 = seq_cnt ? 1.0f / ((float)L * (float)L) : 0.f;
+  const int32_t *sc = seq_cnt ? seq_cnt + (size_t)(t / L) * E : nullptr;
   auto dp_of = [&](int e) {
     float dp = lam * (float)demand[h * Eh + e] * invT2;
+    if (sc) dp += seq_w * (float)sc[h * Eh + e] * invL2;
     for (int j = 0; j < k; ++j)
       if (ti[j] - h * Eh == e) dp += renorm ? (tdg[j] - sdg) / P : tdg[j];
     return dp;
@@ -427,12 +433,32 @@ int launch_bwd_pad(const Shape &s, const int32_t *offsets, const int32_t *src_of
   return launch_status("padding map");
 }
 
+// seq_cnt[s][e] by integer LDS atomics (order-free), one block per sequence
+__global__ __launch_bounds__(256) void seq_counts_kernel(const int32_t *__restrict__ topk_idx, int E, int K, int L,
+                                                         int32_t *__restrict__ seq_cnt) {
+  extern __shared__ int cnt[];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  const long a0 = (long)blockIdx.x * L * K;
+  for (long i = tid; i < (long)L * K; i += 256) atomicAdd(&cnt[topk_idx[a0 + i]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) seq_cnt[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+int launch_seq_counts(const Shape &s, const int32_t *topk_idx, int32_t *seq_cnt, hipStream_t st) {
+  hipLaunchKernelGGL(seq_counts_kernel, dim3((unsigned)(s.T / s.seq_len)), dim3(256), (size_t)s.E * 4, st, topk_idx,
+                     s.E, s.K, s.seq_len, seq_cnt);
+  return launch_status("sequence counts");
+}
+
 int launch_router_bwd(const Shape &s, const float *logits, const int32_t *topk_idx, const float *gates,
-                      const float *dg, const int32_t *demand, float lam, const void *x, float *dl, float *part,
-                      float *dw_router, float *dbias, hipStream_t st) {
+                      const float *dg, const int32_t *demand, float lam, const int32_t *seq_cnt, float seq_w,
+                      const void *x, float *dl, float *part, float *dw_router, float *dbias, hipStream_t st) {
   const long pairs = (long)s.T * s.H;
   hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, logits, topk_idx,
-                     gates, dg, demand, s.T, s.H, s.E, s.Eh, s.K, s.k, s.renorm, lam, dl);
+                     gates, dg, demand, s.T, s.H, s.E, s.Eh, s.K, s.k, s.renorm, lam, seq_cnt, s.seq_len > 0 ? s.seq_len : 1,
+                     seq_w, dl);
   if (int rc = launch_status("router backward")) return rc;
   if (dbias) {
     hipLaunchKernelGGL(router_dbias_kernel, dim3((unsigned)s.E), dim3(256), 0, st, dl, s.T, s.E, dbias);

@@ -73,8 +73,10 @@ inline int router_wgrad_split(const Shape &s) {
   return (int)std::min<long>(64, std::max<long>(1, (4096 + tiles - 1) / std::max<long>(tiles, 1)));
 }
 int launch_router_bwd(const Shape &s, const float *logits, const int32_t *topk_idx, const float *gates,
-                      const float *dg, const int32_t *demand, float lam, const void *x, float *dl, float *part,
-                      float *dw_router, float *dbias, hipStream_t st);
+                      const float *dg, const int32_t *demand, float lam, const int32_t *seq_cnt, float seq_w,
+                      const void *x, float *dl, float *part, float *dw_router, float *dbias, hipStream_t st);
+// seq_cnt[s][e]: choices of expert e within sequence s
+int launch_seq_counts(const Shape &s, const int32_t *topk_idx, int32_t *seq_cnt, hipStream_t st);
 int launch_bwd_dx(const Shape &s, const void *dy, const void *dxs, const void *dXr, const int32_t *row_of,
                   const float *dl, const void *w_router, int residual, void *dx, hipStream_t st);
 int launch_set_kwin(int32_t *kwin, int tpad, hipStream_t st);

@@ -161,7 +161,7 @@ bool bwd_supported(const Shape &s) {
 }
 
 struct BwdBufs {
-  size_t dg, dl, rpart, dY, dH, dAB, Hr, dXr, poff, pmap_r, pmap_x, Xt, dYt, dABt, Ht, prefix, kwin;
+  size_t dg, dl, rpart, seqcnt, dY, dH, dAB, Hr, dXr, poff, pmap_r, pmap_x, Xt, dYt, dABt, Ht, prefix, kwin;
   size_t dHs, dABs, Hs, dxs, dyt, xt, dABst, Hst, dout, du, ot, dut, total;
 };
 
@@ -173,6 +173,7 @@ BwdBufs bwd_layout(const Shape &s) {
   b.dg = o; o += al((size_t)s.T * s.K * 4);
   b.dl = o; o += al((size_t)s.T * s.E * 4);
   b.rpart = o; o += al((size_t)moe::router_wgrad_split(s) * s.E * s.dh * 4);
+  b.seqcnt = o; o += s.seq_len > 0 ? al((size_t)(s.T / s.seq_len) * s.E * 4) : 0;
   b.dY = o; o += al(R * s.dh * esz);
   b.dH = o; o += al(R * s.dff * esz);
   b.dAB = o; o += al(R * m * s.dff * esz);
@@ -459,8 +460,8 @@ int moe_transpose_weights(const moe_config *cfg, const moe_weights *w, const moe
 }
 
 int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights_t *wt, const void *x,
-                  const void *dy, float aux_weight, const moe_layer_io *io, moe_grads *g, void *ws,
-                  size_t ws_bytes, hipStream_t stream) {
+                  const void *dy, float aux_weight, float seq_weight, const moe_layer_io *io, moe_grads *g,
+                  void *ws, size_t ws_bytes, hipStream_t stream) {
   Shape s;
   int rc = make_shape(cfg, &s);
   if (rc) return rc;
@@ -482,6 +483,7 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
     return MOE_ERR_ARG;
   // the aux loss is defined for one routing head
   if (s.H > 1 && aux_weight != 0.0f) return MOE_ERR_UNSUPPORTED;
+  if (seq_weight != 0.0f && s.seq_len == 0) return MOE_ERR_ARG;
   const BwdBufs L = bwd_layout(s);
   if (!ws || ((uintptr_t)ws & 255) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (s.T == 0) return MOE_OK;
@@ -546,7 +548,10 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
                                             s.E, (int)dff, (int)dh, poff, stream))))
     return rc;
   // router: dl, dW_r, dbias
-  if ((rc = rc_of(moe::launch_router_bwd(s, io->logits, io->topk_idx, io->topk_w, dg, io->demand, aux_weight, u, dl,
+  int32_t *seqcnt = seq_weight != 0.0f ? (int32_t *)at(L.seqcnt) : nullptr;
+  if (seqcnt && (rc = rc_of(moe::launch_seq_counts(s, io->topk_idx, seqcnt, stream)))) return rc;
+  if ((rc = rc_of(moe::launch_router_bwd(s, io->logits, io->topk_idx, io->topk_w, dg, io->demand, aux_weight,
+                                         seqcnt, seq_weight, u, dl,
                                          (float *)at(L.rpart), g->dw_router, g->dbias, stream))))
     return rc;
   // shared experts: the same MLP backward over all T tokens with gate 1

@@ -80,19 +80,19 @@ _GRAD = dict(x="dx", w_router="dw_router", bias="dbias", w1="dw1", w3="dw3", w2=
              ws1="dws1", ws3="dws3", ws2="dws2", w_in="dw_in", w_out="dw_out")
 
 
-def _fd_check(cfg, lam, dy_scale=1.0, eps=1e-6, tol=1e-6):
+def _fd_check(cfg, lam, dy_scale=1.0, eps=1e-6, tol=1e-6, seq_w=0.0):
     B, O = _mods()
     inp, out, P, dy = _setup(cfg)
     dy = dy * dy_scale
     idx, kept = out["topk_idx"], out["kept"]
-    G = B.backward(cfg, P, idx, kept, dy, lam)
+    G = B.backward(cfg, P, idx, kept, dy, lam, seq_w)
     rng = np.random.default_rng([7, cfg.tag])
     for name in _names(cfg, P):
         v = rng.standard_normal(P[name].shape)
         Pp = dict(P); Pp[name] = P[name] + eps * v
         Pm = dict(P); Pm[name] = P[name] - eps * v
-        _, Lp = B.forward_fixed(cfg, Pp, idx, kept, lam, dy)
-        _, Lm = B.forward_fixed(cfg, Pm, idx, kept, lam, dy)
+        _, Lp = B.forward_fixed(cfg, Pp, idx, kept, lam, dy, seq_w)
+        _, Lm = B.forward_fixed(cfg, Pm, idx, kept, lam, dy, seq_w)
         fd = (Lp - Lm) / (2 * eps)
         an = float(np.sum(G[_GRAD[name]] * v))
         assert abs(fd - an) <= tol * max(1.0, abs(an)), f"{cfg.name} lam={lam} d{name}: fd {fd} vs {an}"
@@ -108,6 +108,28 @@ def check_fd_all():
         _fd_check(cfg, 0.0)
         if cfg.n_heads == 1:
             _fd_check(cfg, 0.37)
+
+
+def check_fd_seq_term():
+    """The sequence-wise balance term, with and without the aux term, and alone (dy = 0)."""
+    base = tiny_cfgs()[1]
+    for cfg in (base.with_(name="bwd_seq3", T=12, seq_len=4), base.with_(name="bwd_seq_whole", seq_len=12),
+                tiny_cfgs()[3].with_(name="bwd_seq_groups", seq_len=6)):
+        _fd_check(cfg, 0.0, seq_w=0.8)
+        _fd_check(cfg, 0.3, seq_w=0.8)
+        _fd_check(cfg, 0.0, dy_scale=0.0, seq_w=1.0)
+
+
+def check_seq_term_whole_batch_equals_aux():
+    """One sequence over the whole batch: the term equals l_aux, so its gradient equals the aux gradient."""
+    B, O = _mods()
+    cfg = tiny_cfgs()[2].with_(name="bwd_seq_eq_aux", seq_len=12)
+    inp, out, P, dy = _setup(cfg)
+    idx, kept = out["topk_idx"], out["kept"]
+    ga = B.backward(cfg, P, idx, kept, dy, 0.7, 0.0)
+    gs = B.backward(cfg, P, idx, kept, dy, 0.0, 0.7)
+    for k in ("dx", "dw_router", "dbias", "dl"):
+        assert np.allclose(ga[k], gs[k], rtol=1e-12, atol=1e-15), k
 
 
 def check_fd_aux_only():
@@ -168,5 +190,5 @@ def check_restricted_forms():
             assert np.allclose(h2, G["dw2"][e][:, hid], rtol=1e-10, atol=1e-12), (cfg.name, e)
 
 
-ALL = [check_fd_all, check_fd_aux_only, check_forward_fixed_matches_oracle, check_special_cases,
+ALL = [check_fd_all, check_fd_seq_term, check_seq_term_whole_batch_equals_aux, check_fd_aux_only, check_forward_fixed_matches_oracle, check_special_cases,
        check_restricted_forms]

@@ -180,10 +180,8 @@ def test_backward_rejects_bad_arguments_before_launching():
     fake = ctypes.c_void_p(0x1000)
     w, wt, io, g = moe.MoeWeights(), moe.MoeWeightsT(), moe.MoeLayerIO(), moe.MoeGrads()
     # missing weights / io / grads
-    assert lib.moe_layer_bwd(ctypes.byref(c), ctypes.byref(w), ctypes.byref(wt), fake, fake, 0.0, ctypes.byref(io),
-                             ctypes.byref(g), fake, 1 << 40, None) == moe.MOE_ERR_ARG
-    assert lib.moe_layer_bwd(ctypes.byref(c), None, ctypes.byref(wt), fake, fake, 0.0, ctypes.byref(io),
-                             ctypes.byref(g), fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    assert lib.moe_layer_bwd(ctypes.byref(c), ctypes.byref(w), ctypes.byref(wt), fake, fake, 0.0, 0.0, ctypes.byref(io), ctypes.byref(g), fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    assert lib.moe_layer_bwd(ctypes.byref(c), None, ctypes.byref(wt), fake, fake, 0.0, 0.0, ctypes.byref(io), ctypes.byref(g), fake, 1 << 40, None) == moe.MOE_ERR_ARG
     # latent layer: the projections' weights, transposes, z, o and their gradients are required
     c4 = moe.config_struct(CONFIGS[4])
     wf = moe.MoeWeights(**{n: 0x1000 for n, _ in moe.MoeWeights._fields_ if n not in ("w_in", "router_bias",
@@ -191,12 +189,14 @@ def test_backward_rejects_bad_arguments_before_launching():
     wtf = moe.MoeWeightsT(**{n: 0x1000 for n, _ in moe.MoeWeightsT._fields_})
     iof = moe.MoeLayerIO(**{n: 0x1000 for n, _ in moe.MoeLayerIO._fields_ if n not in ("logits_mode",)})
     gf = moe.MoeGrads(**{n: 0x1000 for n, _ in moe.MoeGrads._fields_})
-    assert lib.moe_layer_bwd(ctypes.byref(c4), ctypes.byref(wf), ctypes.byref(wtf), fake, fake, 0.0,
+    assert lib.moe_layer_bwd(ctypes.byref(c4), ctypes.byref(wf), ctypes.byref(wtf), fake, fake, 0.0, 0.0, ctypes.byref(iof), ctypes.byref(gf), fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    # a sequence-term weight needs seq_len
+    c2 = moe.config_struct(CONFIGS[2])
+    assert lib.moe_layer_bwd(ctypes.byref(c2), ctypes.byref(wf), ctypes.byref(wtf), fake, fake, 0.0, 1.0,
                              ctypes.byref(iof), ctypes.byref(gf), fake, 1 << 40, None) == moe.MOE_ERR_ARG
     # several heads: no aux term
     wf.w_in = 0x1000
-    assert lib.moe_layer_bwd(ctypes.byref(c4), ctypes.byref(wf), ctypes.byref(wtf), fake, fake, 0.5,
-                             ctypes.byref(iof), ctypes.byref(gf), fake, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_layer_bwd(ctypes.byref(c4), ctypes.byref(wf), ctypes.byref(wtf), fake, fake, 0.5, 0.0, ctypes.byref(iof), ctypes.byref(gf), fake, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_transpose_weights(ctypes.byref(c), ctypes.byref(w), ctypes.byref(wt), None) == moe.MOE_ERR_ARG
 
 

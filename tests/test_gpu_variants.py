@@ -243,11 +243,12 @@ def test_variant_backward(cfg):
     dy_h = _dy(cfg)
     G = _grads(cfg)
     lam = 0.5
-    moe.moe_layer_bwd(cfg, W, wt, x, dev(dy_h), lam, io, G, moe.backward_workspace(cfg))
+    sw = 2.0 if cfg.seq_len else 0.0  # the sequence-wise balance term, where the layer reports it
+    moe.moe_layer_bwd(cfg, W, wt, x, dev(dy_h), lam, io, G, moe.backward_workspace(cfg), seq_weight=sw)
     torch.cuda.synchronize()
     kept = io["row_of"].cpu().numpy().reshape(-1) >= 0
     P = OB.params_of(inp)
-    ref = OB.backward(cfg, P, io["topk_idx"].cpu().numpy(), kept, oracle.decode(dy_h), lam)
+    ref = OB.backward(cfg, P, io["topk_idx"].cpu().numpy(), kept, oracle.decode(dy_h), lam, sw)
     names = ["dx", "dw_router", "dbias", "dw1", "dw2"] + (["dw3"] if cfg.act == 1 else [])
     if cfg.n_shared:
         names += ["dws1", "dws2"] + (["dws3"] if cfg.act == 1 else [])
@@ -257,6 +258,28 @@ def test_variant_backward(cfg):
         err = np.max(np.abs(got - want))
         log(f"  {k:10s} rel err {err / scale:.3g}")
         assert err <= tol(cfg) * scale, k
+
+
+def test_sequence_term_router_gradient():
+    """The sequence term alone (dy = 0, no aux): only the router moves, and it matches the oracle."""
+    cfg = SMALL_VARIANTS[1]
+    from tests.test_gpu_backward import _transposed, _grads
+    inp = cached_inputs(cfg)
+    out = oracle_out(cfg)
+    y, io, W, x = _layer(cfg, inp, out["logits"])
+    G = _grads(cfg)
+    dy = torch.zeros_like(x)
+    moe.moe_layer_bwd(cfg, W, _transposed(cfg, W), x, dy, 0.0, io, G, moe.backward_workspace(cfg), seq_weight=1.0)
+    torch.cuda.synchronize()
+    kept = io["row_of"].cpu().numpy().reshape(-1) >= 0
+    ref = OB.backward(cfg, OB.params_of(inp), io["topk_idx"].cpu().numpy(), kept,
+                      np.zeros((cfg.T, cfg.d_model)), 0.0, 1.0)
+    assert float(G["dw1"].float().abs().max()) == 0.0
+    for k in ("dw_router", "dbias", "dx"):
+        got, want = f64(G[k]), ref[k]
+        scale = np.max(np.abs(want))
+        assert scale > 0, k
+        assert np.max(np.abs(got - want)) <= 2e-2 * scale, k
 
 
 # ------------------------------------------------------------------ edge cases

@@ -24,14 +24,19 @@ def m_silu_grad_is_sigmoid(a):
 _orig_backward = B.backward
 
 
-def m_no_renorm_correction(cfg, P_, topk_idx, kept, dy, lam=0.0):
-    return _orig_backward(cfg.with_(renorm=0), P_, topk_idx, kept, dy, lam) if cfg.renorm else \
-        _orig_backward(cfg, P_, topk_idx, kept, dy, lam)
+def m_no_renorm_correction(cfg, P_, topk_idx, kept, dy, lam=0.0, seq_w=0.0):
+    return _orig_backward(cfg.with_(renorm=0), P_, topk_idx, kept, dy, lam, seq_w) if cfg.renorm else \
+        _orig_backward(cfg, P_, topk_idx, kept, dy, lam, seq_w)
 
 
-def m_aux_over_S(cfg, P_, topk_idx, kept, dy, lam=0.0):
+def m_aux_over_S(cfg, P_, topk_idx, kept, dy, lam=0.0, seq_w=0.0):
     # aux gradient scaled by 1/S instead of 1/S^2
-    return _orig_backward(cfg, P_, topk_idx, kept, dy, lam * cfg.T)
+    return _orig_backward(cfg, P_, topk_idx, kept, dy, lam * cfg.T, seq_w)
+
+
+def m_seq_over_L(cfg, P_, topk_idx, kept, dy, lam=0.0, seq_w=0.0):
+    # sequence-term gradient scaled by 1/L instead of 1/L^2
+    return _orig_backward(cfg, P_, topk_idx, kept, dy, lam, seq_w * (cfg.seq_len or 1))
 
 
 def m_mlp_transposed(act, v, w1, w3, w2, dF):
@@ -51,6 +56,7 @@ def m_global_softmax_jacobian(cfg, p, dp):
     ("silu_grad", "_silu_grad", m_silu_grad_is_sigmoid),
     ("renorm", "backward", m_no_renorm_correction),
     ("aux_scale", "backward", m_aux_over_S),
+    ("seq_scale", "backward", m_seq_over_L),
     ("dw2_mixed", "_mlp_backward", m_mlp_transposed),
     ("global_softmax", "_head_softmax_backward", m_global_softmax_jacobian),
 ])
