@@ -480,15 +480,13 @@ int launch_router_bwd(const Shape &s, const float *logits, const int32_t *topk_i
   return launch_status("router weight gradient");
 }
 
-__global__ void set_kwin_kernel(int32_t *kwin, int tpad) {
-  if (threadIdx.x == 0) {
-    kwin[0] = 0;
-    kwin[1] = tpad;
-  }
+__global__ void set_kwin_kernel(int32_t *kwin, int tpad, int nsplit) {
+  const int s = threadIdx.x;
+  if (s <= nsplit) kwin[s] = min(tpad, (int)(((long)s * tpad / nsplit + 63) / 64 * 64));
 }
 
-int launch_set_kwin(int32_t *kwin, int tpad, hipStream_t st) {
-  hipLaunchKernelGGL(set_kwin_kernel, dim3(1), dim3(64), 0, st, kwin, tpad);
+int launch_set_kwin(int32_t *kwin, int tpad, int nsplit, hipStream_t st) {
+  hipLaunchKernelGGL(set_kwin_kernel, dim3(1), dim3(64), 0, st, kwin, tpad, nsplit);
   return launch_status("k window");
 }
 

@@ -29,7 +29,10 @@
 
 namespace moe {
 
-enum { EPI_PLAIN = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_RESID = 3, EPI_SWIGLU_BWD = 4, EPI_RELU_BWD = 5 };
+// EPI_F32OUT: the plain product written in float32 (K-grouped mode only: the
+// partial sums of a K-split product, added afterwards in a fixed order)
+enum { EPI_PLAIN = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_RESID = 3, EPI_SWIGLU_BWD = 4, EPI_RELU_BWD = 5,
+       EPI_F32OUT = 6 };
 // epilogues whose B tile pairs gate rows with up rows (SwiGLU forward, and its backward)
 static_assert(GEMM_EPI_PLAIN == EPI_PLAIN && GEMM_EPI_SWIGLU_BWD == EPI_SWIGLU_BWD &&
                   GEMM_EPI_RELU_BWD == EPI_RELU_BWD, "epilogue ids");
@@ -470,6 +473,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
         }
         Quad<TE>::store(C + (size_t)row * ldc + col, h);
       }
+    } else if (EPI == EPI_F32OUT) {
+      float *Cf = (float *)p.C + (size_t)g * p.cstride + (size_t)r0 * ldc;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int col = tn * BN_ + wn * WN + f * 16 + 4 * cq;
+        if (col >= N) continue;
+        *(float4 *)(Cf + (size_t)row * ldc + col) =
+            make_float4(acc[i][f][0], acc[i][f][1], acc[i][f][2], acc[i][f][3]);
+      }
     } else {
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
@@ -614,6 +626,9 @@ static int run_epi(int epi, const GemmArgs &a, int tile, hipStream_t st) {
     case EPI_PLAIN: return run_gemm_one<TE, EPI_PLAIN>(a, tile, st);
     case EPI_SWIGLU_BWD: return run_gemm_one<TE, EPI_SWIGLU_BWD>(a, tile, st);
     case EPI_RELU_BWD: return run_gemm_one<TE, EPI_RELU_BWD>(a, tile, st);
+    case EPI_F32OUT:
+      if constexpr (sizeof(TE) == 2) return run_gemm_one<TE, EPI_F32OUT>(a, tile, st);
+      else return run_gemm_one<TE, EPI_PLAIN>(a, tile, st);  // float32 output already
     default: return -2;
   }
 }
@@ -680,6 +695,49 @@ int gemm_kgrouped(bool f32, const void *A, long lda, const void *B, long ldb, vo
   const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
   a.fixed_tiles = G * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
   return f32 ? run_gemm_one<float, EPI_PLAIN>(a, tile, st) : run_gemm_one<uint16_t, EPI_PLAIN>(a, tile, st);
+}
+
+// One group's C[M, N] = A[:, 0..Kt) B[:, 0..Kt)^T, K split into `nsplit`
+// windows kwin[0..nsplit] (device, multiples of 64): each window's product
+// goes to part[s] (float32, M x N, row stride N), then C = sum over s in
+// order, rounded once.  Fills the chip when one group has few output tiles.
+template <typename TE>
+__global__ void splitk_reduce_kernel(const float *__restrict__ part, long n, int nsplit, TE *__restrict__ C) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < nsplit; ++s) v += part[(size_t)s * n + i];
+    C[i] = Elem<TE>::from_f32(v);
+  }
+}
+
+int gemm_splitk(bool f32, const void *A, long lda, const void *B, long ldb, void *C, int M, int N, int nsplit,
+                const int32_t *kwin, float *part, hipStream_t st) {
+  if (M <= 0 || N <= 0 || nsplit <= 0) return 0;
+  GemmArgs a{};
+  a.A = A; a.lda = lda; a.B = B; a.ldb = ldb; a.C = part; a.ldc = N; a.cstride = (long)M * N;
+  a.kwin = kwin; a.Mk = M; a.N = N; a.E = nsplit; a.G = nsplit; a.split = 0; a.prefix = nullptr;
+  const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
+  a.fixed_tiles = nsplit * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
+  const int rc = f32 ? run_gemm_one<float, EPI_PLAIN>(a, tile, st) : run_gemm_one<uint16_t, EPI_F32OUT>(a, tile, st);
+  if (rc) return rc;
+  const long n = (long)M * N;
+  const unsigned grid = (unsigned)std::min<long>((n + 255) / 256, 8192);
+  if (f32)
+    hipLaunchKernelGGL((splitk_reduce_kernel<float>), dim3(grid), dim3(256), 0, st, part, n, nsplit, (float *)C);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t>), dim3(grid), dim3(256), 0, st, part, n, nsplit,
+                       (uint16_t *)C);
+  return launch_status("split-k reduce");
+}
+
+// K windows for gemm_splitk: splits that fill the chip with output tiles, each
+// at least 1024 deep
+int splitk_count(bool f32, int M, int N, long K) {
+  const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
+  const long tiles = (long)((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
+  long s = (512 + tiles - 1) / tiles;
+  s = std::min<long>(s, std::max<long>(1, K / 1024));
+  return (int)std::max<long>(1, std::min<long>(s, 8));
 }
 
 size_t ffn_ws_bytes(const Shape &s) {

@@ -57,6 +57,11 @@ int gemm_plain(bool f32, int epi, const void *A, long lda, const void *B, const 
                long ldc, int M, int N, int K, const void *dh, long lddh, void *hout, long ldh, hipStream_t st);
 int gemm_kgrouped(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long ldc, long cstride, int G,
                   int M, int N, const int32_t *kwin, hipStream_t st);
+// one group's C[M, N] = A B^T over K windows kwin[0..nsplit] (multiples of 64),
+// through float32 partials part[nsplit][M][N] added in order
+int gemm_splitk(bool f32, const void *A, long lda, const void *B, long ldb, void *C, int M, int N, int nsplit,
+                const int32_t *kwin, float *part, hipStream_t st);
+int splitk_count(bool f32, int M, int N, long K);
 int launch_transpose(bool f32, const void *src, long ld_src, long bs_src, const int32_t *rmap, long nvalid,
                      long njcols, int ncols, int coff, void *dst, long ld_dst, long bs_dst, int batches,
                      hipStream_t st);
@@ -79,7 +84,8 @@ int launch_router_bwd(const Shape &s, const float *logits, const int32_t *topk_i
 int launch_seq_counts(const Shape &s, const int32_t *topk_idx, int32_t *seq_cnt, hipStream_t st);
 int launch_bwd_dx(const Shape &s, const void *dy, const void *dxs, const void *dXr, const int32_t *row_of,
                   const float *dl, const void *w_router, int residual, void *dx, hipStream_t st);
-int launch_set_kwin(int32_t *kwin, int tpad, hipStream_t st);
+// kwin[s] = s * tpad / nsplit rounded up to 64 (kwin[nsplit] = tpad)
+int launch_set_kwin(int32_t *kwin, int tpad, int nsplit, hipStream_t st);
 
 // ---------------------------------------------------------------- grouped GEMM / expert FFN
 size_t ffn_ws_bytes(const Shape &s);

@@ -162,7 +162,7 @@ bool bwd_supported(const Shape &s) {
 
 struct BwdBufs {
   size_t dg, dl, rpart, seqcnt, dY, dH, dAB, Hr, dXr, poff, pmap_r, pmap_x, Xt, dYt, dABt, Ht, prefix, kwin;
-  size_t dHs, dABs, Hs, dxs, dyt, xt, dABst, Hst, dout, du, ot, dut, total;
+  size_t dHs, dABs, Hs, dxs, dyt, xt, dABst, Hst, dout, du, ot, dut, spart, total;
 };
 
 BwdBufs bwd_layout(const Shape &s) {
@@ -187,7 +187,7 @@ BwdBufs bwd_layout(const Shape &s) {
   b.dABt = o; o += al(m * s.dff * Rp * esz);
   b.Ht = o; o += al((size_t)s.dff * Rp * esz);
   b.prefix = o; o += al((size_t)2 * (s.E + 2) * 4);
-  b.kwin = o; o += al(2 * 4);
+  b.kwin = o; o += al(16 * 4);
   if (fs) {
     b.dHs = o; o += al((size_t)s.T * fs * esz);
     b.dABs = o; o += al((size_t)s.T * m * fs * esz);
@@ -197,6 +197,22 @@ BwdBufs bwd_layout(const Shape &s) {
     b.xt = o; o += al((size_t)s.d * Tp * esz);
     b.dABst = o; o += al(m * fs * Tp * esz);
     b.Hst = o; o += al(fs * Tp * esz);
+  }
+  // float32 partials of the split-K one-group products (shared experts, projections)
+  {
+    size_t mx = 0;
+    auto need = [&](long M, long N) {
+      mx = std::max(mx, (size_t)moe::splitk_count(s.act_f32, (int)M, (int)N, Tp) * M * N * 4);
+    };
+    if (fs) {
+      need(s.d, fs);
+      need(fs, s.d);
+    }
+    if (s.latent) {
+      need(s.d, (long)s.H * s.dh);
+      need((long)s.H * s.dh, s.d);
+    }
+    b.spart = o; o += al(mx);
   }
   if (s.latent) {  // the projections: do, du and the transposes of dy, x, o, du
     const size_t D = (size_t)s.H * s.dh;
@@ -501,6 +517,12 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
   const void *u = s.latent ? io->z : x;
   const int epi_bwd = glu ? moe::GEMM_EPI_SWIGLU_BWD : moe::GEMM_EPI_RELU_BWD;
   const int32_t *offsets = io->offsets, *src_of = io->src_of;
+  // one group's C[M, N] = A B^T over the T (padded) tokens: A [M][Tp], B [N][Tp]
+  auto tokens_product = [&](const void *A, const void *B, void *C, int M, int N) -> int {
+    const int S = moe::splitk_count(f32, M, N, Tp);
+    if (int r = rc_of(moe::launch_set_kwin(kwin, (int)Tp, S, stream))) return r;
+    return rc_of(moe::gemm_splitk(f32, A, Tp, B, Tp, C, M, N, S, kwin, (float *)at(L.spart), stream));
+  };
 
   clear_stale_error();
   // latent layer: the gradient of o is do = dy W_out
@@ -579,14 +601,9 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
       return rc;
     if ((rc = rc_of(moe::launch_transpose(f32, Hs, fs, 0, nullptr, s.T, Tp, (int)fs, 0, Hst, Tp, 0, 1, stream))))
       return rc;
-    if ((rc = rc_of(moe::launch_set_kwin(kwin, (int)Tp, stream)))) return rc;
-    if ((rc = rc_of(moe::gemm_kgrouped(f32, dyt, Tp, Hst, Tp, g->dws2, fs, 0, 1, (int)d, (int)fs, kwin, stream))))
-      return rc;
-    if ((rc = rc_of(moe::gemm_kgrouped(f32, dABst, Tp, xt, Tp, g->dws1, d, 0, 1, (int)fs, (int)d, kwin, stream))))
-      return rc;
-    if (glu && (rc = rc_of(moe::gemm_kgrouped(f32, (char *)dABst + fs * Tp * esz, Tp, xt, Tp, g->dws3, d, 0, 1,
-                                              (int)fs, (int)d, kwin, stream))))
-      return rc;
+    if ((rc = tokens_product(dyt, Hst, g->dws2, (int)d, (int)fs))) return rc;
+    if ((rc = tokens_product(dABst, xt, g->dws1, (int)fs, (int)d))) return rc;
+    if (glu && (rc = tokens_product((char *)dABst + fs * Tp * esz, xt, g->dws3, (int)fs, (int)d))) return rc;
   }
   if (!s.latent) {
     // dx = [dy] + [dxs] + sum_j dX rows + dl W_r (per head)
@@ -605,10 +622,8 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
     return rc;
   if ((rc = rc_of(moe::launch_transpose(f32, du, D, 0, nullptr, s.T, Tp, (int)D, 0, dut, Tp, 0, 1, stream))))
     return rc;
-  if ((rc = rc_of(moe::launch_set_kwin(kwin, (int)Tp, stream)))) return rc;
-  if ((rc = rc_of(moe::gemm_kgrouped(f32, dyt, Tp, ot, Tp, g->dw_out, D, 0, 1, (int)d, (int)D, kwin, stream))))
-    return rc;
-  return rc_of(moe::gemm_kgrouped(f32, dut, Tp, xt, Tp, g->dw_in, d, 0, 1, (int)D, (int)d, kwin, stream));
+  if ((rc = tokens_product(dyt, ot, g->dw_out, (int)d, (int)D))) return rc;
+  return tokens_product(dut, xt, g->dw_in, (int)D, (int)d);
 }
 
 }  // extern "C"
