@@ -730,6 +730,69 @@ int gemm_splitk(bool f32, const void *A, long lda, const void *B, long ldb, void
   return launch_status("split-k reduce");
 }
 
+// K-grouped products with each group's window split in `nsplit`: window s of
+// group e is [w_e + (n_e/64 * s / nsplit) * 64, ...) of w_e = kwin[e],
+// n_e = kwin[e+1] - w_e (both multiples of 64)
+__global__ void split_windows_kernel(const int32_t *__restrict__ kwin, int G, int nsplit, int32_t *__restrict__ kw) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i <= G * nsplit; i += gridDim.x * blockDim.x) {
+    if (i == G * nsplit) {
+      kw[i] = kwin[G];
+      continue;
+    }
+    const int e = i / nsplit, s = i % nsplit;
+    const int lo = kwin[e], chunks = (kwin[e + 1] - lo) / 64;
+    kw[i] = lo + (int)((long)chunks * s / nsplit) * 64;
+  }
+}
+
+// C_e[i] = sum over s of part[(e * nsplit + s) * MN + i], in order, rounded once
+template <typename TE>
+__global__ void group_reduce_kernel(const float *__restrict__ part, long MN, int G, int nsplit, long cstride,
+                                    TE *__restrict__ C) {
+  const long n = (long)G * MN;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    const long e = i / MN, j = i - e * MN;
+    float v = 0.f;
+    for (int s = 0; s < nsplit; ++s) v += part[((size_t)e * nsplit + s) * MN + j];
+    C[(size_t)e * cstride + j] = Elem<TE>::from_f32(v);
+  }
+}
+
+int gemm_kgrouped_split(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long cstride, int G,
+                        int M, int N, const int32_t *kwin, int nsplit, int32_t *kw_scratch, float *part,
+                        hipStream_t st) {
+  if (G <= 0 || M <= 0 || N <= 0) return 0;
+  hipLaunchKernelGGL(split_windows_kernel, dim3((unsigned)std::min(1024, (G * nsplit + 256) / 256)), dim3(256), 0,
+                     st, kwin, G, nsplit, kw_scratch);
+  if (int rc = launch_status("split windows")) return rc;
+  GemmArgs a{};
+  a.A = A; a.lda = lda; a.B = B; a.ldb = ldb; a.C = part; a.ldc = N; a.cstride = (long)M * N;
+  a.kwin = kw_scratch; a.Mk = M; a.N = N; a.E = G * nsplit; a.G = G * nsplit; a.split = 0; a.prefix = nullptr;
+  const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
+  a.fixed_tiles = G * nsplit * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
+  const int rc = f32 ? run_gemm_one<float, EPI_PLAIN>(a, tile, st) : run_gemm_one<uint16_t, EPI_F32OUT>(a, tile, st);
+  if (rc) return rc;
+  const long n = (long)G * M * N;
+  const unsigned grid = (unsigned)std::min<long>((n + 255) / 256, 8192);
+  if (f32)
+    hipLaunchKernelGGL((group_reduce_kernel<float>), dim3(grid), dim3(256), 0, st, part, (long)M * N, G, nsplit,
+                       cstride, (float *)C);
+  else
+    hipLaunchKernelGGL((group_reduce_kernel<uint16_t>), dim3(grid), dim3(256), 0, st, part, (long)M * N, G, nsplit,
+                       cstride, (uint16_t *)C);
+  return launch_status("split-k group reduce");
+}
+
+// Splits for G groups of M x N outputs over K_total (all groups' windows):
+// enough tiles to fill the chip, windows of 512 or more on average
+int kgrouped_split_count(bool f32, int G, int M, int N, long K_total) {
+  const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
+  const long tiles = (long)G * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
+  long s = (1024 + tiles - 1) / tiles;
+  s = std::min<long>(s, std::max<long>(1, K_total / ((long)G * 512)));
+  return (int)std::max<long>(1, std::min<long>(s, 8));
+}
+
 // K windows for gemm_splitk: splits that fill the chip with output tiles, each
 // at least 1024 deep
 int splitk_count(bool f32, int M, int N, long K) {

@@ -62,6 +62,12 @@ int gemm_kgrouped(bool f32, const void *A, long lda, const void *B, long ldb, vo
 int gemm_splitk(bool f32, const void *A, long lda, const void *B, long ldb, void *C, int M, int N, int nsplit,
                 const int32_t *kwin, float *part, hipStream_t st);
 int splitk_count(bool f32, int M, int N, long K);
+// gemm_kgrouped with every group's window split in nsplit (nsplit > 1: float32
+// partials part[G * nsplit][M][N], kw_scratch of G * nsplit + 1 ints)
+int gemm_kgrouped_split(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long cstride, int G,
+                        int M, int N, const int32_t *kwin, int nsplit, int32_t *kw_scratch, float *part,
+                        hipStream_t st);
+int kgrouped_split_count(bool f32, int G, int M, int N, long K_total);
 int launch_transpose(bool f32, const void *src, long ld_src, long bs_src, const int32_t *rmap, long nvalid,
                      long njcols, int ncols, int coff, void *dst, long ld_dst, long bs_dst, int batches,
                      hipStream_t st);

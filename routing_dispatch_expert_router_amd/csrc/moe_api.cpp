@@ -162,7 +162,7 @@ bool bwd_supported(const Shape &s) {
 
 struct BwdBufs {
   size_t dg, dl, rpart, seqcnt, dY, dH, dAB, Hr, dXr, poff, pmap_r, pmap_x, Xt, dYt, dABt, Ht, prefix, kwin;
-  size_t dHs, dABs, Hs, dxs, dyt, xt, dABst, Hst, dout, du, ot, dut, spart, total;
+  size_t dHs, dABs, Hs, dxs, dyt, xt, dABst, Hst, dout, du, ot, dut, spart, epart, kwsplit, total;
 };
 
 BwdBufs bwd_layout(const Shape &s) {
@@ -213,6 +213,12 @@ BwdBufs bwd_layout(const Shape &s) {
       need((long)s.H * s.dh, s.d);
     }
     b.spart = o; o += al(mx);
+    // the per-expert weight gradients, split when experts hold few output tiles
+    const int s2 = moe::kgrouped_split_count(s.act_f32, s.E, s.dh, s.dff, (long)R);
+    const int s1 = moe::kgrouped_split_count(s.act_f32, s.E, s.dff, s.dh, (long)R);
+    const size_t me = std::max((s2 > 1 ? (size_t)s2 : 0), (s1 > 1 ? (size_t)s1 : 0));
+    b.epart = o; o += al(me * s.E * s.dh * s.dff * 4);
+    b.kwsplit = o; o += al(((size_t)s.E * 8 + 1) * 4);
   }
   if (s.latent) {  // the projections: do, du and the transposes of dy, x, o, du
     const size_t D = (size_t)s.H * s.dh;
@@ -559,16 +565,18 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
                                         stream))))
     return rc;
   if ((rc = rc_of(moe::launch_transpose(f32, Hr, dff, 0, pmap_r, 0, Rp, (int)dff, 0, Ht, Rp, 0, 1, stream)))) return rc;
-  // dW2_e = dY_e^T H_e, dW1_e = dA_e^T X_e, dW3_e = dB_e^T X_e
-  if ((rc = rc_of(moe::gemm_kgrouped(f32, dYt, Rp, Ht, Rp, g->dw2, dff, dh * dff, s.E, (int)dh, (int)dff, poff,
-                                     stream))))
-    return rc;
-  if ((rc = rc_of(moe::gemm_kgrouped(f32, dABt, Rp, Xt, Rp, g->dw1, dh, dff * dh, s.E, (int)dff, (int)dh, poff,
-                                     stream))))
-    return rc;
-  if (glu && (rc = rc_of(moe::gemm_kgrouped(f32, (char *)dABt + dff * Rp * esz, Rp, Xt, Rp, g->dw3, dh, dff * dh,
-                                            s.E, (int)dff, (int)dh, poff, stream))))
-    return rc;
+  // dW2_e = dY_e^T H_e, dW1_e = dA_e^T X_e, dW3_e = dB_e^T X_e (windows split when
+  // the experts' output tiles alone would not fill the chip)
+  auto expert_wgrad = [&](const void *A, const void *B, void *C, long ldc, int M, int N) -> int {
+    const int S = moe::kgrouped_split_count(f32, s.E, M, N, s.R_max);
+    if (S <= 1)
+      return rc_of(moe::gemm_kgrouped(f32, A, Rp, B, Rp, C, ldc, (long)M * N, s.E, M, N, poff, stream));
+    return rc_of(moe::gemm_kgrouped_split(f32, A, Rp, B, Rp, C, (long)M * N, s.E, M, N, poff, S,
+                                          (int32_t *)at(L.kwsplit), (float *)at(L.epart), stream));
+  };
+  if ((rc = expert_wgrad(dYt, Ht, g->dw2, dff, (int)dh, (int)dff))) return rc;
+  if ((rc = expert_wgrad(dABt, Xt, g->dw1, dh, (int)dff, (int)dh))) return rc;
+  if (glu && (rc = expert_wgrad((char *)dABt + dff * Rp * esz, Xt, g->dw3, dh, (int)dff, (int)dh))) return rc;
   // router: dl, dW_r, dbias
   int32_t *seqcnt = seq_weight != 0.0f ? (int32_t *)at(L.seqcnt) : nullptr;
   if (seqcnt && (rc = rc_of(moe::launch_seq_counts(s, io->topk_idx, seqcnt, stream)))) return rc;

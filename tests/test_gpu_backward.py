@@ -29,6 +29,9 @@ EDGE = [
     # two heads without projections (d_model = 2 * d_head), renormalised top-2 per head, ragged T
     MoEConfig("bwd_edge_two_heads", T=45, d_model=256, n_heads=2, d_head=128, n_experts=10, top_k=2, d_ff=128,
               renorm=1, drop=1, capacity=12, tag=72),
+    # few output tiles per weight gradient and many tokens: the K-split paths (per expert and shared)
+    MoEConfig("bwd_edge_splitk", T=2048, d_model=256, n_heads=1, d_head=256, n_experts=4, top_k=2, d_ff=128,
+              n_shared=1, renorm=1, tag=74),
     # latent heads with a d_head that is not a multiple of 256, float32
     MoEConfig("bwd_edge_latent_f32", T=29, d_model=128, n_heads=3, d_head=64, n_experts=12, top_k=1, d_ff=64,
               latent_proj=1, act=0, act_dtype=0, router_dtype=0, tag=73),
