@@ -155,12 +155,21 @@ def cpu_threads():
     return int(n)
 
 
-def cpu_baseline(cfg, inp, sample):
+def cpu_baseline(cfg, inp, sample, target_s=12.0):
+    """The oracle on a token sample sized for about `target_s` seconds: a first run on
+    `sample` tokens sets the rate, the reported run uses as many tokens (at most T)."""
     import oracle
-    toks = np.linspace(0, cfg.T - 1, sample).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.forward(cfg, inp, tokens=toks)
-    dt = time.perf_counter() - t0
+
+    def run(n):
+        toks = np.linspace(0, cfg.T - 1, n).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.forward(cfg, inp, tokens=toks)
+        return time.perf_counter() - t0
+
+    dt = run(sample)
+    if dt < target_s / 2 and sample < cfg.T:
+        sample = int(min(cfg.T, max(sample + 1, sample * target_s / max(dt, 1e-3))))
+        dt = run(sample)
     return {"value": sample / dt, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
             "sample": f"float64 numpy oracle: routing + keep rule of all {cfg.T} tokens, expert FFN and "
                       f"combine for {sample} evenly spaced tokens; {dt:.1f} s wall"}
