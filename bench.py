@@ -1,4 +1,5 @@
-"""Benchmark: MoE layer forward tokens/s on one MI355X, with roofline fractions.
+"""Benchmark: MoE layer forward tokens/s on one MI355X, with roofline fractions (and the
+backward and a graph replay of the same step reported beside it).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1|c2|c3|c4|c0|c2ec|c2v3] [--no-cpu]
 

@@ -1,6 +1,8 @@
 /*
- * moe.h -- C ABI of libmoe.so: the forward pass of one mixture-of-experts
- * layer on one AMD Instinct MI355X (gfx950).
+ * moe.h -- C ABI of libmoe.so: the forward and backward passes of one
+ * mixture-of-experts layer on one AMD Instinct MI355X (gfx950), with the
+ * routing variants (expert choice, a selection-only balancing bias and its
+ * update, a per-sequence balance statistic).
  *
  * The layer (sources by page title and section):
  *   gating      p_e(x) = softmax(g(x))_e, g(x) = W_r x (+ b)

@@ -1,4 +1,4 @@
-"""Python binding of libmoe.so: the MoE layer forward on MI355X (gfx950).
+"""Python binding of libmoe.so: the MoE layer (forward, backward, routing variants) on MI355X (gfx950).
 
 Argument marshalling only.  Every step of the layer runs in the library's HIP
 kernels; this module passes torch tensors' device pointers and the current
