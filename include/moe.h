@@ -240,7 +240,7 @@ int moe_sel_bias_update(const moe_config *cfg, const int32_t *load, float *sel_b
  *             K = E and a = t*E + e
  *
  *   topk_idx  [T, K] in, values in [0, E) (out-of-range values: undefined behaviour)
- *   topk_w    [T, K] in; read only for AFFINITY (may be NULL otherwise)
+ *   topk_w    [T, K] in; read for AFFINITY and expert choice (may be NULL otherwise)
  *   x         [T, H*d_head] act: expert inputs (x, or z when latent_proj)
  *   demand    [E] out, counts [E] out, offsets [E+1] out (offsets[E] = R)
  *   row_of    [T, K] out: row of a in x_perm, or -1 if dropped
@@ -305,7 +305,7 @@ int moe_expert_ffn_gather(const moe_config *cfg, const void *x, const int32_t *s
  *             + sum_{j in head h, row_of[t,j] >= 0} topk_w[t,j] * y_perm[row_of[t,j], c - h*d_head]
  * accumulated in float32 in that order (residual, shared, then j ascending)
  * and rounded once.  A dropped assignment adds nothing.
- *   y_perm [R_max, d_head], row_of [T, K], topk_w [T, K]
+ *   y_perm [R_max, d_head] (NULL allowed when R_max is 0), row_of [T, K], topk_w [T, K]
  *   residual [T, H*d_head] act or NULL, shared_out [T, H*d_head] act or NULL
  *   y [T, H*d_head] act out (the layer output when H == 1; o when latent_proj)
  */

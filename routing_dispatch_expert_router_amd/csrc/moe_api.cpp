@@ -30,18 +30,18 @@ int make_shape(const moe_config *c, Shape *s) {
   if (!c->latent_proj && (long)c->n_heads * c->d_head != c->d_model) return MOE_ERR_ARG;
   if (c->n_experts < 1 || c->n_experts % c->n_heads) return MOE_ERR_ARG;
   const int Eh = c->n_experts / c->n_heads;
-  if (c->top_k < 1 || c->top_k > Eh) return MOE_ERR_ARG;
+  const bool ec = c->route_mode == MOE_ROUTE_EXPERT_CHOICE;  // top_k unused: every expert is a slot
+  if (!ec && (c->top_k < 1 || c->top_k > Eh)) return MOE_ERR_ARG;
   if (c->n_groups < 0) return MOE_ERR_ARG;
   if (c->n_groups > 0) {
     if (Eh % c->n_groups || c->topk_groups < 1 || c->topk_groups > c->n_groups) return MOE_ERR_ARG;
-    if ((long)c->top_k > (long)c->topk_groups * (Eh / c->n_groups)) return MOE_ERR_ARG;
+    if (!ec && (long)c->top_k > (long)c->topk_groups * (Eh / c->n_groups)) return MOE_ERR_ARG;
   }
   if ((c->renorm != 0 && c->renorm != 1) || c->drop < 0 || c->drop > 2) return MOE_ERR_ARG;
   if ((c->route_mode != MOE_ROUTE_TOKEN_CHOICE && c->route_mode != MOE_ROUTE_EXPERT_CHOICE) ||
       (c->sel_bias_gate != 0 && c->sel_bias_gate != 1) || c->seq_len < 0)
     return MOE_ERR_ARG;
   if (c->seq_len > 0 && c->T % c->seq_len) return MOE_ERR_ARG;
-  const bool ec = c->route_mode == MOE_ROUTE_EXPERT_CHOICE;
   if (ec && (c->drop != MOE_DROP_CAPACITY || c->renorm)) return MOE_ERR_ARG;
   if (c->drop == MOE_DROP_CAPACITY && c->capacity < 0) return MOE_ERR_ARG;
   if (c->drop == MOE_DROP_AFFINITY && (c->keep_num <= 0 || c->keep_den <= 0 || c->keep_num > c->keep_den))
@@ -53,7 +53,7 @@ int make_shape(const moe_config *c, Shape *s) {
       (c->router_dtype != MOE_F32 && c->router_dtype != MOE_BF16))
     return MOE_ERR_ARG;
   // supported subset
-  if (c->top_k > 8 || Eh > 256 || c->n_experts > 1024 || c->n_groups > 32) return MOE_ERR_UNSUPPORTED;
+  if ((!ec && c->top_k > 8) || Eh > 256 || c->n_experts > 1024 || c->n_groups > 32) return MOE_ERR_UNSUPPORTED;
   if (c->act_dtype == MOE_F32 && c->router_dtype == MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 0 && (c->n_heads != 1 || c->latent_proj)) return MOE_ERR_UNSUPPORTED;
   if (ec && (c->n_heads != 1 || c->n_groups || c->latent_proj)) return MOE_ERR_UNSUPPORTED;
@@ -303,7 +303,7 @@ int moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, const float *to
   if (rc) return rc;
   if (!topk_idx || !demand || !counts || !offsets || !row_of || (!src_of && s.R_max) || (x_perm && !x))
     return MOE_ERR_ARG;
-  if (s.drop == MOE_DROP_AFFINITY && !topk_w) return MOE_ERR_ARG;
+  if (s.drop >= moe::DROP_AFFINITY && !topk_w) return MOE_ERR_ARG;  // affinity keep and expert choice read gates
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   if (s.T == 0) return MOE_OK;
   clear_stale_error();
@@ -356,7 +356,7 @@ int moe_combine(const moe_config *cfg, const void *y_perm, const int32_t *row_of
   Shape s;
   int rc = make_shape(cfg, &s);
   if (rc) return rc;
-  if (!y_perm || !row_of || !topk_w || !y) return MOE_ERR_ARG;
+  if ((!y_perm && s.R_max) || !row_of || !topk_w || !y) return MOE_ERR_ARG;
   if (s.T == 0) return MOE_OK;
   clear_stale_error();
   return rc_of(moe::launch_combine(s, y_perm, row_of, topk_w, residual, shared_out, y, stream));

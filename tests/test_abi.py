@@ -230,3 +230,15 @@ def test_routing_variant_checks():
     assert lib.moe_sel_bias_update(ctypes.byref(c), None, fake, 0.001, None) == moe.MOE_ERR_ARG
     assert lib.moe_sel_bias_update(ctypes.byref(c), fake, None, 0.001, None) == moe.MOE_ERR_ARG
     assert lib.moe_sel_bias_update(None, fake, fake, 0.001, None) == moe.MOE_ERR_ARG
+    # expert choice: top_k is not used (any value passes); the dispatch reads the gates
+    assert moe.moe_check_config(ec.with_(top_k=0)) == moe.MOE_OK
+    assert moe.moe_check_config(ec.with_(top_k=50)) == moe.MOE_OK
+    assert moe.moe_rows_upper_bound(ec.with_(top_k=0)) == moe.moe_rows_upper_bound(ec)
+    assert moe.moe_workspace_bytes(ec.with_(top_k=0)) == moe.moe_workspace_bytes(ec)
+    assert lib.moe_dispatch(ctypes.byref(ce), fake, None, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 40,
+                            None) == moe.MOE_ERR_ARG
+    # combine: y_perm may be NULL only when no row can be kept (capacity 0)
+    c0 = moe.config_struct(base.with_(capacity=0))
+    assert moe.moe_rows_upper_bound(base.with_(capacity=0)) == 0
+    assert lib.moe_combine(ctypes.byref(c), None, fake, fake, None, None, fake, None) == moe.MOE_ERR_ARG
+    assert lib.moe_combine(ctypes.byref(c0), None, None, fake, None, None, fake, None) == moe.MOE_ERR_ARG

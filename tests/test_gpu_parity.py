@@ -251,6 +251,23 @@ def test_combine(cfg):
     assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-6 * np.max(np.abs(ref)))
 
 
+
+def test_combine_capacity0_without_yperm():
+    """Capacity 0 keeps no row: y_perm may be NULL and y = residual + shared output, exactly."""
+    cfg = SMALL[2].with_(name="cap0_null_yperm", capacity=0)
+    assert moe.moe_rows_upper_bound(cfg) == 0
+    log(f"combine {cfg.name} with y_perm NULL")
+    inp = cached_inputs(SMALL[2])
+    rng = np.random.default_rng(12)
+    row_of = np.full((cfg.T, cfg.k_total), -1, np.int32)
+    w = rng.random((cfg.T, cfg.k_total)).astype(np.float32)
+    shb = act_round(cfg, rng.standard_normal((cfg.T, cfg.d_model)))
+    y = empty_act(cfg, cfg.T, cfg.d_model)
+    moe.moe_combine(cfg, None, dev(row_of), dev(w), dev(inp.x), dev(shb), y)
+    torch.cuda.synchronize()
+    ref = oracle.decode(inp.x).astype(np.float32) + oracle.decode(shb).astype(np.float32)  # one float32 add
+    assert np.array_equal(f64(y), oracle.decode(act_round(cfg, ref)))
+
 # ------------------------------------------------------------------ whole layer
 def run_layer(cfg, inp, logits=None, extra_io=True, with_xperm=False):
     """The layer; without x_perm the expert FFN gathers its rows from the expert input."""
