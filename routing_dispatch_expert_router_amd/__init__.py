@@ -123,8 +123,19 @@ def _c(cfg):
     return cfg if isinstance(cfg, MoeConfig) else config_struct(cfg)
 
 
+def _addr(t):
+    """Device address of a tensor (None for None); the library reads a dense row-major device buffer."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"expected a GPU tensor, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"expected a contiguous tensor, got strides {tuple(t.stride())} for shape {tuple(t.shape)}")
+    return t.data_ptr()
+
+
 def _p(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else ctypes.c_void_p(_addr(t))
 
 
 def _stream(stream):
@@ -219,10 +230,10 @@ def moe_layer_fwd(cfg, weights, x, y, io=None, ws=None, stream=None):
     """weights: dict with moe_weights field names -> tensors (or None).
     io: dict with moe_layer_io field names -> tensors, plus optional 'logits_mode'."""
     c = _c(cfg)
-    w = MoeWeights(**{k: (v.data_ptr() if v is not None else None) for k, v in weights.items()})
+    w = MoeWeights(**{k: _addr(v) for k, v in weights.items()})
     iob = None
     if io is not None:
-        kw = {k: (v.data_ptr() if v is not None else None) for k, v in io.items() if k != "logits_mode"}
+        kw = {k: _addr(v) for k, v in io.items() if k != "logits_mode"}
         iob = MoeLayerIO(logits_mode=int(io.get("logits_mode", MOE_LOGITS_COMPUTE)), **kw)
     return _check(_lib.moe_layer_fwd(ctypes.byref(c), ctypes.byref(w), _p(x), _p(y),
                                      ctypes.byref(iob) if iob is not None else None, _p(ws), _nbytes(ws),
@@ -246,14 +257,14 @@ def backward_workspace(cfg, device="cuda"):
 
 
 def _weights(weights):
-    return MoeWeights(**{k: (v.data_ptr() if v is not None else None) for k, v in weights.items()})
+    return MoeWeights(**{k: _addr(v) for k, v in weights.items()})
 
 
 def moe_transpose_weights(cfg, weights, wt, stream=None):
     """weights: moe_weights field names -> tensors; wt: moe_weights_t field names -> tensors."""
     c = _c(cfg)
     w = _weights(weights)
-    t = MoeWeightsT(**{k: (v.data_ptr() if v is not None else None) for k, v in wt.items()})
+    t = MoeWeightsT(**{k: _addr(v) for k, v in wt.items()})
     return _check(_lib.moe_transpose_weights(ctypes.byref(c), ctypes.byref(w), ctypes.byref(t), _stream(stream)),
                   "moe_transpose_weights")
 
@@ -262,10 +273,10 @@ def moe_layer_bwd(cfg, weights, wt, x, dy, aux_weight, io, grads, ws, stream=Non
     """io: the forward's moe_layer_io tensors (dict); grads: moe_grads field names -> tensors."""
     c = _c(cfg)
     w = _weights(weights)
-    t = MoeWeightsT(**{k: (v.data_ptr() if v is not None else None) for k, v in wt.items()})
-    kw = {k: (v.data_ptr() if v is not None else None) for k, v in io.items() if k != "logits_mode"}
+    t = MoeWeightsT(**{k: _addr(v) for k, v in wt.items()})
+    kw = {k: _addr(v) for k, v in io.items() if k != "logits_mode"}
     iob = MoeLayerIO(logits_mode=int(io.get("logits_mode", MOE_LOGITS_COMPUTE)), **kw)
-    g = MoeGrads(**{k: (v.data_ptr() if v is not None else None) for k, v in grads.items()})
+    g = MoeGrads(**{k: _addr(v) for k, v in grads.items()})
     return _check(_lib.moe_layer_bwd(ctypes.byref(c), ctypes.byref(w), ctypes.byref(t), _p(x), _p(dy),
                                      float(aux_weight), float(seq_weight), ctypes.byref(iob), ctypes.byref(g),
                                      _p(ws), _nbytes(ws),

@@ -242,3 +242,13 @@ def test_routing_variant_checks():
     assert moe.moe_rows_upper_bound(base.with_(capacity=0)) == 0
     assert lib.moe_combine(ctypes.byref(c), None, fake, fake, None, None, fake, None) == moe.MOE_ERR_ARG
     assert lib.moe_combine(ctypes.byref(c0), None, None, fake, None, None, fake, None) == moe.MOE_ERR_ARG
+
+
+def test_binding_rejects_host_and_strided_tensors():
+    """The binding hands over raw device addresses: a host tensor or a strided view is refused before any call."""
+    import torch
+    with pytest.raises(ValueError):
+        moe._p(torch.zeros(4))
+    with pytest.raises(ValueError):
+        moe._addr(torch.zeros(4))
+    assert moe._p(None) is None and moe._addr(None) is None
