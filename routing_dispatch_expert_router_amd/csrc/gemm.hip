@@ -145,8 +145,9 @@ __global__ __launch_bounds__(1024) void gemm_prep_kernel(PrepArgs a) {
 // inside the row and 8-byte (bf16) / 16-byte (fp32) aligned).
 template <typename TE> struct Quad;
 template <> struct Quad<uint16_t> {
-  __device__ __forceinline__ static void load(const uint16_t *p, float o[4]) {
-    const uint2 u = *(const uint2 *)p;
+  using Raw = uint2;
+  __device__ __forceinline__ static Raw raw(const uint16_t *p) { return *(const uint2 *)p; }
+  __device__ __forceinline__ static void decode(const Raw u, float o[4]) {
     o[0] = bf16_to_f32((uint16_t)(u.x & 0xFFFFu)); o[1] = bf16_to_f32((uint16_t)(u.x >> 16));
     o[2] = bf16_to_f32((uint16_t)(u.y & 0xFFFFu)); o[3] = bf16_to_f32((uint16_t)(u.y >> 16));
   }
@@ -158,8 +159,9 @@ template <> struct Quad<uint16_t> {
   }
 };
 template <> struct Quad<float> {
-  __device__ __forceinline__ static void load(const float *p, float o[4]) {
-    const float4 u = *(const float4 *)p;
+  using Raw = float4;
+  __device__ __forceinline__ static Raw raw(const float *p) { return *(const float4 *)p; }
+  __device__ __forceinline__ static void decode(const Raw u, float o[4]) {
     o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w;
   }
   __device__ __forceinline__ static void store(float *p, const float o[4]) {
@@ -418,6 +420,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   const TE *R = (EPI == EPI_RESID) ? (const TE *)p.res + (size_t)r0 * p.ldres : nullptr;
   const TE *DHp = (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) ? (const TE *)p.dh + (size_t)r0 * p.lddh : nullptr;
   TE *HO = (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) ? (TE *)p.hout + (size_t)r0 * p.ldh : nullptr;
+  // The epilogues that read a second operand (the residual; the backward's
+  // upstream dH) issue all of the wave's loads before its first store: C may
+  // alias that operand as far as the compiler knows, so a load placed after a
+  // store would wait for it, and the load latencies would add up tile by tile.
+  constexpr bool kRd = EPI == EPI_RESID || EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD;
+  constexpr int NQ = kPair<EPI> ? NF / 2 : NF;  // quads per fragment row that the epilogue reads
+  auto qcol = [&](int f) {
+    return kPair<EPI> ? tn * HB + wn * (HB / WGN) + f * 16 + 4 * cq : tn * BN_ + wn * WN + f * 16 + 4 * cq;
+  };
+  typename Quad<TE>::Raw pre[kRd ? MF : 1][kRd ? NQ : 1];
+  if constexpr (kRd) {
+    const TE *src = (EPI == EPI_RESID) ? R : DHp;
+    const long lds = (EPI == EPI_RESID) ? p.ldres : p.lddh;
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int row = m0 + wm * WM + i * 16 + l16;
+#pragma unroll
+      for (int f = 0; f < NQ; ++f) {
+        const int col = qcol(f);
+        pre[i][f] = (row < M && col < N) ? Quad<TE>::raw(src + (size_t)row * lds + col) : typename Quad<TE>::Raw{};
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
     const int row = m0 + wm * WM + i * 16 + l16;
@@ -427,10 +452,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
       // dB = dH * SiLU(g) (C[row][col] and C[row][N + col]), H = SiLU(g) * u
 #pragma unroll
       for (int f = 0; f < NF / 2; ++f) {
-        const int col = tn * HB + wn * (HB / WGN) + f * 16 + 4 * cq;
+        const int col = qcol(f);
         if (col >= N) continue;
         float dh[4], da[4], db[4], h[4];
-        Quad<TE>::load(DHp + (size_t)row * p.lddh + col, dh);
+        Quad<TE>::decode(pre[i][f], dh);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float gt = acc[i][f][v], up = acc[i][f + NF / 2][v];
@@ -447,10 +472,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
       // recomputed a = W1 v with the upstream dH: dA = dH * [a > 0], H = max(a, 0)
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const int col = tn * BN_ + wn * WN + f * 16 + 4 * cq;
+        const int col = qcol(f);
         if (col >= N) continue;
         float dh[4], da[4], h[4];
-        Quad<TE>::load(DHp + (size_t)row * p.lddh + col, dh);
+        Quad<TE>::decode(pre[i][f], dh);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float a = acc[i][f][v];
@@ -488,7 +513,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
         const int col = tn * BN_ + wn * WN + f * 16 + 4 * cq;
         if (col >= N) continue;
         float o[4], r[4] = {0.f, 0.f, 0.f, 0.f};
-        if (EPI == EPI_RESID) Quad<TE>::load(R + (size_t)row * p.ldres + col, r);
+        if constexpr (EPI == EPI_RESID) Quad<TE>::decode(pre[i][f], r);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           o[v] = acc[i][f][v];
