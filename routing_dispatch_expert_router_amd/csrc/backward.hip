@@ -321,66 +321,113 @@ __global__ __launch_bounds__(256) void router_dbias_kernel(const float *__restri
 //               + sum_{e in head h} dl[t][e] W_r[e][cl],
 // float32 in that order (the router term over experts ascending), rounded
 // once: the layer's dx (one head or no latent projection), or the gradient of
-// the latent u.  A thread owns one column of DX_TOK consecutive tokens; a
-// block's 256 columns lie in one head, so the dl reads have block-uniform
-// addresses (scalar loads).
-constexpr int DX_TOK = 8;
+// the latent u.  A block takes DX_TOK consecutive tokens and 2 * blockDim.x
+// columns of one head; each thread owns two adjacent columns, so a router
+// weight load of two elements feeds 2 * DX_TOK multiply-adds.  The block's dl
+// rows (its head's slice) are staged in LDS once and read as broadcasts.
+// Measured on the group-limited shapes (8192 tokens, 5120 columns, 160
+// experts, top-6): the row gather and the router term each take about half
+// of the kernel's time, the former near the HBM rate of its bytes.
+constexpr int DX_TOK = 16;
+template <typename T> struct Pair2;
+template <> struct Pair2<uint16_t> {  // two adjacent bf16 (4-byte aligned)
+  __device__ __forceinline__ static void load(const uint16_t *p, float &a, float &b) {
+    const uint32_t u = *(const uint32_t *)p;
+    a = bf16_to_f32((uint16_t)(u & 0xFFFFu));
+    b = bf16_to_f32((uint16_t)(u >> 16));
+  }
+  __device__ __forceinline__ static void store(uint16_t *p, float a, float b) {
+    *(uint32_t *)p = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  }
+};
+template <> struct Pair2<float> {  // two adjacent float32 (8-byte aligned)
+  __device__ __forceinline__ static void load(const float *p, float &a, float &b) {
+    const float2 u = *(const float2 *)p;
+    a = u.x;
+    b = u.y;
+  }
+  __device__ __forceinline__ static void store(float *p, float a, float b) { *(float2 *)p = make_float2(a, b); }
+};
+
 template <typename TA, typename TR>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const TA *__restrict__ dy, const TA *__restrict__ dxs,
                                                      const TA *__restrict__ dXr, const int32_t *__restrict__ row_of,
                                                      const float *__restrict__ dl, const TR *__restrict__ w_r, int T,
                                                      int D, int dh, int H, int K, int k, int E, int Eh, int residual,
                                                      TA *__restrict__ dx) {
-  const int cpb = (dh + 255) / 256;  // column blocks per head
-  const int h = blockIdx.y / cpb, cl = (blockIdx.y % cpb) * 256 + threadIdx.x;
+  __shared__ float4 sdl4[DX_TOK * 64];  // [DX_TOK][EP] with EP = E_h rounded up to 4 (E_h <= 256)
+  float *sdl = (float *)sdl4;
+  const int EP = (Eh + 3) & ~3;
+  const int ncol = 2 * blockDim.x, cpb = (dh + ncol - 1) / ncol;
+  const int h = blockIdx.y / cpb, cl = (blockIdx.y % cpb) * ncol + 2 * threadIdx.x;
   const int t0 = blockIdx.x * DX_TOK;
-  if (cl >= dh) return;
-  const int c = h * dh + cl;
   const int nt = min(DX_TOK, T - t0);
-  float acc[DX_TOK];
+  for (int i = threadIdx.x; i < DX_TOK * EP; i += blockDim.x) {
+    const int tt = i / EP, e = i - tt * EP;
+    sdl[i] = (tt < nt && e < Eh) ? dl[(size_t)(t0 + tt) * E + (size_t)h * Eh + e] : 0.f;
+  }
+  __syncthreads();
+  if (cl >= dh) return;  // dh is even, so cl + 1 < dh too
+  const int c = h * dh + cl;
+  float a0[DX_TOK], a1[DX_TOK];
 #pragma unroll
   for (int i = 0; i < DX_TOK; ++i) {
-    float v = 0.f;
+    float v0 = 0.f, v1 = 0.f;
     if (i < nt) {
       const int t = t0 + i;
       const size_t o = (size_t)t * D + c;
-      if (residual) v = Elem<TA>::to_f32(dy[o]);
-      if (dxs) v += Elem<TA>::to_f32(dxs[o]);
+      if (residual) Pair2<TA>::load(dy + o, v0, v1);
+      if (dxs) {
+        float u0, u1;
+        Pair2<TA>::load(dxs + o, u0, u1);
+        v0 += u0;
+        v1 += u1;
+      }
       for (int q = 0; q < k; ++q) {
         const int r = row_of[(size_t)t * K + h * k + q];
-        if (r >= 0) v += Elem<TA>::to_f32(dXr[(size_t)r * dh + cl]);
+        if (r >= 0) {
+          float u0, u1;
+          Pair2<TA>::load(dXr + (size_t)r * dh + cl, u0, u1);
+          v0 += u0;
+          v1 += u1;
+        }
       }
     }
-    acc[i] = v;
+    a0[i] = v0;
+    a1[i] = v1;
   }
-  const float *dlb = dl + (size_t)t0 * E + (size_t)h * Eh;
-  const TR *wr = w_r + (size_t)h * Eh * dh;
-  if (nt == DX_TOK && (E & 3) == 0 && (Eh & 3) == 0) {
-    // dl rows are 16-byte aligned (the buffer is, and E, E_h are multiples of 4)
-    for (int e = 0; e < Eh; e += 4) {
-      float w[4];
+  const TR *wr = w_r + (size_t)h * Eh * dh + cl;
+  int e = 0;
+  for (; e + 4 <= Eh; e += 4) {
+    float w0[4], w1[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = Elem<TR>::to_f32(wr[(size_t)(e + u) * dh + cl]);
+    for (int u = 0; u < 4; ++u) Pair2<TR>::load(wr + (size_t)(e + u) * dh, w0[u], w1[u]);
 #pragma unroll
-      for (int i = 0; i < DX_TOK; ++i) {
-        const float4 l = *(const float4 *)(dlb + (size_t)i * E + e);
-        acc[i] += l.x * w[0];
-        acc[i] += l.y * w[1];
-        acc[i] += l.z * w[2];
-        acc[i] += l.w * w[3];
-      }
+    for (int i = 0; i < DX_TOK; ++i) {
+      const float4 l = sdl4[(i * EP + e) >> 2];
+      a0[i] += l.x * w0[0];
+      a0[i] += l.y * w0[1];
+      a0[i] += l.z * w0[2];
+      a0[i] += l.w * w0[3];
+      a1[i] += l.x * w1[0];
+      a1[i] += l.y * w1[1];
+      a1[i] += l.z * w1[2];
+      a1[i] += l.w * w1[3];
     }
-  } else {
-    for (int e = 0; e < Eh; ++e) {
-      const float w = Elem<TR>::to_f32(wr[(size_t)e * dh + cl]);
+  }
+  for (; e < Eh; ++e) {
+    float w0, w1;
+    Pair2<TR>::load(wr + (size_t)e * dh, w0, w1);
 #pragma unroll
-      for (int i = 0; i < DX_TOK; ++i)
-        if (i < nt) acc[i] += dlb[(size_t)i * E + e] * w;
+    for (int i = 0; i < DX_TOK; ++i) {
+      const float l = sdl[i * EP + e];
+      a0[i] += l * w0;
+      a1[i] += l * w1;
     }
   }
 #pragma unroll
   for (int i = 0; i < DX_TOK; ++i)
-    if (i < nt) dx[(size_t)(t0 + i) * D + c] = Elem<TA>::from_f32(acc[i]);
+    if (i < nt) Pair2<TA>::store(dx + (size_t)(t0 + i) * D + c, a0[i], a1[i]);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -493,18 +540,20 @@ int launch_set_kwin(int32_t *kwin, int tpad, int nsplit, hipStream_t st) {
 int launch_bwd_dx(const Shape &s, const void *dy, const void *dxs, const void *dXr, const int32_t *row_of,
                   const float *dl, const void *w_router, int residual, void *dx, hipStream_t st) {
   if (s.T == 0) return 0;
+  // two columns per thread: 256 threads for heads of 512 columns or more, fewer for narrow heads
+  const int nthr = std::min(256, (s.dh / 2 + 63) / 64 * 64);
+  const dim3 grid((unsigned)((s.T + DX_TOK - 1) / DX_TOK), (unsigned)(s.H * ((s.dh + 2 * nthr - 1) / (2 * nthr))));
   const int D = s.H * s.dh;
-  const dim3 grid((unsigned)((s.T + DX_TOK - 1) / DX_TOK), (unsigned)(s.H * ((s.dh + 255) / 256)));
   if (s.act_f32) {
-    hipLaunchKernelGGL((bwd_dx_kernel<float, float>), dim3(grid), dim3(256), 0, st, (const float *)dy,
-                       (const float *)dxs, (const float *)dXr, row_of, dl, (const float *)w_router, s.T, D, s.dh,
-                       s.H, s.K, s.k, s.E, s.Eh, residual, (float *)dx);
+    hipLaunchKernelGGL((bwd_dx_kernel<float, float>), grid, dim3(nthr), 0, st, (const float *)dy, (const float *)dxs,
+                       (const float *)dXr, row_of, dl, (const float *)w_router, s.T, D, s.dh, s.H, s.K, s.k, s.E,
+                       s.Eh, residual, (float *)dx);
   } else if (s.router_f32) {
-    hipLaunchKernelGGL((bwd_dx_kernel<uint16_t, float>), dim3(grid), dim3(256), 0, st, (const uint16_t *)dy,
+    hipLaunchKernelGGL((bwd_dx_kernel<uint16_t, float>), grid, dim3(nthr), 0, st, (const uint16_t *)dy,
                        (const uint16_t *)dxs, (const uint16_t *)dXr, row_of, dl, (const float *)w_router, s.T, D,
                        s.dh, s.H, s.K, s.k, s.E, s.Eh, residual, (uint16_t *)dx);
   } else {
-    hipLaunchKernelGGL((bwd_dx_kernel<uint16_t, uint16_t>), dim3(grid), dim3(256), 0, st, (const uint16_t *)dy,
+    hipLaunchKernelGGL((bwd_dx_kernel<uint16_t, uint16_t>), grid, dim3(nthr), 0, st, (const uint16_t *)dy,
                        (const uint16_t *)dxs, (const uint16_t *)dXr, row_of, dl, (const uint16_t *)w_router, s.T,
                        D, s.dh, s.H, s.K, s.k, s.E, s.Eh, residual, (uint16_t *)dx);
   }
