@@ -14,6 +14,9 @@ loaded and checks:
   * the per-sequence statistic within 1e-5 relative;
   * every gradient of moe_layer_bwd against the backward oracle for those
     decisions, within the same bars.
+moe_route also runs on each case computing its own scores (the router
+product's shape variants): scores within 1e-5 of max|l|, choices equal up to
+near-ties, gates within 1e-5.
 The draws are fixed (seed per case), so a failure names a reproducible case.
 """
 import numpy as np
@@ -161,3 +164,37 @@ def test_random_layer_forward_backward(cfg):
         assert np.all(np.isfinite(got)), n
         # router gradients are float32 throughout: an absolute floor covers a ~0 reference
         assert e <= tol(cfg) * sc + (1e-6 if n in ("dw_router", "dbias") else 0.0), n
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+def test_random_route_compute(cfg):
+    """moe_route computing its own scores: within 1e-5 * max|l| of the oracle's; choices differ only at near-ties."""
+    log(f"random route COMPUTE {cfg.name}")
+    inp = generate(cfg, threads=1)
+    out = oracle.forward(cfg, inp)
+    xin = bf16_bits_from_f32(out["z"].astype(np.float32)) if (cfg.latent_proj and cfg.act_dtype == 1) else (
+        out["z"].astype(np.float32) if cfg.latent_proj else inp.x)
+    ref = oracle.route(cfg, oracle.decode(xin), inp.w_router, inp.bias, sel_bias=inp.sel_bias)
+    T, K, E = cfg.T, cfg.k_total, cfg.n_experts
+    idx, w, logits = i32(T, K), f32(T, K), f32(T, E)
+    moe.moe_route(cfg, dev(xin), dev(inp.w_router), dev(inp.bias), logits, moe.MOE_LOGITS_COMPUTE_STORE, idx, w,
+                  None, moe.workspace(cfg), sel_bias=dev(inp.sel_bias))
+    torch.cuda.synchronize()
+    l = logits.cpu().numpy().astype(np.float64)
+    lmax = max(np.max(np.abs(ref["logits"])), 1e-30)
+    err = np.max(np.abs(l - ref["logits"]))
+    log(f"  scores rel err {err / lmax:.3g}")
+    assert err <= 1e-5 * lmax
+    got = idx.cpu().numpy()
+    diff = np.nonzero(np.any(got != ref["topk_idx"], axis=1))[0]
+    if len(diff):
+        if inp.sel_bias is not None:
+            margin = routing_margin(cfg, ref["p"] + np.asarray(inp.sel_bias, np.float64)[None, :])
+            assert np.all(margin[diff] < 1e-5)
+        else:
+            margin = routing_margin(cfg, ref["logits"])
+            assert np.all(margin[diff] <= 4 * err + 1e-30)
+        log(f"  near-tie tokens: {len(diff)}")
+    same = np.setdiff1d(np.arange(T), diff)
+    assert np.max(np.abs(w.cpu().numpy().astype(np.float64)[same] - ref["topk_w"][same]), initial=0.0) <= 1e-5
