@@ -15,8 +15,11 @@ namespace moe {
 
 // One thread per 16 bytes of an output row (grid-stride over T x chunks).  KH
 // (>= the choices per head) is a compile-time bound so every expert-row load
-// of the token is issued before the first add.
-template <typename TA, int KH>
+// of the token is issued before the first add.  WU: a head's row holds a multiple of 64
+// chunks, so the 64 lanes of a wave share one token and head (grid strides are
+// multiples of 64) and its row indices and gates are read once per wave, as
+// scalar loads.
+template <typename TA, int KH, bool WU>
 __global__ __launch_bounds__(256) void combine_kernel(
     const TA *__restrict__ y_perm, const int32_t *__restrict__ row_of, const float *__restrict__ topk_w,
     const TA *__restrict__ res, const TA *__restrict__ sh, TA *__restrict__ y, int T, int H, int k, int dh,
@@ -27,10 +30,14 @@ __global__ __launch_bounds__(256) void combine_kernel(
   const int K = H * k;
   const long total = (long)T * cpr;
   for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
-    const long t = i / cpr;
+    long t = i / cpr;
     const int q = (int)(i - t * cpr);
     const int c0 = q * EPC;
-    const int h = c0 / dh;
+    int h = c0 / dh;
+    if constexpr (WU) {
+      t = __builtin_amdgcn_readfirstlane((int)t);
+      h = __builtin_amdgcn_readfirstlane(h);
+    }
     constexpr int KA = KH > 0 ? KH : 1;  // KH == 0: a runtime loop over k (expert choice)
     int row[KA];
     float w[KA];
@@ -46,6 +53,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
           w[j] = topk_w[t * K + h * k + j];
         }
       }
+      // a dropped slot loads nothing (a stand-in address would cost HBM reads
+      // when many slots are dropped)
 #pragma unroll
       for (int j = 0; j < KH; ++j)
         v[j] = row[j] >= 0 ? reinterpret_cast<const u32x4 *>(y_perm + (size_t)row[j] * dh + (c0 - h * dh))[0]
@@ -70,10 +79,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
     if constexpr (KH > 0) {
 #pragma unroll
       for (int j = 0; j < KH; ++j) {
-        if (row[j] < 0) continue;
         const TA *p = reinterpret_cast<const TA *>(&v[j]);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] += w[j] * Elem<TA>::to_f32(p[e]);
+        for (int e = 0; e < EPC; ++e) {
+          const float a = acc[e] + w[j] * Elem<TA>::to_f32(p[e]);
+          acc[e] = row[j] >= 0 ? a : acc[e];  // a dropped slot adds nothing
+        }
       }
     } else {
       // slots scanned four at a time (16-byte loads) when the row allows it
@@ -114,8 +125,13 @@ static void launch_c(const Shape &s, const void *y_perm, const int32_t *row_of, 
   const long total = (long)s.T * (s.H * s.dh * (long)sizeof(TA) / 16);
   long blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((combine_kernel<TA, KH>), dim3(blocks), dim3(256), 0, st, (const TA *)y_perm, row_of, topk_w,
-                     (const TA *)residual, (const TA *)shared_out, (TA *)y, s.T, s.H, s.k, s.dh, s.R_max);
+  const bool wu = (s.dh * (long)sizeof(TA) / 16) % 64 == 0;  // a head's chunks fill whole waves
+  if (wu)
+    hipLaunchKernelGGL((combine_kernel<TA, KH, true>), dim3(blocks), dim3(256), 0, st, (const TA *)y_perm, row_of,
+                       topk_w, (const TA *)residual, (const TA *)shared_out, (TA *)y, s.T, s.H, s.k, s.dh, s.R_max);
+  else
+    hipLaunchKernelGGL((combine_kernel<TA, KH, false>), dim3(blocks), dim3(256), 0, st, (const TA *)y_perm, row_of,
+                       topk_w, (const TA *)residual, (const TA *)shared_out, (TA *)y, s.T, s.H, s.k, s.dh, s.R_max);
 }
 
 template <typename TA>
