@@ -177,25 +177,28 @@ __global__ __launch_bounds__(256) void disp_rank_kernel(
 }
 
 // ---------------------------------------------------------------- affinity keep (per expert block)
+// Exclusive scan of the values of the block's first 256 threads (fixed
+// order); every thread of the block takes part in the barriers.
 __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
-  // 256 threads, fixed order
   const int tid = threadIdx.x;
-  tmp[tid] = v;
+  const bool own = tid < 256;
+  if (own) tmp[tid] = v;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
-    int u = (tid >= o) ? tmp[tid - o] : 0;
+    int u = (own && tid >= o) ? tmp[tid - o] : 0;
     __syncthreads();
-    tmp[tid] += u;
+    if (own) tmp[tid] += u;
     __syncthreads();
   }
-  int incl = tmp[tid];
+  int incl = own ? tmp[tid] : v;
   *total = tmp[255];
   __syncthreads();
   return incl - v;
 }
 
-// Exclusive count of set flags over a 256-thread block (thread order) and the
+// Exclusive count of set flags over an NT-thread block (thread order) and the
 // total: in-wave ballot prefix plus the earlier waves' counts.
+template <int NT>
 __device__ __forceinline__ int block_excl_count(bool f, int *wsum, int *total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint64_t b = __ballot(f);
@@ -204,7 +207,7 @@ __device__ __forceinline__ int block_excl_count(bool f, int *wsum, int *total) {
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NT / 64; ++q) {
     const int v = wsum[q];
     before += q < w ? v : 0;
     tot += v;
@@ -214,14 +217,16 @@ __device__ __forceinline__ int block_excl_count(bool f, int *wsum, int *total) {
   return before + in_wave;
 }
 
-// One block per expert.  The expert's gate keys and assignments (up to `cap`
-// of them, in dynamic LDS) are staged once; a 4-pass radix select (8 bits per
+// One block of NT threads per expert (1024 when experts hold many
+// assignments, as with expert choice, else 256).  The expert's gate keys and
+// assignments (up to `cap` of them, in dynamic LDS) are staged once; a 4-pass radix select (8 bits per
 // pass, digit found by a suffix scan over the 256 bins) gives the keep-th
 // largest key; two ordered scans then pick the kept assignments and their rows.
 // An expert with more than `cap` assignments reads them from global memory.
 constexpr int AFF_LDS_MAX = (160 * 1024 - 4096) / 8;  // keys + indices beside ~2 KiB of static LDS
 
-__global__ __launch_bounds__(256) void disp_affinity_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void disp_affinity_kernel(
     const int32_t *__restrict__ seg, const int32_t *__restrict__ all_off, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, const float *__restrict__ topk_w, int32_t *__restrict__ row_of,
     int32_t *__restrict__ src_of, int cap) {
@@ -238,12 +243,12 @@ __global__ __launch_bounds__(256) void disp_affinity_kernel(
   const int out0 = offsets[e];
   if (n == 0) return;
   if (keep == 0) {  // nothing kept (capacity 0): every assignment of e is dropped
-    for (int i = tid; i < n; i += 256) row_of[seg[beg + i]] = -1;
+    for (int i = tid; i < n; i += NT) row_of[seg[beg + i]] = -1;
     return;
   }
   const bool staged = n <= cap;
   if (staged) {
-    for (int i = tid; i < n; i += 256) {
+    for (int i = tid; i < n; i += NT) {
       const int a = seg[beg + i];
       sa[i] = a;
       skey[i] = __float_as_uint(topk_w[a]);  // gates are >= 0: their bits order like the values
@@ -256,19 +261,19 @@ __global__ __launch_bounds__(256) void disp_affinity_kernel(
   int need = keep;  // how many keys still to take among those matching prefix
   if (keep < n) {
     for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
+      if (tid < 256) hist[tid] = 0;
       __syncthreads();
-      for (int i = tid; i < n; i += 256) {
+      for (int i = tid; i < n; i += NT) {
         const uint32_t key = key_of(i);
         if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
       }
       __syncthreads();
       // thread t looks at digit d = 255 - t; `above` = keys with a larger digit
       const int d = 255 - tid;
-      const int v = hist[d];
+      const int v = tid < 256 ? hist[d] : 0;
       int tot;
       const int above = block_excl_scan(v, tmp, &tot);
-      if (above < need && above + v >= need) {
+      if (tid < 256 && above < need && above + v >= need) {
         s_prefix = prefix | ((uint32_t)d << shift);
         s_need = need - above;
       }
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(256) void disp_affinity_kernel(
   }
   // kept iff key > thr, or key == thr and among the first `need` equal keys (by a)
   int eq_seen = 0, kept_seen = 0;
-  for (int i0 = 0; i0 < n; i0 += 256) {
+  for (int i0 = 0; i0 < n; i0 += NT) {
     const int i = i0 + tid;
     const bool act = i < n;
     const int a = act ? a_of(i) : 0;
@@ -292,11 +297,11 @@ __global__ __launch_bounds__(256) void disp_affinity_kernel(
       kept = act;
     } else {
       const bool eq = act && key == prefix;
-      const int eq_before = block_excl_count(eq, tmp, &tot);
+      const int eq_before = block_excl_count<NT>(eq, tmp, &tot);
       kept = act && (key > prefix || (eq && eq_seen + eq_before < need));
       eq_seen += tot;
     }
-    const int kb = block_excl_count(kept, tmp, &tot);
+    const int kb = block_excl_count<NT>(kept, tmp, &tot);
     if (act) {
       // never past this expert's `keep` rows, even if the selection were off
       kept = kept && (kept_seen + kb < keep);
@@ -389,8 +394,13 @@ int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w
   if (s.drop >= DROP_AFFINITY) {
     // an expert holds at most T assignments (one per token of its head)
     const int cap = (int)std::min<long>(std::max(s.T, 1), AFF_LDS_MAX);
-    hipLaunchKernelGGL(disp_affinity_kernel, dim3(s.E), dim3(256), (size_t)cap * 8, st, seg, all_off, counts,
-                       offsets, topk_w, row_of, src_of, cap);
+    // experts holding thousands of assignments each (expert choice: T) take 1024-thread blocks
+    if (s.drop == DROP_TOPC || n / s.E >= 4096)
+      hipLaunchKernelGGL(disp_affinity_kernel<1024>, dim3(s.E), dim3(1024), (size_t)cap * 8, st, seg, all_off,
+                         counts, offsets, topk_w, row_of, src_of, cap);
+    else
+      hipLaunchKernelGGL(disp_affinity_kernel<256>, dim3(s.E), dim3(256), (size_t)cap * 8, st, seg, all_off,
+                         counts, offsets, topk_w, row_of, src_of, cap);
     if (int rc = launch_status("dispatch affinity")) return rc;
   }
   if (x_perm) {
