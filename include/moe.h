@@ -235,9 +235,10 @@ int moe_sel_bias_update(const moe_config *cfg, const int32_t *load, float *sel_b
  *   CAPACITY  a kept iff fewer than C earlier assignments (smaller a) chose e(a)
  *   AFFINITY  per expert, the ceil(keep_num*n_e/keep_den) assignments with the
  *             largest topk_w are kept (equal gates: smaller a first)
- *   expert choice (cfg->route_mode): per expert, the min(C, n_e) assignments
+ *   expert choice (cfg->route_mode): per expert, the min(C, T) assignments
  *             with the largest topk_w are kept (equal gates: smaller a first);
- *             K = E and a = t*E + e
+ *             K = E and a = t*E + e: slot j of every token is expert j (as
+ *             moe_route writes it), so topk_idx is not read in this mode
  *
  *   topk_idx  [T, K] in, values in [0, E) (out-of-range values: undefined behaviour)
  *   topk_w    [T, K] in; read for AFFINITY and expert choice (may be NULL otherwise)

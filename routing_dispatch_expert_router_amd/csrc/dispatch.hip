@@ -229,7 +229,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void disp_affinity_kernel(
     const int32_t *__restrict__ seg, const int32_t *__restrict__ all_off, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, const float *__restrict__ topk_w, int32_t *__restrict__ row_of,
-    int32_t *__restrict__ src_of, int cap) {
+    int32_t *__restrict__ src_of, int cap, int ecE) {
   extern __shared__ uint32_t dyn_lds[];
   uint32_t *skey = dyn_lds;
   int *sa = (int *)(dyn_lds + cap);
@@ -242,21 +242,24 @@ __global__ __launch_bounds__(NT) void disp_affinity_kernel(
   const int keep = counts[e];
   const int out0 = offsets[e];
   if (n == 0) return;
+  // the expert's i-th assignment in flat order: from the expert-sorted
+  // segments, or (expert choice, ecE = E) token i's slot e, a = i * E + e
+  auto a_src = [&](int i) -> int { return ecE ? i * ecE + e : seg[beg + i]; };
   if (keep == 0) {  // nothing kept (capacity 0): every assignment of e is dropped
-    for (int i = tid; i < n; i += NT) row_of[seg[beg + i]] = -1;
+    for (int i = tid; i < n; i += NT) row_of[a_src(i)] = -1;
     return;
   }
   const bool staged = n <= cap;
   if (staged) {
     for (int i = tid; i < n; i += NT) {
-      const int a = seg[beg + i];
+      const int a = a_src(i);
       sa[i] = a;
       skey[i] = __float_as_uint(topk_w[a]);  // gates are >= 0: their bits order like the values
     }
     __syncthreads();
   }
-  auto key_of = [&](int i) -> uint32_t { return staged ? skey[i] : __float_as_uint(topk_w[seg[beg + i]]); };
-  auto a_of = [&](int i) -> int { return staged ? sa[i] : seg[beg + i]; };
+  auto key_of = [&](int i) -> uint32_t { return staged ? skey[i] : __float_as_uint(topk_w[a_src(i)]); };
+  auto a_of = [&](int i) -> int { return staged ? sa[i] : a_src(i); };
   uint32_t prefix = 0, pmask = 0;
   int need = keep;  // how many keys still to take among those matching prefix
   if (keep < n) {
@@ -310,6 +313,24 @@ __global__ __launch_bounds__(NT) void disp_affinity_kernel(
       if (kept) src_of[row] = a;
     }
     kept_seen += tot;
+  }
+}
+
+// Expert choice: every token offers one slot to every expert, so expert e's
+// assignments are a = t * E + e for t = 0..T-1, already in flat order:
+// demand T, kept min(C, T), offsets in closed form.  One block.
+__global__ __launch_bounds__(256) void disp_ec_counts_kernel(int E, int T, int C, int32_t *__restrict__ demand,
+                                                             int32_t *__restrict__ counts,
+                                                             int32_t *__restrict__ offsets,
+                                                             int32_t *__restrict__ all_off) {
+  const int kept = min(C, T);
+  for (int e = threadIdx.x; e <= E; e += 256) {
+    if (e < E) {
+      demand[e] = T;
+      counts[e] = kept;
+    }
+    offsets[e] = e * kept;
+    all_off[e] = e * T;
   }
 }
 
@@ -386,21 +407,29 @@ int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w
   p += align_up((size_t)(s.E + 1) * 4, 256);
   int32_t *seg = (s.drop >= DROP_AFFINITY) ? (int32_t *)p : nullptr;
 
-  hipLaunchKernelGGL(disp_hist_kernel, dim3(nc), dim3(256), s.E * 4, st, topk_idx, n, s.E, hist);
-  if (int rc = launch_status("dispatch histogram")) return rc;
-  hipLaunchKernelGGL(disp_rank_kernel, dim3(nc), dim3(256), 9 * s.E * 4, st, topk_idx, n, s.E, (int)nc, hist,
-                     s.drop, s.C, s.keep_num, s.keep_den, demand, counts, offsets, all_off, row_of, src_of, seg);
-  if (int rc = launch_status("dispatch rank")) return rc;
+  if (s.expert_choice) {
+    // the slots are fixed (slot j of every token is expert j): counts in closed form, no ranking
+    hipLaunchKernelGGL(disp_ec_counts_kernel, dim3(1), dim3(256), 0, st, s.E, s.T, s.C, demand, counts, offsets,
+                       all_off);
+    if (int rc = launch_status("dispatch counts")) return rc;
+  } else {
+    hipLaunchKernelGGL(disp_hist_kernel, dim3(nc), dim3(256), s.E * 4, st, topk_idx, n, s.E, hist);
+    if (int rc = launch_status("dispatch histogram")) return rc;
+    hipLaunchKernelGGL(disp_rank_kernel, dim3(nc), dim3(256), 9 * s.E * 4, st, topk_idx, n, s.E, (int)nc, hist,
+                       s.drop, s.C, s.keep_num, s.keep_den, demand, counts, offsets, all_off, row_of, src_of, seg);
+    if (int rc = launch_status("dispatch rank")) return rc;
+  }
   if (s.drop >= DROP_AFFINITY) {
     // an expert holds at most T assignments (one per token of its head)
     const int cap = (int)std::min<long>(std::max(s.T, 1), AFF_LDS_MAX);
     // experts holding thousands of assignments each (expert choice: T) take 1024-thread blocks
+    const int ecE = s.expert_choice ? s.E : 0;
     if (s.drop == DROP_TOPC || n / s.E >= 4096)
       hipLaunchKernelGGL(disp_affinity_kernel<1024>, dim3(s.E), dim3(1024), (size_t)cap * 8, st, seg, all_off,
-                         counts, offsets, topk_w, row_of, src_of, cap);
+                         counts, offsets, topk_w, row_of, src_of, cap, ecE);
     else
       hipLaunchKernelGGL(disp_affinity_kernel<256>, dim3(s.E), dim3(256), (size_t)cap * 8, st, seg, all_off,
-                         counts, offsets, topk_w, row_of, src_of, cap);
+                         counts, offsets, topk_w, row_of, src_of, cap, ecE);
     if (int rc = launch_status("dispatch affinity")) return rc;
   }
   if (x_perm) {
