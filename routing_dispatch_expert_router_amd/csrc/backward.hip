@@ -165,8 +165,9 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TA *__restrict__ s
 // p = the head's softmax of the logits; dp from the gate gradients of the
 // head's k slots (renormalised: (dg_j - sum dg g) / P at the chosen experts)
 // plus lam * demand_e / T^2 (aux loss, one head) plus seq_w * c_{s,e} / L^2 for
-// the token's sequence s (sequence-wise balance term, one head).  One wave per
-// (token, head).
+// the token's sequence s (sequence-wise balance term, one head).  W lanes per
+// (token, head) (W a power of two, at least min(E_h, 64)), 64 / W pairs per wave.
+template <int W>
 __global__ __launch_bounds__(256) void router_bwd_kernel(const float *__restrict__ logits,
                                                          const int32_t *__restrict__ topk_idx,
                                                          const float *__restrict__ gates,
@@ -175,20 +176,20 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float *__restrict
                                                          int Eh, int K, int k, int renorm, float lam,
                                                          const int32_t *__restrict__ seq_cnt, int L, float seq_w,
                                                          float *__restrict__ dl) {
-  const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (pair >= (long)T * H) return;
+  const long pair = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / W) + ((threadIdx.x & 63) / W);
+  const int lane = threadIdx.x & (W - 1);
+  if (pair >= (long)T * H) return;  // whole groups of W lanes: the shuffles below stay inside a group
   const int t = (int)(pair / H), h = (int)(pair % H);
   const float *l = logits + (size_t)t * E + (size_t)h * Eh;
   const int32_t *ti = topk_idx + (size_t)t * K + (size_t)h * k;
   const float *tg = gates + (size_t)t * K + (size_t)h * k;
   const float *tdg = dg + (size_t)t * K + (size_t)h * k;
   float m = -INFINITY;
-  for (int e = lane; e < Eh; e += 64) m = fmaxf(m, l[e]);
-  m = wave_max(m, WAVE);
+  for (int e = lane; e < Eh; e += W) m = fmaxf(m, l[e]);
+  m = wave_max(m, W);
   float z = 0.f;
-  for (int e = lane; e < Eh; e += 64) z += __expf(l[e] - m);
-  z = group_sum_fixed(z, WAVE);
+  for (int e = lane; e < Eh; e += W) z += __expf(l[e] - m);
+  z = group_sum_fixed(z, W);
   // chosen experts: P = sum p, S = sum dg * g
   float P = 0.f, sdg = 0.f;
   for (int j = 0; j < k; ++j) {
@@ -208,9 +209,9 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float *__restrict
   };
   // dp_e for this lane's experts, then sum p * dp
   float spdp = 0.f;
-  for (int e = lane; e < Eh; e += 64) spdp += __expf(l[e] - m) / z * dp_of(e);
-  spdp = group_sum_fixed(spdp, WAVE);
-  for (int e = lane; e < Eh; e += 64) dl[(size_t)t * E + (size_t)h * Eh + e] = __expf(l[e] - m) / z * (dp_of(e) - spdp);
+  for (int e = lane; e < Eh; e += W) spdp += __expf(l[e] - m) / z * dp_of(e);
+  spdp = group_sum_fixed(spdp, W);
+  for (int e = lane; e < Eh; e += W) dl[(size_t)t * E + (size_t)h * Eh + e] = __expf(l[e] - m) / z * (dp_of(e) - spdp);
 }
 
 // ---------------------------------------------------------------- float32 tile
@@ -290,29 +291,275 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float *__restri
   }
 }
 
+// dw = sum of the nsplit partials in ascending order; n is a multiple of 4
+// (d_head is a multiple of 64).  Four columns per thread, eight partials'
+// loads in flight at a time (the adds keep the ascending order).
 __global__ void router_wgrad_sum_kernel(const float *__restrict__ part, long n, int nsplit, float *__restrict__ dw) {
-  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-    float s = 0.f;
-    for (int ts = 0; ts < nsplit; ++ts) s += part[(size_t)ts * n + i];
-    dw[i] = s;
+  const long n4 = n / 4;
+  const float4 *p4 = (const float4 *)part;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x) {
+    float4 s = p4[i];
+    int ts = 1;
+    for (; ts + 8 <= nsplit; ts += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p4[(size_t)(ts + u) * n4 + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+      }
+    }
+    for (; ts < nsplit; ++ts) {
+      const float4 v = p4[(size_t)ts * n4 + i];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    ((float4 *)dw)[i] = s;
   }
 }
 
-// dbias[e] = sum_t dl[t][e]: one block per expert, strided partials then a
-// fixed-order tree
-__global__ __launch_bounds__(256) void router_dbias_kernel(const float *__restrict__ dl, int T, int E,
-                                                           float *__restrict__ dbias) {
-  __shared__ float s[256];
-  const int e = blockIdx.x, tid = threadIdx.x;
-  float v = 0.f;
-  for (int t = tid; t < T; t += 256) v += dl[(size_t)t * E + e];
-  s[tid] = v;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) s[tid] += s[tid + o];
-    __syncthreads();
+// ---------------------------------------------------------------- router weight gradient on MFMA (bf16 layers)
+// The contraction runs over tokens, which neither operand holds contiguously:
+// dl is [T][E] and x is [T][H*dh].  dl is small, so a first pass rewrites it
+// token-contiguous as three bf16 planes (hi = bf16(v), mid = bf16(v - hi),
+// lo = bf16(v - hi - mid); each difference is exact in float32, so the three
+// sum to v within about 2^-24 |v|).  bf16 x bf16 products are exact in float32,
+// so the MFMA product with float32 accumulation keeps the float32 result.  x
+// stays where it is: its rows go to LDS as they are and transposing LDS reads
+// (ds_read_b64_tr_b16) hand each lane the k values it needs.
+//
+// A transposing read gives lane group q (lanes 16q .. 16q+15) the tokens
+// 4q .. 4q+3 and 16+4q .. 16+4q+3 of a 32-token step.  A plain 16-byte read of
+// a token-contiguous row gives lane group q positions 8q .. 8q+7, so the
+// planes store, within every 32-token block, position 8q + j = token 4q + j
+// (j < 4) or 16 + 4q + j - 4 (j >= 4): both operands then agree on the token
+// of every byte a lane feeds to the MFMA.
+__device__ __forceinline__ int rw_token_of_pos(int pos) {  // 0 <= pos < 32
+  const int q = pos >> 3, j = pos & 7;
+  return j < 4 ? 4 * q + j : 12 + 4 * q + j;
+}
+
+// planes[h][p][e][t'] (e < ep, t' < tp; zero past T and past E_h).  Block
+// (64-token chunk, 64 experts, head): dl staged through LDS (coalesced reads),
+// each thread then writes 8 positions (16 bytes) of one expert per plane.
+__global__ __launch_bounds__(256) void router_dl_planes_kernel(const float *__restrict__ dl, int T, int E, int Eh,
+                                                               int ep, int tp, uint16_t *__restrict__ planes) {
+  __shared__ float sv[64][65];
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64, h = blockIdx.z;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i >> 6, c = i & 63, t = t0 + r, e = e0 + c;
+    sv[r][c] = (t < T && e < Eh) ? dl[(size_t)t * E + (size_t)h * Eh + e] : 0.f;
   }
-  if (tid == 0) dbias[e] = s[0];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int c = i >> 3, g = i & 7, e = e0 + c;  // expert, group of 8 positions in the chunk
+    if (e >= ep) continue;
+    uint32_t w[3][4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      uint32_t pk[3] = {0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int pos = 8 * (g & 3) + j + u;
+        const float v = sv[32 * (g >> 2) + rw_token_of_pos(pos)][c];
+        const uint16_t b0 = f32_to_bf16(v);
+        const float r1 = v - bf16_to_f32(b0);
+        const uint16_t b1 = f32_to_bf16(r1);
+        const uint16_t b2 = f32_to_bf16(r1 - bf16_to_f32(b1));
+        pk[0] |= (uint32_t)b0 << (16 * u);
+        pk[1] |= (uint32_t)b1 << (16 * u);
+        pk[2] |= (uint32_t)b2 << (16 * u);
+      }
+#pragma unroll
+      for (int p = 0; p < 3; ++p) w[p][j >> 1] = pk[p];
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      *(u32x4 *)(planes + (((size_t)h * 3 + p) * ep + e) * tp + t0 + 8 * g) = u32x4{w[p][0], w[p][1], w[p][2], w[p][3]};
+  }
+}
+
+// x rows in LDS: 64 token rows of 256 columns (512 bytes) per stage, stored as
+// 32 row pairs of 1056 bytes (two rows + 32 bytes of padding), so pair j starts
+// at bank 8 * (j % 8): the 16 rows one transposing read covers spread over all
+// banks, two rows per bank, the minimum for 512 bytes.  One direct-load
+// instruction (64 lanes x 16 bytes) fills one pair.
+constexpr int RW_PAIR = 1056, RW_BSTAGE = 32 * RW_PAIR;
+__device__ __forceinline__ int rw_rowoff(int r) { return (r >> 1) * RW_PAIR + (r & 1) * 512; }
+typedef short rw_v4s __attribute__((ext_vector_type(4)));
+
+// part[ts][h*E_h + e][c] = sum over tokens t of range ts of dl[t][h*E_h + e] *
+// x[t][h*dh + c].  Block tile: BM experts (all three planes) x 256 columns; 4
+// waves side by side in n (64 columns each, BM/16 x 4 fragments of 16 x 16);
+// 64-token chunks in a two-stage ring.  The planes' rows (128 bytes per chunk)
+// use the 16-byte-slot XOR swizzle of the grouped GEMM and plain ds_read_b128.
+// Tiles go to XCDs in contiguous runs, experts fastest, so the tiles that read
+// the same x columns share an L2.
+template <int BM>
+__global__ __launch_bounds__(256) void router_wgrad_mfma_kernel(const uint16_t *__restrict__ planes,
+                                                                const uint16_t *__restrict__ x, long ldx, int T,
+                                                                int tp, int E, int Eh, int ep, int dh, int H, int per,
+                                                                int nsplit, float *__restrict__ part) {
+  constexpr int MF = BM / 16, SA = 3 * BM * 8;  // A: 16-byte slots per stage (3 planes x BM rows x 8)
+  constexpr int LA = (SA + 255) / 256, LAMIN = SA / 256, LB = 8;
+  static_assert(SA % 64 == 0, "whole waves of A slots");
+  extern __shared__ u32x4 rw_smem[];
+  u32x4 *sA = rw_smem;                                // [2][SA]
+  char *sB = (char *)(rw_smem + 2 * SA);              // [2][RW_BSTAGE]
+
+  const int mt = ep / BM, nt = (dh + 255) / 256;
+  const int total = mt * nt * nsplit * H;
+  const int b = blockIdx.x;
+  const int q8 = total >> 3;
+  const int lt = (b < 8 * q8) ? (b & 7) * q8 + (b >> 3) : b;
+  const int tm = lt % mt, tn = (lt / mt) % nt, ts = (lt / (mt * nt)) % nsplit, h = lt / (mt * nt * nsplit);
+  const int m0 = tm * BM, n0 = tn * 256;
+  const int t_beg = min(T, ts * per), t_end = min(T, t_beg + per), klen = t_end - t_beg;
+  const int nk = (klen + 63) / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int gq = lane >> 4, li = lane & 15;
+
+  // A: slot s = i*256 + tid holds chunk swz(row, s % 8) of plane row `row`
+  const uint16_t *asrc[LA];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int s = min(i * 256 + tid, SA - 1), row = s >> 3, q = (s & 7) ^ (row & 7);
+    const int p = row / BM, e = m0 + row % BM;
+    asrc[i] = planes + (((size_t)h * 3 + p) * ep + e) * tp + t_beg + 8 * q;
+  }
+  // B: instruction i of wave wv fills pair j = 4i + wv; lane -> row 2j + lane/32,
+  // columns 8*(lane % 32) .. +7 (clamped into the head: duplicates, never stored)
+  const int lrow = lane >> 5, lcol = min(n0 + (lane & 31) * 8, dh - 8);
+  const uint16_t *xb = x + (size_t)h * dh + lcol;
+  auto issue = [&](int kc, int st) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      if (i * 256 + wv * 64 < SA) load_lds16(asrc[i] + kc * 64, sA + st * SA + i * 256 + wv * 64);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int j = 4 * i + wv;
+      const int t = min(t_beg + kc * 64 + 2 * j + lrow, T - 1);  // rows past T: re-read, zeroed below
+      load_lds16(xb + (size_t)t * ldx, sB + st * RW_BSTAGE + j * RW_PAIR);
+    }
+  };
+
+  f32x4 acc[MF][4];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // per lane: byte offsets of its two transposing reads of k-step ks (column 0 of the wave)
+  int roff[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      roff[ks][hh] = rw_rowoff(32 * ks + 16 * hh + 4 * gq + (li >> 2)) + 8 * (li & 3) + 2 * 64 * wv;
+  auto fragb = [&](const char *stage, int ks, int f) -> u32x4 {
+    const rw_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) rw_v4s *)(stage + roff[ks][0] + 32 * f));
+    const rw_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) rw_v4s *)(stage + roff[ks][1] + 32 * f));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
+  };
+  // zero the tokens at or past the range's end (last chunk only): element w
+  // of a fragment holds tokens kb + 2w, kb + 2w + 1 (w < 2) or kb + 12 + 2w, +1
+  auto maskb = [&](u32x4 &fr, int kc, int ks) {
+    const int kb = kc * 64 + 32 * ks + 4 * gq;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int k = kb + (w < 2 ? 2 * w : 12 + 2 * w);
+      fr[w] &= ((k < klen) ? 0xFFFFu : 0u) | ((k + 1 < klen) ? 0xFFFF0000u : 0u);
+    }
+  };
+  auto readk = [&](int kc, int ks, u32x4 (&fa)[3][MF], u32x4 (&fb)[4]) {
+    const u32x4 *st = sA + (kc & 1) * SA;
+    const int sw = (gq + 4 * ks) ^ (li & 7);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int i = 0; i < MF; ++i) fa[p][i] = st[(p * BM + i * 16 + li) * 8 + sw];
+    const bool last = kc == nk - 1 && (klen & 63);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      fb[f] = fragb(sB + (kc & 1) * RW_BSTAGE, ks, f);
+      if (last) maskb(fb[f], kc, ks);
+    }
+  };
+  auto mfma = [&](const u32x4 (&fa)[3][MF], const u32x4 (&fb)[4]) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[i][f] = mma16(fb[f], fa[p][i], acc[i][f], uint16_t());
+  };
+
+  if (nk > 0) {
+    issue(0, 0);
+    if (nk > 1) {
+      issue(1, 1);
+      wait_vmcnt<LAMIN + LB>();  // chunk 0 landed (a wave with more A slots also waits for one of chunk 1)
+    } else {
+      wait_vmcnt0();
+    }
+    __syncthreads();
+    u32x4 fa0[3][MF], fb0[4], fa1[3][MF], fb1[4];
+    readk(0, 0, fa0, fb0);
+    for (int kc = 0; kc < nk; ++kc) {
+      readk(kc, 1, fa1, fb1);
+      mfma(fa0, fb0);
+      if (kc + 1 < nk) {
+        wait_vmcnt0();    // chunk kc+1 landed (chunk kc+2 is not issued yet)
+        wait_lgkmcnt0();  // this wave's reads of stage kc&1 are done
+        __syncthreads();
+        if (kc + 2 < nk) issue(kc + 2, kc & 1);
+        readk(kc + 1, 0, fa0, fb0);
+      }
+      mfma(fa1, fb1);
+    }
+  }
+  const int c0 = n0 + wv * 64 + 4 * gq;
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    const int e = m0 + i * 16 + li;
+    if (e >= Eh) continue;
+    float *prow = part + ((size_t)ts * E + (size_t)h * Eh + e) * dh;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int c = c0 + f * 16;
+      if (c < dh) *(f32x4 *)(prow + c) = acc[i][f];
+    }
+  }
+}
+
+// dbias[e] = sum_t dl[t][e] in two passes: block (64 experts, token chunk c)
+// sums its chunk's rows (lane = expert: coalesced rows; wave w takes every
+// fourth token, then the four waves are added in order) into part[c][e]; then
+// one wave per expert adds the chunks (lane l: chunks l, l + 64, ... in order,
+// then a fixed butterfly over the lanes).  The order is fixed: reproducible.
+__global__ __launch_bounds__(256) void router_dbias_part_kernel(const float *__restrict__ dl, int T, int E, int per,
+                                                                float *__restrict__ part) {
+  __shared__ float sw[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, e = blockIdx.x * 64 + lane, c = blockIdx.y;
+  const int t0 = c * per, t1 = min(T, t0 + per);
+  float v = 0.f;
+  if (e < E) {
+#pragma unroll 4
+    for (int t = t0 + w; t < t1; t += 4) v += dl[(size_t)t * E + e];
+  }
+  sw[w][lane] = v;
+  __syncthreads();
+  if (w == 0 && e < E) part[(size_t)c * E + e] = ((sw[0][lane] + sw[1][lane]) + sw[2][lane]) + sw[3][lane];
+}
+__global__ __launch_bounds__(256) void router_dbias_sum_kernel(const float *__restrict__ part, int E, int nch,
+                                                               float *__restrict__ dbias) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (e >= E) return;  // whole waves
+  float v = 0.f;
+  for (int c = lane; c < nch; c += 64) v += part[(size_t)c * E + e];
+  v = group_sum_fixed(v, WAVE);
+  if (lane == 0) dbias[e] = v;
 }
 
 // ---------------------------------------------------------------- input gradient
@@ -501,28 +748,66 @@ int launch_seq_counts(const Shape &s, const int32_t *topk_idx, int32_t *seq_cnt,
 
 int launch_router_bwd(const Shape &s, const float *logits, const int32_t *topk_idx, const float *gates,
                       const float *dg, const int32_t *demand, float lam, const int32_t *seq_cnt, float seq_w,
-                      const void *x, float *dl, float *part, float *dw_router, float *dbias, hipStream_t st) {
+                      const void *x, float *dl, uint16_t *planes, float *part, float *dw_router, float *dbias,
+                      hipStream_t st) {
   const long pairs = (long)s.T * s.H;
-  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, logits, topk_idx,
-                     gates, dg, demand, s.T, s.H, s.E, s.Eh, s.K, s.k, s.renorm, lam, seq_cnt, s.seq_len > 0 ? s.seq_len : 1,
-                     seq_w, dl);
-  if (int rc = launch_status("router backward")) return rc;
+  if (pairs > 0) {
+    const int L = s.seq_len > 0 ? s.seq_len : 1;
+    auto go = [&](auto kern, int w) {
+      const long waves = (pairs * w + 63) / 64;
+      hipLaunchKernelGGL(kern, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, logits, topk_idx, gates, dg,
+                         demand, s.T, s.H, s.E, s.Eh, s.K, s.k, s.renorm, lam, seq_cnt, L, seq_w, dl);
+    };
+    if (s.Eh <= 8) go(router_bwd_kernel<8>, 8);
+    else if (s.Eh <= 16) go(router_bwd_kernel<16>, 16);
+    else if (s.Eh <= 32) go(router_bwd_kernel<32>, 32);
+    else go(router_bwd_kernel<64>, 64);
+    if (int rc = launch_status("router backward")) return rc;
+  }
   if (dbias) {
-    hipLaunchKernelGGL(router_dbias_kernel, dim3((unsigned)s.E), dim3(256), 0, st, dl, s.T, s.E, dbias);
+    // partials in `part` (at least ROUTER_DBIAS_CHUNKS * E floats; the weight
+    // gradient overwrites them afterwards, in stream order)
+    const int per = (int)std::max<long>(16, ((long)s.T + ROUTER_DBIAS_CHUNKS - 1) / ROUTER_DBIAS_CHUNKS);
+    const int nch = (int)std::max<long>(1, ((long)s.T + per - 1) / per);
+    hipLaunchKernelGGL(router_dbias_part_kernel, dim3((unsigned)((s.E + 63) / 64), (unsigned)nch), dim3(256), 0, st,
+                       dl, s.T, s.E, per, part);
+    if (int rc = launch_status("router bias gradient")) return rc;
+    hipLaunchKernelGGL(router_dbias_sum_kernel, dim3((unsigned)((s.E + 3) / 4)), dim3(256), 0, st, part, s.E,
+                       nch, dbias);
     if (int rc = launch_status("router bias gradient")) return rc;
   }
-  const int nsplit = router_wgrad_split(s);
-  const long ldx = (long)s.H * s.dh;
-  const dim3 grid((unsigned)((s.Eh + 63) / 64), (unsigned)((s.dh + 63) / 64), (unsigned)(nsplit * s.H));
-  if (s.act_f32)
+  const long ldx = (long)s.H * s.dh, n = (long)s.E * s.dh;
+  int nsplit;
+  if (s.act_f32) {
+    nsplit = router_wgrad_split(s);
+    const dim3 grid((unsigned)((s.Eh + 63) / 64), (unsigned)((s.dh + 63) / 64), (unsigned)(nsplit * s.H));
     hipLaunchKernelGGL((router_wgrad_kernel<float>), grid, dim3(256), 0, st, dl, (const float *)x, ldx, s.T, s.E,
                        s.Eh, s.dh, nsplit, part);
-  else
-    hipLaunchKernelGGL((router_wgrad_kernel<uint16_t>), grid, dim3(256), 0, st, dl, (const uint16_t *)x, ldx, s.T,
-                       s.E, s.Eh, s.dh, nsplit, part);
+  } else {
+    const RouterWgradGeom g = router_wgrad_geom(s);
+    nsplit = g.nsplit;
+    if (g.tp > 0) {
+      const dim3 pg((unsigned)(g.tp / 64), (unsigned)((g.ep + 63) / 64), (unsigned)s.H);
+      hipLaunchKernelGGL(router_dl_planes_kernel, pg, dim3(256), 0, st, dl, s.T, s.E, s.Eh, g.ep, g.tp, planes);
+      if (int rc = launch_status("router gradient planes")) return rc;
+    }
+    float *out = nsplit == 1 ? dw_router : part;
+    const unsigned blocks = (unsigned)((long)(g.ep / g.bm) * ((s.dh + 255) / 256) * nsplit * s.H);
+    const size_t lds = (size_t)2 * 3 * g.bm * 8 * 16 + 2 * RW_BSTAGE;
+    const uint16_t *xb = (const uint16_t *)x;
+    if (g.bm == 16)
+      hipLaunchKernelGGL((router_wgrad_mfma_kernel<16>), dim3(blocks), dim3(256), lds, st, planes, xb, ldx, s.T,
+                         g.tp, s.E, s.Eh, g.ep, s.dh, s.H, g.per, nsplit, out);
+    else if (g.bm == 32)
+      hipLaunchKernelGGL((router_wgrad_mfma_kernel<32>), dim3(blocks), dim3(256), lds, st, planes, xb, ldx, s.T,
+                         g.tp, s.E, s.Eh, g.ep, s.dh, s.H, g.per, nsplit, out);
+    else
+      hipLaunchKernelGGL((router_wgrad_mfma_kernel<64>), dim3(blocks), dim3(256), lds, st, planes, xb, ldx, s.T,
+                         g.tp, s.E, s.Eh, g.ep, s.dh, s.H, g.per, nsplit, out);
+    if (nsplit == 1) return launch_status("router weight gradient");
+  }
   if (int rc = launch_status("router weight gradient")) return rc;
-  const long n = (long)s.E * s.dh;
-  hipLaunchKernelGGL(router_wgrad_sum_kernel, dim3((unsigned)std::min<long>((n + 255) / 256, 4096)), dim3(256), 0,
+  hipLaunchKernelGGL(router_wgrad_sum_kernel, dim3((unsigned)std::min<long>((n / 4 + 63) / 64, 8192)), dim3(64), 0,
                      st, part, n, nsplit, dw_router);
   return launch_status("router weight gradient");
 }

@@ -76,16 +76,53 @@ int launch_bwd_rows(const Shape &s, const void *dy, long ld_dy, const void *y_pe
                     hipStream_t st);
 int launch_bwd_pad(const Shape &s, const int32_t *offsets, const int32_t *src_of, int32_t *poff, int32_t *pmap_r,
                    int32_t *pmap_x, long npad, hipStream_t st);
-// the router weight gradient sums router_wgrad_split(s) token ranges
-// separately (enough 64 x 64 tiles to fill the chip), then adds them in order;
-// `part` holds router_wgrad_split(s) * E * d_head floats
+// float32 layers: the router weight gradient sums router_wgrad_split(s) token
+// ranges separately (enough 64 x 64 tiles to fill the chip), then adds them in
+// order
 inline int router_wgrad_split(const Shape &s) {
   const long tiles = (long)s.H * ((s.Eh + 63) / 64) * ((s.dh + 63) / 64);
   return (int)std::min<long>(64, std::max<long>(1, (4096 + tiles - 1) / std::max<long>(tiles, 1)));
 }
+// bf16 layers take the router weight gradient on MFMA: dl as three bf16
+// planes (hi + mid + lo = dl to float32 accuracy), transposed per head to
+// [H][3][ep][tp] (ep = E_h rounded up to the tile's bm experts, tp = T rounded
+// up to 64), against x rows read through transposing LDS reads.  Tiles of bm
+// experts x 256 columns; the tokens split in nsplit ranges of `per` (a
+// multiple of 64), float32 partials added in order.
+struct RouterWgradGeom {
+  int bm, ep, tp, per, nsplit;
+};
+inline RouterWgradGeom router_wgrad_geom(const Shape &s) {
+  RouterWgradGeom g;
+  g.bm = s.Eh <= 16 ? 16 : s.Eh <= 32 ? 32 : 64;
+  g.ep = (s.Eh + g.bm - 1) / g.bm * g.bm;
+  g.tp = (int)(((long)s.T + 63) / 64 * 64);
+  const long tiles = (long)s.H * (g.ep / g.bm) * ((s.dh + 255) / 256);
+  const long slots = g.bm == 64 ? 256 : 512;  // resident blocks: one (two) per CU
+  const long chunks = std::max<long>(1, g.tp / 64);
+  const long want = std::min<long>(64, std::max<long>(1, slots / tiles));
+  g.per = (int)((chunks + want - 1) / want * 64);
+  g.nsplit = (int)std::max<long>(1, ((long)s.T + g.per - 1) / g.per);
+  return g;
+}
+inline size_t router_planes_bytes(const Shape &s) {
+  if (s.act_f32) return 0;
+  const RouterWgradGeom g = router_wgrad_geom(s);
+  return (size_t)s.H * 3 * g.ep * g.tp * 2;
+}
+// float32 partials of the router weight and bias gradients: the weight
+// gradient's token ranges (E x d_head each), and ROUTER_DBIAS_CHUNKS x E for
+// the bias gradient (used first, in stream order)
+constexpr int ROUTER_DBIAS_CHUNKS = 256;
+inline size_t router_part_floats(const Shape &s) {
+  const long parts = s.act_f32 ? router_wgrad_split(s) : router_wgrad_geom(s).nsplit;
+  return (size_t)std::max<long>(parts * s.dh, ROUTER_DBIAS_CHUNKS) * s.E;
+}
+// planes: router_planes_bytes(s) of workspace (bf16 layers)
 int launch_router_bwd(const Shape &s, const float *logits, const int32_t *topk_idx, const float *gates,
                       const float *dg, const int32_t *demand, float lam, const int32_t *seq_cnt, float seq_w,
-                      const void *x, float *dl, float *part, float *dw_router, float *dbias, hipStream_t st);
+                      const void *x, float *dl, uint16_t *planes, float *part, float *dw_router, float *dbias,
+                      hipStream_t st);
 // seq_cnt[s][e]: choices of expert e within sequence s
 int launch_seq_counts(const Shape &s, const int32_t *topk_idx, int32_t *seq_cnt, hipStream_t st);
 int launch_bwd_dx(const Shape &s, const void *dy, const void *dxs, const void *dXr, const int32_t *row_of,

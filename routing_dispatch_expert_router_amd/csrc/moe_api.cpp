@@ -161,7 +161,7 @@ bool bwd_supported(const Shape &s) {
 }
 
 struct BwdBufs {
-  size_t dg, dl, rpart, seqcnt, dY, dH, dAB, Hr, dXr, poff, pmap_r, pmap_x, Xt, dYt, dABt, Ht, prefix, kwin;
+  size_t dg, dl, rpart, rplanes, seqcnt, dY, dH, dAB, Hr, dXr, poff, pmap_r, pmap_x, Xt, dYt, dABt, Ht, prefix, kwin;
   size_t dHs, dABs, Hs, dxs, dyt, xt, dABst, Hst, dout, du, ot, dut, spart, epart, kwsplit, total;
 };
 
@@ -172,7 +172,8 @@ BwdBufs bwd_layout(const Shape &s) {
   size_t o = 0;
   b.dg = o; o += al((size_t)s.T * s.K * 4);
   b.dl = o; o += al((size_t)s.T * s.E * 4);
-  b.rpart = o; o += al((size_t)moe::router_wgrad_split(s) * s.E * s.dh * 4);
+  b.rpart = o; o += al(moe::router_part_floats(s) * 4);
+  b.rplanes = o; o += al(moe::router_planes_bytes(s));
   b.seqcnt = o; o += s.seq_len > 0 ? al((size_t)(s.T / s.seq_len) * s.E * 4) : 0;
   b.dY = o; o += al(R * s.dh * esz);
   b.dH = o; o += al(R * s.dff * esz);
@@ -581,7 +582,7 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
   int32_t *seqcnt = seq_weight != 0.0f ? (int32_t *)at(L.seqcnt) : nullptr;
   if (seqcnt && (rc = rc_of(moe::launch_seq_counts(s, io->topk_idx, seqcnt, stream)))) return rc;
   if ((rc = rc_of(moe::launch_router_bwd(s, io->logits, io->topk_idx, io->topk_w, dg, io->demand, aux_weight,
-                                         seqcnt, seq_weight, u, dl,
+                                         seqcnt, seq_weight, u, dl, (uint16_t *)at(L.rplanes),
                                          (float *)at(L.rpart), g->dw_router, g->dbias, stream))))
     return rc;
   // shared experts: the same MLP backward over all T tokens with gate 1
