@@ -808,8 +808,24 @@ int gemm_kgrouped_split(bool f32, const void *A, long lda, const void *B, long l
   return launch_status("split-k group reduce");
 }
 
+// blocks of a tile kind resident on the chip at once: a 256 x 256 tile holds
+// 128 KiB of LDS (one block per CU), the 128 x 128 tiles fit two per CU
+static long resident_blocks(int tile) { return tile == TILE_256x256_W8 ? 256 : 512; }
+
+// Split count of one dense weight-gradient product.  Splitting K only pays while
+// the output tiles alone leave CUs idle: with `tiles` blocks of full depth
+// already filling a round, s splits take ceil(s * tiles / resident) rounds of
+// depth K / s (no shorter) plus a float32 reduction.  So take the largest s
+// whose blocks still fit in one round (1 when the tiles alone fill it).
+static int fill_split(long tiles, long resident, long max_by_depth) {  // 1 .. 8
+  const long s = std::min<long>(resident / std::max<long>(tiles, 1), max_by_depth);
+  return (int)std::max<long>(1, std::min<long>(s, 8));
+}
 // Splits for G groups of M x N outputs over K_total (all groups' windows):
-// enough tiles to fill the chip, windows of 512 or more on average
+// up to four rounds of tiles, windows of 512 or more on average.  Unlike one
+// dense product, the groups' windows differ in depth, and splitting them
+// shortens the deepest (measured: the multi-head workload's skewed experts
+// run faster split in two than unsplit in one round).
 int kgrouped_split_count(bool f32, int G, int M, int N, long K_total) {
   const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
   const long tiles = (long)G * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
@@ -818,14 +834,11 @@ int kgrouped_split_count(bool f32, int G, int M, int N, long K_total) {
   return (int)std::max<long>(1, std::min<long>(s, 8));
 }
 
-// K windows for gemm_splitk: splits that fill the chip with output tiles, each
-// at least 1024 deep
+// K windows for gemm_splitk: each at least 1024 deep
 int splitk_count(bool f32, int M, int N, long K) {
   const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
   const long tiles = (long)((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
-  long s = (512 + tiles - 1) / tiles;
-  s = std::min<long>(s, std::max<long>(1, K / 1024));
-  return (int)std::max<long>(1, std::min<long>(s, 8));
+  return fill_split(tiles, resident_blocks(tile), K / 1024);
 }
 
 size_t ffn_ws_bytes(const Shape &s) {
