@@ -44,6 +44,8 @@
  *     aux loss are float32; indices are int32.
  *   - The workspace `ws` must hold at least moe_workspace_bytes(cfg) bytes and
  *     be 256-byte aligned; its contents need not be initialised.
+ *   - Every other device pointer must be 16-byte aligned (the kernels move
+ *     16-byte vectors); a misaligned one returns MOE_ERR_ARG before any launch.
  */
 #ifndef MOE_H
 #define MOE_H

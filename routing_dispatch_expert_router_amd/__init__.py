@@ -131,7 +131,14 @@ def _addr(t):
         raise ValueError(f"expected a GPU tensor, got one on {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"expected a contiguous tensor, got strides {tuple(t.stride())} for shape {tuple(t.shape)}")
-    return t.data_ptr()
+    return _check_alignment(t.data_ptr())
+
+
+def _check_alignment(addr):
+    """The library moves 16-byte vectors: every device address must be 16-byte aligned."""
+    if addr % 16:
+        raise ValueError(f"expected a 16-byte aligned device buffer, got address {addr:#x}")
+    return addr
 
 
 def _p(t):

@@ -726,13 +726,31 @@ int gemm_kgrouped(bool f32, const void *A, long lda, const void *B, long ldb, vo
 // windows kwin[0..nsplit] (device, multiples of 64): each window's product
 // goes to part[s] (float32, M x N, row stride N), then C = sum over s in
 // order, rounded once.  Fills the chip when one group has few output tiles.
+// c[0..3] = sum over s < nsplit of p[s * stride + 0..3], in order s = 0, 1, ...,
+// rounded once; up to eight partials' loads in flight before their adds
+template <typename TE>
+__device__ __forceinline__ void reduce_quad(const float *__restrict__ p, size_t stride, int nsplit,
+                                            TE *__restrict__ c) {
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < nsplit) v[u] = *(const float4 *)(p + (size_t)(s0 + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < nsplit) {
+        o[0] += v[u].x; o[1] += v[u].y; o[2] += v[u].z; o[3] += v[u].w;
+      }
+  }
+  Quad<TE>::store(c, o);
+}
+
+// C = sum of the partials in order (n a multiple of 4: four columns per thread)
 template <typename TE>
 __global__ void splitk_reduce_kernel(const float *__restrict__ part, long n, int nsplit, TE *__restrict__ C) {
-  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-    float v = 0.f;
-    for (int s = 0; s < nsplit; ++s) v += part[(size_t)s * n + i];
-    C[i] = Elem<TE>::from_f32(v);
-  }
+  for (long i = 4 * (blockIdx.x * (long)blockDim.x + threadIdx.x); i < n; i += 4L * gridDim.x * blockDim.x)
+    reduce_quad(part + i, (size_t)n, nsplit, C + i);
 }
 
 int gemm_splitk(bool f32, const void *A, long lda, const void *B, long ldb, void *C, int M, int N, int nsplit,
@@ -745,8 +763,8 @@ int gemm_splitk(bool f32, const void *A, long lda, const void *B, long ldb, void
   a.fixed_tiles = nsplit * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
   const int rc = f32 ? run_gemm_one<float, EPI_PLAIN>(a, tile, st) : run_gemm_one<uint16_t, EPI_F32OUT>(a, tile, st);
   if (rc) return rc;
-  const long n = (long)M * N;
-  const unsigned grid = (unsigned)std::min<long>((n + 255) / 256, 8192);
+  const long n = (long)M * N;  // N is a multiple of 64
+  const unsigned grid = (unsigned)std::min<long>((n / 4 + 255) / 256, 8192);
   if (f32)
     hipLaunchKernelGGL((splitk_reduce_kernel<float>), dim3(grid), dim3(256), 0, st, part, n, nsplit, (float *)C);
   else
@@ -770,17 +788,15 @@ __global__ void split_windows_kernel(const int32_t *__restrict__ kwin, int G, in
   }
 }
 
-// C_e[i] = sum over s of part[(e * nsplit + s) * MN + i], in order, rounded once
+// C_e[i] = sum over s of part[(e * nsplit + s) * MN + i], in order, rounded once;
+// group e = blockIdx.y, four columns per thread (MN a multiple of 4)
 template <typename TE>
-__global__ void group_reduce_kernel(const float *__restrict__ part, long MN, int G, int nsplit, long cstride,
+__global__ void group_reduce_kernel(const float *__restrict__ part, long MN, int nsplit, long cstride,
                                     TE *__restrict__ C) {
-  const long n = (long)G * MN;
-  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
-    const long e = i / MN, j = i - e * MN;
-    float v = 0.f;
-    for (int s = 0; s < nsplit; ++s) v += part[((size_t)e * nsplit + s) * MN + j];
-    C[(size_t)e * cstride + j] = Elem<TE>::from_f32(v);
-  }
+  const long e = blockIdx.y;
+  const float *pe = part + (size_t)e * nsplit * MN;
+  for (long j = 4 * (blockIdx.x * (long)blockDim.x + threadIdx.x); j < MN; j += 4L * gridDim.x * blockDim.x)
+    reduce_quad(pe + j, (size_t)MN, nsplit, C + (size_t)e * cstride + j);
 }
 
 int gemm_kgrouped_split(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long cstride, int G,
@@ -797,14 +813,13 @@ int gemm_kgrouped_split(bool f32, const void *A, long lda, const void *B, long l
   a.fixed_tiles = G * nsplit * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
   const int rc = f32 ? run_gemm_one<float, EPI_PLAIN>(a, tile, st) : run_gemm_one<uint16_t, EPI_F32OUT>(a, tile, st);
   if (rc) return rc;
-  const long n = (long)G * M * N;
-  const unsigned grid = (unsigned)std::min<long>((n + 255) / 256, 8192);
+  const long mn = (long)M * N;  // N is a multiple of 64
+  const dim3 grid((unsigned)std::min<long>((mn / 4 + 255) / 256, std::max<long>(1, 8192 / G)), (unsigned)G);
   if (f32)
-    hipLaunchKernelGGL((group_reduce_kernel<float>), dim3(grid), dim3(256), 0, st, part, (long)M * N, G, nsplit,
-                       cstride, (float *)C);
+    hipLaunchKernelGGL((group_reduce_kernel<float>), grid, dim3(256), 0, st, part, mn, nsplit, cstride, (float *)C);
   else
-    hipLaunchKernelGGL((group_reduce_kernel<uint16_t>), dim3(grid), dim3(256), 0, st, part, (long)M * N, G, nsplit,
-                       cstride, (uint16_t *)C);
+    hipLaunchKernelGGL((group_reduce_kernel<uint16_t>), grid, dim3(256), 0, st, part, mn, nsplit, cstride,
+                       (uint16_t *)C);
   return launch_status("split-k group reduce");
 }
 

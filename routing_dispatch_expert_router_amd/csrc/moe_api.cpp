@@ -1,6 +1,7 @@
 // C-ABI entry points of libmoe.so (declared and documented in include/moe.h).
 // Host code only: validation, workspace layout and launch order.  Every check
 // runs before the first launch, so a rejected call launches nothing.
+#include <initializer_list>
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -236,6 +237,29 @@ BwdBufs bwd_layout(const Shape &s) {
 
 }  // namespace
 
+// Every device pointer must be 16-byte aligned: the kernels move 16-byte
+// vectors (direct global->LDS loads, row copies, combine).  NULL passes.
+static bool misaligned(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if ((uintptr_t)p & 15) return true;
+  return false;
+}
+static bool misaligned_w(const moe_weights *w) {
+  return misaligned({w->w_router, w->router_bias, w->w1, w->w3, w->w2, w->ws1, w->ws3, w->ws2, w->w_in, w->w_out,
+                     w->sel_bias});
+}
+static bool misaligned_wt(const moe_weights_t *t) {
+  return misaligned({t->w13t, t->w2t, t->ws13t, t->ws2t, t->w_in_t, t->w_out_t});
+}
+static bool misaligned_io(const moe_layer_io *io) {
+  return misaligned({io->logits, io->topk_idx, io->topk_w, io->demand, io->counts, io->offsets, io->row_of,
+                     io->src_of, io->aux_loss, io->seq_loss, io->z, io->x_perm, io->y_perm, io->shared_out, io->o});
+}
+static bool misaligned_g(const moe_grads *g) {
+  return misaligned({g->dx, g->dw_router, g->dbias, g->dw1, g->dw3, g->dw2, g->dws1, g->dws3, g->dws2, g->dw_in,
+                     g->dw_out});
+}
+
 extern "C" {
 
 size_t moe_workspace_bytes(const moe_config *cfg) {
@@ -276,6 +300,7 @@ int moe_route(const moe_config *cfg, const void *x, const void *w_router, const 
   if (!topk_idx || !topk_w) return MOE_ERR_ARG;
   if (mode != MOE_LOGITS_LOAD && (!x || !w_router)) return MOE_ERR_ARG;
   if (mode != MOE_LOGITS_COMPUTE && !logits) return MOE_ERR_ARG;
+  if (misaligned({x, w_router, bias, sel_bias, logits, topk_idx, topk_w, aux_loss, seq_loss})) return MOE_ERR_ARG;
   if (aux_loss && s.H != 1) return MOE_ERR_UNSUPPORTED;
   if (seq_loss && s.seq_len == 0) return MOE_ERR_ARG;
   if (sel_bias && s.expert_choice) return MOE_ERR_UNSUPPORTED;
@@ -292,6 +317,7 @@ int moe_sel_bias_update(const moe_config *cfg, const int32_t *load, float *sel_b
   int rc = make_shape(cfg, &s);
   if (rc) return rc;
   if (!load || !sel_bias) return MOE_ERR_ARG;
+  if (misaligned({load, sel_bias})) return MOE_ERR_ARG;
   clear_stale_error();
   return rc_of(moe::launch_sel_bias_update(s, load, sel_bias, gamma, stream));
 }
@@ -305,6 +331,7 @@ int moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, const float *to
   if (!topk_idx || !demand || !counts || !offsets || !row_of || (!src_of && s.R_max) || (x_perm && !x))
     return MOE_ERR_ARG;
   if (s.drop >= moe::DROP_AFFINITY && !topk_w) return MOE_ERR_ARG;  // affinity keep and expert choice read gates
+  if (misaligned({topk_idx, topk_w, x, demand, counts, offsets, row_of, src_of, x_perm})) return MOE_ERR_ARG;
   if ((rc = check_ws(s, ws, ws_bytes))) return rc;
   if (s.T == 0) return MOE_OK;
   clear_stale_error();
@@ -319,6 +346,7 @@ int moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *off
   int rc = make_shape(cfg, &s);
   if (rc) return rc;
   if (((!x_perm || !y_perm) && s.R_max) || !offsets || !w1 || !w2) return MOE_ERR_ARG;
+  if (misaligned({x_perm, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out})) return MOE_ERR_ARG;
   if ((s.act == MOE_ACT_SWIGLU) != (w3 != nullptr)) return MOE_ERR_ARG;
   if (s.n_shared) {
     if (!x_shared || !ws1 || !ws2 || !shared_out) return MOE_ERR_ARG;
@@ -339,6 +367,7 @@ int moe_expert_ffn_gather(const moe_config *cfg, const void *x, const int32_t *s
   int rc = make_shape(cfg, &s);
   if (rc) return rc;
   if (((!x || !src_of || !y_perm) && s.R_max) || !offsets || !w1 || !w2) return MOE_ERR_ARG;
+  if (misaligned({x, src_of, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out})) return MOE_ERR_ARG;
   if ((s.act == MOE_ACT_SWIGLU) != (w3 != nullptr)) return MOE_ERR_ARG;
   if (s.n_shared) {
     if (!x_shared || !ws1 || !ws2 || !shared_out) return MOE_ERR_ARG;
@@ -358,6 +387,7 @@ int moe_combine(const moe_config *cfg, const void *y_perm, const int32_t *row_of
   int rc = make_shape(cfg, &s);
   if (rc) return rc;
   if ((!y_perm && s.R_max) || !row_of || !topk_w || !y) return MOE_ERR_ARG;
+  if (misaligned({y_perm, row_of, topk_w, residual, shared_out, y})) return MOE_ERR_ARG;
   if (s.T == 0) return MOE_OK;
   clear_stale_error();
   return rc_of(moe::launch_combine(s, y_perm, row_of, topk_w, residual, shared_out, y, stream));
@@ -373,6 +403,7 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
   if (!io) io = &none;
   const int mode = io->logits_mode;
   if (!w || !x || !y || x == y) return MOE_ERR_ARG;
+  if (misaligned({x, y}) || misaligned_w(w) || misaligned_io(io)) return MOE_ERR_ARG;
   if (mode < MOE_LOGITS_COMPUTE || mode > MOE_LOGITS_LOAD) return MOE_ERR_ARG;
   if (mode != MOE_LOGITS_COMPUTE && !io->logits) return MOE_ERR_ARG;
   if (mode != MOE_LOGITS_LOAD && !w->w_router) return MOE_ERR_ARG;
@@ -441,6 +472,7 @@ int moe_transpose_weights(const moe_config *cfg, const moe_weights *w, const moe
   int rc = make_shape(cfg, &s);
   if (rc) return rc;
   if (!w || !wt || !w->w1 || !w->w2 || !wt->w13t || !wt->w2t) return MOE_ERR_ARG;
+  if (misaligned_w(w) || misaligned_wt(wt)) return MOE_ERR_ARG;
   const bool glu = s.act == MOE_ACT_SWIGLU;
   if (glu && !w->w3) return MOE_ERR_ARG;
   if (s.n_shared && (!w->ws1 || !w->ws2 || (glu && !w->ws3) || !wt->ws13t || !wt->ws2t)) return MOE_ERR_ARG;
@@ -489,6 +521,8 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
   int rc = make_shape(cfg, &s);
   if (rc) return rc;
   if (!w || !wt || !x || !dy || !io || !g) return MOE_ERR_ARG;
+  if (misaligned({x, dy}) || misaligned_w(w) || misaligned_wt(wt) || misaligned_io(io) || misaligned_g(g))
+    return MOE_ERR_ARG;
   if (!bwd_supported(s)) return MOE_ERR_UNSUPPORTED;
   // a bias inside renormalised gates changes the renormalisation's derivative
   if (w->sel_bias && s.sel_gate && s.renorm) return MOE_ERR_UNSUPPORTED;

@@ -252,3 +252,62 @@ def test_binding_rejects_host_and_strided_tensors():
     with pytest.raises(ValueError):
         moe._addr(torch.zeros(4))
     assert moe._p(None) is None and moe._addr(None) is None
+
+
+def test_calls_reject_misaligned_device_pointers():
+    """Every device pointer must be 16-byte aligned.  With T = 0 a call that passes its checks returns MOE_OK
+    without launching anything (the control); the same call with one pointer 8 bytes off returns MOE_ERR_ARG."""
+    lib = moe._lib
+    cfg = CONFIGS[2].with_(T=0)  # one head, SwiGLU, two shared experts; never dereferenced below
+    assert cfg.act == 1 and cfg.n_shared > 0 and cfg.n_heads == 1
+    c = moe.config_struct(cfg)
+    ws, big = ctypes.c_void_p(0x100000), 1 << 40
+    ok, bad = moe.MOE_OK, moe.MOE_ERR_ARG
+
+    def both(call, n, skip=()):
+        """slot i holds the distinct aligned address 0x10000 + 0x100 i; all aligned -> MOE_OK, then slot i moved
+        8 bytes off -> MOE_ERR_ARG, for every slot not in `skip` (slots the call then forces to NULL)."""
+        addrs = [0x10000 + 0x100 * i for i in range(n)]
+        assert call(addrs) == ok
+        for i in range(n):
+            if i in skip:
+                continue
+            p = list(addrs)
+            p[i] += 8
+            assert call(p) == bad, i
+
+    v = ctypes.c_void_p
+    # route, COMPUTE mode: x, w_router, bias, logits, topk_idx, topk_w, aux_loss
+    both(lambda p: lib.moe_route(ctypes.byref(c), v(p[0]), v(p[1]), v(p[2]), None, v(p[3]), 0, v(p[4]), v(p[5]),
+                                 v(p[6]), None, ws, big, None), 7)
+    both(lambda p: lib.moe_dispatch(ctypes.byref(c), *[v(q) for q in p], ws, big, None), 9)
+    both(lambda p: lib.moe_expert_ffn(ctypes.byref(c), *[v(q) for q in p], ws, big, None), 11)
+    both(lambda p: lib.moe_expert_ffn_gather(ctypes.byref(c), *[v(q) for q in p], ws, big, None), 12)
+    both(lambda p: lib.moe_combine(ctypes.byref(c), *[v(q) for q in p], None), 6)
+
+    wf = [f for f, _ in moe.MoeWeights._fields_]
+    iof = [f for f, _ in moe.MoeLayerIO._fields_ if f != "logits_mode"]
+    nulls_w, nulls_io = ("w_in", "w_out"), ("aux_loss", "seq_loss", "z", "o")  # one head, no sequences or latent
+
+    def fwd(p):
+        w = moe.MoeWeights(**{f: (None if f in nulls_w else p[i]) for i, f in enumerate(wf)})
+        io = moe.MoeLayerIO(**{f: (None if f in nulls_io else p[len(wf) + i]) for i, f in enumerate(iof)})
+        io.logits_mode = 0
+        return lib.moe_layer_fwd(ctypes.byref(c), ctypes.byref(w), v(p[-2]), v(p[-1]), ctypes.byref(io), ws, big,
+                                 None)
+    skip = {wf.index(f) for f in nulls_w} | {len(wf) + iof.index(f) for f in nulls_io}
+    both(fwd, len(wf) + len(iof) + 2, skip)
+
+    # no T makes these two a no-op: only the rejection is checked, with every other pointer aligned and present
+    assert lib.moe_sel_bias_update(ctypes.byref(c), v(0x10008), v(0x10100), ctypes.c_float(0.001), None) == bad
+    w = moe.MoeWeights(w1=0x10000, w3=0x10100, w2=0x10200, ws1=0x10300, ws3=0x10400, ws2=0x10500)
+    wt = moe.MoeWeightsT(w13t=0x10600, w2t=0x10708, ws13t=0x10800, ws2t=0x10900)
+    assert lib.moe_transpose_weights(ctypes.byref(c), ctypes.byref(w), ctypes.byref(wt), None) == bad
+
+
+def test_binding_rejects_misaligned_tensors():
+    import torch
+    t = torch.zeros(16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe._check_alignment(t[1:].data_ptr())
+    moe._check_alignment(t.data_ptr())
