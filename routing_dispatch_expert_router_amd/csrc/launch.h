@@ -98,7 +98,9 @@ inline RouterWgradGeom router_wgrad_geom(const Shape &s) {
   g.ep = (s.Eh + g.bm - 1) / g.bm * g.bm;
   g.tp = (int)(((long)s.T + 63) / 64 * 64);
   const long tiles = (long)s.H * (g.ep / g.bm) * ((s.dh + 255) / 256);
-  const long slots = g.bm == 64 ? 256 : 512;  // resident blocks: one (two) per CU
+  // resident blocks: LDS per block is 2 x (3 bm x 128 + 33792) bytes, so two
+  // 16-expert blocks fit a CU's 160 KiB, one of the wider ones
+  const long slots = g.bm == 16 ? 512 : 256;
   const long chunks = std::max<long>(1, g.tp / 64);
   const long want = std::min<long>(64, std::max<long>(1, slots / tiles));
   g.per = (int)((chunks + want - 1) / want * 64);
