@@ -10,6 +10,7 @@
 // gating equation, "DeepSeekMoE" item 1); l_aux = sum_e m_e c_e / S ("GShard"
 // item 1).  Every reduction runs in a fixed order (bit-reproducible).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -23,9 +24,9 @@ __global__ void zero_f32_kernel(float *p, long n) {
 // ---------------------------------------------------------------- per kept row
 // dg[a] = <dy_{t,h}, y_perm_r> and dY_r = g_a * dy_{t,h} for row r holding
 // assignment a = t*K + j on expert e of head h = e / E_h (dy_{t,h}: columns
-// [h*dh, (h+1)*dh) of row t).  One wave per row; dg of dropped assignments
-// stays 0.
-template <typename TA>
+// [h*dh, (h+1)*dh) of row t).  W lanes per row (W = the row's 16-byte chunks,
+// at most 64), 64 / W rows per wave; dg of dropped assignments stays 0.
+template <typename TA, int W>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(const TA *__restrict__ dy, const TA *__restrict__ y_perm,
                                                        const float *__restrict__ gates,
                                                        const int32_t *__restrict__ src_of,
@@ -34,15 +35,16 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const TA *__restrict__ dy
                                                        int dh, long ld_dy, TA *__restrict__ dY,
                                                        float *__restrict__ dg) {
   constexpr int EPC = 16 / sizeof(TA);
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (r >= offsets[E]) return;
+  const int r = (blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / W) + (threadIdx.x & 63) / W;
+  const int lane = threadIdx.x & (W - 1);
+  if (r >= offsets[E]) return;  // whole groups of W lanes: the sum below stays inside a group
   const int a = src_of[r], t = a / K, h = topk_idx[a] / Eh;
   const float g = gates[a];
   const u32x4 *s = (const u32x4 *)(dy + (size_t)t * ld_dy + (size_t)h * dh);
   const u32x4 *yp = (const u32x4 *)(y_perm + (size_t)r * dh);
   u32x4 *o = (u32x4 *)(dY + (size_t)r * dh);
   float dot = 0.f;
-  for (int c = lane; c < dh / EPC; c += 64) {
+  for (int c = lane; c < dh / EPC; c += W) {
     const u32x4 vs = s[c], vy = yp[c];
     u32x4 vo;
     if constexpr (sizeof(TA) == 2) {
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const TA *__restrict__ dy
     }
     o[c] = vo;
   }
-  dot = group_sum_fixed(dot, WAVE);
+  dot = group_sum_fixed(dot, W);
   if (lane == 0) dg[a] = dot;
 }
 
@@ -705,15 +707,26 @@ int launch_bwd_rows(const Shape &s, const void *dy, long ld_dy, const void *y_pe
                      tk);
   if (int rc = launch_status("zero gate gradients")) return rc;
   if (s.R_max == 0) return 0;
-  const unsigned grid = (unsigned)((s.R_max + 3) / 4);
-  if (s.act_f32)
-    hipLaunchKernelGGL((bwd_rows_kernel<float>), dim3(grid), dim3(256), 0, st, (const float *)dy,
-                       (const float *)y_perm, gates, src_of, topk_idx, offsets, s.E, s.Eh, s.K, s.dh, ld_dy,
-                       (float *)dY, dg);
-  else
-    hipLaunchKernelGGL((bwd_rows_kernel<uint16_t>), dim3(grid), dim3(256), 0, st, (const uint16_t *)dy,
-                       (const uint16_t *)y_perm, gates, src_of, topk_idx, offsets, s.E, s.Eh, s.K, s.dh, ld_dy,
-                       (uint16_t *)dY, dg);
+  // W lanes per row: the row's 16-byte chunks (d_head is a multiple of 64), at most 64
+  const int chunks = s.dh * (s.act_f32 ? 4 : 2) / 16;
+  const int W = chunks >= 64 ? 64 : chunks >= 32 ? 32 : chunks >= 16 ? 16 : 8;
+  const long waves = (s.R_max * W + 63) / 64;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  auto go = [&](auto kern, auto *typed) {
+    using T = std::remove_pointer_t<decltype(typed)>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const T *)dy, (const T *)y_perm, gates, src_of, topk_idx,
+                       offsets, s.E, s.Eh, s.K, s.dh, ld_dy, (T *)dY, dg);
+  };
+  if (s.act_f32) {
+    if (W == 64) go(bwd_rows_kernel<float, 64>, (float *)nullptr);
+    else if (W == 32) go(bwd_rows_kernel<float, 32>, (float *)nullptr);
+    else go(bwd_rows_kernel<float, 16>, (float *)nullptr);  // f32 rows hold at least 16 chunks
+  } else {
+    if (W == 64) go(bwd_rows_kernel<uint16_t, 64>, (uint16_t *)nullptr);
+    else if (W == 32) go(bwd_rows_kernel<uint16_t, 32>, (uint16_t *)nullptr);
+    else if (W == 16) go(bwd_rows_kernel<uint16_t, 16>, (uint16_t *)nullptr);
+    else go(bwd_rows_kernel<uint16_t, 8>, (uint16_t *)nullptr);
+  }
   return launch_status("backward rows");
 }
 
