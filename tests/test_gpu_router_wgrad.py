@@ -17,7 +17,8 @@ float32 meets it (the float32 floor), while dl cut to two bf16 planes
 dl, fails the GPU test.
 
 The shapes cover the three expert-tile widths (16, 32, 64 experts; 100 experts
-per head padded to two 64-expert tiles), two heads, renormalised gates, the
+per head padded to two 64-expert tiles), two heads (with one and with two
+expert tiles per head), renormalised gates, the
 affinity keep rule, ragged token counts with several token ranges (the last
 one partial, so its final chunk is masked) and head widths of 320 and 576
 columns (a partial 256-column tile).
@@ -44,6 +45,9 @@ CFGS = [
               drop=0, act_dtype=1, router_dtype=1, tag=303),
     MoEConfig("rw_e100_dh576_affinity", T=2100, d_model=576, n_heads=1, d_head=576, n_experts=100, top_k=6,
               d_ff=64, act=1, drop=2, keep_num=9, keep_den=10, act_dtype=1, router_dtype=1, tag=304),
+    # two heads of 80 experts: each head padded to 128, two 64-expert tiles per head
+    MoEConfig("rw_h2_e80", T=1500, d_model=256, n_heads=2, d_head=128, n_experts=160, top_k=2, d_ff=64, act=1,
+              drop=0, act_dtype=1, router_dtype=1, tag=305),
 ]
 
 
