@@ -10,15 +10,27 @@ already resident in HBM.  K steps run back to back on one stream between two
 device synchronisations; value = T * K / elapsed.
 
 The layer runs without an x_perm buffer: dispatch moves indices only and the
-expert FFN gathers each row from x inside its GEMM operand loads.  Per-stage
-times come from HIP events recorded on the stream the kernels run on, around
-separate calls of moe_route / moe_dispatch / moe_expert_ffn_gather /
-moe_combine on the same data.  The roofline object is for the grouped GEMM of
-the expert FFN (its gate/up launches with the SwiGLU epilogue, then its down
-launches), the dominant kernel: achieved = algorithmic FLOPs of the kept rows
-and shared experts / measured stage time, against the bf16 dense MFMA peak.
-The CPU baseline is the float64 numpy oracle on a bounded sample of the same
-workload (routing of every token, expert FFN and combine for a token sample).
+expert FFN gathers each row from x inside its GEMM operand loads.
+
+Per-stage times: separate calls of moe_route / moe_dispatch /
+moe_expert_ffn_gather / moe_combine on the same data, timed with HIP events
+recorded on the stream the kernels run on, two ways:
+  cold   each call preceded (outside its events) by a read-modify-write of a
+         1 GiB scratch buffer, which evicts the L2 caches and the 256 MiB
+         Infinity Cache; the GPU is still busy with that write when the call
+         is issued, so the events bracket device time only.  The headline
+         fractions use these.
+  warm   the same call captured `reps` times in one HIP graph and replayed:
+         back-to-back device time with whatever the caches kept.
+The roofline object is for the grouped GEMM of the expert FFN (its gate/up
+launches with the SwiGLU epilogue, then its down launches), the dominant
+kernel: achieved = algorithmic FLOPs of the kept rows and shared experts /
+cold stage time, against the bf16 dense MFMA peak.  Beside the headline
+workload (--config, default the coarse 4096-token one) the other bf16
+workloads (--also, default c2,c3,c4) are measured the same way and reported
+under "configs".  The CPU baseline is the float64 numpy oracle on a bounded
+sample of the headline workload (routing of every token, expert FFN and
+combine for a token sample).
 """
 import argparse
 import json
@@ -53,6 +65,8 @@ def parse():
     ap.add_argument("--json-out", default="", help="also append the JSON line to this file")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-graph", action="store_true", help="skip timing the step as a captured HIP graph")
+    ap.add_argument("--also", default="c2,c3,c4",
+                    help="further workloads measured in the same run and reported under 'configs' ('' for none)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB (a known-size "
                          "reference for the HBM byte counters of a profiler run)")
@@ -156,6 +170,17 @@ def cpu_threads():
     return int(n)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, inp, sample, target_s=12.0):
     """The oracle on a token sample sized for about `target_s` seconds (at most all T tokens).
 
@@ -183,26 +208,77 @@ def cpu_baseline(cfg, inp, sample, target_s=12.0):
         if want > n2:
             n, dt = want, run(want)
     return {"value": n / dt, "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"float64 numpy oracle: routing + keep rule of all {cfg.T} tokens, expert FFN and "
                       f"combine for {n} evenly spaced tokens; {dt:.1f} s wall"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
-              file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import routing_dispatch_expert_router_amd as moe
-    from moe_inputs import CONFIGS, VARIANTS, generate
-
+def workload(name):
+    from moe_inputs import CONFIGS, VARIANTS
     short = {"c0": CONFIGS[0], "c1": CONFIGS[1], "c2": CONFIGS[2], "c3": CONFIGS[3], "c4": CONFIGS[4],
              "c2ec": VARIANTS[0], "c2v3": VARIANTS[1]}
-    cfg = short[args.config] if args.config in short else next(c for c in CONFIGS + VARIANTS if c.name == args.config)
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev_name = torch.cuda.get_device_properties(0).name
-    log(f"[bench] {cfg.name} on {dev_name}: generating inputs")
+    return short[name] if name in short else next(c for c in CONFIGS + VARIANTS if c.name == name)
+
+
+class Evict:
+    """A 1 GiB device buffer; touch() reads and writes all of it, which evicts the L2 caches and the
+    256 MiB Infinity Cache (and keeps the GPU busy for a few hundred microseconds)."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
+
+    def touch(self):
+        self.buf.add_(1)
+
+
+def time_stage(fn, stream, evict, reps):
+    """Device time of one call of fn, in seconds: (cold, warm).
+
+    cold: mean over `reps` calls, each after evict.touch() and bracketed by its own events (the
+    eviction is still running when the call is issued, so the events see device time only).
+    warm: `reps` calls captured in one HIP graph, replayed between two events, per call."""
+    import torch
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        evict.touch()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    cold = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e-3
+    # warm: a graph of reps calls on a side stream (capture needs a non-default stream)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(reps):
+                fn()
+    stream.wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    warm = a.elapsed_time(b) / reps * 1e-3
+    del g
+    return cold, warm
+
+
+def measure(cfg, args, evict, headline):
+    """Step time, per-stage times and roofline fractions of one workload (dict)."""
+    import torch
+    import routing_dispatch_expert_router_amd as moe
+    from moe_inputs import generate
+    log(f"[bench] {cfg.name}: generating inputs")
     t0 = time.perf_counter()
     inp = generate(cfg)
     log(f"[bench] inputs in {time.perf_counter() - t0:.1f} s; moving to HBM")
@@ -245,22 +321,23 @@ def main():
         step()
     torch.cuda.synchronize()
     R = int(io["offsets"][E].item())
-    log(f"[bench] R = {R} kept rows; timing {args.steps} steps")
+    steps = args.steps if headline else max(5, min(args.steps, 20))
+    log(f"[bench] R = {R} kept rows; timing {steps} steps")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {ms_step:.3f} ms/step (events), {wall / args.steps * 1e3:.3f} ms/step (wall)")
+    ms_step = ev0.elapsed_time(ev1) / steps
+    log(f"[bench] {ms_step:.3f} ms/step (events), {wall / steps * 1e3:.3f} ms/step (wall)")
 
     # ---- the same step captured once in a HIP graph and replayed (no per-launch host work)
     graph = None
-    if not args.no_graph:
+    if headline and not args.no_graph:
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -274,51 +351,102 @@ def main():
         torch.cuda.synchronize()
         ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ga.record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             g.replay()
         gb.record(stream)
         torch.cuda.synchronize()
-        gms = ga.elapsed_time(gb) / args.steps
-        graph = {"ms_per_step": gms, "tokens_per_s": T / (gms * 1e-3), "steps": args.steps}
+        gms = ga.elapsed_time(gb) / steps
+        graph = {"ms_per_step": gms, "tokens_per_s": T / (gms * 1e-3), "steps": steps}
         log(f"[bench] graph replay {gms:.3f} ms/step")
         del g
 
-    # ---- per-stage times: the four C-ABI calls on the same data, HIP events on this stream
+    # ---- per-stage times: the four C-ABI calls on the same data
     xin = io["z"] if cfg.latent_proj else x
-    reps = max(5, min(50, args.steps))
-
-    def timed(fn):
-        for _ in range(2):
-            fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e-3  # seconds
-
+    reps = 20
     st = {}
-    st["route"] = timed(lambda: moe.moe_route(cfg, xin, W["w_router"], W["router_bias"], None,
-                                              moe.MOE_LOGITS_COMPUTE, io["topk_idx"], io["topk_w"], None, ws,
-                                              sel_bias=W["sel_bias"], seq_loss=io["seq_loss"]))
-    st["dispatch"] = timed(lambda: moe.moe_dispatch(cfg, io["topk_idx"], io["topk_w"], None, io["demand"],
-                                                    io["counts"], io["offsets"], io["row_of"], io["src_of"],
-                                                    None, ws))
-    st["expert_ffn"] = timed(lambda: moe.moe_expert_ffn_gather(cfg, xin, io["src_of"], io["offsets"], W["w1"],
-                                                               W["w3"], W["w2"], io["y_perm"],
-                                                               x if cfg.n_shared else None, W["ws1"], W["ws3"],
-                                                               W["ws2"], io["shared_out"], ws))
-    st["combine"] = timed(lambda: moe.moe_combine(cfg, io["y_perm"], io["row_of"], io["topk_w"],
-                                                  x if (cfg.residual and not cfg.latent_proj) else None,
-                                                  io["shared_out"], io["o"] if cfg.latent_proj else y))
+    st["route"] = time_stage(lambda: moe.moe_route(cfg, xin, W["w_router"], W["router_bias"], None,
+                                                   moe.MOE_LOGITS_COMPUTE, io["topk_idx"], io["topk_w"], None, ws,
+                                                   sel_bias=W["sel_bias"], seq_loss=io["seq_loss"]),
+                             stream, evict, reps)
+    st["dispatch"] = time_stage(lambda: moe.moe_dispatch(cfg, io["topk_idx"], io["topk_w"], None, io["demand"],
+                                                         io["counts"], io["offsets"], io["row_of"], io["src_of"],
+                                                         None, ws), stream, evict, reps)
+    st["expert_ffn"] = time_stage(lambda: moe.moe_expert_ffn_gather(cfg, xin, io["src_of"], io["offsets"],
+                                                                    W["w1"], W["w3"], W["w2"], io["y_perm"],
+                                                                    x if cfg.n_shared else None, W["ws1"],
+                                                                    W["ws3"], W["ws2"], io["shared_out"], ws),
+                                  stream, evict, min(reps, 10))
+    st["combine"] = time_stage(lambda: moe.moe_combine(cfg, io["y_perm"], io["row_of"], io["topk_w"],
+                                                       x if (cfg.residual and not cfg.latent_proj) else None,
+                                                       io["shared_out"], io["o"] if cfg.latent_proj else y),
+                               stream, evict, reps)
     if W["sel_bias"] is not None:
         # one balancing-bias update from this batch's loads, on a scratch copy of the bias
         b_tmp = W["sel_bias"].clone()
-        st["sel_bias_update"] = timed(lambda: moe.moe_sel_bias_update(cfg, io["demand"], b_tmp, 0.001))
+        st["sel_bias_update"] = time_stage(lambda: moe.moe_sel_bias_update(cfg, io["demand"], b_tmp, 0.001),
+                                           stream, evict, reps)
     bwd = None
-    if not args.no_backward and moe.moe_backward_workspace_bytes(cfg) > 0:
+    if headline and not args.no_backward and moe.moe_backward_workspace_bytes(cfg) > 0:
         bwd = time_backward(cfg, moe, W, x, inp, args, stream)
+    alg = algorithmic(cfg, R)
+    peak = PEAK_F32_TFLOPS if cfg.act_dtype == 0 else PEAK_BF16_TFLOPS
+    stages = {}
+    for k, nb in (("route", "route_bytes"), ("dispatch", "dispatch_bytes"), ("combine", "combine_bytes")):
+        cold, warm = st[k]
+        stages[k] = {"us": cold * 1e6, "us_warm": warm * 1e6, "GBs": alg[nb] / cold / 1e9,
+                     "hbm_frac": alg[nb] / cold / 1e9 / PEAK_HBM_GBS,
+                     "hbm_frac_warm": alg[nb] / warm / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": alg[nb]}
+    cold, warm = st["expert_ffn"]
+    ffn_tf = alg["ffn_flops"] / cold / 1e12
+    stages["expert_ffn"] = {"us": cold * 1e6, "us_warm": warm * 1e6, "TFLOPs": ffn_tf, "mfma_frac": ffn_tf / peak,
+                            "mfma_frac_warm": alg["ffn_flops"] / warm / 1e12 / peak,
+                            "algorithmic_flops": alg["ffn_flops"]}
+    if "sel_bias_update" in st:
+        stages["sel_bias_update"] = {"us": st["sel_bias_update"][0] * 1e6, "us_warm": st["sel_bias_update"][1] * 1e6}
+    for k, v in stages.items():
+        log(f"[bench]   {k:10s} " + "  ".join(f"{a}={b:.4g}" for a, b in v.items()))
+    res = {"workload": cfg.name, "T": T, "kept_rows": R, "ms_per_step": ms_step, "tokens_per_s": T / (ms_step * 1e-3),
+           "stages": stages, "graph": graph, "backward": bwd,
+           "roofline": {"kernel": "grouped_gemm_kernel, expert FFN (gate/up and down launches, rows gathered from x)",
+                        "bound": "mfma", "achieved": ffn_tf, "peak": peak, "unit": "TFLOP/s", "frac": ffn_tf / peak,
+                        "frac_warm": alg["ffn_flops"] / warm / 1e12 / peak,
+                        "traffic": measured_traffic(cfg),
+                        "traffic_unit": "HBM bytes per expert-FFN call (all its launches)",
+                        "algorithmic_flops": alg["ffn_flops"], "timing": "cold (L2 and Infinity Cache evicted)"}}
+    if bwd is not None:
+        bwd["fwd_bwd_tokens_per_s"] = T / ((ms_step + bwd["ms_per_step"]) * 1e-3)
+    res["_inp"] = inp
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import routing_dispatch_expert_router_amd  # noqa: F401  (fails loudly if libmoe.so is missing)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev_name = torch.cuda.get_device_properties(0).name
+    cfg = workload(args.config)
+    evict = Evict()
+    log(f"[bench] {cfg.name} on {dev_name}")
+    head = measure(cfg, args, evict, headline=True)
+    inp = head.pop("_inp")
+    others = {}
+    for name in [n for n in args.also.split(",") if n.strip()]:
+        oc = workload(name.strip())
+        if oc.name == cfg.name:
+            continue
+        torch.cuda.empty_cache()
+        r = measure(oc, args, evict, headline=False)
+        r.pop("_inp")
+        for k in ("graph", "backward"):
+            r.pop(k)
+        others[oc.name] = r
+        torch.cuda.empty_cache()
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -327,46 +455,25 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    alg = algorithmic(cfg, R)
-    peak = PEAK_F32_TFLOPS if cfg.act_dtype == 0 else PEAK_BF16_TFLOPS
-    ffn_tf = alg["ffn_flops"] / st["expert_ffn"] / 1e12
-    stages = {
-        "route": {"us": st["route"] * 1e6, "GBs": alg["route_bytes"] / st["route"] / 1e9},
-        "dispatch": {"us": st["dispatch"] * 1e6, "GBs": alg["dispatch_bytes"] / st["dispatch"] / 1e9},
-        "expert_ffn": {"us": st["expert_ffn"] * 1e6, "TFLOPs": ffn_tf},
-        "combine": {"us": st["combine"] * 1e6, "GBs": alg["combine_bytes"] / st["combine"] / 1e9},
-    }
-    for k in ("route", "dispatch", "combine"):
-        stages[k]["hbm_frac"] = stages[k]["GBs"] / PEAK_HBM_GBS
-    if "sel_bias_update" in st:
-        stages["sel_bias_update"] = {"us": st["sel_bias_update"] * 1e6}
-    stages["expert_ffn"]["mfma_frac"] = ffn_tf / peak
-    for k, v in stages.items():
-        log(f"[bench]   {k:10s} " + "  ".join(f"{a}={b:.4g}" for a, b in v.items()))
-
-    value = T / (ms_step * 1e-3)
+    T, E = cfg.T, cfg.n_experts
     line = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32" if cfg.act_dtype == 0 else "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "d_model": cfg.d_model, "n_experts": E, "top_k": cfg.top_k,
-                   "n_heads": cfg.n_heads, "d_ff": cfg.d_ff, "n_shared": cfg.n_shared, "kept_rows": R,
+                   "n_heads": cfg.n_heads, "d_ff": cfg.d_ff, "n_shared": cfg.n_shared, "kept_rows": head["kept_rows"],
                    "act": "swiglu" if cfg.act == 1 else "relu",
                    "drop": "expert_choice" if cfg.route_mode == 1 else ["none", "capacity", "affinity"][cfg.drop],
                    "capacity": cfg.capacity if cfg.drop == 1 else None,
                    "selection_bias": inp.sel_bias is not None, "seq_len": cfg.seq_len or None,
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": "grouped_gemm_kernel, expert FFN (gate/up and down launches, rows gathered from x)",
-                     "bound": "mfma", "achieved": ffn_tf, "peak": peak, "unit": "TFLOP/s", "frac": ffn_tf / peak,
-                     "traffic": measured_traffic(cfg), "traffic_unit": "HBM bytes per expert-FFN call (all its launches)",
-                     "algorithmic_flops": alg["ffn_flops"]},
-        "stages": stages,
-        "backward": bwd,
-        "graph": graph,
+        "roofline": head["roofline"],
+        "stages": head["stages"],
+        "backward": head["backward"],
+        "graph": head["graph"],
+        "configs": others,
         "device": dev_name,
     }
-    if bwd is not None:
-        bwd["fwd_bwd_tokens_per_s"] = T / ((ms_step + bwd["ms_per_step"]) * 1e-3)
     if not args.no_cpu:
         sample = args.cpu_tokens or {"c0": 256, "c1": 384, "c2": 1024, "c3": 96, "c4": 2048, "c2ec": 1024,
                                      "c2v3": 1024}.get(args.config, 384)

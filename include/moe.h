@@ -186,15 +186,28 @@ int moe_check_config(const moe_config *cfg);
  *   w_router  [E, d_head] router_dtype; head h uses rows [h*E_h, (h+1)*E_h)
  *             and reads columns [h*d_head, (h+1)*d_head) of x
  *   bias      [E] float32 or NULL
- *   logits    [T, E] float32, per `mode`
+ *   logits    [T, E] float32, per `mode` (a moe_logits_mode)
  *   topk_idx  [T, H*top_k] out: global expert ids (h*E_h + local); the k
  *             entries of a head are ordered by score descending, lower expert
  *             index first on equal scores (-0.0 and +0.0 are equal)
  *   topk_w    [T, H*top_k] out: softmax probability of each chosen expert over
- *             its head's E_h experts, divided by the chosen sum if cfg->renorm
+ *             its head's E_h experts, divided by the chosen sum if cfg->renorm;
+ *             evaluated in float64 and rounded to float32 once
  *   aux_loss  [1] float32 out or NULL: sum_e m_e * c_e / T with m_e the mean
  *             probability and c_e the number of choices of e; H == 1 only
  *             (MOE_ERR_UNSUPPORTED otherwise)
+ * Expert choice (cfg->route_mode): topk_idx/topk_w are [T, E] with slot j =
+ * expert j and the gate p_{t,j}; the experts choose in moe_dispatch.
+ * Scores must be finite; non-finite scores give unspecified routing.
+ * One kernel launch (two with aux_loss).
+ */
+int moe_route(const moe_config *cfg, const void *x, const void *w_router, const float *bias,
+              float *logits, int mode, int32_t *topk_idx, float *topk_w,
+              float *aux_loss, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_route_ex -- moe_route with the routing variants' extra inputs and outputs.
+ * Arguments as for moe_route, plus:
  *   sel_bias  [E] float32 or NULL: balancing bias ["MoE技术演进", "DeepSeek-V3"
  *             item 1].  The top-k (and group scores) are taken on the float32
  *             keys p + b instead of the scores; the gate of a chosen expert is
@@ -205,13 +218,11 @@ int moe_check_config(const moe_config *cfg);
  *             f_e = (choices of e in the run) / seq_len and P_e the mean
  *             probability of e over the run ["MoE技术演进", "DeepSeek-V3"
  *             item 4: the sequence-wise balance loss is alpha times this]
- * Expert choice (cfg->route_mode): topk_idx/topk_w are [T, E] with slot j =
- * expert j and the gate p_{t,j}; the experts choose in moe_dispatch.
- * Scores must be finite; non-finite scores give unspecified routing.
+ * moe_route(...) is moe_route_ex with sel_bias = seq_loss = NULL.
  */
-int moe_route(const moe_config *cfg, const void *x, const void *w_router, const float *bias,
-              const float *sel_bias, float *logits, int mode, int32_t *topk_idx, float *topk_w,
-              float *aux_loss, float *seq_loss, void *ws, size_t ws_bytes, hipStream_t stream);
+int moe_route_ex(const moe_config *cfg, const void *x, const void *w_router, const float *bias,
+                 const float *sel_bias, float *logits, int mode, int32_t *topk_idx, float *topk_w,
+                 float *aux_loss, float *seq_loss, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * moe_sel_bias_update -- one step of the balancing-bias update

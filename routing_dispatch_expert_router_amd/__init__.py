@@ -40,7 +40,7 @@ _OPTIONAL_FIELDS = {"route_mode", "sel_bias_gate", "seq_len"}
 
 # exported symbols, as declared in include/moe.h
 SYMBOLS = ["moe_workspace_bytes", "moe_rows_upper_bound", "moe_status_str", "moe_check_config",
-           "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd",
+           "moe_route", "moe_route_ex", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd",
            "moe_sel_bias_update", "moe_backward_workspace_bytes", "moe_transpose_weights", "moe_layer_bwd"]
 
 
@@ -89,7 +89,8 @@ def _load():
         "moe_rows_upper_bound": (ctypes.c_int64, [Z]),
         "moe_status_str": (ctypes.c_char_p, [I]),
         "moe_check_config": (I, [Z]),
-        "moe_route": (I, [Z, P, P, P, P, P, I, P, P, P, P, P, S, P]),
+        "moe_route": (I, [Z, P, P, P, P, I, P, P, P, P, S, P]),
+        "moe_route_ex": (I, [Z, P, P, P, P, P, I, P, P, P, P, P, S, P]),
         "moe_sel_bias_update": (I, [Z, P, P, ctypes.c_float, P]),
         "moe_dispatch": (I, [Z, P, P, P, P, P, P, P, P, P, P, S, P]),
         "moe_expert_ffn": (I, [Z, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
@@ -191,10 +192,22 @@ def _nbytes(ws):
 
 def moe_route(cfg, x, w_router, bias, logits, mode, topk_idx, topk_w, aux_loss, ws, stream=None, sel_bias=None,
               seq_loss=None):
+    """moe_route; with a selection bias or a sequence statistic, moe_route_ex."""
+    if sel_bias is not None or seq_loss is not None:
+        return moe_route_ex(cfg, x, w_router, bias, sel_bias, logits, mode, topk_idx, topk_w, aux_loss, seq_loss, ws,
+                            stream)
     c = _c(cfg)
-    return _check(_lib.moe_route(ctypes.byref(c), _p(x), _p(w_router), _p(bias), _p(sel_bias), _p(logits),
-                                 int(mode), _p(topk_idx), _p(topk_w), _p(aux_loss), _p(seq_loss), _p(ws),
-                                 _nbytes(ws), _stream(stream)), "moe_route")
+    return _check(_lib.moe_route(ctypes.byref(c), _p(x), _p(w_router), _p(bias), _p(logits), int(mode),
+                                 _p(topk_idx), _p(topk_w), _p(aux_loss), _p(ws), _nbytes(ws), _stream(stream)),
+                  "moe_route")
+
+
+def moe_route_ex(cfg, x, w_router, bias, sel_bias, logits, mode, topk_idx, topk_w, aux_loss, seq_loss, ws,
+                 stream=None):
+    c = _c(cfg)
+    return _check(_lib.moe_route_ex(ctypes.byref(c), _p(x), _p(w_router), _p(bias), _p(sel_bias), _p(logits),
+                                    int(mode), _p(topk_idx), _p(topk_w), _p(aux_loss), _p(seq_loss), _p(ws),
+                                    _nbytes(ws), _stream(stream)), "moe_route_ex")
 
 
 def moe_sel_bias_update(cfg, load, sel_bias, gamma, stream=None):

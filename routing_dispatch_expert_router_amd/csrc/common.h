@@ -56,24 +56,6 @@ __device__ __forceinline__ f32x4 mma16(const u32x4 &a, const u32x4 &b, f32x4 acc
   return acc;
 }
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// One 32x32 output block.  Lane l holds A row (l % 32) and B column (l % 32)
-// and one 16-byte k-slot (8 bf16 or 4 f32); lanes 0-31 and 32-63 hold two
-// different slots, so one call contracts 32 bytes of k per row.
-// Result layout: acc[q] = C[8*(q/4) + 4*(l/32) + (q%4)][l % 32].
-__device__ __forceinline__ f32x16 mma32(const u32x4 &a, const u32x4 &b, f32x16 acc, uint16_t) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
-                                                 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mma32(const u32x4 &a, const u32x4 &b, f32x16 acc, float) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[0]), __uint_as_float(b[0]), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[1]), __uint_as_float(b[1]), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[2]), __uint_as_float(b[2]), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[3]), __uint_as_float(b[3]), acc, 0, 0, 0);
-  return acc;
-}
-
 // ---------------------------------------------------------------- gfx950 memory ops
 // 16 bytes per lane straight from global memory into LDS (global_load_lds_dwordx4):
 // lane l's data lands at lds_wave_base + 16*l, so lds_wave_base must be

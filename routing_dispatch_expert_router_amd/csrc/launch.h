@@ -29,16 +29,22 @@ struct Shape {
 };
 
 // ---------------------------------------------------------------- route
+// route_kernel's launch: grid nbx x H blocks of tb tokens (wt token groups of
+// mw*16 tokens, each split over wk waves along d_head); L lanes per token in
+// the selection (Lg per expert group with group-limited routing), epl experts
+// per lane; st: scores from LDS-staged chunks, the waves splitting the experts
 struct RouteGeom {
-  int Epad, nf, nplanes, mw, tb, ksplit, kchunk_per_split;
-  int L, epl, sel_blocks;
+  int nf, nplanes, mw, wt, wk, tb, nbx;
+  int L, Lg, epl, st;
 };
 RouteGeom route_geometry(const Shape &s);
 bool route_supported(const Shape &s);
 size_t route_ws_bytes(const Shape &s);
+// hist_out: [nbx][E] per-block choice counts (blocks of route_geometry(s).tb
+// tokens), or NULL
 int launch_route(const Shape &s, const void *x, const void *w_router, const float *bias, const float *sel_bias,
                  float *logits, int mode, int32_t *topk_idx, float *topk_w, float *aux_loss, float *seq_loss,
-                 void *ws, hipStream_t st);
+                 void *ws, hipStream_t st, int32_t *hist_out = nullptr);
 int launch_sel_bias_update(const Shape &s, const int32_t *load, float *sel_bias, float gamma, hipStream_t st);
 
 // ---------------------------------------------------------------- dispatch

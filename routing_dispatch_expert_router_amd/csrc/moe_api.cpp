@@ -290,9 +290,15 @@ int moe_check_config(const moe_config *cfg) {
   return make_shape(cfg, &s);
 }
 
-int moe_route(const moe_config *cfg, const void *x, const void *w_router, const float *bias,
-              const float *sel_bias, float *logits, int mode, int32_t *topk_idx, float *topk_w,
-              float *aux_loss, float *seq_loss, void *ws, size_t ws_bytes, hipStream_t stream) {
+int moe_route(const moe_config *cfg, const void *x, const void *w_router, const float *bias, float *logits, int mode,
+              int32_t *topk_idx, float *topk_w, float *aux_loss, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_route_ex(cfg, x, w_router, bias, nullptr, logits, mode, topk_idx, topk_w, aux_loss, nullptr, ws,
+                      ws_bytes, stream);
+}
+
+int moe_route_ex(const moe_config *cfg, const void *x, const void *w_router, const float *bias,
+                 const float *sel_bias, float *logits, int mode, int32_t *topk_idx, float *topk_w,
+                 float *aux_loss, float *seq_loss, void *ws, size_t ws_bytes, hipStream_t stream) {
   Shape s;
   int rc = make_shape(cfg, &s);
   if (rc) return rc;

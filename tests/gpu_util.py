@@ -68,18 +68,62 @@ def weights_dev(cfg, inp):
 
 
 def routing_margin(cfg, l32):
-    """Per token, the smallest gap between a chosen and an unchosen score (per head), on the oracle's scores."""
+    """Per token, the smallest gap between scores that decides its choices (per head), on the oracle's
+    scores: the chosen experts' order and the gap to the best unchosen one, within the groups the token
+    keeps when routing is group-limited, and the gap between the last kept and the best dropped group."""
     T, H, Eh, k = cfg.T, cfg.n_heads, cfg.e_per_head, cfg.top_k
     gap = np.full(T, np.inf)
     for h in range(H):
-        s = np.sort(l32[:, h * Eh:(h + 1) * Eh].astype(np.float64), axis=1)[:, ::-1]
-        if k < Eh:
-            gap = np.minimum(gap, s[:, k - 1] - s[:, k])
-        if k > 1:
-            gap = np.minimum(gap, np.min(s[:, :k - 1] - s[:, 1:k], axis=1))
+        lh = l32[:, h * Eh:(h + 1) * Eh].astype(np.float64)
         if cfg.n_groups:
-            g = np.sort(l32[:, h * Eh:(h + 1) * Eh].astype(np.float64).reshape(T, cfg.n_groups, -1).max(axis=2),
-                        axis=1)[:, ::-1]
+            gs = lh.reshape(T, cfg.n_groups, -1).max(axis=2)
+            g = np.sort(gs, axis=1)[:, ::-1]
             if cfg.topk_groups < cfg.n_groups:
                 gap = np.minimum(gap, g[:, cfg.topk_groups - 1] - g[:, cfg.topk_groups])
+            keep = np.argsort(-gs, axis=1, kind="stable")[:, :cfg.topk_groups]
+            allowed = np.zeros((T, cfg.n_groups), bool)
+            allowed[np.arange(T)[:, None], keep] = True
+            lh = np.where(np.repeat(allowed, Eh // cfg.n_groups, axis=1), lh, -np.inf)
+        s = np.sort(lh, axis=1)[:, ::-1]
+        if k < Eh and np.all(np.isfinite(s[:, k])):
+            gap = np.minimum(gap, s[:, k - 1] - s[:, k])
+        elif k < Eh:
+            fin = np.isfinite(s[:, k])
+            gap[fin] = np.minimum(gap[fin], (s[:, k - 1] - s[:, k])[fin])
+        if k > 1:
+            gap = np.minimum(gap, np.min(s[:, :k - 1] - s[:, 1:k], axis=1))
     return gap
+
+
+def check_keep(cfg, io, out):
+    """The GPU's keep rule and permutation against the oracle's.
+
+    (1) The oracle's keep rule applied to the GPU's own routing and float32
+        gates gives exactly the GPU's demand, counts, offsets, row_of and
+        src_of: the kernels implement the rule bit for bit.
+    (2) Where the GPU's kept set differs from the oracle's own (the two sides'
+        gates can differ in the last bits), the assignment's oracle gate lies
+        within 4 float32 ulp of its expert's keep threshold, the keep-th
+        largest oracle gate of that expert: a near-tie, not a rule error.
+    Returns the flat indices of the assignments whose kept state differs."""
+    idx = io["topk_idx"].cpu().numpy()
+    w32 = io["topk_w"].cpu().numpy().astype(np.float32)
+    own = oracle.keep(cfg, idx, w32)
+    for k in ("demand", "counts", "offsets"):
+        assert np.array_equal(io[k].cpu().numpy(), own[k]), k
+    R = int(own["offsets"][-1])
+    row_of = io["row_of"].cpu().numpy()
+    assert np.array_equal(row_of, own["row_of"])
+    assert np.array_equal(io["src_of"].cpu().numpy()[:R], own["src_of"])
+    diff = np.nonzero((row_of.reshape(-1) >= 0) != (out["row_of"].reshape(-1) >= 0))[0]
+    if len(diff):
+        e_flat = np.asarray(out["topk_idx"]).reshape(-1)
+        ow = np.asarray(out["topk_w32"], np.float32).reshape(-1)
+        for a in diff:
+            e = e_flat[a]
+            gates = np.sort(ow[e_flat == e])[::-1]
+            keep = int(out["counts"][e])
+            thr = gates[keep - 1] if keep > 0 else gates[0]
+            assert abs(float(ow[a]) - float(thr)) <= 4 * float(np.spacing(np.float32(thr))), \
+                f"assignment {a} (expert {e}) kept differently away from a gate near-tie"
+    return diff

@@ -6,6 +6,8 @@ the oracle with a planted mistake, to show that each plausible mistake is
 caught by at least one of them.
 
 What pins what:
+  router scores  a hand-worked two-head example with a bias (tests/golden):
+                 per-head slices, the bias added once
   softmax        rows sum to 1; p_i/p_j = exp(l_i - l_j); equal logits -> 1/E;
                  scipy.special.softmax (library routine)
   top-k          brute-force subset enumeration with the total-order invariant
@@ -33,6 +35,38 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 def _o():
     import oracle.moe_oracle as m
     return m
+
+
+# ---------------------------------------------------------------- router scores
+def check_router_logits():
+    """The hand-worked two-head example of tests/golden/hand_router_logits.json.
+
+    Checked twice: on router_logits itself, one head slice at a time, and
+    through route(), which must give head h the columns of its own slice of
+    the router input and its own rows of W_r and the bias."""
+    O = _o()
+    with open(os.path.join(GOLDEN, "hand_router_logits.json")) as f:
+        g = json.load(f)
+    z = np.array(g["z"], np.float64)
+    w = np.array(g["w_router"], np.float32)
+    b = np.array(g["bias"], np.float32)
+    want = np.array(g["logits"], np.float32)
+    H, dh, Eh = g["n_heads"], g["d_head"], g["experts_per_head"]
+    for h in range(H):
+        got = O.router_logits(z[:, h * dh:(h + 1) * dh], O.decode(w[h * Eh:(h + 1) * Eh]), b[h * Eh:(h + 1) * Eh])
+        assert got.dtype == np.float32
+        assert np.array_equal(got, want[:, h * Eh:(h + 1) * Eh]), (h, got)
+        nob = O.router_logits(z[:, h * dh:(h + 1) * dh], O.decode(w[h * Eh:(h + 1) * Eh]))
+        assert np.array_equal(nob, np.array(g["logits_no_bias"], np.float32)[:, h * Eh:(h + 1) * Eh])
+    from moe_inputs import MoEConfig
+    cfg = MoEConfig("hand_logits", T=2, d_model=H * dh, n_heads=H, d_head=dh, n_experts=H * Eh, top_k=1,
+                    d_ff=64, act_dtype=0, router_dtype=0)
+    r = O.route(cfg, z, w, b)
+    assert np.array_equal(r["logits"], want)
+    assert r["topk_idx"].tolist() == g["top1_idx"]
+    # -0.0 folds to +0.0: a score that cancels exactly is a +0.0 key
+    zero = O.router_logits(np.array([[1.0, -1.0]]), np.array([[1.0, 1.0]]), np.array([-0.0], np.float32))
+    assert np.signbit(zero).tolist() == [[False]]
 
 
 # ---------------------------------------------------------------- softmax
@@ -365,7 +399,7 @@ def check_capacity_zero_and_xperm():
     assert int(out["counts"].sum()) == cfg.T * K
 
 
-ALL = [check_softmax, check_topk, check_topk_groups, check_hand_example, check_capacity,
+ALL = [check_router_logits, check_softmax, check_topk, check_topk_groups, check_hand_example, check_capacity,
        check_affinity, check_permutation, check_ffn_library, check_dense_special_case,
        check_identical_experts, check_dense_masked, check_shared_concat,
        check_multihead_reductions, check_capacity_zero_and_xperm]

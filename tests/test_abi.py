@@ -23,10 +23,41 @@ def declared():
 
 def test_header_declares_the_five_calls_and_helpers():
     names = declared()
-    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd",
+    for n in ("moe_route", "moe_route_ex", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd",
               "moe_workspace_bytes", "moe_rows_upper_bound", "moe_status_str", "moe_check_config"):
         assert n in names
     assert sorted(moe.SYMBOLS) == names
+
+
+# The five calls of the boundary, with their parameters in the order the
+# specification of the library gives them (names, then the pointer/value kind).
+SPEC = {
+    "moe_route": "cfg x w_router bias logits mode topk_idx topk_w aux_loss ws ws_bytes stream",
+    "moe_dispatch": "cfg topk_idx topk_w x demand counts offsets row_of src_of x_perm ws ws_bytes stream",
+    "moe_expert_ffn": "cfg x_perm offsets w1 w3 w2 y_perm x_shared ws1 ws3 ws2 shared_out ws ws_bytes stream",
+    "moe_combine": "cfg y_perm row_of topk_w residual shared_out y stream",
+    "moe_layer_fwd": "cfg w x y io ws ws_bytes stream",
+}
+
+
+def _prototype(name):
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", src)
+    assert m, name
+    params = [" ".join(p.split()) for p in m.group(1).split(",")]
+    return [re.findall(r"(\w+)\s*$", p)[0] for p in params]
+
+
+def test_boundary_prototypes_keep_the_specified_order():
+    """A C caller written to the boundary's specification passes its pointers positionally: the declared
+    parameter order of the five calls must be exactly the specified one."""
+    for name, spec in SPEC.items():
+        assert _prototype(name) == spec.split(), name
+    # the variants' inputs live in moe_route_ex: moe_route's arguments in order, with sel_bias before logits
+    # and seq_loss after aux_loss
+    assert _prototype("moe_route_ex") == ("cfg x w_router bias sel_bias logits mode topk_idx topk_w aux_loss "
+                                          "seq_loss ws ws_bytes stream").split()
 
 
 def test_library_exports_every_declared_symbol():
@@ -102,23 +133,23 @@ def test_calls_reject_bad_arguments_before_launching():
     c = moe.config_struct(CONFIGS[2])
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
     # null config
-    assert lib.moe_route(None, fake, fake, None, None, None, 0, fake, fake, None, None, fake, 1 << 40, None) == moe.MOE_ERR_ARG
+    assert lib.moe_route(None, fake, fake, None, None, 0, fake, fake, None, fake, 1 << 40, None) == moe.MOE_ERR_ARG
     # missing outputs
-    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, 0, None, fake, None, None, fake, 1 << 40, None) \
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 0, None, fake, None, fake, 1 << 40, None) \
         == moe.MOE_ERR_ARG
     # LOAD mode needs logits
-    assert lib.moe_route(ctypes.byref(c), None, None, None, None, None, 2, fake, fake, None, None, fake, 1 << 40, None) \
+    assert lib.moe_route(ctypes.byref(c), None, None, None, None, 2, fake, fake, None, fake, 1 << 40, None) \
         == moe.MOE_ERR_ARG
     # bad mode
-    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, 5, fake, fake, None, None, fake, 1 << 40, None) \
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 5, fake, fake, None, fake, 1 << 40, None) \
         == moe.MOE_ERR_ARG
     # workspace too small / misaligned
-    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, 0, fake, fake, None, None, fake, 16, None) \
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 0, fake, fake, None, fake, 16, None) \
         == moe.MOE_ERR_WORKSPACE
-    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, 0, fake, fake, None, None, ctypes.c_void_p(0x1001), 1 << 40, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, 0, fake, fake, None, ctypes.c_void_p(0x1001), 1 << 40, None) == moe.MOE_ERR_WORKSPACE
     # aux loss is defined for one head only
     c4 = moe.config_struct(CONFIGS[4])
-    assert lib.moe_route(ctypes.byref(c4), fake, fake, None, None, None, 0, fake, fake, fake, None, fake, 1 << 40, None) \
+    assert lib.moe_route(ctypes.byref(c4), fake, fake, None, None, 0, fake, fake, fake, fake, 1 << 40, None) \
         == moe.MOE_ERR_UNSUPPORTED
     # affinity keep needs the gates
     c3 = moe.config_struct(CONFIGS[3])
@@ -222,11 +253,11 @@ def test_routing_variant_checks():
     assert moe.moe_check_config(CONFIGS[4].with_(seq_len=4096)) == moe.MOE_ERR_UNSUPPORTED
     c = moe.config_struct(base)
     # a sequence statistic needs seq_len; a selection bias is for token choice only
-    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, 0, fake, fake, None, fake, fake, 1 << 40,
-                         None) == moe.MOE_ERR_ARG
+    assert lib.moe_route_ex(ctypes.byref(c), fake, fake, None, None, None, 0, fake, fake, None, fake, fake, 1 << 40,
+                            None) == moe.MOE_ERR_ARG
     ce = moe.config_struct(ec)
-    assert lib.moe_route(ctypes.byref(ce), fake, fake, None, fake, None, 0, fake, fake, None, None, fake, 1 << 40,
-                         None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_ex(ctypes.byref(ce), fake, fake, None, fake, None, 0, fake, fake, None, None, fake, 1 << 40,
+                            None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_sel_bias_update(ctypes.byref(c), None, fake, 0.001, None) == moe.MOE_ERR_ARG
     assert lib.moe_sel_bias_update(ctypes.byref(c), fake, None, 0.001, None) == moe.MOE_ERR_ARG
     assert lib.moe_sel_bias_update(None, fake, fake, 0.001, None) == moe.MOE_ERR_ARG
@@ -278,8 +309,11 @@ def test_calls_reject_misaligned_device_pointers():
 
     v = ctypes.c_void_p
     # route, COMPUTE mode: x, w_router, bias, logits, topk_idx, topk_w, aux_loss
-    both(lambda p: lib.moe_route(ctypes.byref(c), v(p[0]), v(p[1]), v(p[2]), None, v(p[3]), 0, v(p[4]), v(p[5]),
-                                 v(p[6]), None, ws, big, None), 7)
+    both(lambda p: lib.moe_route(ctypes.byref(c), v(p[0]), v(p[1]), v(p[2]), v(p[3]), 0, v(p[4]), v(p[5]),
+                                 v(p[6]), ws, big, None), 7)
+    # route_ex: x, w_router, bias, sel_bias, logits, topk_idx, topk_w, aux_loss (no sequences: seq_loss NULL)
+    both(lambda p: lib.moe_route_ex(ctypes.byref(c), v(p[0]), v(p[1]), v(p[2]), v(p[3]), v(p[4]), 0, v(p[5]),
+                                    v(p[6]), v(p[7]), None, ws, big, None), 8)
     both(lambda p: lib.moe_dispatch(ctypes.byref(c), *[v(q) for q in p], ws, big, None), 9)
     both(lambda p: lib.moe_expert_ffn(ctypes.byref(c), *[v(q) for q in p], ws, big, None), 11)
     both(lambda p: lib.moe_expert_ffn_gather(ctypes.byref(c), *[v(q) for q in p], ws, big, None), 12)

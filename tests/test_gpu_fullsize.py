@@ -14,7 +14,7 @@ import torch
 import oracle
 import routing_dispatch_expert_router_amd as moe
 from moe_inputs import CONFIGS
-from tests.gpu_util import log, dev, f64, tol, weights_dev, routing_margin, cached_inputs
+from tests.gpu_util import log, dev, f64, tol, weights_dev, routing_margin, cached_inputs, check_keep
 
 pytestmark = pytest.mark.gpu
 
@@ -64,13 +64,12 @@ def test_fullsize_layer(cfg):
     R = int(out["offsets"][-1])
     row_of = io["row_of"].cpu().numpy()
     src_of = io["src_of"].cpu().numpy()[:R]
-    if cfg.drop == 2:
-        flips = int(np.sum((row_of >= 0) != (out["row_of"] >= 0)))
-        log(f"  affinity keep-boundary flips: {flips} of {row_of.size}")
-        assert flips <= 8
-        # whatever was kept, the permutation is consistent and expert-contiguous
-        assert np.all(row_of.reshape(-1)[src_of] == np.arange(R))
-    else:
+    # the keep rule on the GPU's own gates, exactly; differences from the
+    # oracle's own keep only at gate near-ties
+    flips = check_keep(cfg, io, out)
+    log(f"  keep decisions that differ from the oracle's: {len(flips)} of {row_of.size}")
+    if cfg.drop != 2:
+        assert len(flips) == 0
         assert np.array_equal(row_of, out["row_of"])
         assert np.array_equal(src_of, out["src_of"])
     # x_perm rows are bitwise copies of their source rows (sample of rows)
@@ -89,9 +88,9 @@ def test_fullsize_layer(cfg):
         assert np.max(np.abs(zg - out["z"][toks])) <= 2e-2 * np.max(np.abs(out["z"][toks]))
     got = f64(y)[toks]
     ref = out["y"]
-    ok = np.ones(len(toks), bool)
-    if cfg.drop == 2:
-        ok = np.all((row_of[toks] >= 0) == (out["row_of"][toks] >= 0), axis=1)
+    # a sampled token with a near-tie keep flip has another correct output; none is expected
+    ok = np.all((row_of[toks] >= 0) == (out["row_of"][toks] >= 0), axis=1)
+    assert ok.sum() >= len(toks) - 1
     err = np.max(np.abs(got[ok] - ref[ok]))
     log(f"  sampled rows: max err {err:.3g}, rel {err / np.max(np.abs(ref)):.3g}")
     assert err <= tol(cfg) * np.max(np.abs(ref))

@@ -20,7 +20,7 @@ import oracle
 import oracle.moe_backward as OB
 import routing_dispatch_expert_router_amd as moe
 from moe_inputs import SMALL_VARIANTS, VARIANTS, generate
-from tests.gpu_util import log, dev, f64, empty_act, i32, f32, cached_inputs, tol, weights_dev
+from tests.gpu_util import log, dev, f64, empty_act, i32, f32, cached_inputs, tol, weights_dev, check_keep
 
 pytestmark = pytest.mark.gpu
 
@@ -132,18 +132,22 @@ def test_variant_layer(cfg):
     out = oracle_out(cfg)
     y, io, _, _ = _layer(cfg, inp, out["logits"])
     idx = io["topk_idx"].cpu().numpy()
-    same = np.all(idx == out["topk_idx"], axis=1)
+    diff = np.nonzero(np.any(idx != out["topk_idx"], axis=1))[0]
     if inp.sel_bias is None:
-        assert np.all(same)
-    keep_same = np.all((io["row_of"].cpu().numpy() >= 0) == (out["row_of"] >= 0), axis=1)
-    ok = same & keep_same
-    log(f"  tokens with the oracle's routing and keep decisions: {int(ok.sum())} of {cfg.T}")
-    assert ok.sum() >= cfg.T - 2
-    if cfg.route_mode == 1:
-        # a token's keep decisions are the experts' choices, which couple tokens: all must agree
-        assert np.all(keep_same)
-    got, ref = f64(y), out["y"]
-    err = np.max(np.abs(got[ok] - ref[ok]))
+        assert len(diff) == 0
+    else:
+        margin = key_margin(cfg, out["p"], inp.sel_bias)
+        log(f"  tokens routed differently: {len(diff)}")
+        assert np.all(margin[diff] < 1e-6), "routing differs at a token whose keys are not a near-tie"
+    # keep rule exact on the GPU's gates; differences from the oracle's own keep only at near-ties
+    if len(diff) == 0:
+        flips = check_keep(cfg, io, out)
+        log(f"  keep decisions that differ from the oracle's: {len(flips)}")
+    # every token against the oracle's output for the GPU's own decisions
+    import oracle.moe_backward as OB
+    kept = io["row_of"].cpu().numpy().reshape(-1) >= 0
+    ref, _ = OB.forward_fixed(cfg, OB.params_of(inp), idx, kept)
+    err = np.max(np.abs(f64(y) - ref))
     log(f"  max err {err:.3g} (rel {err / np.max(np.abs(ref)):.3g})")
     assert err <= tol(cfg) * np.max(np.abs(ref))
     if cfg.seq_len:
@@ -209,7 +213,8 @@ def test_variant_fullsize(cfg):
     row_of = io["row_of"].cpu().numpy()
     if inp.sel_bias is None:
         assert np.array_equal(idx, out["topk_idx"])
-        assert np.array_equal(row_of, out["row_of"])
+        flips = check_keep(cfg, io, out)
+        log(f"  keep decisions that differ from the oracle's: {len(flips)}")
         assert np.array_equal(io["counts"].cpu().numpy(), out["counts"])
     else:
         diff = np.nonzero(np.any(idx != out["topk_idx"], axis=1))[0]

@@ -9,9 +9,23 @@ import pytest
 import oracle.moe_oracle as O
 from tests import oracle_pins as P
 
-_orig = {n: getattr(O, n) for n in ("select_topk", "softmax", "gates", "aux_loss", "keep_capacity",
+_orig = {n: getattr(O, n) for n in ("router_logits", "select_topk", "softmax", "gates", "aux_loss", "keep_capacity",
                                      "keep_affinity", "permutation", "expert_ffn", "silu", "forward",
                                      "route")}
+
+
+def m_logits_no_bias(xr, w_r, bias=None):
+    return _orig["router_logits"](xr, w_r, None)
+
+
+def m_logits_bias_twice(xr, w_r, bias=None):
+    return _orig["router_logits"](xr, w_r, None if bias is None else 2 * np.asarray(bias, np.float64))
+
+
+def m_logits_transposed(xr, w_r, bias=None):
+    # the head's weight block used transposed (it is square in the hand example)
+    w = w_r.T if w_r.shape[0] == w_r.shape[1] else w_r
+    return _orig["router_logits"](xr, w, bias)
 
 
 def m_ties_high(l32, k, n_groups=0, topk_groups=0):
@@ -131,6 +145,8 @@ def m_route_head0(cfg, zr, w_router, bias=None, logits=None, sel_bias=None):
 
 
 MUTANTS = [
+    ("router_logits", m_logits_no_bias), ("router_logits", m_logits_bias_twice),
+    ("router_logits", m_logits_transposed),
     ("select_topk", m_ties_high), ("select_topk", m_group_sum), ("softmax", m_softmax_noexp),
     ("gates", m_no_renorm), ("aux_loss", m_aux_top1), ("keep_capacity", m_cap_le),
     ("keep_affinity", m_aff_floor), ("keep_affinity", m_aff_ties_high),
