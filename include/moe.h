@@ -271,6 +271,26 @@ int moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, const float *to
                  void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Arguments, results and errors as for moe_dispatch,
+ * without ws/ws_bytes: its scratch (per-chunk expert histograms and, for the
+ * affinity rule and expert choice, the expert-sorted assignment list) lives in
+ * a library-held device array of 8 MiB per GPU, allocated with the library's
+ * code object and held until the process ends.  A configuration that needs
+ * more (moe_dispatch's scratch grows with T*K and E) returns MOE_ERR_WORKSPACE
+ * before any launch.  The array belongs to the current device: `stream` must be
+ * a stream of the current device.  Every call on one GPU uses the same array,
+ * so calls that overlap on one GPU (different streams, or threads) race;
+ * calls in order on one stream do not.  The kernels overwrite every scratch
+ * byte they read, so no clearing is needed between calls.  The entry point
+ * itself allocates nothing and never synchronises.
+ */
+int moe_dispatch_noalloc(const moe_config *cfg, const int32_t *topk_idx, const float *topk_w, const void *x,
+                         int32_t *demand, int32_t *counts, int32_t *offsets, int32_t *row_of, int32_t *src_of,
+                         void *x_perm, hipStream_t stream);
+
+/*
  * moe_expert_ffn -- every routed expert on its rows of x_perm, plus the shared experts.
  * ["MoE技术演进", "GShard" item 3 (FFN_e); "DeepSeekMoE" item 2 (shared experts);
  * "大语言模型并行策略（七）：专家并行", "MoE 模型的参数量分析" (SwiGLU, 3 matrices)]

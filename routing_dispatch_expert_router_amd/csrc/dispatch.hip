@@ -23,10 +23,38 @@
 //             to every kept row of their token (head slice)
 // Every count is an integer and every order is fixed by a, so the result is
 // bit-reproducible.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
+
+// ---------------------------------------------------------------- library-held scratch
+// The dispatch scratch of the workspace-free entry point: one array per GPU,
+// held until the process ends.  Its name is a host-side stand-in for the
+// device array; host code uses only the address hipGetSymbolAddress returns
+// for the current device.
+static __device__ __align__(256) unsigned char scratch[DISPATCH_SCRATCH_MAX];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device: the device address of `scratch`, or NULL before first use
+}  // namespace
+
+int dispatch_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -4;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -4;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
+}
 
 constexpr int CH = 1024;  // assignments per chunk (256 threads x 4)
 

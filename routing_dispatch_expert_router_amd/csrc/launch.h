@@ -49,6 +49,10 @@ int launch_sel_bias_update(const Shape &s, const int32_t *load, float *sel_bias,
 
 // ---------------------------------------------------------------- dispatch
 size_t dispatch_ws_bytes(const Shape &s);
+// the library-held dispatch scratch (moe_dispatch_noalloc): its size, and
+// its device address on the current device (0, or -4 when HIP fails)
+constexpr size_t DISPATCH_SCRATCH_MAX = (size_t)8 << 20;
+int dispatch_scratch(void **out);
 int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w, const void *x,
                     int32_t *demand, int32_t *counts, int32_t *offsets, int32_t *row_of, int32_t *src_of,
                     void *x_perm, void *ws, hipStream_t st);

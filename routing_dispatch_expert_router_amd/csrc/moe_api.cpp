@@ -345,6 +345,30 @@ int moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, const float *to
                                     stream));
 }
 
+int moe_dispatch_noalloc(const moe_config *cfg, const int32_t *topk_idx, const float *topk_w, const void *x,
+                         int32_t *demand, int32_t *counts, int32_t *offsets, int32_t *row_of, int32_t *src_of,
+                         void *x_perm, hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, &s);
+  if (rc) return rc;
+  if (!topk_idx || !demand || !counts || !offsets || !row_of || (!src_of && s.R_max) || (x_perm && !x))
+    return MOE_ERR_ARG;
+  if (s.drop >= moe::DROP_AFFINITY && !topk_w) return MOE_ERR_ARG;
+  if (misaligned({topk_idx, topk_w, x, demand, counts, offsets, row_of, src_of, x_perm})) return MOE_ERR_ARG;
+  if (moe::dispatch_ws_bytes(s) > moe::DISPATCH_SCRATCH_MAX) {
+    if (getenv("MOE_DEBUG"))
+      fprintf(stderr, "moe: moe_dispatch_noalloc needs %zu bytes of scratch, the library holds %zu\n",
+              moe::dispatch_ws_bytes(s), moe::DISPATCH_SCRATCH_MAX);
+    return MOE_ERR_WORKSPACE;
+  }
+  if (s.T == 0) return MOE_OK;
+  void *scr = nullptr;
+  if (moe::dispatch_scratch(&scr)) return MOE_ERR_HIP;
+  clear_stale_error();
+  return rc_of(moe::launch_dispatch(s, topk_idx, topk_w, x, demand, counts, offsets, row_of, src_of, x_perm, scr,
+                                    stream));
+}
+
 int moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *offsets, const void *w1, const void *w3,
                    const void *w2, void *y_perm, const void *x_shared, const void *ws1, const void *ws3,
                    const void *ws2, void *shared_out, void *ws, size_t ws_bytes, hipStream_t stream) {

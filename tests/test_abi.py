@@ -345,3 +345,22 @@ def test_binding_rejects_misaligned_tensors():
     with pytest.raises(ValueError):
         moe._check_alignment(t[1:].data_ptr())
     moe._check_alignment(t.data_ptr())
+
+
+def test_noalloc_dispatch_checks_before_launching():
+    """The workspace-free dispatch: argument checks, and a configuration whose scratch exceeds the
+    library-held array (8 MiB) is refused with MOE_ERR_WORKSPACE before any HIP call."""
+    lib = moe._lib
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
+    c3 = moe.config_struct(CONFIGS[3])
+    # affinity keep needs the gates; outputs must be given
+    assert lib.moe_dispatch_noalloc(ctypes.byref(c3), fake, None, fake, fake, fake, fake, fake, fake, None,
+                                    None) == moe.MOE_ERR_ARG
+    assert lib.moe_dispatch_noalloc(ctypes.byref(c3), fake, fake, fake, None, fake, fake, fake, fake, None,
+                                    None) == moe.MOE_ERR_ARG
+    assert lib.moe_dispatch_noalloc(None, fake, fake, fake, fake, fake, fake, fake, fake, None, None) == moe.MOE_ERR_ARG
+    # 1.5 M tokens x 6 choices of the affinity rule: 36 MB of expert-sorted assignments
+    big = moe.config_struct(CONFIGS[3].with_(T=1_500_000, d_model=320, d_head=320, d_ff=64, n_shared=0))
+    assert moe.moe_check_config(CONFIGS[3].with_(T=1_500_000, d_model=320, d_head=320, d_ff=64, n_shared=0)) == 0
+    assert lib.moe_dispatch_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, fake, fake, fake, None,
+                                    None) == moe.MOE_ERR_WORKSPACE
