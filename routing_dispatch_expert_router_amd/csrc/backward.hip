@@ -127,12 +127,16 @@ __global__ void bwd_pmap_kernel(const int32_t *__restrict__ offsets, const int32
 // ---------------------------------------------------------------- transpose
 // dst[b][c][j] = source row j's column (coff + c), for c < ncols, j < njcols:
 //   rmap: source row rmap[j] (zero when -1); else row j when j < nvalid (zero after).
+// kchunk: dst k-chunked for the K-grouped products, (c, j) at (j / KC) * ld_dst *
+// KC + c * KC + j % KC with KC the elements of 128 bytes (ld_dst = rows of dst),
+// so one k-step of a product tile reads a contiguous block; else row-major.
 // Tiles of 64 columns x 64 rows through LDS, 16-byte global accesses both ways.
 template <typename TA>
 __global__ __launch_bounds__(256) void transpose_kernel(const TA *__restrict__ src, long ld_src, long bs_src,
                                                         const int32_t *__restrict__ rmap, long nvalid, long njcols,
                                                         int ncols, int coff, TA *__restrict__ dst, long ld_dst,
-                                                        long bs_dst) {
+                                                        long bs_dst, int kchunk) {
+  constexpr int KC = 128 / sizeof(TA);
   constexpr int EPC = 16 / sizeof(TA), CH = 64 / EPC;  // 16-byte chunks per 64 elements
   __shared__ TA tile[64][64 + EPC];
   const long j0 = (long)blockIdx.x * 64;
@@ -158,7 +162,10 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TA *__restrict__ s
     TA *pv = (TA *)&v;
 #pragma unroll
     for (int q = 0; q < EPC; ++q) pv[q] = tile[ch * EPC + q][cc];
-    *(u32x4 *)(dst + (size_t)(c0 + cc) * ld_dst + j0 + ch * EPC) = v;
+    const long j = j0 + ch * EPC;
+    const size_t o = kchunk ? (size_t)(j / KC) * ld_dst * KC + (size_t)(c0 + cc) * KC + j % KC
+                            : (size_t)(c0 + cc) * ld_dst + j;
+    *(u32x4 *)(dst + o) = v;
   }
 }
 
@@ -682,21 +689,23 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const TA *__restrict__ dy, 
 // ---------------------------------------------------------------- launchers
 template <typename TA>
 static int transpose_t(const void *src, long ld_src, long bs_src, const int32_t *rmap, long nvalid, long njcols,
-                       int ncols, int coff, void *dst, long ld_dst, long bs_dst, int batches, hipStream_t st) {
+                       int ncols, int coff, void *dst, long ld_dst, long bs_dst, int batches, int kchunk,
+                       hipStream_t st) {
   if (njcols <= 0 || ncols <= 0 || batches <= 0) return 0;
+  if (kchunk && (njcols % 64 || ncols > ld_dst)) return -2;  // whole k-chunks, rows inside dst
   dim3 grid((unsigned)((njcols + 63) / 64), (unsigned)((ncols + 63) / 64), (unsigned)batches);
   hipLaunchKernelGGL((transpose_kernel<TA>), grid, dim3(256), 0, st, (const TA *)src, ld_src, bs_src, rmap, nvalid,
-                     njcols, ncols, coff, (TA *)dst, ld_dst, bs_dst);
+                     njcols, ncols, coff, (TA *)dst, ld_dst, bs_dst, kchunk);
   return launch_status("transpose");
 }
 
 int launch_transpose(bool f32, const void *src, long ld_src, long bs_src, const int32_t *rmap, long nvalid,
                      long njcols, int ncols, int coff, void *dst, long ld_dst, long bs_dst, int batches,
-                     hipStream_t st) {
+                     hipStream_t st, int kchunk) {
   return f32 ? transpose_t<float>(src, ld_src, bs_src, rmap, nvalid, njcols, ncols, coff, dst, ld_dst, bs_dst,
-                                  batches, st)
+                                  batches, kchunk, st)
              : transpose_t<uint16_t>(src, ld_src, bs_src, rmap, nvalid, njcols, ncols, coff, dst, ld_dst, bs_dst,
-                                     batches, st);
+                                     batches, kchunk, st);
 }
 
 int launch_bwd_rows(const Shape &s, const void *dy, long ld_dy, const void *y_perm, const float *gates,

@@ -31,8 +31,11 @@ namespace moe {
 
 // EPI_F32OUT: the plain product written in float32 (K-grouped mode only: the
 // partial sums of a K-split product, added afterwards in a fixed order)
+// EPI_PIECE: K-grouped pieces (pieces table): a whole window's product in the
+// element type to its group's C block, a cut window's float32 partial to
+// its slot of `part`
 enum { EPI_PLAIN = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_RESID = 3, EPI_SWIGLU_BWD = 4, EPI_RELU_BWD = 5,
-       EPI_F32OUT = 6 };
+       EPI_F32OUT = 6, EPI_PIECE = 7 };
 // epilogues whose B tile pairs gate rows with up rows (SwiGLU forward, and its backward)
 static_assert(GEMM_EPI_PLAIN == EPI_PLAIN && GEMM_EPI_SWIGLU_BWD == EPI_SWIGLU_BWD &&
                   GEMM_EPI_RELU_BWD == EPI_RELU_BWD, "epilogue ids");
@@ -55,8 +58,14 @@ struct GemmArgs {
   const void *dh; long lddh;                  // *_BWD: upstream gradient of the hidden activation (rows as C)
   void *hout; long ldh;                       // *_BWD: the recomputed hidden activation (rows as C)
   const int32_t *kwin;                        // K-grouped mode: group g contracts columns [kwin[g], kwin[g+1])
-  long cstride;                               //   of A and B (both [M or N][ld]); its C block at C + g * cstride
+  long cstride;                               //   of A and B; its C block at C + g * cstride.  A and B are
+                                              //   k-chunked: element (row, k) at (k / KC) * ld * KC + row * KC
+                                              //   + k % KC, KC = 128 bytes of elements, ld (lda, ldb) = the
+                                              //   buffer's row count
   int Mk;                                     //   rows of A in that mode
+  const int32_t *pieces;                      // K-grouped pieces: [npieces][4] = (group, k0, k1, slot or -1),
+  const int32_t *npieces;                     //   the count on the device; slot >= 0: float32 partial at
+  float *part;                                //   part + slot * M * N (row stride N), else C of the group
   const int32_t *prefix;                      // [G+1] tile prefix, or NULL: E == 0 and fixed_tiles tiles
   int fixed_tiles;
   int G;
@@ -192,19 +201,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
 
   // tile count: the device-built prefix, or (no routed groups: a plain
   // product whose size the host knows) the fixed count
-  const int total = p.prefix ? p.prefix[p.G] : p.fixed_tiles;
+  const int tpg_k = p.kwin ? ((p.Mk + BM_ - 1) / BM_) * n_tiles<EPI, BN_>(p.N) : 0;
+  const int total = p.prefix ? p.prefix[p.G] : (p.pieces ? *p.npieces * tpg_k : p.fixed_tiles);
   const int b = blockIdx.x;
   if (b >= total) return;
   // blocks go round-robin to the 8 XCDs; give each XCD a contiguous run of
   // tiles so tiles sharing operands share an L2
+  // (K-grouped pieces: tiles of unequal depth, listed deepest first; they go
+  // round-robin, so every XCD gets its share of each depth)
   const int q8 = total >> 3;
-  const int lt = (b < 8 * q8) ? (b & 7) * q8 + (b >> 3) : b;
+  const int lt = (b < 8 * q8 && !p.pieces) ? (b & 7) * q8 + (b >> 3) : b;
   int g = 0, local = lt;
   if (p.kwin) {
-    // K-grouped: every group has the same (Mk x N) tile grid
-    const int tpg = ((p.Mk + BM_ - 1) / BM_) * n_tiles<EPI, BN_>(p.N);
-    g = lt / tpg;
-    local = lt - g * tpg;
+    // K-grouped: every group (or piece) has the same (Mk x N) tile grid
+    g = lt / tpg_k;
+    local = lt - g * tpg_k;
   } else if (p.prefix) {
     int lo = 0, hi = p.G - 1;
     while (lo < hi) {
@@ -217,19 +228,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
 
   const TE *A, *B, *B2;
   TE *C;
-  long lda, ldb, ldc;
+  long lda, ldb, ldc;           // row strides
+  size_t akc = BKE, bkc = BKE;  // k-chunk strides
   int M, N, K;
   int r0;
   const int32_t *gat = nullptr;  // routed rows gathered from the expert input
+  int slot = -1;                 // EPI_PIECE: float32 partial slot of a cut window, or -1
   if (p.kwin) {
-    const int k0 = p.kwin[g];
+    int grp = g, k0, k1;
+    if (p.pieces) {
+      const int32_t *pc = p.pieces + 4 * (size_t)g;
+      grp = pc[0]; k0 = pc[1]; k1 = pc[2]; slot = pc[3];
+    } else {
+      k0 = p.kwin[g]; k1 = p.kwin[g + 1];
+    }
     r0 = 0;
-    M = p.Mk; N = p.N; K = p.kwin[g + 1] - k0;
-    lda = p.lda; ldb = p.ldb; ldc = p.ldc;
-    A = (const TE *)p.A + k0;
-    B = (const TE *)p.B + k0;
+    M = p.Mk; N = p.N; K = k1 - k0;
+    lda = BKE; ldb = BKE; ldc = p.ldc;
+    akc = (size_t)p.lda * BKE; bkc = (size_t)p.ldb * BKE;
+    A = (const TE *)p.A + (size_t)(k0 / BKE) * akc;
+    B = (const TE *)p.B + (size_t)(k0 / BKE) * bkc;
     B2 = nullptr;
-    C = (TE *)p.C + (size_t)g * p.cstride;
+    C = (TE *)p.C + (size_t)grp * p.cstride;
   } else if (g < p.E) {
     r0 = p.offsets[g];
     M = p.offsets[g + 1] - r0;
@@ -317,12 +337,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   };
 
   auto issue_a = [&](int kc, int st) {
-    const size_t ko = (size_t)kc * BKE;
+    const size_t ko = (size_t)kc * akc;
 #pragma unroll
     for (int i = 0; i < LA; ++i) load_lds16(A + oa[i] + ko, sA + st * SA + i * NT + wv * 64);
   };
   auto issue_b = [&](int kc, int st) {
-    const size_t ko = (size_t)kc * BKE;
+    const size_t ko = (size_t)kc * bkc;
 #pragma unroll
     for (int i = 0; i < LB; ++i) load_lds16(bsrc(i) + ob[i] + ko, sB + st * SB + i * NT + wv * 64);
   };
@@ -497,6 +517,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
           h[v] = gt / (1.0f + __expf(-gt)) * up;
         }
         Quad<TE>::store(C + (size_t)row * ldc + col, h);
+      }
+    } else if (EPI == EPI_PIECE) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int col = tn * BN_ + wn * WN + f * 16 + 4 * cq;
+        if (col >= N) continue;
+        if (slot >= 0) {
+          *(float4 *)(p.part + (size_t)slot * M * N + (size_t)row * N + col) =
+              make_float4(acc[i][f][0], acc[i][f][1], acc[i][f][2], acc[i][f][3]);
+        } else {
+          const float o[4] = {acc[i][f][0], acc[i][f][1], acc[i][f][2], acc[i][f][3]};
+          Quad<TE>::store(C + (size_t)row * ldc + col, o);
+        }
       }
     } else if (EPI == EPI_F32OUT) {
       float *Cf = (float *)p.C + (size_t)g * p.cstride + (size_t)r0 * ldc;
@@ -708,22 +741,9 @@ int gemm_plain(bool f32, int epi, const void *A, long lda, const void *B, const 
   return 0;
 }
 
-// Weight gradients: for g < G, C_g[M, N] = A[:, kwin[g]..kwin[g+1]] B[:, same]^T
-// (A [M][lda], B [N][ldb], both contracted along their rows' columns; every
-// window a multiple of the k-chunk); C_g at C + g * cstride, ldc
-int gemm_kgrouped(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long ldc, long cstride, int G,
-                  int M, int N, const int32_t *kwin, hipStream_t st) {
-  if (G <= 0 || M <= 0 || N <= 0) return 0;
-  GemmArgs a{};
-  a.A = A; a.lda = lda; a.B = B; a.ldb = ldb; a.C = C; a.ldc = ldc; a.cstride = cstride;
-  a.kwin = kwin; a.Mk = M; a.N = N; a.E = G; a.G = G; a.split = 0; a.prefix = nullptr;
-  const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
-  a.fixed_tiles = G * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
-  return f32 ? run_gemm_one<float, EPI_PLAIN>(a, tile, st) : run_gemm_one<uint16_t, EPI_PLAIN>(a, tile, st);
-}
-
-// One group's C[M, N] = A[:, 0..Kt) B[:, 0..Kt)^T, K split into `nsplit`
-// windows kwin[0..nsplit] (device, multiples of 64): each window's product
+// One group's C[M, N] = A[:, 0..Kt) B[:, 0..Kt)^T, A and B k-chunked with lda and
+// ldb rows, K split into `nsplit` windows kwin[0..nsplit] (device, multiples
+// of 64): each window's product
 // goes to part[s] (float32, M x N, row stride N), then C = sum over s in
 // order, rounded once.  Fills the chip when one group has few output tiles.
 // c[0..3] = sum over s < nsplit of p[s * stride + 0..3], in order s = 0, 1, ...,
@@ -773,54 +793,151 @@ int gemm_splitk(bool f32, const void *A, long lda, const void *B, long ldb, void
   return launch_status("split-k reduce");
 }
 
-// K-grouped products with each group's window split in `nsplit`: window s of
-// group e is [w_e + (n_e/64 * s / nsplit) * 64, ...) of w_e = kwin[e],
-// n_e = kwin[e+1] - w_e (both multiples of 64)
-__global__ void split_windows_kernel(const int32_t *__restrict__ kwin, int G, int nsplit, int32_t *__restrict__ kw) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i <= G * nsplit; i += gridDim.x * blockDim.x) {
-    if (i == G * nsplit) {
-      kw[i] = kwin[G];
-      continue;
+// ---------------------------------------------------------------- K-grouped pieces
+// The per-expert windows cut in pieces of at most `depth` columns each
+// (multiples of 64, near-equal within an expert): expert e's window of n_e
+// columns gives P_e = max(1, ceil(n_e / depth)) pieces.  A whole window (P_e
+// == 1) writes its product straight to C_e; the pieces of a cut window write
+// float32 partials to consecutive slots (in expert, then piece order), added
+// afterwards in order.  The table lists the pieces deepest first, so the
+// tiles dispatched first are the longest (the hardware hands blocks to free
+// CUs in order: longest-first list scheduling); the order of equal depths is
+// free, and no result depends on it.  One block of 1024 threads: tab[p] =
+// (e, k0, k1, slot), tab[4 * maxp] = P (maxp bounds P), and for the
+// reduction red[e] = (first slot, P_e or 0 when whole).
+constexpr int PIECE_BUCKETS = 2048;  // depth classes (64-column chunks; deeper pieces share the last)
+__global__ __launch_bounds__(1024) void kgroup_pieces_kernel(const int32_t *__restrict__ kwin, int G, int depth,
+                                                             long maxp, int32_t *__restrict__ tab,
+                                                             int32_t *__restrict__ red) {
+  __shared__ int sp[1024], ss[1024], hist[PIECE_BUCKETS];
+  const int tid = threadIdx.x, per = (G + 1023) / 1024;
+  for (int b = tid; b < PIECE_BUCKETS; b += 1024) hist[b] = 0;
+  int np[8], ns[8], sum_p = 0, sum_s = 0;
+  // bucket of a piece: deepest first
+  auto bucket = [](int chunks) { return PIECE_BUCKETS - 1 - min(chunks, PIECE_BUCKETS - 1); };
+  __syncthreads();
+  for (int i = 0; i < per && i < 8; ++i) {
+    const int e = tid * per + i;
+    int pe = 0;
+    if (e < G) {
+      const int n = kwin[e + 1] - kwin[e], chunks = n / 64;
+      pe = n > depth ? (n + depth - 1) / depth : 1;
+      for (int j = 0; j < pe; ++j)
+        atomicAdd(&hist[bucket((int)((long)chunks * (j + 1) / pe) - (int)((long)chunks * j / pe))], 1);
     }
-    const int e = i / nsplit, s = i % nsplit;
-    const int lo = kwin[e], chunks = (kwin[e + 1] - lo) / 64;
-    kw[i] = lo + (int)((long)chunks * s / nsplit) * 64;
+    np[i] = pe;
+    ns[i] = pe > 1 ? pe : 0;
+    sum_p += pe;
+    sum_s += ns[i];
   }
+  sp[tid] = sum_p;
+  ss[tid] = sum_s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int up = tid >= o ? sp[tid - o] : 0, us = tid >= o ? ss[tid - o] : 0;
+    __syncthreads();
+    sp[tid] += up;
+    ss[tid] += us;
+    __syncthreads();
+  }
+  const int total = sp[1023];
+  int rs = ss[tid] - sum_s;
+  // exclusive prefix over the buckets (two per thread): a bucket's first position
+  constexpr int BPT = PIECE_BUCKETS / 1024;
+  static_assert(BPT * 1024 == PIECE_BUCKETS, "buckets per thread");
+  int hb[BPT], hs = 0;
+#pragma unroll
+  for (int u = 0; u < BPT; ++u) { hb[u] = hist[tid * BPT + u]; hs += hb[u]; }
+  __syncthreads();
+  sp[tid] = hs;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int up = tid >= o ? sp[tid - o] : 0;
+    __syncthreads();
+    sp[tid] += up;
+    __syncthreads();
+  }
+  int run = sp[tid] - hs;
+#pragma unroll
+  for (int u = 0; u < BPT; ++u) { hist[tid * BPT + u] = run; run += hb[u]; }
+  __syncthreads();
+  for (int i = 0; i < per && i < 8; ++i) {
+    const int e = tid * per + i;
+    if (e < G) {
+      const int lo = kwin[e], chunks = (kwin[e + 1] - lo) / 64, pe = np[i];
+      for (int j = 0; j < pe; ++j) {
+        const int c0 = (int)((long)chunks * j / pe), c1 = (int)((long)chunks * (j + 1) / pe);
+        int32_t *t = tab + 4 * (size_t)atomicAdd(&hist[bucket(c1 - c0)], 1);
+        t[0] = e;
+        t[1] = lo + c0 * 64;
+        t[2] = lo + c1 * 64;
+        t[3] = pe > 1 ? rs + j : -1;
+      }
+      red[2 * e] = rs;
+      red[2 * e + 1] = pe > 1 ? pe : 0;
+    }
+    rs += ns[i];
+  }
+  if (tid == 0) tab[4 * maxp] = total;
 }
 
-// C_e[i] = sum over s of part[(e * nsplit + s) * MN + i], in order, rounded once;
+// C_e = sum over its pieces' partials in order, rounded once (cut experts only);
 // group e = blockIdx.y, four columns per thread (MN a multiple of 4)
 template <typename TE>
-__global__ void group_reduce_kernel(const float *__restrict__ part, long MN, int nsplit, long cstride,
-                                    TE *__restrict__ C) {
+__global__ void piece_reduce_kernel(const float *__restrict__ part, long MN, const int32_t *__restrict__ red,
+                                    long cstride, TE *__restrict__ C) {
   const long e = blockIdx.y;
-  const float *pe = part + (size_t)e * nsplit * MN;
+  const int first = red[2 * e], n = red[2 * e + 1];
+  if (n == 0) return;
+  const float *pe = part + (size_t)first * MN;
   for (long j = 4 * (blockIdx.x * (long)blockDim.x + threadIdx.x); j < MN; j += 4L * gridDim.x * blockDim.x)
-    reduce_quad(pe + j, (size_t)MN, nsplit, C + (size_t)e * cstride + j);
+    reduce_quad(pe + j, (size_t)MN, n, C + (size_t)e * cstride + j);
 }
 
-int gemm_kgrouped_split(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long cstride, int G,
-                        int M, int N, const int32_t *kwin, int nsplit, int32_t *kw_scratch, float *part,
-                        hipStream_t st) {
+static int kgroup_tile(bool f32, int M, int N) {
+  return f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
+}
+
+// Piece depth for G groups of M x N outputs over at most Rp padded columns:
+// the total depth over as many pieces as one round of resident tiles holds
+// (at least 512 columns).  Windows of an even routing stay whole; a hot
+// expert's window is cut into pieces no deeper than that.  (Finer pieces
+// balance better but each cut piece writes and reads back an M x N float32
+// partial; one round measured fastest on the skewed 64-expert workload.)
+int kgroup_piece_depth(bool f32, int G, int M, int N, long Rp) {
+  const int tile = kgroup_tile(f32, M, N);
+  const long tpg = (long)((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
+  const long want = std::max<long>(1, ((tile == TILE_256x256_W8 ? 256 : 512) + tpg - 1) / tpg);
+  const long d = (Rp + want - 1) / want;
+  return (int)std::max<long>(512, (d + 63) / 64 * 64);
+}
+// bounds: pieces <= G + Rp / depth; partial slots (pieces of cut windows,
+// each window deeper than depth) <= 2 * Rp / depth
+long kgroup_max_pieces(int G, long Rp, int depth) { return G + Rp / depth + 1; }
+long kgroup_max_slots(long Rp, int depth) { return 2 * Rp / depth + 1; }
+
+int gemm_kgrouped_pieces(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long ldc, long cstride,
+                         int G, int M, int N, const int32_t *kwin, int depth, long max_pieces, int32_t *tab,
+                         int32_t *red, float *part, hipStream_t st) {
   if (G <= 0 || M <= 0 || N <= 0) return 0;
-  hipLaunchKernelGGL(split_windows_kernel, dim3((unsigned)std::min(1024, (G * nsplit + 256) / 256)), dim3(256), 0,
-                     st, kwin, G, nsplit, kw_scratch);
-  if (int rc = launch_status("split windows")) return rc;
+  hipLaunchKernelGGL(kgroup_pieces_kernel, dim3(1), dim3(1024), 0, st, kwin, G, depth, max_pieces, tab, red);
+  if (int rc = launch_status("weight-gradient pieces")) return rc;
   GemmArgs a{};
-  a.A = A; a.lda = lda; a.B = B; a.ldb = ldb; a.C = part; a.ldc = N; a.cstride = (long)M * N;
-  a.kwin = kw_scratch; a.Mk = M; a.N = N; a.E = G * nsplit; a.G = G * nsplit; a.split = 0; a.prefix = nullptr;
-  const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
-  a.fixed_tiles = G * nsplit * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
-  const int rc = f32 ? run_gemm_one<float, EPI_PLAIN>(a, tile, st) : run_gemm_one<uint16_t, EPI_F32OUT>(a, tile, st);
+  a.A = A; a.lda = lda; a.B = B; a.ldb = ldb; a.C = C; a.ldc = ldc; a.cstride = cstride;
+  a.kwin = kwin; a.Mk = M; a.N = N; a.E = G; a.G = G; a.split = 0; a.prefix = nullptr;
+  a.pieces = tab; a.npieces = tab + 4 * max_pieces; a.part = part;
+  const int tile = kgroup_tile(f32, M, N);
+  a.fixed_tiles = (int)(max_pieces * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N));
+  const int rc = f32 ? run_gemm_one<float, EPI_PIECE>(a, tile, st) : run_gemm_one<uint16_t, EPI_PIECE>(a, tile, st);
   if (rc) return rc;
   const long mn = (long)M * N;  // N is a multiple of 64
   const dim3 grid((unsigned)std::min<long>((mn / 4 + 255) / 256, std::max<long>(1, 8192 / G)), (unsigned)G);
   if (f32)
-    hipLaunchKernelGGL((group_reduce_kernel<float>), grid, dim3(256), 0, st, part, mn, nsplit, cstride, (float *)C);
+    hipLaunchKernelGGL((piece_reduce_kernel<float>), grid, dim3(256), 0, st, part, mn, red, cstride, (float *)C);
   else
-    hipLaunchKernelGGL((group_reduce_kernel<uint16_t>), grid, dim3(256), 0, st, part, mn, nsplit, cstride,
+    hipLaunchKernelGGL((piece_reduce_kernel<uint16_t>), grid, dim3(256), 0, st, part, mn, red, cstride,
                        (uint16_t *)C);
-  return launch_status("split-k group reduce");
+  return launch_status("weight-gradient piece reduce");
 }
 
 // blocks of a tile kind resident on the chip at once: a 256 x 256 tile holds
@@ -836,19 +953,6 @@ static int fill_split(long tiles, long resident, long max_by_depth) {  // 1 .. 8
   const long s = std::min<long>(resident / std::max<long>(tiles, 1), max_by_depth);
   return (int)std::max<long>(1, std::min<long>(s, 8));
 }
-// Splits for G groups of M x N outputs over K_total (all groups' windows):
-// up to four rounds of tiles, windows of 512 or more on average.  Unlike one
-// dense product, the groups' windows differ in depth, and splitting them
-// shortens the deepest (measured: the multi-head workload's skewed experts
-// run faster split in two than unsplit in one round).
-int kgrouped_split_count(bool f32, int G, int M, int N, long K_total) {
-  const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);
-  const long tiles = (long)G * ((M + tile_rows(tile) - 1) / tile_rows(tile)) * col_tiles(EPI_PLAIN, tile, N);
-  long s = (1024 + tiles - 1) / tiles;
-  s = std::min<long>(s, std::max<long>(1, K_total / ((long)G * 512)));
-  return (int)std::max<long>(1, std::min<long>(s, 8));
-}
-
 // K windows for gemm_splitk: each at least 1024 deep
 int splitk_count(bool f32, int M, int N, long K) {
   const int tile = f32 ? TILE_128x128 : (M >= 256 && N >= 256 ? TILE_256x256_W8 : TILE_128x128_W8);

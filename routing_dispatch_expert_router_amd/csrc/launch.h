@@ -65,22 +65,28 @@ int gemm_routed(const Shape &s, int epi, const void *A, long lda, const int32_t 
                 const void *dh, long lddh, void *hout, long ldh, int32_t *prefix, hipStream_t st);
 int gemm_plain(bool f32, int epi, const void *A, long lda, const void *B, const void *B2, long ldb, void *C,
                long ldc, int M, int N, int K, const void *dh, long lddh, void *hout, long ldh, hipStream_t st);
-int gemm_kgrouped(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long ldc, long cstride, int G,
-                  int M, int N, const int32_t *kwin, hipStream_t st);
+// The K-grouped products below read A [M rows][K] and B [N rows][K] k-chunked
+// (launch_transpose with kchunk): (row, k) at (k / KC) * ld * KC + row * KC +
+// k % KC, KC = the elements of 128 bytes, lda / ldb = the buffers' row counts.
 // one group's C[M, N] = A B^T over K windows kwin[0..nsplit] (multiples of 64),
 // through float32 partials part[nsplit][M][N] added in order
 int gemm_splitk(bool f32, const void *A, long lda, const void *B, long ldb, void *C, int M, int N, int nsplit,
                 const int32_t *kwin, float *part, hipStream_t st);
 int splitk_count(bool f32, int M, int N, long K);
-// gemm_kgrouped with every group's window split in nsplit (nsplit > 1: float32
-// partials part[G * nsplit][M][N], kw_scratch of G * nsplit + 1 ints)
-int gemm_kgrouped_split(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long cstride, int G,
-                        int M, int N, const int32_t *kwin, int nsplit, int32_t *kw_scratch, float *part,
-                        hipStream_t st);
-int kgrouped_split_count(bool f32, int G, int M, int N, long K_total);
+// K-grouped products with every group's window cut in pieces of at most
+// `depth` columns (kgroup_piece_depth): whole windows write C directly, cut
+// ones go through float32 partials (part: kgroup_max_slots x M x N floats)
+// added in order.  tab: 4 * max_pieces + 1 ints; red: 2 * G ints.
+int kgroup_piece_depth(bool f32, int G, int M, int N, long Rp);
+long kgroup_max_pieces(int G, long Rp, int depth);
+long kgroup_max_slots(long Rp, int depth);
+int gemm_kgrouped_pieces(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long ldc, long cstride,
+                         int G, int M, int N, const int32_t *kwin, int depth, long max_pieces, int32_t *tab,
+                         int32_t *red, float *part, hipStream_t st);
+// kchunk: dst k-chunked (ld_dst = its row count, njcols a multiple of 64), else row-major
 int launch_transpose(bool f32, const void *src, long ld_src, long bs_src, const int32_t *rmap, long nvalid,
                      long njcols, int ncols, int coff, void *dst, long ld_dst, long bs_dst, int batches,
-                     hipStream_t st);
+                     hipStream_t st, int kchunk = 0);
 int launch_bwd_rows(const Shape &s, const void *dy, long ld_dy, const void *y_perm, const float *gates,
                     const int32_t *src_of, const int32_t *topk_idx, const int32_t *offsets, void *dY, float *dg,
                     hipStream_t st);

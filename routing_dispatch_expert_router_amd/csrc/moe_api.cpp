@@ -215,12 +215,13 @@ BwdBufs bwd_layout(const Shape &s) {
       need((long)s.H * s.dh, s.d);
     }
     b.spart = o; o += al(mx);
-    // the per-expert weight gradients, split when experts hold few output tiles
-    const int s2 = moe::kgrouped_split_count(s.act_f32, s.E, s.dh, s.dff, (long)R);
-    const int s1 = moe::kgrouped_split_count(s.act_f32, s.E, s.dff, s.dh, (long)R);
-    const size_t me = std::max((s2 > 1 ? (size_t)s2 : 0), (s1 > 1 ? (size_t)s1 : 0));
-    b.epart = o; o += al(me * s.E * s.dh * s.dff * 4);
-    b.kwsplit = o; o += al(((size_t)s.E * 8 + 1) * 4);
+    // the per-expert weight gradients: windows cut in pieces of bounded depth,
+    // float32 partials for the pieces of cut windows
+    const int d2 = moe::kgroup_piece_depth(s.act_f32, s.E, s.dh, s.dff, Rp);
+    const int d1 = moe::kgroup_piece_depth(s.act_f32, s.E, s.dff, s.dh, Rp);
+    const int dmin = std::min(d1, d2);
+    b.epart = o; o += al((size_t)moe::kgroup_max_slots(Rp, dmin) * s.dh * s.dff * 4);
+    b.kwsplit = o; o += al(((size_t)4 * moe::kgroup_max_pieces(s.E, Rp, dmin) + 1 + 2 * (size_t)s.E) * 4);
   }
   if (s.latent) {  // the projections: do, du and the transposes of dy, x, o, du
     const size_t D = (size_t)s.H * s.dh;
@@ -588,12 +589,14 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
   const void *u = s.latent ? io->z : x;
   const int epi_bwd = glu ? moe::GEMM_EPI_SWIGLU_BWD : moe::GEMM_EPI_RELU_BWD;
   const int32_t *offsets = io->offsets, *src_of = io->src_of;
-  // one group's C[M, N] = A B^T over the T (padded) tokens: A [M][Tp], B [N][Tp]
-  auto tokens_product = [&](const void *A, const void *B, void *C, int M, int N) -> int {
+  // one group's C[M, N] = A B^T over the T (padded) tokens: A [M][Tp], B [N][Tp],
+  // k-chunked with arows and brows rows
+  auto tokens_product = [&](const void *A, long arows, const void *B, long brows, void *C, int M, int N) -> int {
     const int S = moe::splitk_count(f32, M, N, Tp);
     if (int r = rc_of(moe::launch_set_kwin(kwin, (int)Tp, S, stream))) return r;
-    return rc_of(moe::gemm_splitk(f32, A, Tp, B, Tp, C, M, N, S, kwin, (float *)at(L.spart), stream));
+    return rc_of(moe::gemm_splitk(f32, A, arows, B, brows, C, M, N, S, kwin, (float *)at(L.spart), stream));
   };
+  const long KC = 128 / esz;  // elements per k-chunk of the transposed buffers
 
   clear_stale_error();
   // latent layer: the gradient of o is do = dy W_out
@@ -624,24 +627,31 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
     return rc;
   // transposed, per-expert padded activations for the weight gradients
   // (u viewed as [T*H, dh]: pmap_x holds t*H + h)
-  if ((rc = rc_of(moe::launch_transpose(f32, u, dh, 0, pmap_x, 0, Rp, (int)dh, 0, Xt, Rp, 0, 1, stream)))) return rc;
-  if ((rc = rc_of(moe::launch_transpose(f32, dY, dh, 0, pmap_r, 0, Rp, (int)dh, 0, dYt, Rp, 0, 1, stream)))) return rc;
-  if ((rc = rc_of(moe::launch_transpose(f32, dAB, m * dff, 0, pmap_r, 0, Rp, (int)(m * dff), 0, dABt, Rp, 0, 1,
-                                        stream))))
+  if ((rc = rc_of(moe::launch_transpose(f32, u, dh, 0, pmap_x, 0, Rp, (int)dh, 0, Xt, dh, 0, 1, stream, 1))))
     return rc;
-  if ((rc = rc_of(moe::launch_transpose(f32, Hr, dff, 0, pmap_r, 0, Rp, (int)dff, 0, Ht, Rp, 0, 1, stream)))) return rc;
+  if ((rc = rc_of(moe::launch_transpose(f32, dY, dh, 0, pmap_r, 0, Rp, (int)dh, 0, dYt, dh, 0, 1, stream, 1))))
+    return rc;
+  if ((rc = rc_of(moe::launch_transpose(f32, dAB, m * dff, 0, pmap_r, 0, Rp, (int)(m * dff), 0, dABt, m * dff, 0, 1,
+                                        stream, 1))))
+    return rc;
+  if ((rc = rc_of(moe::launch_transpose(f32, Hr, dff, 0, pmap_r, 0, Rp, (int)dff, 0, Ht, dff, 0, 1, stream, 1))))
+    return rc;
   // dW2_e = dY_e^T H_e, dW1_e = dA_e^T X_e, dW3_e = dB_e^T X_e (windows split when
   // the experts' output tiles alone would not fill the chip)
-  auto expert_wgrad = [&](const void *A, const void *B, void *C, long ldc, int M, int N) -> int {
-    const int S = moe::kgrouped_split_count(f32, s.E, M, N, s.R_max);
-    if (S <= 1)
-      return rc_of(moe::gemm_kgrouped(f32, A, Rp, B, Rp, C, ldc, (long)M * N, s.E, M, N, poff, stream));
-    return rc_of(moe::gemm_kgrouped_split(f32, A, Rp, B, Rp, C, (long)M * N, s.E, M, N, poff, S,
-                                          (int32_t *)at(L.kwsplit), (float *)at(L.epart), stream));
+  // (each expert's window cut in pieces of bounded depth, so one hot expert
+  // does not leave the chip idle while its tiles contract every row)
+  auto expert_wgrad = [&](const void *A, long arows, const void *B, long brows, void *C, long ldc, int M,
+                          int N) -> int {
+    const int depth = moe::kgroup_piece_depth(f32, s.E, M, N, Rp);
+    const long maxp = moe::kgroup_max_pieces(s.E, Rp, depth);
+    int32_t *tab = (int32_t *)at(L.kwsplit);
+    return rc_of(moe::gemm_kgrouped_pieces(f32, A, arows, B, brows, C, ldc, (long)M * N, s.E, M, N, poff, depth,
+                                           maxp, tab, tab + 4 * maxp + 1, (float *)at(L.epart), stream));
   };
-  if ((rc = expert_wgrad(dYt, Ht, g->dw2, dff, (int)dh, (int)dff))) return rc;
-  if ((rc = expert_wgrad(dABt, Xt, g->dw1, dh, (int)dff, (int)dh))) return rc;
-  if (glu && (rc = expert_wgrad((char *)dABt + dff * Rp * esz, Xt, g->dw3, dh, (int)dff, (int)dh))) return rc;
+  if ((rc = expert_wgrad(dYt, dh, Ht, dff, g->dw2, dff, (int)dh, (int)dff))) return rc;
+  if ((rc = expert_wgrad(dABt, m * dff, Xt, dh, g->dw1, dh, (int)dff, (int)dh))) return rc;
+  if (glu && (rc = expert_wgrad((char *)dABt + dff * KC * esz, m * dff, Xt, dh, g->dw3, dh, (int)dff, (int)dh)))
+    return rc;
   // router: dl, dW_r, dbias
   int32_t *seqcnt = seq_weight != 0.0f ? (int32_t *)at(L.seqcnt) : nullptr;
   if (seqcnt && (rc = rc_of(moe::launch_seq_counts(s, io->topk_idx, seqcnt, stream)))) return rc;
@@ -665,18 +675,19 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
     if ((rc = rc_of(moe::gemm_plain(f32, moe::GEMM_EPI_PLAIN, dABs, m * fs, wt->ws13t, nullptr, m * fs, dxs, d, s.T,
                                     (int)d, (int)(m * fs), nullptr, 0, nullptr, 0, stream))))
       return rc;
-    if ((rc = rc_of(moe::launch_transpose(f32, dy, d, 0, nullptr, s.T, Tp, (int)d, 0, dyt, Tp, 0, 1, stream))))
+    if ((rc = rc_of(moe::launch_transpose(f32, dy, d, 0, nullptr, s.T, Tp, (int)d, 0, dyt, d, 0, 1, stream, 1))))
       return rc;
-    if ((rc = rc_of(moe::launch_transpose(f32, x, d, 0, nullptr, s.T, Tp, (int)d, 0, xt, Tp, 0, 1, stream))))
+    if ((rc = rc_of(moe::launch_transpose(f32, x, d, 0, nullptr, s.T, Tp, (int)d, 0, xt, d, 0, 1, stream, 1))))
       return rc;
-    if ((rc = rc_of(moe::launch_transpose(f32, dABs, m * fs, 0, nullptr, s.T, Tp, (int)(m * fs), 0, dABst, Tp, 0, 1,
-                                          stream))))
+    if ((rc = rc_of(moe::launch_transpose(f32, dABs, m * fs, 0, nullptr, s.T, Tp, (int)(m * fs), 0, dABst, m * fs, 0,
+                                          1, stream, 1))))
       return rc;
-    if ((rc = rc_of(moe::launch_transpose(f32, Hs, fs, 0, nullptr, s.T, Tp, (int)fs, 0, Hst, Tp, 0, 1, stream))))
+    if ((rc = rc_of(moe::launch_transpose(f32, Hs, fs, 0, nullptr, s.T, Tp, (int)fs, 0, Hst, fs, 0, 1, stream, 1))))
       return rc;
-    if ((rc = tokens_product(dyt, Hst, g->dws2, (int)d, (int)fs))) return rc;
-    if ((rc = tokens_product(dABst, xt, g->dws1, (int)fs, (int)d))) return rc;
-    if (glu && (rc = tokens_product((char *)dABst + fs * Tp * esz, xt, g->dws3, (int)fs, (int)d))) return rc;
+    if ((rc = tokens_product(dyt, d, Hst, fs, g->dws2, (int)d, (int)fs))) return rc;
+    if ((rc = tokens_product(dABst, m * fs, xt, d, g->dws1, (int)fs, (int)d))) return rc;
+    if (glu && (rc = tokens_product((char *)dABst + fs * KC * esz, m * fs, xt, d, g->dws3, (int)fs, (int)d)))
+      return rc;
   }
   if (!s.latent) {
     // dx = [dy] + [dxs] + sum_j dX rows + dl W_r (per head)
@@ -688,15 +699,16 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
     return rc;
   if ((rc = rc_of(moe::launch_dense(f32, du, wt->w_in_t, g->dx, dy, s.T, (int)d, (int)D, nullptr, stream))))
     return rc;
-  if ((rc = rc_of(moe::launch_transpose(f32, dy, d, 0, nullptr, s.T, Tp, (int)d, 0, dyt, Tp, 0, 1, stream))))
+  if ((rc = rc_of(moe::launch_transpose(f32, dy, d, 0, nullptr, s.T, Tp, (int)d, 0, dyt, d, 0, 1, stream, 1))))
     return rc;
-  if ((rc = rc_of(moe::launch_transpose(f32, x, d, 0, nullptr, s.T, Tp, (int)d, 0, xt, Tp, 0, 1, stream)))) return rc;
-  if ((rc = rc_of(moe::launch_transpose(f32, io->o, D, 0, nullptr, s.T, Tp, (int)D, 0, ot, Tp, 0, 1, stream))))
+  if ((rc = rc_of(moe::launch_transpose(f32, x, d, 0, nullptr, s.T, Tp, (int)d, 0, xt, d, 0, 1, stream, 1))))
     return rc;
-  if ((rc = rc_of(moe::launch_transpose(f32, du, D, 0, nullptr, s.T, Tp, (int)D, 0, dut, Tp, 0, 1, stream))))
+  if ((rc = rc_of(moe::launch_transpose(f32, io->o, D, 0, nullptr, s.T, Tp, (int)D, 0, ot, D, 0, 1, stream, 1))))
     return rc;
-  if ((rc = tokens_product(dyt, ot, g->dw_out, (int)d, (int)D))) return rc;
-  return tokens_product(dut, xt, g->dw_in, (int)D, (int)d);
+  if ((rc = rc_of(moe::launch_transpose(f32, du, D, 0, nullptr, s.T, Tp, (int)D, 0, dut, D, 0, 1, stream, 1))))
+    return rc;
+  if ((rc = tokens_product(dyt, d, ot, D, g->dw_out, (int)d, (int)D))) return rc;
+  return tokens_product(dut, D, xt, d, g->dw_in, (int)D, (int)d);
 }
 
 }  // extern "C"
