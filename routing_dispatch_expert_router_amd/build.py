@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
-SOURCES = ["route.hip", "dispatch.hip", "gemm.hip", "combine.hip", "backward.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "dispatch.hip", "gemm.hip", "mlp.hip", "combine.hip", "backward.hip", "moe_api.cpp"]
 
 
 def _compile(src, obj, verbose):

@@ -80,6 +80,17 @@ __device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
 // wait until this wave's LDS (and scalar-memory) operations have completed
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Workgroup barrier without a memory fence, for the k-loops that stream
+// operands into LDS with global -> LDS loads.  __syncthreads() also issues a
+// workgroup release fence, and on gfx950 that fence waits for every
+// outstanding vector-memory load (LDS DMA counts as an LDS write), so a chunk
+// prefetched two steps ahead would be waited for at the next barrier.  The
+// caller waits itself for what the other waves must see: its LDS reads
+// (wait_lgkmcnt0) and its global -> LDS loads of the chunk about to be read
+// (wait_vmcnt<N>).  The memory clobber keeps the compiler from moving LDS
+// accesses across the barrier.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 // wave index in the workgroup, as a scalar (wave-uniform) value

@@ -398,7 +398,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
       if (i + STB >= 0 && i + STB < nk) issue_b(i + STB, i + STB);
     }
     wait_chunk(0);
-    __syncthreads();
+    barrier_nofence();
     read(nl, 0, 0, 0, fa0, fb0);
     int sa = 0, sb = 0;
     for (int kc = 0; kc < nk; ++kc) {
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
         // chunk kc+1 landed for this wave; this wave's reads of chunk kc are done
         wait_chunk(kc + 1);
         wait_lgkmcnt0();
-        __syncthreads();
+        barrier_nofence();
         if (kc + STA < nk) issue_a(kc + STA, sa);
         if (kc + STB < nk) issue_b(kc + STB, sb);
       }
@@ -985,6 +985,11 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
   int32_t *pre = (int32_t *)p;  // [launch][E+2]: tile prefixes of the (up to four) launches
   const bool glu = s.act == 1;
   const int has_x = s.n_shared ? 1 : 0;
+  // narrow experts: the fused MLP (no hidden round trip through HBM)
+  const bool fused = sizeof(TE) == 2 && mlp_fused_supported(s);
+  if (fused) {
+    if (int rc = launch_mlp_fused(s, xin, gather, offsets, w1, w3, w2, y_perm, pre, st)) return rc;
+  }
   // f32 layers are parity-sized: the small tile is plenty
   const int tile = sizeof(TE) == 4 ? TILE_128x128 : pick_tile_routed(s);
   const int epi1 = glu ? EPI_SWIGLU : EPI_RELU;
@@ -1014,15 +1019,17 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
     pa.c[i] = prep_cfg(epi1, l[i], a.N, 0);
     pa.c[nl + i] = prep_cfg(EPI_PLAIN, l[i], b.N, 0);
   }
-  hipLaunchKernelGGL(gemm_prep_kernel, dim3(2 * nl), dim3(1024), 0, st, pa);
-  if (int rc = launch_status("gemm tile prefix")) return rc;
-  for (int i = 0; i < nl; ++i) {
+  for (int i = 0; i < nl && !fused; ++i) {
+    if (i == 0) {
+      hipLaunchKernelGGL(gemm_prep_kernel, dim3(2 * nl), dim3(1024), 0, st, pa);
+      if (int rc = launch_status("gemm tile prefix")) return rc;
+    }
     a.split = l[i].split;
     a.prefix = pre + (size_t)i * (s.E + 2);
     int rc = glu ? run_gemm_one<TE, EPI_SWIGLU>(a, l[i].tile, st) : run_gemm_one<TE, EPI_RELU>(a, l[i].tile, st);
     if (rc) return rc;
   }
-  for (int i = 0; i < nl; ++i) {
+  for (int i = 0; i < nl && !fused; ++i) {
     b.split = l[i].split;
     b.prefix = pre + (size_t)(nl + i) * (s.E + 2);
     if (int rc = run_gemm_one<TE, EPI_PLAIN>(b, l[i].tile, st)) return rc;

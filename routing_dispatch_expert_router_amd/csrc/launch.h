@@ -83,6 +83,11 @@ long kgroup_max_slots(long Rp, int depth);
 int gemm_kgrouped_pieces(bool f32, const void *A, long lda, const void *B, long ldb, void *C, long ldc, long cstride,
                          int G, int M, int N, const int32_t *kwin, int depth, long max_pieces, int32_t *tab,
                          int32_t *red, float *part, hipStream_t st);
+// fused expert MLP (mlp.hip): bf16, d_e of 64, 128 or 256, d_ff a multiple
+// of 32; prefix: E + 1 ints of workspace
+bool mlp_fused_supported(const Shape &s);
+int launch_mlp_fused(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets, const void *w1,
+                     const void *w3, const void *w2, void *y_perm, int32_t *prefix, hipStream_t st);
 // kchunk: dst k-chunked (ld_dst = its row count, njcols a multiple of 64), else row-major
 int launch_transpose(bool f32, const void *src, long ld_src, long bs_src, const int32_t *rmap, long nvalid,
                      long njcols, int ncols, int coff, void *dst, long ld_dst, long bs_dst, int batches,
