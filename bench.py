@@ -90,20 +90,33 @@ def algorithmic(cfg, R):
     return out
 
 
+def ffn_source_sha256():
+    """sha256 over the expert FFN's kernel sources (grouped GEMM, fused MLP), in that order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "mlp.hip"):
+        with open(os.path.join(ROOT, "routing_dispatch_expert_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def measured_traffic(cfg):
     """HBM bytes per expert-FFN call measured with rocprofv3 for this workload, if the
-    grouped-GEMM source is unchanged since the measurement (else None)."""
-    import hashlib
-    f = os.path.join(ROOT, "profiles", f"traffic__grouped_gemm__{cfg.name}.json")
+    FFN kernels' sources are unchanged since the measurement (else None)."""
+    f = os.path.join(ROOT, "profiles", f"traffic__expert_ffn__{cfg.name}.json")
     if not os.path.exists(f):
         return None
     with open(f) as fh:
         rec = json.load(fh)
-    src = os.path.join(ROOT, "routing_dispatch_expert_router_amd", "csrc", "gemm.hip")
-    with open(src, "rb") as fh:
-        if hashlib.sha256(fh.read()).hexdigest() != rec.get("gemm_source_sha256"):
-            return None
+    if rec.get("ffn_source_sha256") != ffn_source_sha256():
+        return None
     return rec["traffic_bytes"]
+
+
+def fused_mlp(cfg):
+    """Whether the library runs this workload's routed experts through the fused MLP kernel
+    (bf16 experts of width 64, 128 or 256, hidden width a multiple of 32)."""
+    return cfg.act_dtype == 1 and cfg.d_head in (64, 128, 256) and cfg.d_ff % 32 == 0
 
 
 def time_backward(cfg, moe, W, x, inp, args, stream):
@@ -407,7 +420,10 @@ def measure(cfg, args, evict, headline):
         log(f"[bench]   {k:10s} " + "  ".join(f"{a}={b:.4g}" for a, b in v.items()))
     res = {"workload": cfg.name, "T": T, "kept_rows": R, "ms_per_step": ms_step, "tokens_per_s": T / (ms_step * 1e-3),
            "stages": stages, "graph": graph, "backward": bwd,
-           "roofline": {"kernel": "grouped_gemm_kernel, expert FFN (gate/up and down launches, rows gathered from x)",
+           "roofline": {"kernel": ("mlp_kernel, expert FFN (fused gate/up, activation and down product, rows "
+                                   "gathered from the latent input)" if fused_mlp(cfg) else
+                                   "grouped_gemm_kernel, expert FFN (gate/up and down launches, rows gathered from x)")
+                        + (" + shared experts (plain grouped_gemm_kernel launches)" if cfg.n_shared else ""),
                         "bound": "mfma", "achieved": ffn_tf, "peak": peak, "unit": "TFLOP/s", "frac": ffn_tf / peak,
                         "frac_warm": alg["ffn_flops"] / warm / 1e12 / peak,
                         "traffic": measured_traffic(cfg),

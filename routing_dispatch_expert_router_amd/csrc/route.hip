@@ -416,9 +416,12 @@ __device__ __forceinline__ void route_scores_staged(const RouteArgs &a, u32x4 *r
   for (int c = 0; c < ROUTE_STAGES - 1; ++c)
     if (c < nch) issue(c, c);
   for (int c = 0; c < nch; ++c) {
-    // chunk c landed (the loads of the chunks after it, if all were issued, may still be in flight)
+    // chunk c landed (the loads of the chunks after it, if all were issued, may
+    // still be in flight) and this wave's reads of the stage refilled next are
+    // done; a fence-free barrier, so those later chunks stay in flight
     if (c + ROUTE_STAGES - 2 < nch) wait_vmcnt<(ROUTE_STAGES - 2) * G::NL>(); else wait_vmcnt0();
-    __syncthreads();
+    wait_lgkmcnt0();
+    barrier_nofence();
     if (c + ROUTE_STAGES - 1 < nch) issue(c + ROUTE_STAGES - 1, (c + ROUTE_STAGES - 1) % ROUTE_STAGES);
     compute(c % ROUTE_STAGES);
   }
