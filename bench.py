@@ -234,15 +234,19 @@ def workload(name):
 
 
 class Evict:
-    """A 1 GiB device buffer; touch() reads and writes all of it, which evicts the L2 caches and the
-    256 MiB Infinity Cache (and keeps the GPU busy for a few hundred microseconds)."""
+    """A 1 GiB device buffer.  touch() writes all of it (a scratch write that evicts the L2 caches
+    and the 256 MiB Infinity Cache), then reads it back: the read pass forces the write-back of the
+    dirty lines the write left in the caches, so the timed call that follows finds its inputs out
+    of cache without paying for another buffer's write-back.  A few hundred microseconds."""
 
     def __init__(self):
         import torch
         self.buf = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
+        self.sink = None
 
     def touch(self):
         self.buf.add_(1)
+        self.sink = self.buf.max()
 
 
 def time_stage(fn, stream, evict, reps):
