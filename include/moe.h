@@ -291,6 +291,27 @@ int moe_dispatch_noalloc(const moe_config *cfg, const int32_t *topk_idx, const f
                          void *x_perm, hipStream_t stream);
 
 /*
+ * moe_check_topk -- checked mode for caller-supplied routing, to run before moe_dispatch.
+ * [the top-K selector of "MoE技术演进", "Adaptive Mixtures of Local Experts":
+ * each token names K distinct experts; per head inside the head's own experts,
+ * "多头 LatentMoE 与 Head Parallel", 方法论 item 2]
+ *
+ * moe_dispatch's behaviour is undefined for a topk_idx it could not have got
+ * from moe_route; this call tells whether one is such.  It counts the slots of
+ * topk_idx [T, K] that name an expert outside their head's range
+ * [h*E_h, (h+1)*E_h) (h = slot / top_k) or repeat an expert an earlier slot of
+ * the same token and head named (expert choice: every slot j must be expert j),
+ * and writes the count to *status: 0 means valid.
+ *   topk_idx  [T, K] int32 in (device)
+ *   status    [1] int32 out (device); written by one launch, so the caller may
+ *             read it after synchronising the stream, or pass it on to its own
+ *             kernels
+ * Errors: MOE_ERR_ARG for a bad config or a NULL pointer.  One launch of one
+ * block; allocates nothing, never synchronises.
+ */
+int moe_check_topk(const moe_config *cfg, const int32_t *topk_idx, int32_t *status, hipStream_t stream);
+
+/*
  * moe_expert_ffn -- every routed expert on its rows of x_perm, plus the shared experts.
  * ["MoE技术演进", "GShard" item 3 (FFN_e); "DeepSeekMoE" item 2 (shared experts);
  * "大语言模型并行策略（七）：专家并行", "MoE 模型的参数量分析" (SwiGLU, 3 matrices)]

@@ -40,7 +40,7 @@ _OPTIONAL_FIELDS = {"route_mode", "sel_bias_gate", "seq_len"}
 
 # exported symbols, as declared in include/moe.h
 SYMBOLS = ["moe_workspace_bytes", "moe_rows_upper_bound", "moe_status_str", "moe_check_config",
-           "moe_route", "moe_route_ex", "moe_dispatch", "moe_dispatch_noalloc", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd",
+           "moe_route", "moe_route_ex", "moe_dispatch", "moe_dispatch_noalloc", "moe_check_topk", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd",
            "moe_sel_bias_update", "moe_backward_workspace_bytes", "moe_transpose_weights", "moe_layer_bwd"]
 
 
@@ -94,6 +94,7 @@ def _load():
         "moe_sel_bias_update": (I, [Z, P, P, ctypes.c_float, P]),
         "moe_dispatch": (I, [Z, P, P, P, P, P, P, P, P, P, P, S, P]),
         "moe_dispatch_noalloc": (I, [Z, P, P, P, P, P, P, P, P, P, P]),
+        "moe_check_topk": (I, [Z, P, P, P]),
         "moe_expert_ffn": (I, [Z, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
         "moe_expert_ffn_gather": (I, [Z, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]),
         "moe_combine": (I, [Z, P, P, P, P, P, P, P]),
@@ -229,6 +230,12 @@ def moe_dispatch_noalloc(cfg, topk_idx, topk_w, x, demand, counts, offsets, row_
     return _check(_lib.moe_dispatch_noalloc(ctypes.byref(c), _p(topk_idx), _p(topk_w), _p(x), _p(demand), _p(counts),
                                             _p(offsets), _p(row_of), _p(src_of), _p(x_perm), _stream(stream)),
                   "moe_dispatch_noalloc")
+
+
+def moe_check_topk(cfg, topk_idx, status, stream=None):
+    """Checked mode: the count of invalid slots of topk_idx written to status (int32 [1], device)."""
+    c = _c(cfg)
+    return _check(_lib.moe_check_topk(ctypes.byref(c), _p(topk_idx), _p(status), _stream(stream)), "moe_check_topk")
 
 
 def moe_expert_ffn(cfg, x_perm, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws,

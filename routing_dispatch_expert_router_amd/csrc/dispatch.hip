@@ -397,6 +397,47 @@ __global__ __launch_bounds__(256) void disp_scatter_kernel(
   }
 }
 
+// ---------------------------------------------------------------- checked mode
+// Validation of caller-supplied routing (moe_check_topk): one block counts the
+// slots whose expert lies outside its head's range [h*E_h, (h+1)*E_h) and the
+// slots that repeat an expert an earlier slot of the same token and head
+// already named (expert choice: slot j of every token must be expert j), and
+// writes the count; no atomics on global memory, no initial value needed.
+__global__ __launch_bounds__(1024) void topk_check_kernel(const int32_t *__restrict__ idx, int T, int H, int k,
+                                                          int Eh, int all_experts, int32_t *__restrict__ status) {
+  __shared__ int part[1024];
+  const int K = H * k;
+  int bad = 0;
+  for (long t = threadIdx.x; t < T; t += 1024) {
+    const int32_t *row = idx + t * K;
+    for (int h = 0; h < H; ++h) {
+      for (int j = 0; j < k; ++j) {
+        const int e = row[h * k + j];
+        if (all_experts) {
+          bad += e != h * k + j;
+          continue;
+        }
+        bool b = e < h * Eh || e >= (h + 1) * Eh;
+        for (int i = 0; i < j && !b; ++i) b = row[h * k + i] == e;
+        bad += b;
+      }
+    }
+  }
+  part[threadIdx.x] = bad;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *status = part[0];
+}
+
+int launch_topk_check(const Shape &s, const int32_t *topk_idx, int32_t *status, hipStream_t st) {
+  hipLaunchKernelGGL(topk_check_kernel, dim3(1), dim3(1024), 0, st, topk_idx, s.T, s.H, s.expert_choice ? s.E : s.k,
+                     s.Eh, s.expert_choice ? 1 : 0, status);
+  return launch_status("routing check");
+}
+
 // ---------------------------------------------------------------- host
 static long n_chunks(const Shape &s) { return ((long)s.T * s.K + CH - 1) / CH; }
 

@@ -48,6 +48,8 @@ int launch_route(const Shape &s, const void *x, const void *w_router, const floa
 int launch_sel_bias_update(const Shape &s, const int32_t *load, float *sel_bias, float gamma, hipStream_t st);
 
 // ---------------------------------------------------------------- dispatch
+// checked mode: the count of invalid topk_idx slots into *status (one block)
+int launch_topk_check(const Shape &s, const int32_t *topk_idx, int32_t *status, hipStream_t st);
 size_t dispatch_ws_bytes(const Shape &s);
 // the library-held dispatch scratch (moe_dispatch_noalloc): its size, and
 // its device address on the current device (0, or -4 when HIP fails)

@@ -370,6 +370,16 @@ int moe_dispatch_noalloc(const moe_config *cfg, const int32_t *topk_idx, const f
                                     stream));
 }
 
+int moe_check_topk(const moe_config *cfg, const int32_t *topk_idx, int32_t *status, hipStream_t stream) {
+  Shape s;
+  int rc = make_shape(cfg, &s);
+  if (rc) return rc;
+  if (!status || (!topk_idx && s.T)) return MOE_ERR_ARG;
+  if (misaligned({topk_idx, status})) return MOE_ERR_ARG;
+  clear_stale_error();
+  return rc_of(moe::launch_topk_check(s, topk_idx, status, stream));
+}
+
 int moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *offsets, const void *w1, const void *w3,
                    const void *w2, void *y_perm, const void *x_shared, const void *ws1, const void *ws3,
                    const void *ws2, void *shared_out, void *ws, size_t ws_bytes, hipStream_t stream) {

@@ -364,3 +364,17 @@ def test_noalloc_dispatch_checks_before_launching():
     assert moe.moe_check_config(CONFIGS[3].with_(T=1_500_000, d_model=320, d_head=320, d_ff=64, n_shared=0)) == 0
     assert lib.moe_dispatch_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, fake, fake, fake, None,
                                     None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_check_topk_argument_checks():
+    """The checked mode's entry point refuses a NULL status, NULL indices (T > 0), a NULL or
+    invalid config, and a misaligned pointer, before any HIP call."""
+    lib = moe._lib
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
+    c1 = moe.config_struct(CONFIGS[1])
+    assert lib.moe_check_topk(ctypes.byref(c1), fake, None, None) == moe.MOE_ERR_ARG
+    assert lib.moe_check_topk(ctypes.byref(c1), None, fake, None) == moe.MOE_ERR_ARG
+    assert lib.moe_check_topk(None, fake, fake, None) == moe.MOE_ERR_ARG
+    assert lib.moe_check_topk(ctypes.byref(c1), ctypes.c_void_p(0x1002), fake, None) == moe.MOE_ERR_ARG
+    bad = moe.config_struct(CONFIGS[1].with_(n_experts=0))
+    assert lib.moe_check_topk(ctypes.byref(bad), fake, fake, None) != moe.MOE_OK
