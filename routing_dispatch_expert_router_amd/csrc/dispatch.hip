@@ -8,15 +8,18 @@
 // "DeepSeek-V3" item 5.  Count tokens per expert first, then fill each
 // expert's buffer: "大语言模型并行策略（七）：专家并行", "MoE 中的 all-to-all 通信".
 //
-// Pipeline (flat assignment a = t*K + j, chunks of CH consecutive a):
-//   hist      per-chunk expert histogram (LDS integer atomics: order-free)
-//   rank      each chunk's block sums the earlier chunks' histograms (its base
-//             per expert), applies the keep rule to the demand and scans the
-//             kept counts into offsets (block 0 writes demand, counts,
-//             offsets); then the stable rank of every a among the earlier a of
-//             its expert = chunk base + per-wave prefix + in-wave ballot
-//             match; writes row_of / src_of (NONE, CAPACITY) or the
-//             expert-sorted segment list (AFFINITY)
+// Pipeline (flat assignment a = t*K + j):
+//   hist      per-chunk expert histogram of HIST_CA consecutive a (LDS integer
+//             atomics: order-free); skipped when the router's per-block choice
+//             counts are at hand (the layer), which are the same histogram
+//             over chunks of its blocks' tokens
+//   rank      each block adds the histograms of the chunks before its own (its
+//             base per expert) and of all chunks (the demand), applies the keep
+//             rule to the demand and scans the kept counts into offsets (block
+//             0 writes demand, counts, offsets); then the stable rank of every
+//             a among the earlier a of its expert = base + per-wave prefix +
+//             in-wave ballot match; writes row_of / src_of (NONE, CAPACITY) or
+//             the expert-sorted segment list (AFFINITY)
 //   affinity  one block per expert: radix select of the keep-th largest gate,
 //             then two ordered scans -> row_of / src_of
 //   scatter   token-major copy: each 16 bytes of x are read once and stored
@@ -56,52 +59,32 @@ int dispatch_scratch(void **out) {
   return 0;
 }
 
-constexpr int CH = 1024;  // assignments per chunk (256 threads x 4)
+// ---------------------------------------------------------------- counting and ranking
+// A chunk histogram hist[q][E] holds the expert counts of the assignments
+// [q*ca, (q+1)*ca).  disp_hist_kernel writes one with ca = HIST_CA; the
+// router writes one as a by-product (each of its blocks counts the choices
+// of its tokens: ca = tokens per router block x K), which lets the layer skip
+// the histogram launch.
+constexpr int HIST_CA = 1024;     // assignments per histogram block (256 threads x 4)
+constexpr int RANK_NT = 256;      // threads per ranking block
+constexpr int RANK_WAVES = RANK_NT / 64;
+constexpr int RANK_TARGET = 1024; // assignments per ranking block, about
+constexpr int RANK_PF = 4;        // expert ids per lane held in registers (256 per wave)
 
 __global__ __launch_bounds__(256) void disp_hist_kernel(const int32_t *__restrict__ idx, long n, int E,
                                                         int32_t *__restrict__ hist) {
   extern __shared__ int32_t h[];
+  const long a0 = (long)blockIdx.x * HIST_CA + threadIdx.x;
+  int ev[HIST_CA / 256];
+#pragma unroll
+  for (int i = 0; i < HIST_CA / 256; ++i) ev[i] = a0 + i * 256 < n ? idx[a0 + i * 256] : -1;
   for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
   __syncthreads();
-  long a0 = (long)blockIdx.x * CH;
-  for (int i = threadIdx.x; i < CH; i += 256) {
-    long a = a0 + i;
-    if (a < n) atomicAdd(&h[idx[a]], 1);
-  }
+#pragma unroll
+  for (int i = 0; i < HIST_CA / 256; ++i)
+    if (ev[i] >= 0) atomicAdd(&h[ev[i]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) hist[(long)blockIdx.x * E + e] = h[e];
-}
-
-// exclusive scan of v[0..E) by a 256-thread block (E <= 1024, 4 per thread),
-// in integers and a fixed order; returns the total
-__device__ int block_scan_experts(const int *v, int *out, int E, int *tmp) {
-  const int tid = threadIdx.x;
-  int loc[4], sum = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
-    loc[i] = e < E ? v[e] : 0;
-    sum += loc[i];
-  }
-  tmp[tid] = sum;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    int u = tid >= o ? tmp[tid - o] : 0;
-    __syncthreads();
-    tmp[tid] += u;
-    __syncthreads();
-  }
-  int run = tmp[tid] - sum;
-  const int total = tmp[255];
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
-    if (e < E) out[e] = run;
-    run += loc[i];
-  }
-  __syncthreads();
-  return total;
 }
 
 // lanes of this wave holding the same expert id (E <= 1024 -> 10 bits)
@@ -115,92 +98,232 @@ __device__ __forceinline__ uint64_t match_mask(int e, bool active) {
   return active ? m : 0ull;
 }
 
-// One block (4 waves) per chunk; wave w owns a in [a0 + w*CH/4, a0 + (w+1)*CH/4).
-__global__ __launch_bounds__(256) void disp_rank_kernel(
-    const int32_t *__restrict__ idx, long n, int E, int nchunks, const int32_t *__restrict__ hist, int drop,
-    int C, int keep_num, int keep_den, int32_t *__restrict__ demand, int32_t *__restrict__ counts,
+// Exclusive scans of two values per thread over a RANK_NT-thread block (thread
+// order) and their totals; integer sums, so the order of the additions does
+// not matter.  wsum is not reused afterwards.
+__device__ __forceinline__ int2 rank_block_scan2(int v0, int v1, int2 *wsum, int2 *total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x0 = v0, x1 = v1;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y0 = __shfl_up(x0, o), y1 = __shfl_up(x1, o);
+    if (lane >= o) {
+      x0 += y0;
+      x1 += y1;
+    }
+  }
+  if (lane == 63) wsum[w] = make_int2(x0, x1);
+  __syncthreads();
+  int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
+#pragma unroll
+  for (int q = 0; q < RANK_WAVES; ++q) {
+    const int2 s = wsum[q];
+    b0 += q < w ? s.x : 0;
+    b1 += q < w ? s.y : 0;
+    t0 += s.x;
+    t1 += s.y;
+  }
+  *total = make_int2(t0, t1);
+  return make_int2(b0 + x0 - v0, b1 + x1 - v1);
+}
+
+// Geometry of the histogram read: groups of W consecutive experts (W = 4
+// when E is a multiple of 4: 16-byte loads), P parts per group; thread
+// (part p, group g) adds chunks p, p + P, ...
+struct RankGeom {
+  int W, G, P;
+};
+__host__ __device__ inline RankGeom rank_geom(int E, int nq) {
+  RankGeom r;
+  r.W = (E % 4 == 0) ? 4 : 1;
+  r.G = E / r.W;
+  r.P = RANK_NT / r.G > 0 ? RANK_NT / r.G : 1;
+  if (r.P > nq) r.P = nq > 0 ? nq : 1;
+  return r;
+}
+// dynamic LDS of disp_rank_kernel, in ints: per-wave counts [4][E], the two
+// partial-sum matrices [P][E], offsets [2][E]
+__host__ __device__ inline long rank_lds_ints(int E, int nq) {
+  return (long)RANK_WAVES * E + 2L * rank_geom(E, nq).P * E + 2L * E;
+}
+
+// One block (4 waves) per m consecutive histogram chunks; wave w owns the
+// w-th quarter of the block's assignments.  The block adds the chunk
+// histograms (the earlier chunks: its base per expert; all: the demand),
+// applies the keep rule and scans the kept counts into offsets (block 0
+// writes demand, counts, offsets); each wave counts its own assignments per
+// expert, and the stable rank of an assignment among the earlier ones of its
+// expert is base + the earlier waves' counts + the earlier steps of its wave
+// + the lower lanes of its step holding the same expert (ballot match).
+// Writes row_of / src_of (NONE, CAPACITY) or the expert-sorted segment list
+// (AFFINITY).
+__global__ __launch_bounds__(RANK_NT) void disp_rank_kernel(
+    const int32_t *__restrict__ idx, long n, int E, const int32_t *__restrict__ hist, int nq, long ca, int m,
+    int drop, int C, int keep_num, int keep_den, int32_t *__restrict__ demand, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ all_off_out, int32_t *__restrict__ row_of,
     int32_t *__restrict__ src_of, int32_t *__restrict__ seg) {
   extern __shared__ int32_t sm[];
-  int32_t *cnt = sm;            // [4][E] per-wave counts, then running ranks
-  int32_t *base = sm + 4 * E;   // [E] this chunk's base per expert
-  int32_t *dem = base + E;      // [E] demand
-  int32_t *kept = dem + E;      // [E] kept counts
-  int32_t *off = kept + E;      // [E] first row of each expert
-  int32_t *aoff = off + E;      // [E] first slot of each expert in the affinity segments
-  __shared__ int tmp[256];
+  const RankGeom rg = rank_geom(E, nq);
+  int32_t *cnt = sm;                         // [4][E] per-wave counts, then running ranks
+  int32_t *pb = cnt + RANK_WAVES * E;        // [P][E] partial sums over the earlier chunks
+  int32_t *pt = pb + (size_t)rg.P * E;       // [P][E] partial sums over all chunks
+  int32_t *off = pt + (size_t)rg.P * E;      // [E] first row of each expert
+  int32_t *aoff = off + E;                   // [E] first slot of each expert in the affinity segments
+  __shared__ int2 wsum[RANK_WAVES];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int c = blockIdx.x;
-  for (int e = tid; e < E; e += 256) {
-    int b = 0, tot = 0;
-#pragma unroll 8
-    for (int q = 0; q < nchunks; ++q) {
-      const int v = hist[(long)q * E + e];
-      b += q < c ? v : 0;
-      tot += v;
+  const int q0 = blockIdx.x * m;
+  const long a_beg = (long)q0 * ca, a_end = min(n, (long)min(nq, q0 + m) * ca);
+  const long sg = (a_end - a_beg + RANK_WAVES - 1) / RANK_WAVES;
+  const long s0 = min(a_end, a_beg + (long)w * sg), s1 = min(a_end, s0 + sg);
+  // the wave's first RANK_PF * 64 expert ids, loaded once
+  int ev[RANK_PF];
+#pragma unroll
+  for (int i = 0; i < RANK_PF; ++i) {
+    const long a = s0 + i * 64 + lane;
+    ev[i] = a < s1 ? idx[a] : 0;
+  }
+  // partial sums of the chunk histograms (coalesced rows, W experts per load):
+  // slot (part p, group g) adds chunks p, p + P, ...; P * G <= max(RANK_NT, G)
+  for (int slot = tid; slot < rg.P * rg.G; slot += RANK_NT) {
+    int sb[4] = {0, 0, 0, 0}, st[4] = {0, 0, 0, 0};
+    const int g = slot % rg.G, p = slot / rg.G;
+    if (rg.W == 4) {
+#pragma unroll 16
+      for (int q = p; q < nq; q += rg.P) {
+        const int4 v = reinterpret_cast<const int4 *>(hist + (size_t)q * E)[g];
+        const bool before = q < q0;
+        st[0] += v.x; st[1] += v.y; st[2] += v.z; st[3] += v.w;
+        sb[0] += before ? v.x : 0; sb[1] += before ? v.y : 0;
+        sb[2] += before ? v.z : 0; sb[3] += before ? v.w : 0;
+      }
+    } else {
+#pragma unroll 16
+      for (int q = p; q < nq; q += rg.P) {
+        const int v = hist[(size_t)q * E + g];
+        st[0] += v;
+        sb[0] += q < q0 ? v : 0;
+      }
     }
-    base[e] = b;
-    dem[e] = tot;
-    kept[e] = drop == DROP_NONE       ? tot
-              : drop == DROP_AFFINITY ? (int)(((long)keep_num * tot + keep_den - 1) / keep_den)
-                                      : min(tot, C);  // capacity, or the experts' top-C choice
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < rg.W) {
+        pb[(size_t)p * E + g * rg.W + j] = sb[j];
+        pt[(size_t)p * E + g * rg.W + j] = st[j];
+      }
+  }
+  // per-wave counts of the wave's own assignments (the row is the wave's own)
+  for (int e = lane; e < E; e += 64) cnt[w * E + e] = 0;
+#pragma unroll
+  for (int i = 0; i < RANK_PF; ++i)
+    if (s0 + i * 64 + lane < s1) atomicAdd(&cnt[w * E + ev[i]], 1);
+  for (long a = s0 + RANK_PF * 64 + lane; a < s1; a += 64) atomicAdd(&cnt[w * E + idx[a]], 1);
+  __syncthreads();
+  // base (earlier chunks) and demand of every expert: groups of L lanes (L the
+  // power of two >= P, at most 64) add the P partial sums of one expert each
+  {
+    int L = 1;
+    while (L < rg.P && L < 64) L <<= 1;
+    const int per = 64 / L, sub = lane % L;
+    for (int e0 = w * per; e0 < E; e0 += RANK_WAVES * per) {  // wave-uniform
+      const int e = e0 + lane / L;
+      int vb = 0, vt = 0;
+      if (e < E)
+        for (int p = sub; p < rg.P; p += L) {
+          vb += pb[(size_t)p * E + e];
+          vt += pt[(size_t)p * E + e];
+        }
+      for (int o = L >> 1; o > 0; o >>= 1) {
+        vb += __shfl_xor(vb, o);
+        vt += __shfl_xor(vt, o);
+      }
+      if (e < E && sub == 0) {
+        off[e] = vb;   // base, until the offsets replace it
+        aoff[e] = vt;  // demand, until the segment offsets replace it
+      }
+    }
   }
   __syncthreads();
-  const int R = block_scan_experts(kept, off, E, tmp);
-  if (drop >= DROP_AFFINITY) block_scan_experts(dem, aoff, E, tmp);
-  if (c == 0) {
-    for (int e = tid; e < E; e += 256) {
-      demand[e] = dem[e];
-      counts[e] = kept[e];
-      offsets[e] = off[e];
-      if (drop >= DROP_AFFINITY) all_off_out[e] = aoff[e];
+  // experts 4*tid .. 4*tid + 3: kept counts, and the per-wave counts turned
+  // into running ranks
+  int kept[4], tot[4];
+  int skept = 0, stot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    kept[i] = tot[i] = 0;
+    if (e < E) {
+      const int vt = aoff[e];
+      tot[i] = vt;
+      kept[i] = drop == DROP_NONE       ? vt
+                : drop == DROP_AFFINITY ? (int)(((long)keep_num * vt + keep_den - 1) / keep_den)
+                                        : min(vt, C);  // capacity
+      int run = off[e];
+#pragma unroll
+      for (int q = 0; q < RANK_WAVES; ++q) {
+        const int v = cnt[q * E + e];
+        cnt[q * E + e] = run;
+        run += v;
+      }
     }
-    if (tid == 0) {
-      offsets[E] = R;
-      if (drop >= DROP_AFFINITY) all_off_out[E] = (int)n;
+    skept += kept[i];
+    stot += tot[i];
+  }
+  int2 total;
+  const int2 ex = rank_block_scan2(skept, stot, wsum, &total);
+  {
+    int ok = ex.x, ot = ex.y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid * 4 + i;
+      if (e < E) {
+        off[e] = ok;
+        aoff[e] = ot;
+        if (blockIdx.x == 0) {
+          demand[e] = tot[i];
+          counts[e] = kept[i];
+          offsets[e] = ok;
+          if (drop >= DROP_AFFINITY) all_off_out[e] = ot;
+        }
+      }
+      ok += kept[i];
+      ot += tot[i];
     }
   }
-  constexpr int SUB = CH / 4;
-  const long a0 = (long)c * CH + (long)w * SUB;
-  for (int i = tid; i < 4 * E; i += 256) cnt[i] = 0;
-  __syncthreads();
-  for (int i = lane; i < SUB; i += 64) {
-    long a = a0 + i;
-    if (a < n) atomicAdd(&cnt[w * E + idx[a]], 1);
-  }
-  __syncthreads();
-  // exclusive prefix over the block's waves, plus the chunk base
-  for (int e = tid; e < E; e += 256) {
-    int run = base[e];
-    for (int q = 0; q < 4; ++q) {
-      int v = cnt[q * E + e];
-      cnt[q * E + e] = run;
-      run += v;
-    }
+  if (blockIdx.x == 0 && tid == 0) {
+    offsets[E] = total.x;
+    if (drop >= DROP_AFFINITY) all_off_out[E] = (int)n;
   }
   __syncthreads();
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int i0 = 0; i0 < SUB; i0 += 64) {
-    long a = a0 + i0 + lane;
-    bool act = a < n;
-    int e = act ? idx[a] : 0;
-    uint64_t m = match_mask(e, act);
-    int before = __popcll(m & lt);
+  auto rank_step = [&](long a, int e, bool act) {
+    const uint64_t mm = match_mask(e, act);
+    const int before = __popcll(mm & lt);
     int rank = 0;
     if (act) rank = cnt[w * E + e] + before;
     // the highest lane of each group advances the counter (after every lane read it)
-    bool leader = act && ((m >> lane) >> 1) == 0ull;
+    const bool leader = act && ((mm >> lane) >> 1) == 0ull;
     if (leader) cnt[w * E + e] = rank + 1;
     if (act) {
       if (drop >= DROP_AFFINITY) {
         seg[aoff[e] + rank] = (int32_t)a;
       } else {
-        bool kp = (drop == DROP_NONE) || rank < C;
-        int row = kp ? off[e] + rank : -1;
+        const bool kp = (drop == DROP_NONE) || rank < C;
+        const int row = kp ? off[e] + rank : -1;
         row_of[a] = row;
         if (kp) src_of[row] = (int32_t)a;
       }
     }
+  };
+#pragma unroll
+  for (int i = 0; i < RANK_PF; ++i) {
+    if (s0 + i * 64 >= s1) break;  // wave-uniform
+    const long a = s0 + i * 64 + lane;
+    rank_step(a, ev[i], a < s1);
+  }
+  for (long a0 = s0 + RANK_PF * 64; a0 < s1; a0 += 64) {  // wave-uniform
+    const long a = a0 + lane;
+    const bool act = a < s1;
+    rank_step(a, act ? idx[a] : 0, act);
   }
 }
 
@@ -439,14 +562,19 @@ int launch_topk_check(const Shape &s, const int32_t *topk_idx, int32_t *status, 
 }
 
 // ---------------------------------------------------------------- host
-static long n_chunks(const Shape &s) { return ((long)s.T * s.K + CH - 1) / CH; }
+static long n_chunks(const Shape &s) { return ((long)s.T * s.K + HIST_CA - 1) / HIST_CA; }
 
-size_t dispatch_ws_bytes(const Shape &s) {
-  size_t b = align_up((size_t)n_chunks(s) * s.E * 4, 256);  // chunk histograms
-  b += align_up((size_t)(s.E + 1) * 4, 256);                  // all_off
+static size_t dispatch_tail_bytes(const Shape &s) {
+  size_t b = align_up((size_t)(s.E + 1) * 4, 256);                         // all_off
   if (s.drop >= DROP_AFFINITY) b += align_up((size_t)s.T * s.K * 4, 256);  // expert-sorted segments
   return b;
 }
+
+size_t dispatch_ws_bytes(const Shape &s) {
+  return align_up((size_t)n_chunks(s) * s.E * 4, 256) + dispatch_tail_bytes(s);  // + chunk histograms
+}
+
+size_t dispatch_after_route_ws_bytes(const Shape &s) { return route_stats_bytes(s) + dispatch_tail_bytes(s); }
 
 template <typename TA>
 static void launch_scatter(const Shape &s, const void *x, const int32_t *row_of, void *x_perm, hipStream_t st) {
@@ -466,12 +594,16 @@ static void launch_scatter(const Shape &s, const void *x, const int32_t *row_of,
 
 int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w, const void *x,
                     int32_t *demand, int32_t *counts, int32_t *offsets, int32_t *row_of, int32_t *src_of,
-                    void *x_perm, void *ws, hipStream_t st) {
+                    void *x_perm, void *ws, hipStream_t st, const int32_t *route_hist) {
   const long n = (long)s.T * s.K;
-  const long nc = n_chunks(s);
+  const bool rh = route_hist != nullptr;
+  const RouteGeom rgeo = route_geometry(s);
+  // chunk histograms: the router's (chunks of its blocks' tokens) or this call's own
+  const long nq = rh ? rgeo.nbx : n_chunks(s);
+  const long ca = rh ? (long)rgeo.tb * s.K : HIST_CA;
   char *p = (char *)ws;
-  int32_t *hist = (int32_t *)p;
-  p += align_up((size_t)nc * s.E * 4, 256);
+  const int32_t *hist = rh ? route_hist : (const int32_t *)p;
+  p += rh ? route_stats_bytes(s) : align_up((size_t)nq * s.E * 4, 256);
   int32_t *all_off = (int32_t *)p;
   p += align_up((size_t)(s.E + 1) * 4, 256);
   int32_t *seg = (s.drop >= DROP_AFFINITY) ? (int32_t *)p : nullptr;
@@ -482,10 +614,17 @@ int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w
                        all_off);
     if (int rc = launch_status("dispatch counts")) return rc;
   } else {
-    hipLaunchKernelGGL(disp_hist_kernel, dim3(nc), dim3(256), s.E * 4, st, topk_idx, n, s.E, hist);
-    if (int rc = launch_status("dispatch histogram")) return rc;
-    hipLaunchKernelGGL(disp_rank_kernel, dim3(nc), dim3(256), 9 * s.E * 4, st, topk_idx, n, s.E, (int)nc, hist,
-                       s.drop, s.C, s.keep_num, s.keep_den, demand, counts, offsets, all_off, row_of, src_of, seg);
+    if (!rh) {
+      hipLaunchKernelGGL(disp_hist_kernel, dim3((unsigned)nq), dim3(256), s.E * 4, st, topk_idx, n, s.E,
+                         const_cast<int32_t *>(hist));
+      if (int rc = launch_status("dispatch histogram")) return rc;
+    }
+    const int m = (int)std::max<long>(1, RANK_TARGET / ca);
+    const long nb = (nq + m - 1) / m;
+    const size_t lds = (size_t)rank_lds_ints(s.E, (int)nq) * 4;
+    hipLaunchKernelGGL(disp_rank_kernel, dim3((unsigned)nb), dim3(RANK_NT), lds, st, topk_idx, n, s.E, hist,
+                       (int)nq, ca, m, s.drop, s.C, s.keep_num, s.keep_den, demand, counts, offsets, all_off, row_of,
+                       src_of, seg);
     if (int rc = launch_status("dispatch rank")) return rc;
   }
   if (s.drop >= DROP_AFFINITY) {

@@ -40,6 +40,11 @@ struct RouteGeom {
 RouteGeom route_geometry(const Shape &s);
 bool route_supported(const Shape &s);
 size_t route_ws_bytes(const Shape &s);
+// the router's per-block statistics at the start of its workspace: the
+// probability sums [nbx][E], then the choice counts [nbx][E] at
+// route_hist_offset(s); route_stats_bytes(s) covers both
+size_t route_hist_offset(const Shape &s);
+size_t route_stats_bytes(const Shape &s);
 // hist_out: [nbx][E] per-block choice counts (blocks of route_geometry(s).tb
 // tokens), or NULL
 int launch_route(const Shape &s, const void *x, const void *w_router, const float *bias, const float *sel_bias,
@@ -51,13 +56,16 @@ int launch_sel_bias_update(const Shape &s, const int32_t *load, float *sel_bias,
 // checked mode: the count of invalid topk_idx slots into *status (one block)
 int launch_topk_check(const Shape &s, const int32_t *topk_idx, int32_t *status, hipStream_t st);
 size_t dispatch_ws_bytes(const Shape &s);
+// workspace of a dispatch that takes the router's choice counts (route_hist,
+// left in the same workspace at route_hist_offset(s) by launch_route)
+size_t dispatch_after_route_ws_bytes(const Shape &s);
 // the library-held dispatch scratch (moe_dispatch_noalloc): its size, and
 // its device address on the current device (0, or -4 when HIP fails)
 constexpr size_t DISPATCH_SCRATCH_MAX = (size_t)8 << 20;
 int dispatch_scratch(void **out);
 int launch_dispatch(const Shape &s, const int32_t *topk_idx, const float *topk_w, const void *x,
                     int32_t *demand, int32_t *counts, int32_t *offsets, int32_t *row_of, int32_t *src_of,
-                    void *x_perm, void *ws, hipStream_t st);
+                    void *x_perm, void *ws, hipStream_t st, const int32_t *route_hist = nullptr);
 
 // ---------------------------------------------------------------- backward
 // grouped-GEMM epilogues the backward selects at run time

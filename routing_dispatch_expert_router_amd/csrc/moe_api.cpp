@@ -90,6 +90,8 @@ size_t scratch_bytes(const Shape &s) {
   size_t m = moe::route_ws_bytes(s);
   size_t v = moe::dispatch_ws_bytes(s);
   if (v > m) m = v;
+  v = moe::dispatch_after_route_ws_bytes(s);  // the layer's dispatch keeps the router's counts
+  if (v > m) m = v;
   v = moe::ffn_ws_bytes(s);
   if (v > m) m = v;
   v = moe::dense_ws_bytes();
@@ -482,11 +484,13 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
       return rc;
     xin = z;
   }
+  // the router's per-block choice counts are the histogram dispatch needs: no histogram launch
+  int32_t *route_hist = (int32_t *)((char *)scratch + moe::route_hist_offset(s));
   if ((rc = rc_of(moe::launch_route(s, xin, w->w_router, w->router_bias, w->sel_bias, io->logits, mode, topk_idx,
-                                    topk_w, io->aux_loss, io->seq_loss, scratch, stream))))
+                                    topk_w, io->aux_loss, io->seq_loss, scratch, stream, route_hist))))
     return rc;
   if ((rc = rc_of(moe::launch_dispatch(s, topk_idx, topk_w, xin, demand, counts, offsets, row_of, src_of, x_perm,
-                                       scratch, stream))))
+                                       scratch, stream, s.expert_choice ? nullptr : route_hist))))
     return rc;
   if ((rc = rc_of(moe::launch_expert_ffn(s, x_perm ? x_perm : xin, x_perm ? nullptr : src_of, offsets, w->w1,
                                          w->w3, w->w2, y_perm, x, w->ws1, w->ws3, w->ws2, shared, scratch,

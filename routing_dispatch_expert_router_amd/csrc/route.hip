@@ -817,11 +817,14 @@ static size_t route_lds_bytes(const Shape &s, const RouteGeom &g, bool load) {
   return ((size_t)(load ? 1 : g.wk) * g.tb * s.Eh + 2 * s.Eh) * 4;
 }
 
+size_t route_hist_offset(const Shape &s) {
+  return align_up((size_t)route_geometry(s).nbx * s.E * 4, 256);  // past the per-block probability sums
+}
+
+size_t route_stats_bytes(const Shape &s) { return 2 * route_hist_offset(s); }
+
 size_t route_ws_bytes(const Shape &s) {
-  const RouteGeom g = route_geometry(s);
-  size_t b = 0;
-  b += align_up((size_t)g.nbx * s.E * 4, 256);  // per-block probability sums
-  b += align_up((size_t)g.nbx * s.E * 4, 256);  // per-block choice counts
+  size_t b = route_stats_bytes(s);  // per-block probability sums and choice counts
   if (s.seq_len > 0) {
     const size_t nb = (size_t)(s.T / s.seq_len) * ((s.seq_len + SEQ_CH - 1) / SEQ_CH);
     b += align_up((size_t)s.T * s.E * 4, 256);  // probabilities
@@ -887,9 +890,8 @@ int launch_route(const Shape &s, const void *x, const void *w_router, const floa
   const RouteGeom g = route_geometry(s);
   char *p = (char *)ws;
   float *psum = (float *)p;
-  p += align_up((size_t)g.nbx * s.E * 4, 256);
-  int32_t *hist = (int32_t *)p;
-  p += align_up((size_t)g.nbx * s.E * 4, 256);
+  int32_t *hist = (int32_t *)(p + route_hist_offset(s));
+  p += route_stats_bytes(s);
   float *probs = nullptr, *spsum = nullptr;
   int32_t *pcnt = nullptr;
   const int nseq = s.seq_len > 0 ? s.T / s.seq_len : 0, nch = s.seq_len > 0 ? (s.seq_len + SEQ_CH - 1) / SEQ_CH : 0;
