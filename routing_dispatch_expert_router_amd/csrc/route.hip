@@ -149,25 +149,64 @@ constexpr int ROUTE_EPL = 8;   // experts per lane at most (E_h <= 256, L <= 64)
 constexpr int ROUTE_KMAX = 8;
 
 // The scores of the block's TB tokens, finalised in LDS row-major [TB][Eh]
-// at sc: the WK partial sums added in wave order plus the bias, or (LOAD) the
-// given scores; -0.0 folded to +0.0; copied out when they are asked for.
-// Global traffic is coalesced rows; sc may alias the first partial sums.
-__device__ __forceinline__ void route_scores(const RouteArgs &a, const float *part, float *sc, int tb0) {
+// at sc: the WK partial sums added in wave order plus the bias (bsh: the
+// head's bias in LDS, or NULL), or (LOAD) the given scores; -0.0 folded to
+// +0.0; copied out when they are asked for.  Global traffic is coalesced
+// rows, the LOAD reads four per thread at a time; sc may alias the first
+// partial sums.
+__device__ __forceinline__ void route_scores(const RouteArgs &a, const float *part, float *sc, const float *bsh,
+                                             int tb0) {
   const int Eh = a.Eh, TB = a.TB, h = blockIdx.y;
   const int nt = min(TB, a.T - tb0);
-  for (int idx = threadIdx.x; idx < nt * Eh; idx += 256) {
-    const int tl = idx / Eh, e = idx - tl * Eh;
-    const size_t g = (size_t)(tb0 + tl) * a.E + (size_t)h * Eh + e;
-    float v;
-    if (a.load) {
-      v = a.logits_in[g];
-    } else {
-      v = part[idx];
-      for (int q = 1; q < a.WK; ++q) v += part[(size_t)q * TB * Eh + idx];
-      if (a.bias) v += a.bias[h * Eh + e];
-      if (a.logits_out) a.logits_out[g] = v + 0.0f;
+  const int n = nt * Eh;
+  if (a.load) {
+    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * 256) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = i0 + u * 256;
+        const int tl = idx / Eh, e = idx - tl * Eh;
+        v[u] = idx < n ? a.logits_in[(size_t)(tb0 + tl) * a.E + (size_t)h * Eh + e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * 256 < n) sc[i0 + u * 256] = v[u] + 0.0f;
     }
+    return;
+  }
+  for (int idx = threadIdx.x; idx < n; idx += 256) {
+    const int tl = idx / Eh, e = idx - tl * Eh;
+    float v = part[idx];
+    for (int q = 1; q < a.WK; ++q) v += part[(size_t)q * TB * Eh + idx];
+    if (bsh) v += bsh[e];
+    if (a.logits_out) a.logits_out[(size_t)(tb0 + tl) * a.E + (size_t)h * Eh + e] = v + 0.0f;
     sc[idx] = v + 0.0f;
+  }
+}
+
+// The head's router bias and selection bias for this thread's expert
+// (E_h <= 256 threads), loaded when the block starts so that the loads
+// overlap the scores, and stored to LDS (with the choice counts zeroed)
+// before the barrier that precedes route_scores.
+struct HeadBias {
+  float b, sb;
+};
+__device__ __forceinline__ HeadBias head_bias_load(const RouteArgs &a) {
+  HeadBias r{0.f, 0.f};
+  const int e = threadIdx.x, h = blockIdx.y;
+  if (e < a.Eh) {
+    if (a.bias) r.b = a.bias[h * a.Eh + e];
+    if (a.sel_bias) r.sb = a.sel_bias[h * a.Eh + e];
+  }
+  return r;
+}
+__device__ __forceinline__ void head_bias_store(const RouteArgs &a, const HeadBias &r, int32_t *cnt, float *sbias,
+                                                float *bsh) {
+  const int e = threadIdx.x;
+  if (e < a.Eh) {
+    cnt[e] = 0;
+    if (sbias) sbias[e] = r.sb;
+    if (bsh) bsh[e] = r.b;
   }
 }
 
@@ -351,6 +390,7 @@ __device__ __forceinline__ void route_select(const RouteArgs &a, float *sc, cons
 // so every W_r byte is fetched once per block and read from LDS once, and
 // the scores need no cross-wave sum.  Writes the unbiased scores to sc.
 constexpr int ROUTE_STAGES = 3;
+
 template <typename TE, int NF, int MW> struct StagedGeom {
   static constexpr int ROWS = 16 * NF + 16 * MW;       // W_r rows, then token rows
   static constexpr int NL = (ROWS * 8 + 255) / 256;     // direct loads per thread per stage
@@ -486,18 +526,17 @@ __global__ __launch_bounds__(256, (ST ? 2 : RouteRegs<TIN, TW, NF, MW>::OCC)) vo
   // counts, [Eh] bias, and (staged scores) the chunk ring
   extern __shared__ float rsm[];
   if constexpr (ST) {
-    const int Eh = a.Eh, TB = a.TB, h = blockIdx.y, tb0 = blockIdx.x * TB;
+    const int Eh = a.Eh, TB = a.TB, tb0 = blockIdx.x * TB;
     float *sc = rsm;
     int32_t *cnt = (int32_t *)(sc + (size_t)TB * Eh);
     float *sbias = a.sel_bias ? (float *)(cnt + Eh) : nullptr;
-    u32x4 *ring = (u32x4 *)(rsm + align_up((size_t)TB * Eh + 2 * Eh, 4));
-    for (int e = threadIdx.x; e < Eh; e += 256) {
-      cnt[e] = 0;
-      if (sbias) sbias[e] = a.sel_bias[h * Eh + e];
-    }
+    float *bsh = a.bias ? (float *)(cnt + 2 * Eh) : nullptr;
+    u32x4 *ring = (u32x4 *)(rsm + align_up((size_t)TB * Eh + 3 * Eh, 4));
+    const HeadBias hb = head_bias_load(a);
     if (!a.load) route_scores_staged<TIN, NF, MW>(a, ring, sc, tb0);
+    head_bias_store(a, hb, cnt, sbias, bsh);
     __syncthreads();
-    route_scores(a, sc, sc, tb0);  // one set of scores (WK == 1): bias, or the loaded scores
+    route_scores(a, sc, sc, bsh, tb0);  // one set of scores (WK == 1): bias, or the loaded scores
     __syncthreads();
     route_select(a, sc, sbias, cnt, tb0);
     __syncthreads();
@@ -517,10 +556,8 @@ __global__ __launch_bounds__(256, (ST ? 2 : RouteRegs<TIN, TW, NF, MW>::OCC)) vo
   float *part = rsm;
   int32_t *cnt = (int32_t *)(rsm + (size_t)(a.load ? 1 : a.WK) * TB * Eh);
   float *sbias = a.sel_bias ? (float *)(cnt + Eh) : nullptr;  // the head's selection bias
-  for (int e = tid; e < Eh; e += 256) {
-    cnt[e] = 0;
-    if (sbias) sbias[e] = a.sel_bias[h * Eh + e];
-  }
+  float *bsh = a.bias ? (float *)(cnt + 2 * Eh) : nullptr;     // the head's router bias
+  const HeadBias hb = head_bias_load(a);
 
   if (!a.load) {
     const int wt = wv / a.WK, wk = wv % a.WK;
@@ -618,9 +655,10 @@ __global__ __launch_bounds__(256, (ST ? 2 : RouteRegs<TIN, TW, NF, MW>::OCC)) vo
         }
     }
   }
+  head_bias_store(a, hb, cnt, sbias, bsh);
   __syncthreads();
 
-  route_scores(a, part, part, tb0);
+  route_scores(a, part, part, bsh, tb0);
   __syncthreads();
   route_select(a, part, sbias, cnt, tb0);
   __syncthreads();
@@ -808,13 +846,13 @@ RouteGeom route_geometry(const Shape &s) {
 }
 
 // LDS: the partial scores [WK][TB][E_h] (one set with LOAD), the choice
-// counts [E_h] and the head's selection bias [E_h]
+// counts [E_h], the head's selection bias [E_h] and router bias [E_h]
 static size_t route_lds_bytes(const Shape &s, const RouteGeom &g, bool load) {
-  if (g.st) {  // scores [TB][E_h], counts, bias, then the ring of staged chunks
+  if (g.st) {  // scores [TB][E_h], counts, biases, then the ring of staged chunks
     const size_t nl = ((size_t)(16 * g.nf + 16 * g.mw) * 8 + 255) / 256;
-    return align_up((size_t)g.tb * s.Eh + 2 * s.Eh, 4) * 4 + (load ? 0 : ROUTE_STAGES * nl * 256 * 16);
+    return align_up((size_t)g.tb * s.Eh + 3 * s.Eh, 4) * 4 + (load ? 0 : ROUTE_STAGES * nl * 256 * 16);
   }
-  return ((size_t)(load ? 1 : g.wk) * g.tb * s.Eh + 2 * s.Eh) * 4;
+  return ((size_t)(load ? 1 : g.wk) * g.tb * s.Eh + 3 * s.Eh) * 4;
 }
 
 size_t route_hist_offset(const Shape &s) {
