@@ -60,6 +60,7 @@ struct RouteArgs {
   float *psum;                 // [nbx][E] or NULL: per-block probability sums
   int32_t *hist;               // [nbx][E] or NULL: per-block choice counts
   int T, H, E, Eh, dh, ldx, k, L, Lg, n_groups, topk_groups, renorm, sel_gate, all_experts, load, WT, WK, TB;
+  int epl;                     // selection register slots per lane: 1, 2, 4 or ROUTE_EPL
   int exact;                   // probabilities in float64 (they decide the keep rule or the choice)
 };
 
@@ -218,9 +219,12 @@ __device__ __forceinline__ void head_bias_store(const RouteArgs &a, const HeadBi
 // L lanes per token.  Without groups lane j owns experts j, j+L, ...  With
 // groups the lanes are dealt to groups: Lg lanes per group (a power of two),
 // lane j = g*Lg + r owning experts g*gsz + r, g*gsz + r + Lg, ... of group g,
-// so a group's score is a reduction over its own Lg lanes only.
-__device__ __forceinline__ void route_select(const RouteArgs &a, float *sc, const float *sbias, int32_t *cnt,
-                                             int tb0) {
+// so a group's score is a reduction over its own Lg lanes only.  EPL: the
+// register slots per lane (at least the most experts a lane owns); the
+// unused slots hold -inf scores and zero weights, which change no result.
+template <int EPL>
+__device__ __forceinline__ void route_select_n(const RouteArgs &a, float *sc, const float *sbias, int32_t *cnt,
+                                               int tb0) {
   const int tid = threadIdx.x;
   const int h = blockIdx.y, Eh = a.Eh, TB = a.TB;
   const int L = a.L, Lg = a.Lg, ppb = 256 / L, pr = tid / L, j = tid % L;
@@ -240,40 +244,40 @@ __device__ __forceinline__ void route_select(const RouteArgs &a, float *sc, cons
     const int t = tb0 + tl;
     const bool valid = tl < TB && t < a.T;
     float *srow = sc + (valid ? tl : 0) * Eh + e0;
-    float lv[ROUTE_EPL];
+    float lv[EPL];
 #pragma unroll
-    for (int i = 0; i < ROUTE_EPL; ++i) lv[i] = (valid && i < nown) ? srow[step * i] : NEG;
+    for (int i = 0; i < EPL; ++i) lv[i] = (valid && i < nown) ? srow[step * i] : NEG;
     float m = NEG;
 #pragma unroll
-    for (int i = 0; i < ROUTE_EPL; ++i) m = fmaxf(m, lv[i]);
+    for (int i = 0; i < EPL; ++i) m = fmaxf(m, lv[i]);
     m = lanes_max(m, L);
     // probabilities: in float64, rounded once, where a gate decides an
     // integer result (exact); in float32 otherwise
-    float pf[ROUTE_EPL];
-    double ex[ROUTE_EPL];  // exp(l - m): float64 (exact), or float32 widened
+    float pf[EPL];
+    double ex[EPL];  // exp(l - m): float64 (exact), or float32 widened
     double sum;
     if (a.exact) {
       double sd = 0.0;
 #pragma unroll
-      for (int i = 0; i < ROUTE_EPL; ++i) {
+      for (int i = 0; i < EPL; ++i) {
         ex[i] = (valid && i < nown) ? exp((double)lv[i] - (double)m) : 0.0;
         sd += ex[i];
       }
       sum = lanes_sum_d(sd, L);
 #pragma unroll
-      for (int i = 0; i < ROUTE_EPL; ++i) pf[i] = (float)(ex[i] / sum);
+      for (int i = 0; i < EPL; ++i) pf[i] = (float)(ex[i] / sum);
     } else {
-      float exf[ROUTE_EPL];
+      float exf[EPL];
       float sf = 0.0f;
 #pragma unroll
-      for (int i = 0; i < ROUTE_EPL; ++i) {
+      for (int i = 0; i < EPL; ++i) {
         exf[i] = (valid && i < nown) ? __expf(lv[i] - m) : 0.0f;
         sf += exf[i];
       }
       sf = lanes_sum_f(sf, L);
       sum = sf;
 #pragma unroll
-      for (int i = 0; i < ROUTE_EPL; ++i) {
+      for (int i = 0; i < EPL; ++i) {
         ex[i] = exf[i];
         pf[i] = exf[i] / sf;
       }
@@ -282,28 +286,28 @@ __device__ __forceinline__ void route_select(const RouteArgs &a, float *sc, cons
       // the probabilities replace this lane's scores (read back by the
       // block's copy-out, the aux partials and expert choice)
 #pragma unroll
-      for (int i = 0; i < ROUTE_EPL; ++i)
+      for (int i = 0; i < EPL; ++i)
         if (i < nown) srow[step * i] = pf[i];
     }
     if (a.all_experts) {  // expert choice: every expert is a slot; gates are copied out by the block
       if (valid) {
 #pragma unroll
-        for (int i = 0; i < ROUTE_EPL; ++i)
+        for (int i = 0; i < EPL; ++i)
           if (i < nown) atomicAdd(&cnt[e0 + step * i], 1);
       }
       continue;
     }
     // selection keys: the scores, or p + b under the balancing bias
-    uint32_t ky[ROUTE_EPL];
+    uint32_t ky[EPL];
 #pragma unroll
-    for (int i = 0; i < ROUTE_EPL; ++i)
+    for (int i = 0; i < EPL; ++i)
       ky[i] = score_key((valid && i < nown) ? (sbias ? (pf[i] + sbias[e0 + step * i]) + 0.0f : lv[i]) : NEG);
     bool allowed = true;
     if (grouped) {
       // group score: the largest key of the group, over the group's Lg lanes
       uint32_t gk = 0;
 #pragma unroll
-      for (int i = 0; i < ROUTE_EPL; ++i) gk = max(gk, ky[i]);
+      for (int i = 0; i < EPL; ++i) gk = max(gk, ky[i]);
       uint64_t gkey = (uint64_t)gk;
       for (int o = 0; (1 << o) < Lg; ++o) {  // levels below Lg: max within the group
         uint64_t x2;
@@ -325,26 +329,26 @@ __device__ __forceinline__ void route_select(const RouteArgs &a, float *sc, cons
         if (gkey == best) allowed = true;
       }
     }
-    uint64_t kk[ROUTE_EPL];
+    uint64_t kk[EPL];
 #pragma unroll
-    for (int i = 0; i < ROUTE_EPL; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       const int e = e0 + step * i;
       kk[i] = (valid && i < nown && allowed) ? (((uint64_t)ky[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)) : 0ull;
     }
     // k rounds: the largest remaining key over the token's lanes; the lane
     // holding it records the round
-    int rnk[ROUTE_EPL];
+    int rnk[EPL];
 #pragma unroll
-    for (int i = 0; i < ROUTE_EPL; ++i) rnk[i] = -1;
+    for (int i = 0; i < EPL; ++i) rnk[i] = -1;
 #pragma unroll
     for (int r = 0; r < ROUTE_KMAX; ++r) {
       if (r >= a.k) break;
       uint64_t best = 0;
 #pragma unroll
-      for (int i = 0; i < ROUTE_EPL; ++i) best = kk[i] > best ? kk[i] : best;
+      for (int i = 0; i < EPL; ++i) best = kk[i] > best ? kk[i] : best;
       best = lanes_max_u64(best, L);
 #pragma unroll
-      for (int i = 0; i < ROUTE_EPL; ++i) {
+      for (int i = 0; i < EPL; ++i) {
         if (kk[i] == best) {
           kk[i] = 0;
           rnk[i] = r;
@@ -353,9 +357,9 @@ __device__ __forceinline__ void route_select(const RouteArgs &a, float *sc, cons
     }
     // gates of the chosen experts, by the lanes that hold them: the
     // probability (+ bias), renormalised by the sum over the chosen
-    double gw[ROUTE_EPL], gs = 0.0;
+    double gw[EPL], gs = 0.0;
 #pragma unroll
-    for (int i = 0; i < ROUTE_EPL; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       gw[i] = 0.0;
       if (rnk[i] >= 0) {
         gw[i] = a.exact ? ex[i] / sum : (double)pf[i];
@@ -368,7 +372,7 @@ __device__ __forceinline__ void route_select(const RouteArgs &a, float *sc, cons
       int32_t *oi = a.topk_idx + (size_t)t * a.H * a.k + (size_t)h * a.k;
       float *ow = a.topk_w + (size_t)t * a.H * a.k + (size_t)h * a.k;
 #pragma unroll
-      for (int i = 0; i < ROUTE_EPL; ++i) {
+      for (int i = 0; i < EPL; ++i) {
         if (rnk[i] >= 0) {
           const int e = e0 + step * i;
           oi[rnk[i]] = Ebase + e;
@@ -377,6 +381,18 @@ __device__ __forceinline__ void route_select(const RouteArgs &a, float *sc, cons
         }
       }
     }
+  }
+}
+
+// the selection with as few register slots per lane as the launch's lanes need
+// (narrow partitions; the staged kernels take the ROUTE_EPL form directly)
+__device__ __forceinline__ void route_select(const RouteArgs &a, float *sc, const float *sbias, int32_t *cnt,
+                                             int tb0) {
+  switch (a.epl) {
+    case 1: route_select_n<1>(a, sc, sbias, cnt, tb0); break;
+    case 2: route_select_n<2>(a, sc, sbias, cnt, tb0); break;
+    case 4: route_select_n<4>(a, sc, sbias, cnt, tb0); break;
+    default: route_select_n<ROUTE_EPL>(a, sc, sbias, cnt, tb0); break;
   }
 }
 
@@ -538,7 +554,7 @@ __global__ __launch_bounds__(256, (ST ? 2 : RouteRegs<TIN, TW, NF, MW>::OCC)) vo
     __syncthreads();
     route_scores(a, sc, sc, bsh, tb0);  // one set of scores (WK == 1): bias, or the loaded scores
     __syncthreads();
-    route_select(a, sc, sbias, cnt, tb0);
+    route_select_n<ROUTE_EPL>(a, sc, sbias, cnt, tb0);  // wide partitions: at least 4 experts per lane
     __syncthreads();
     route_block_stats(a, sc, cnt, tb0);
     return;
@@ -954,6 +970,7 @@ int launch_route(const Shape &s, const void *x, const void *w_router, const floa
   a.exact = (s.drop == DROP_AFFINITY || s.expert_choice || (sel_bias && !s.expert_choice)) ? 1 : 0;
   a.n_groups = s.n_groups; a.topk_groups = s.topk_groups; a.renorm = s.renorm; a.sel_gate = s.sel_gate;
   a.all_experts = s.expert_choice; a.load = load ? 1 : 0; a.WT = g.wt; a.WK = g.wk; a.TB = g.tb;
+  a.epl = g.epl <= 1 ? 1 : (g.epl <= 2 ? 2 : (g.epl <= 4 ? 4 : ROUTE_EPL));
   const size_t lds = route_lds_bytes(s, g, load);
   int rc;
   if (s.act_f32) rc = launch_route_nf<float, float, 1>(a, g, lds, st);
