@@ -69,7 +69,7 @@ struct GemmArgs {
   const int32_t *prefix;                      // [G+1] tile prefix, or NULL: E == 0 and fixed_tiles tiles
   int fixed_tiles;
   int G;
-  int split;  // 0: all rows of a group; 1: rows [0, cut); 2: rows [cut, M) (see row_window)
+  int split;  // 0: all rows of a group; 1: rows [0, cut); 2: rows [cut, M); 3, 4: see row_window
 };
 
 // Rows of a group a launch covers.  With split launches, a group's rows are
@@ -77,12 +77,20 @@ struct GemmArgs {
 // to 256-row tiles, the short tail to 128-row tiles in a second launch (a tail
 // tile in the head launch would hold a CU for nearly as long as a full tile,
 // since the tile's time goes to streaming its weight columns).
+// A launch pair for groups of very unequal size (split 3 and 4): groups of
+// at least SPLIT_HOT rows put their head in 256-row tiles (split 3), and the
+// rest (their tails, and every row of the smaller groups) goes to 128-row
+// tiles (split 4).
 constexpr int SPLIT_BM = 256;
+constexpr int SPLIT_HOT = 1024;
 __host__ __device__ inline void row_window(int split, int M, int *beg, int *len) {
   const int rem = M % SPLIT_BM;
   const int cut = (rem == 0 || rem > SPLIT_BM / 2) ? M : M - rem;
+  const bool hot = M >= SPLIT_HOT;
   if (split == 1) { *beg = 0; *len = cut; }
   else if (split == 2) { *beg = cut; *len = M - cut; }
+  else if (split == 3) { *beg = 0; *len = hot ? cut : 0; }
+  else if (split == 4) { *beg = hot ? cut : 0; *len = M - *beg; }
   else { *beg = 0; *len = M; }
 }
 
@@ -565,6 +573,7 @@ enum TileCfg {
   TILE_128x128 = 0,     // 4 waves (2 x 2), wave tile 64 x 64 (also the float32 tile)
   TILE_256x256_W8 = 1,  // 8 waves (2 x 4), wave tile 128 x 64; head + tail launches
   TILE_128x128_W8 = 2,  // 8 waves (2 x 4), wave tile 64 x 32
+  TILE_MIXED = 3,       // routed groups of very unequal size: 256-row tiles for the large, 128 for the rest
 };
 
 static long max_tiles(long rows_bound, int groups, int bm, int ntiles) {
@@ -586,6 +595,10 @@ static int run_gemm_t(GemmArgs a, hipStream_t st) {
   else
     grid = (a.E ? max_tiles(a.Mr_bound, a.E, BM_, n_tiles<EPI, BN_>(a.N)) : 0) +
            (a.has_x ? max_tiles(a.Mx, 0, BM_, n_tiles<EPI, BN_>(a.Nx)) : 0);
+  // the large groups' launch of a mixed pair: its windows are whole 256-row
+  // tiles, so at most Mr_bound / 256 tile rows (blocks past the prefix total,
+  // all of them when no group is large, exit at once)
+  if (a.split == 3) grid = (a.Mr_bound / BM_) * n_tiles<EPI, BN_>(a.N);
   if (grid <= 0) return 0;
   // dynamic LDS up to the device's per-workgroup limit (160 KiB on gfx950)
   constexpr size_t lds = (size_t)(STA * BM_ + STB * BN_) * KS * 16;
@@ -627,6 +640,11 @@ static int plan_launches(int tile, Launch out[2]) {
     out[1] = {TILE_128x128_W8, 2};
     return 2;
   }
+  if (tile == TILE_MIXED) {
+    out[0] = {TILE_256x256_W8, 3};
+    out[1] = {TILE_128x128_W8, 4};
+    return 2;
+  }
   out[0] = {tile, 0};
   return 1;
 }
@@ -648,14 +666,20 @@ static int pick_tile(long rows, int groups) {
 
 // Routed products.  With expert choice every expert holds exactly min(C, T)
 // rows (known here): the big tile unless its last row tile would be mostly
-// padding.  Otherwise only the average is known.
+// padding.  Otherwise only the average and the largest possible group are
+// known here (the rows per expert are on the device): tall groups on average
+// take the big tile; short ones the small tile, in a mixed pair when a group
+// can reach SPLIT_HOT rows (no capacity, or a capacity that large), so that
+// hot experts still get the big tile.
 static int pick_tile_routed(const Shape &s) {
   if (s.expert_choice) {
     const long n = std::min<long>(s.C, s.T);
     const long waste = (n + 255) / 256 * 256 - n;
     return (n >= 256 && waste * 8 <= n) ? TILE_256x256_W8 : TILE_128x128_W8;
   }
-  return pick_tile(s.R_max, s.E);
+  const int t = pick_tile(s.R_max, s.E);
+  const long most = s.drop == DROP_CAPACITY ? std::min<long>(s.C, s.T) : s.T;  // rows one expert can hold
+  return (t == TILE_128x128_W8 && most >= SPLIT_HOT) ? TILE_MIXED : t;
 }
 
 // A plain product (one group, no routed rows: a.E == 0, a.has_x == 1): the
