@@ -458,7 +458,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
     return kPair<EPI> ? tn * HB + wn * (HB / WGN) + f * 16 + 4 * cq : tn * BN_ + wn * WN + f * 16 + 4 * cq;
   };
   typename Quad<TE>::Raw pre[kRd ? MF : 1][kRd ? NQ : 1];
-  if constexpr (kRd) {
+  // The residual (bf16, when the stages hold a whole tile of it) comes in
+  // through LDS: whole rows in coalesced 16-byte direct loads, into slots
+  // XOR-swizzled by row (slot q of row r at r * QR + (q ^ r % QR)) so that
+  // the 16 rows one quad read touches fall in distinct banks.  Read straight
+  // from global memory, each wave load instruction would touch 16 rows for 32
+  // bytes of each.
+  constexpr int RQR = BN_ * (int)sizeof(TE) / 16;  // 16-byte slots per residual row
+  constexpr bool kResLds = EPI == EPI_RESID && sizeof(TE) == 2 && BM_ * RQR <= STA * SA + STB * SB &&
+                           (RQR & (RQR - 1)) == 0;
+  if constexpr (kResLds) {
+    // every wave's LDS reads of the last chunk are done before the stages are overwritten
+    wait_lgkmcnt0();
+    barrier_nofence();
+    const int cmax = N - tn * BN_;  // columns of this tile inside N (a multiple of 64)
+#pragma unroll 4
+    for (int s0 = 0; s0 < BM_ * RQR; s0 += NT) {
+      const int sl = s0 + tid, r = sl / RQR, q = (sl % RQR) ^ (r % RQR);
+      // rows past M and columns past N read the tile's first element (never used)
+      const bool in = m0 + r < M && q * 8 < cmax;
+      load_lds16(R + (in ? (size_t)(m0 + r) * p.ldres + tn * BN_ + q * 8 : (size_t)m0 * p.ldres + tn * BN_),
+                 smem + s0 + wv * 64);
+    }
+    wait_vmcnt0();
+    barrier_nofence();
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int rt = wm * WM + i * 16 + l16;
+#pragma unroll
+      for (int f = 0; f < NQ; ++f) {
+        const int ct = qcol(f) - tn * BN_, q = ct / 8;
+        const char *src = (const char *)(smem + rt * RQR + (q ^ (rt % RQR))) + (ct % 8) * 2;
+        pre[i][f] = *(const typename Quad<TE>::Raw *)src;
+      }
+    }
+  } else if constexpr (kRd) {
     const TE *src = (EPI == EPI_RESID) ? R : DHp;
     const long lds = (EPI == EPI_RESID) ? p.ldres : p.lddh;
 #pragma unroll
