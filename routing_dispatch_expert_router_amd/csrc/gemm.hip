@@ -505,6 +505,43 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
       }
     }
   }
+  // The plain, ReLU and residual epilogues (bf16) hand their output tile to
+  // the global stores through LDS as well: each wave writes its quads into
+  // the swizzled slots, then every thread stores whole 16-byte slots of
+  // whole rows.
+  constexpr bool kStageC = (EPI == EPI_PLAIN || EPI == EPI_RELU || EPI == EPI_RESID) && sizeof(TE) == 2 &&
+                           BM_ * RQR <= STA * SA + STB * SB && (RQR & (RQR - 1)) == 0;
+  if constexpr (kStageC) {
+    // every wave's LDS reads (last chunk, staged residual) are done
+    wait_lgkmcnt0();
+    barrier_nofence();
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int rt = wm * WM + i * 16 + l16;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int ct = wn * WN + f * 16 + 4 * cq;
+        float o[4], r[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (EPI == EPI_RESID) Quad<TE>::decode(pre[i][f], r);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          o[v] = acc[i][f][v];
+          if (EPI == EPI_RELU) o[v] = fmaxf(o[v], 0.0f);
+          if (EPI == EPI_RESID) o[v] += r[v];
+        }
+        Quad<TE>::store((TE *)((char *)(smem + rt * RQR + ((ct / 8) ^ (rt % RQR))) + (ct % 8) * 2), o);
+      }
+    }
+    wait_lgkmcnt0();
+    barrier_nofence();
+    const int cmax = N - tn * BN_;
+#pragma unroll 4
+    for (int s0 = 0; s0 < BM_ * RQR; s0 += NT) {
+      const int sl = s0 + tid, r = sl / RQR, q = (sl % RQR) ^ (r % RQR);
+      if (m0 + r < M && q * 8 < cmax) *(u32x4 *)(C + (size_t)(m0 + r) * ldc + tn * BN_ + q * 8) = smem[sl];
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
     const int row = m0 + wm * WM + i * 16 + l16;
