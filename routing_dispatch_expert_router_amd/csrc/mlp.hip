@@ -266,7 +266,38 @@ __global__ __launch_bounds__(MLP_NT) void mlp_kernel(MlpArgs p) {
   else if (live > 0) run(std::integral_constant<int, 1>{});
   else run(std::integral_constant<int, 0>{});
 
-  // lane (l16, cq) holds output columns 16 o + 4 cq .. + 3 of row 32 w + 16 i + l16
+  // lane (l16, cq) holds output columns 16 o + 4 cq .. + 3 of row 32 w + 16 i + l16.
+  // Where the ring holds a whole output tile, the tile goes out through it:
+  // quads into 16-byte slots XOR-swizzled by row (slot q of row r at
+  // r * RQY + (q ^ r % RQY)), then whole slots of whole rows per thread; a
+  // quad store straight from the registers touches 16 rows for 32 bytes of
+  // each per wave instruction.
+  constexpr int RQY = DH * 2 / 16;  // 16-byte slots per output row
+  if constexpr ((size_t)MLP_ROWS * RQY * 16 <= G::lds && (RQY & (RQY - 1)) == 0) {
+    wait_vmcnt0();    // no ring load of this wave still in flight
+    wait_lgkmcnt0();  // and its reads of the ring are done
+    barrier_nofence();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rt = 32 * w + 16 * i + l16;
+#pragma unroll
+      for (int o = 0; o < G::NO; ++o) {
+        const int ct = 16 * o + 4 * cq;
+        uint2 u;
+        u.x = (uint32_t)f32_to_bf16(yacc[i][o][0]) | ((uint32_t)f32_to_bf16(yacc[i][o][1]) << 16);
+        u.y = (uint32_t)f32_to_bf16(yacc[i][o][2]) | ((uint32_t)f32_to_bf16(yacc[i][o][3]) << 16);
+        *(uint2 *)((char *)(smem + rt * RQY + ((ct / 8) ^ (rt % RQY))) + (ct % 8) * 2) = u;
+      }
+    }
+    wait_lgkmcnt0();
+    barrier_nofence();
+#pragma unroll 4
+    for (int s0 = 0; s0 < MLP_ROWS * RQY; s0 += MLP_NT) {
+      const int sl = s0 + tid, r = sl / RQY, q = (sl % RQY) ^ (r % RQY);
+      if (r < M) *(u32x4 *)(p.y + (size_t)(r0 + r) * p.ldy + q * 8) = smem[sl];
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 32 * w + 16 * i + l16;
