@@ -12,7 +12,7 @@
 // [offsets[e], offsets[e+1]) of A and C; an optional extra group (shared
 // experts, or a plain dense product) has its own pointers and sizes.  Both
 // operands are K-contiguous.  Tiles: 256 x 256 outputs with 8 waves (tall
-// groups; a group's short tail goes to a second launch of 128 x 128 tiles) or
+// groups; a group's short tail goes to a second launch of 128 x 64 tiles) or
 // 128 x 128 with 8 waves (SwiGLU: half the tile's B rows are gate rows, half
 // up rows, so the output tile is BN/2 hidden columns wide); k-chunks of 128
 // bytes per row in LDS rings with XOR-swizzled 16-byte slots, one barrier per
@@ -645,7 +645,17 @@ enum TileCfg {
   TILE_256x256_W8 = 1,  // 8 waves (2 x 4), wave tile 128 x 64; head + tail launches
   TILE_128x128_W8 = 2,  // 8 waves (2 x 4), wave tile 64 x 32
   TILE_MIXED = 3,       // routed groups of very unequal size: 256-row tiles for the large, 128 for the rest
+  TILE_TAIL = 4,        // 8 waves (4 x 2), wave tile 32 x 32, deep rings: the short tails of 256-row launches
 };
+// The tail launch of a 256-row product holds at most 128 rows per group, so
+// each of its tiles streams a weight column tile once for few rows.  When
+// its 128 x 128 tiles are too few to give every CU two (a narrow, deep
+// product: the down projection, d_model columns over d_ff), it runs 128 x 64
+// tiles instead, twice the blocks, with the weight chunks kTailStagesB deep:
+// measured on the coarse 8-expert layer, that tail launch 160 -> 108 us.  A
+// wide product keeps the 128-wide tile (its 64-wide tiles would read every
+// row chunk twice as often: gate/up tail 174 -> 205 us).
+constexpr int kTailStagesA = 3, kTailStagesB = 8;
 
 static long max_tiles(long rows_bound, int groups, int bm, int ntiles) {
   return ((rows_bound + bm - 1) / bm + groups) * ntiles;
@@ -695,20 +705,24 @@ static int run_gemm_one(GemmArgs a, int tile, hipStream_t st) {
           return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 3, true>(a, st);
         else
           return run_gemm_t<TE, EPI, 128, 128, 2, 4, 8, 2, 2, true>(a, st);
+      case TILE_TAIL: return run_gemm_t<TE, EPI, 128, 64, 4, 2, 8, kTailStagesA, kTailStagesB, true>(a, st);
       default: return run_gemm_t<TE, EPI, 128, 128, 2, 2, 8, 2, 2>(a, st);
     }
   }
 }
 
 // One launch of a product: its tile shape and row window.  256-row tiles run
-// as a head launch (split 1) plus a tail launch of 128-row tiles (split 2).
+// as a head launch (split 1) plus a tail launch (split 2) of 128-row tiles,
+// 64 columns wide when the groups' 128 x 128 tail tiles would not give every
+// CU two (groups: the groups of the product, N its output columns).
 struct Launch {
   int tile, split;
 };
-static int plan_launches(int tile, Launch out[2]) {
+static int col_tiles(int epi, int tile, int N);
+static int plan_launches(int tile, int epi, int N, int groups, Launch out[2]) {
   if (tile == TILE_256x256_W8) {
     out[0] = {TILE_256x256_W8, 1};
-    out[1] = {TILE_128x128_W8, 2};
+    out[1] = {(long)groups * col_tiles(epi, TILE_128x128_W8, N) < 2 * 256 ? TILE_TAIL : TILE_128x128_W8, 2};
     return 2;
   }
   if (tile == TILE_MIXED) {
@@ -720,7 +734,7 @@ static int plan_launches(int tile, Launch out[2]) {
   return 1;
 }
 static int tile_rows(int tile) { return tile == TILE_256x256_W8 ? 256 : 128; }
-static int tile_cols(int tile) { return tile == TILE_256x256_W8 ? 256 : 128; }
+static int tile_cols(int tile) { return tile == TILE_256x256_W8 ? 256 : tile == TILE_TAIL ? 64 : 128; }
 static int col_tiles(int epi, int tile, int N) {
   const int bn = tile_cols(tile);
   return (epi == EPI_SWIGLU || epi == EPI_SWIGLU_BWD) ? (N + bn / 2 - 1) / (bn / 2) : (N + bn - 1) / bn;
@@ -759,7 +773,7 @@ static int pick_tile_routed(const Shape &s) {
 template <typename TE, int EPI>
 static int run_plain(GemmArgs a, int tile, hipStream_t st) {
   Launch l[2];
-  const int nl = plan_launches(tile, l);
+  const int nl = plan_launches(tile, EPI, a.Nx, 1, l);
   for (int i = 0; i < nl; ++i) {
     int beg, len;
     row_window(l[i].split, a.Mx, &beg, &len);
@@ -798,7 +812,7 @@ int gemm_routed(const Shape &s, int epi, const void *A, long lda, const int32_t 
   a.dh = dh; a.lddh = lddh; a.hout = hout; a.ldh = ldh;
   const int tile = s.act_f32 ? TILE_128x128 : pick_tile_routed(s);
   Launch l[2];
-  const int nl = plan_launches(tile, l);
+  const int nl = plan_launches(tile, epi, N, s.E, l);
   PrepArgs pa{};
   pa.offsets = offsets; pa.E = s.E; pa.has_x = 0; pa.Mx = 0; pa.prefix = prefix;
   for (int i = 0; i < nl; ++i) pa.c[i] = prep_cfg(epi, l[i], N, 0);
@@ -822,7 +836,7 @@ int gemm_plain(bool f32, int epi, const void *A, long lda, const void *B, const 
   a.dh = dh; a.lddh = lddh; a.hout = hout; a.ldh = ldh;
   const int tile = f32 ? TILE_128x128 : pick_tile(M, 1);
   Launch l[2];
-  const int nl = plan_launches(tile, l);
+  const int nl = plan_launches(tile, epi, N, 1, l);
   for (int i = 0; i < nl; ++i) {
     int beg, len;
     row_window(l[i].split, M, &beg, &len);
@@ -1088,8 +1102,10 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
   // f32 layers are parity-sized: the small tile is plenty
   const int tile = sizeof(TE) == 4 ? TILE_128x128 : pick_tile_routed(s);
   const int epi1 = glu ? EPI_SWIGLU : EPI_RELU;
-  Launch l[2];
-  const int nl = plan_launches(tile, l);
+  // the two GEMMs split their rows alike; only their tail tiles can differ
+  Launch l[2], l2[2];
+  const int nl = plan_launches(tile, epi1, s.dff, s.E, l);
+  plan_launches(tile, EPI_PLAIN, s.dh, s.E, l2);
 
   GemmArgs a{};
   // ---- GEMM 1: H = act(x_perm W1^T [, x_perm W3^T])
@@ -1112,7 +1128,7 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
   pa.offsets = offsets; pa.E = s.E; pa.has_x = 0; pa.Mx = 0; pa.prefix = pre;
   for (int i = 0; i < nl; ++i) {
     pa.c[i] = prep_cfg(epi1, l[i], a.N, 0);
-    pa.c[nl + i] = prep_cfg(EPI_PLAIN, l[i], b.N, 0);
+    pa.c[nl + i] = prep_cfg(EPI_PLAIN, l2[i], b.N, 0);
   }
   for (int i = 0; i < nl && !fused; ++i) {
     if (i == 0) {
@@ -1125,9 +1141,9 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
     if (rc) return rc;
   }
   for (int i = 0; i < nl && !fused; ++i) {
-    b.split = l[i].split;
+    b.split = l2[i].split;
     b.prefix = pre + (size_t)(nl + i) * (s.E + 2);
-    if (int rc = run_gemm_one<TE, EPI_PLAIN>(b, l[i].tile, st)) return rc;
+    if (int rc = run_gemm_one<TE, EPI_PLAIN>(b, l2[i].tile, st)) return rc;
   }
   if (!has_x) return 0;
 
