@@ -7,7 +7,12 @@
 //
 // Each thread owns 8 (bf16) or 4 (f32) consecutive columns of one token row and
 // accumulates in float32 in a fixed order: residual, shared, then the head's
-// assignments j ascending; the sum is rounded once.
+// assignments j ascending; the sum is rounded once.  The expert rows and the
+// residual are read once and the output written once, so those accesses are
+// non-temporal (streamed past the caches): measured on MI355X, the
+// group-limited layer's combine 135 -> 126 us from cold caches (139 -> 110
+// back to back) and the coarse layer's 28.2 -> 26.7 us cold (21.7 -> 23.3 us
+// back to back).
 #include "common.h"
 #include "launch.h"
 
@@ -57,10 +62,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
       // when many slots are dropped)
 #pragma unroll
       for (int j = 0; j < KH; ++j)
-        v[j] = row[j] >= 0 ? reinterpret_cast<const u32x4 *>(y_perm + (size_t)row[j] * dh + (c0 - h * dh))[0]
+        v[j] = row[j] >= 0 ? __builtin_nontemporal_load(
+                                 reinterpret_cast<const u32x4 *>(y_perm + (size_t)row[j] * dh + (c0 - h * dh)))
                            : u32x4{0u, 0u, 0u, 0u};
     }
-    u32x4 rv = res ? reinterpret_cast<const u32x4 *>(res + (size_t)t * width)[q] : u32x4{0u, 0u, 0u, 0u};
+    u32x4 rv = res ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(res + (size_t)t * width) + q)
+                   : u32x4{0u, 0u, 0u, 0u};
     u32x4 sv = sh ? reinterpret_cast<const u32x4 *>(sh + (size_t)t * width)[q] : u32x4{0u, 0u, 0u, 0u};
     float acc[EPC];
 #pragma unroll
@@ -115,7 +122,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     TA *ov = reinterpret_cast<TA *>(&o);
 #pragma unroll
     for (int e = 0; e < EPC; ++e) ov[e] = Elem<TA>::from_f32(acc[e]);
-    reinterpret_cast<u32x4 *>(y + (size_t)t * width)[q] = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(y + (size_t)t * width) + q);
   }
 }
 
