@@ -1080,7 +1080,8 @@ size_t ffn_ws_bytes(const Shape &s) {
 template <typename TE>
 static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets,
                      const void *w1, const void *w3, const void *w2, void *y_perm, const void *x_shared,
-                     const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st) {
+                     const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st,
+                     const FoldOut &fold) {
   const int esz = sizeof(TE);
   char *p = (char *)ws;
   TE *H = (TE *)p;
@@ -1096,8 +1097,9 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
   const int has_x = s.n_shared ? 1 : 0;
   // narrow experts: the fused MLP (no hidden round trip through HBM)
   const bool fused = sizeof(TE) == 2 && mlp_fused_supported(s);
+  if (fold.o && !(fused && fold_supported(s))) return -2;
   if (fused) {
-    if (int rc = launch_mlp_fused(s, xin, gather, offsets, w1, w3, w2, y_perm, pre, st)) return rc;
+    if (int rc = launch_mlp_fused(s, xin, gather, offsets, w1, w3, w2, y_perm, pre, st, fold)) return rc;
   }
   // f32 layers are parity-sized: the small tile is plenty
   const int tile = sizeof(TE) == 4 ? TILE_128x128 : pick_tile_routed(s);
@@ -1168,11 +1170,13 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
 
 int launch_expert_ffn(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets,
                       const void *w1, const void *w3, const void *w2, void *y_perm, const void *x_shared,
-                      const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st) {
+                      const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st,
+                      const FoldOut &fold) {
   if (s.act_f32)
-    return ffn_typed<float>(s, xin, gather, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws, st);
+    return ffn_typed<float>(s, xin, gather, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws, st,
+                            fold);
   return ffn_typed<uint16_t>(s, xin, gather, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws,
-                             st);
+                             st, fold);
 }
 
 size_t dense_ws_bytes() { return 0; }  // the tile counts come from the host

@@ -96,8 +96,19 @@ int gemm_kgrouped_pieces(bool f32, const void *A, long lda, const void *B, long 
 // fused expert MLP (mlp.hip): bf16, d_e of 64, 128 or 256, d_ff a multiple
 // of 32; prefix: E + 1 ints of workspace
 bool mlp_fused_supported(const Shape &s);
+// The combine of a layer whose every (token, head) holds exactly one kept
+// assignment, done by the expert FFN's epilogue: row r's output, times its
+// gate w[asg[r]], goes to o[asg[r] / K][h * d_head ..] (h = the row's
+// expert's head), rounded as the combine rounds it.  o == NULL: no fold.
+struct FoldOut {
+  void *o;
+  const float *w;
+  const int32_t *asg;
+};
+bool fold_supported(const Shape &s);
 int launch_mlp_fused(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets, const void *w1,
-                     const void *w3, const void *w2, void *y_perm, int32_t *prefix, hipStream_t st);
+                     const void *w3, const void *w2, void *y_perm, int32_t *prefix, hipStream_t st,
+                     const FoldOut &fold = FoldOut{});
 // kchunk: dst k-chunked (ld_dst = its row count, njcols a multiple of 64), else row-major
 int launch_transpose(bool f32, const void *src, long ld_src, long bs_src, const int32_t *rmap, long nvalid,
                      long njcols, int ncols, int coff, void *dst, long ld_dst, long bs_dst, int batches,
@@ -168,9 +179,12 @@ size_t ffn_ws_bytes(const Shape &s);
 // gather == NULL: `xin` is x_perm (row r of the routed operand is xin[r]);
 // else `xin` is the expert input x and row r is read from x[gather[r] / K]
 // at column offset (e / E_h) * d_head
+// fold.o != NULL (fold_supported(s) only): the combine folded into the
+// epilogue (see FoldOut); y_perm may then be NULL (not written)
 int launch_expert_ffn(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets,
                       const void *w1, const void *w3, const void *w2, void *y_perm, const void *x_shared,
-                      const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st);
+                      const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st,
+                      const FoldOut &fold = FoldOut{});
 // dense C[M,N] = A[M,K] B[N,K]^T (+ residual R[M,N]), act dtype, float32 accumulate
 size_t dense_ws_bytes();
 int launch_dense(bool f32, const void *A, const void *B, void *C, const void *residual, int M, int N, int K,

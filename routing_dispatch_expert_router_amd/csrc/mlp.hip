@@ -34,11 +34,43 @@ struct MlpArgs {
   const uint16_t *x; long ldx;            // expert input rows (see gather)
   const int32_t *gather; int gK, gEh, gdh; // routed row r = x[gather[r] / gK] + (e / gEh) * gdh, or x[r]
   const uint16_t *w1, *w3, *w2;           // [E][dff][DH], [E][dff][DH] (SwiGLU), [E][DH][dff]
-  uint16_t *y; long ldy;                  // y_perm rows [R][DH]
+  uint16_t *y; long ldy;                  // y_perm rows [R][DH], or NULL (not written)
   const int32_t *offsets;                 // [E + 1] rows of each expert
   const int32_t *prefix;                  // [E + 1] blocks before each expert
   int E, dff;
+  // the folded combine (o != NULL): row r times fw[asg[r]] to o[asg[r] / fK]
+  // at column (e / gEh) * DH, row stride ldo
+  uint16_t *o; long ldo;
+  const float *fw;
+  const int32_t *asg;
+  int fK;
 };
+
+// The folded combine's value of two bf16 outputs packed in a word: the gate
+// times each, formed as the combine forms it (0 + w * y in float32, rounded
+// once to bf16), so o is bitwise the combine's output.
+__device__ __forceinline__ uint32_t mlp_gated(float g, uint32_t v) {
+  const float lo = 0.0f + g * bf16_to_f32((uint16_t)(v & 0xFFFFu));
+  const float hi = 0.0f + g * bf16_to_f32((uint16_t)(v >> 16));
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+// Where row r's output goes in o (folded combine): its token's row, its head's slice.
+__device__ __forceinline__ uint16_t *mlp_orow(const MlpArgs &p, int e, int a) {
+  return p.o + (size_t)(a / p.fK) * p.ldo + (size_t)(e / p.gEh) * p.gdh;
+}
+// One 16-byte slot (8 bf16, columns 8q ..) of row r's output to y_perm and,
+// folded, gated to o.
+__device__ __forceinline__ void mlp_put(const MlpArgs &p, int e, int r, int q, u32x4 v) {
+  if (p.y) *(u32x4 *)(p.y + (size_t)r * p.ldy + q * 8) = v;
+  if (p.o) {
+    const int a = p.asg[r];
+    const float g = p.fw[a];
+    u32x4 u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) u[c] = mlp_gated(g, v[c]);
+    *(u32x4 *)(mlp_orow(p, e, a) + q * 8) = u;
+  }
+}
 
 // blocks per expert: ceil(n_e / MLP_ROWS); prefix[e] = blocks before expert e
 __global__ __launch_bounds__(1024) void mlp_prefix_kernel(const int32_t *__restrict__ offsets, int E,
@@ -294,7 +326,7 @@ __global__ __launch_bounds__(MLP_NT) void mlp_kernel(MlpArgs p) {
 #pragma unroll 4
     for (int s0 = 0; s0 < MLP_ROWS * RQY; s0 += MLP_NT) {
       const int sl = s0 + tid, r = sl / RQY, q = (sl % RQY) ^ (r % RQY);
-      if (r < M) *(u32x4 *)(p.y + (size_t)(r0 + r) * p.ldy + q * 8) = smem[sl];
+      if (r < M) mlp_put(p, e, r0 + r, q, smem[sl]);
     }
     return;
   }
@@ -302,13 +334,22 @@ __global__ __launch_bounds__(MLP_NT) void mlp_kernel(MlpArgs p) {
   for (int i = 0; i < 2; ++i) {
     const int row = 32 * w + 16 * i + l16;
     if (row >= M) continue;
-    uint16_t *yr = p.y + (size_t)(r0 + row) * p.ldy + 4 * cq;
+    uint16_t *yr = p.y ? p.y + (size_t)(r0 + row) * p.ldy + 4 * cq : nullptr;
+    // the folded combine: the row's gate and its slice of o
+    float g = 0.f;
+    uint16_t *orow = nullptr;
+    if (p.o) {
+      const int a = p.asg[r0 + row];
+      g = p.fw[a];
+      orow = mlp_orow(p, e, a) + 4 * cq;
+    }
 #pragma unroll
     for (int o = 0; o < G::NO; ++o) {
       uint2 u;
       u.x = (uint32_t)f32_to_bf16(yacc[i][o][0]) | ((uint32_t)f32_to_bf16(yacc[i][o][1]) << 16);
       u.y = (uint32_t)f32_to_bf16(yacc[i][o][2]) | ((uint32_t)f32_to_bf16(yacc[i][o][3]) << 16);
-      *(uint2 *)(yr + 16 * o) = u;
+      if (yr) *(uint2 *)(yr + 16 * o) = u;
+      if (orow) *(uint2 *)(orow + 16 * o) = make_uint2(mlp_gated(g, u.x), mlp_gated(g, u.y));
     }
   }
 }
@@ -316,6 +357,15 @@ __global__ __launch_bounds__(MLP_NT) void mlp_kernel(MlpArgs p) {
 bool mlp_fused_supported(const Shape &s) {
   return !s.act_f32 && (s.dh == 64 || s.dh == 128 || s.dh == 256) && s.dff > 0 && s.dff % MLP_HC == 0 &&
          s.E <= 8192;
+}
+
+// Layers whose combine the fused MLP can do: multi-head latent layers (the
+// combine writes o with no residual or shared part) where every (token, head)
+// keeps its one choice (top-1 per head, nothing dropped), so each slice of o
+// is one gated expert row.
+bool fold_supported(const Shape &s) {
+  return mlp_fused_supported(s) && s.latent && s.k == 1 && s.drop == DROP_NONE && !s.expert_choice &&
+         s.n_shared == 0;
 }
 
 template <int DH, bool GLU>
@@ -327,8 +377,11 @@ static int run_mlp(const MlpArgs &a, long grid, hipStream_t st) {
 }
 
 int launch_mlp_fused(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets, const void *w1,
-                     const void *w3, const void *w2, void *y_perm, int32_t *prefix, hipStream_t st) {
+                     const void *w3, const void *w2, void *y_perm, int32_t *prefix, hipStream_t st,
+                     const FoldOut &fold) {
   if (!mlp_fused_supported(s)) return -2;
+  if (fold.o && !fold_supported(s)) return -2;
+  if (!fold.o && !y_perm && s.R_max) return -1;
   hipLaunchKernelGGL(mlp_prefix_kernel, dim3(1), dim3(1024), 0, st, offsets, s.E, prefix);
   if (int rc = launch_status("fused mlp prefix")) return rc;
   MlpArgs a{};
@@ -337,6 +390,7 @@ int launch_mlp_fused(const Shape &s, const void *xin, const int32_t *gather, con
   a.w1 = (const uint16_t *)w1; a.w3 = (const uint16_t *)w3; a.w2 = (const uint16_t *)w2;
   a.y = (uint16_t *)y_perm; a.ldy = s.dh;
   a.offsets = offsets; a.prefix = prefix; a.E = s.E; a.dff = s.dff;
+  a.o = (uint16_t *)fold.o; a.ldo = (long)s.H * s.dh; a.fw = fold.w; a.asg = fold.asg; a.fK = s.K;
   const long grid = (s.R_max + MLP_ROWS - 1) / MLP_ROWS + s.E;  // blocks past the prefix total exit
   const bool glu = s.act == 1;
   switch (s.dh) {

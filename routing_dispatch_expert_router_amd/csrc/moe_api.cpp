@@ -492,12 +492,20 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
   if ((rc = rc_of(moe::launch_dispatch(s, topk_idx, topk_w, xin, demand, counts, offsets, row_of, src_of, x_perm,
                                        scratch, stream, s.expert_choice ? nullptr : route_hist))))
     return rc;
+  // Where every (token, head) keeps its one choice (multi-head latent, top-1
+  // per head, nothing dropped), the expert FFN's epilogue writes each row,
+  // gated, straight into its slice of o: the combine pass (a read of y_perm
+  // and a write of o) is not run, and y_perm is written only when the caller
+  // asks for it.  o is bitwise what the combine would write.
+  const bool fold = moe::fold_supported(s);
+  moe::FoldOut fo{};
+  if (fold) fo = moe::FoldOut{o, topk_w, src_of};
   if ((rc = rc_of(moe::launch_expert_ffn(s, x_perm ? x_perm : xin, x_perm ? nullptr : src_of, offsets, w->w1,
-                                         w->w3, w->w2, y_perm, x, w->ws1, w->ws3, w->ws2, shared, scratch,
-                                         stream))))
+                                         w->w3, w->w2, (fold && !io->y_perm) ? nullptr : y_perm, x, w->ws1, w->ws3,
+                                         w->ws2, shared, scratch, stream, fo))))
     return rc;
   const void *res = (!s.latent && s.residual) ? x : nullptr;
-  if ((rc = rc_of(moe::launch_combine(s, y_perm, row_of, topk_w, res, shared, s.latent ? o : y, stream))))
+  if (!fold && (rc = rc_of(moe::launch_combine(s, y_perm, row_of, topk_w, res, shared, s.latent ? o : y, stream))))
     return rc;
   if (s.latent) {
     if ((rc = rc_of(moe::launch_dense(s.act_f32, o, w->w_out, y, x, s.T, s.d, s.H * s.dh, scratch, stream))))

@@ -366,6 +366,55 @@ def test_layer_gather_equals_xperm_path(cfg):
         assert np.array_equal(f64(io1["x_perm"][:R]), expected_xperm(cfg, xin, out))
 
 
+def _fold_cfgs():
+    c4s = SMALL[4]
+    return [c4s,  # expert width 64: the epilogue's direct quad stores
+            c4s.with_(name="c4s_dh256", T=301, d_model=512, n_heads=2, d_head=256, n_experts=32, d_ff=128,
+                      tag=41),  # width 256: the tile goes out through LDS
+            c4s.with_(name="c4s_dh128_relu", T=130, n_heads=2, d_head=128, n_experts=16, d_ff=64, act=0,
+                      tag=42)]
+
+
+@pytest.mark.parametrize("cfg", _fold_cfgs(), ids=lambda c: c.name)
+@pytest.mark.parametrize("want_yperm", [True, False], ids=["yperm", "no_yperm"])
+def test_layer_folded_combine_bitwise(cfg, want_yperm):
+    """Top-1 per head with nothing dropped: the layer folds the combine into the
+    fused MLP's epilogue.  Its o (and y_perm, when asked for) are bitwise what
+    the separate calls give: the expert FFN on the same rows, then moe_combine."""
+    log(f"folded combine {cfg.name} y_perm={want_yperm}")
+    inp = cached_inputs(cfg)
+    out = oracle.forward(cfg, inp)
+    T, K, E = cfg.T, cfg.k_total, cfg.n_experts
+    Rm = moe.moe_rows_upper_bound(cfg)
+    ws = moe.workspace(cfg)
+    y = empty_act(cfg, T, cfg.d_model)
+    io = dict(topk_idx=i32(T, K), topk_w=f32(T, K), demand=i32(E), counts=i32(E), offsets=i32(E + 1),
+              row_of=i32(T, K), src_of=i32(Rm), z=empty_act(cfg, T, cfg.d_latent),
+              o=empty_act(cfg, T, cfg.d_latent), logits=dev(out["logits"]), logits_mode=moe.MOE_LOGITS_LOAD)
+    if want_yperm:
+        io["y_perm"] = empty_act(cfg, Rm, cfg.d_head)
+    wd = weights_dev(cfg, inp)
+    moe.moe_layer_fwd(cfg, wd, dev(inp.x), y, io, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(io["topk_idx"].cpu().numpy(), out["topk_idx"])
+    assert np.all(io["row_of"].cpu().numpy() >= 0)
+    # the same rows through the separate calls
+    yp = empty_act(cfg, Rm, cfg.d_head)
+    moe.moe_expert_ffn_gather(cfg, io["z"], io["src_of"], io["offsets"], wd["w1"], wd["w3"], wd["w2"], yp,
+                              None, None, None, None, None, ws)
+    o_ref = empty_act(cfg, T, cfg.d_latent)
+    moe.moe_combine(cfg, yp, io["row_of"], io["topk_w"], None, None, o_ref)
+    torch.cuda.synchronize()
+    R = int(io["offsets"][-1].item())
+    assert R == T * K
+    if want_yperm:
+        assert torch.equal(_bits(io["y_perm"][:R]), _bits(yp[:R]))
+    assert torch.equal(_bits(io["o"]), _bits(o_ref))
+    err = np.max(np.abs(f64(y) - out["y"]))
+    log(f"  o bitwise equal; layer max err {err:.3g} rel {err / np.max(np.abs(out['y'])):.3g}")
+    assert err <= tol(cfg) * np.max(np.abs(out["y"]))
+
+
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("cfg", _edge_cfgs(), ids=lambda c: c.name)
 def test_edge_layer(cfg):
