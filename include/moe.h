@@ -375,6 +375,10 @@ int moe_combine(const moe_config *cfg, const void *y_perm, const int32_t *row_of
  * expert input directly (as moe_expert_ffn_gather); y is the same either way.  x [T, d_model] act in, y [T, d_model] act out (distinct
  * from x).  `io` may be NULL.  Sources as for the four calls above, and
  * "多头 LatentMoE 与 Head Parallel", 方法论 item 1 (latent routing space).
+ * A multi-head latent layer with top-1 per head, nothing dropped and a fused
+ * expert MLP (bf16, d_head 64, 128 or 256) runs its combine inside the
+ * expert FFN: io->o is then bitwise what moe_combine writes, and io->y_perm
+ * is written only when given (the backward needs it).
  */
 int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
                   moe_layer_io *io, void *ws, size_t ws_bytes, hipStream_t stream);
