@@ -13,6 +13,16 @@ call, HBM bytes per dispatch) and profiles/traffic__expert_ffn__NAME.json
 (the HBM bytes of one expert-FFN call, which bench.py reports as the
 roofline's `traffic` while the FFN kernels' sources are unchanged).
 
+    python bench_profile.py counters --workload NAME --runs DIR [DIR ...] [--commands FILE]
+
+writes profiles/mfma_counters__expert_ffn__NAME.md from --pmc runs (CSV) of
+bench.py restricted to the FFN kernels: per kernel (name and grid), the
+averages per dispatch of the clock, MFMA busy, MFMA FLOP rate, wave wait,
+LDS bank conflicts, L2 hit rate and HBM bytes, from whichever of these
+counters the runs hold: SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16,
+SQ_WAIT_INST_ANY, SQ_WAVE_CYCLES, SQ_LDS_BANK_CONFLICT, GRBM_GUI_ACTIVE,
+TCC_HIT_sum, TCC_MISS_sum, FETCH_SIZE, WRITE_SIZE.
+
 An expert-FFN call is the run of dispatches that starts at its tile-prefix
 kernel (gemm_prep_kernel or mlp_prefix_kernel) and holds only FFN kernels
 (grouped_gemm_kernel, mlp_kernel); it is cold when the dispatch before it is
@@ -133,7 +143,85 @@ def calib(rows, mib):
     return mib * 1024.0 / kib, kib
 
 
+def load_all_counters(d):
+    """Every counter of a counter run, per dispatch: {dispatch: (name, grid, dur_ns, {counter: value})}."""
+    out = {}
+    with open(_one(d, "*counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            i = int(_col(r, "Dispatch_Id"))
+            if i not in out:
+                dur = int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))
+                out[i] = (short(_col(r, "Kernel_Name")), _grid(r), dur, {})
+            c = _col(r, "Counter_Name")
+            out[i][3][c] = out[i][3].get(c, 0.0) + float(_col(r, "Counter_Value"))
+    return out
+
+
+def counters_main(argv):
+    ap = argparse.ArgumentParser(prog="bench_profile.py counters")
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--runs", nargs="+", required=True)
+    ap.add_argument("--commands", default="")
+    a = ap.parse_args(argv)
+    agg = {}  # (name, grid) -> counter -> [values]; "_dur" -> durations
+    order = []
+    for d in a.runs:
+        for _, (name, grid, dur, cs) in sorted(load_all_counters(d).items()):
+            if not is_ffn(name):
+                continue
+            k = (name, grid)
+            if k not in agg:
+                agg[k] = {}
+                order.append(k)
+            for c, v in cs.items():
+                agg[k].setdefault(c, []).append(v)
+            if "GRBM_GUI_ACTIVE" in cs:
+                agg[k].setdefault("_dur", []).append(dur)
+    mean = lambda k, c: (sum(agg[k][c]) / len(agg[k][c])) if agg[k].get(c) else None
+    lines = [f"# rocprofv3 counters: expert-FFN kernels, {a.workload}", "",
+             "Commands (from the repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`; one counter "
+             "set per run):", ""]
+    if a.commands:
+        lines += ["    " + c.strip() for c in open(a.commands) if c.strip()]
+    lines += ["    python bench_profile.py counters --workload " + a.workload + " --runs " + " ".join(a.runs), "",
+              "Averages per dispatch over every traced call of each kernel (warm-up, timed steps and the stage "
+              "timing; kernels serialised by the counter collection).  `GRBM_GUI_ACTIVE` is summed over the 8 XCDs, "
+              "so the clock is GUI / 8 / duration; MFMA busy = `SQ_VALU_MFMA_BUSY_CYCLES` / (GUI / 8 x 1024 SIMDs); "
+              "`SQ_INSTS_VALU_MFMA_MOPS_BF16` x 512 = the MFMA FLOPs; L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS); HBM "
+              "bytes: FETCH_SIZE x 2 (see the forward summary's copy calibration) and WRITE_SIZE x 1, in GB.", "",
+              "| kernel | grid | calls | avg us (counter run) | clock GHz | MFMA busy | MFMA TFLOP/s | wait "
+              "(SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES) | LDS bank conflict cycles | L2 hit | read GB | write GB |",
+              "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    f1 = lambda v, fmt: (fmt % v) if v is not None else "-"
+    for k in order:
+        n, g = k
+        dur = mean(k, "_dur")
+        gui = mean(k, "GRBM_GUI_ACTIVE")
+        clk = gui / 8 / dur if gui and dur else None
+        busy = mean(k, "SQ_VALU_MFMA_BUSY_CYCLES")
+        mb = busy / (gui / 8 * 1024) if busy is not None and gui else None
+        mops = mean(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        tf = mops * 512 / dur / 1e3 if mops is not None and dur else None
+        wt, wc = mean(k, "SQ_WAIT_INST_ANY"), mean(k, "SQ_WAVE_CYCLES")
+        hit, miss = mean(k, "TCC_HIT_sum"), mean(k, "TCC_MISS_sum")
+        fe, wr = mean(k, "FETCH_SIZE"), mean(k, "WRITE_SIZE")
+        calls = max(len(v) for c, v in agg[k].items())
+        lines.append(f"| `{n}` | {g} | {calls} | {f1(dur / 1e3 if dur else None, '%.1f')} | {f1(clk, '%.2f')} | "
+                     f"{f1(100 * mb if mb is not None else None, '%.1f %%')} | {f1(tf, '%.0f')} | "
+                     f"{f1(100 * wt / wc if wt is not None and wc else None, '%.0f %%')} | "
+                     f"{f1(mean(k, 'SQ_LDS_BANK_CONFLICT'), '%.0f')} | "
+                     f"{f1(100 * hit / (hit + miss) if hit is not None and miss is not None and hit + miss > 0 else None, '%.0f %%')} | "
+                     f"{f1(fe * 2 * 1024 / 1e9 if fe is not None else None, '%.3f')} | "
+                     f"{f1(wr * 1024 / 1e9 if wr is not None else None, '%.3f')} |")
+    lines.append("")
+    with open(os.path.join(ROOT, "profiles", f"mfma_counters__expert_ffn__{a.workload}.md"), "w") as f:
+        f.write("\n".join(lines))
+    print(f"{a.workload}: {len(order)} FFN kernels")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        return counters_main(sys.argv[2:])
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
     ap.add_argument("--trace", required=True)
