@@ -9,6 +9,9 @@ loaded and checks:
   * the choices equal the oracle's (with a selection bias the GPU forms the
     keys p + b from its own exp: a token may differ only at an oracle key
     near-tie);
+  * the keep rule: the oracle's rule on the GPU's own choices and gates
+    gives exactly the GPU's counts, offsets and permutation, and (choices
+    equal) a keep decision differs from the oracle's only at a gate near-tie;
   * y against the oracle's y for the GPU's own decisions (top-k and keep
     mask), within 2e-2 (bf16) or 1e-4 (float32) of max|y|;
   * the per-sequence statistic within 1e-5 relative;
@@ -28,7 +31,7 @@ import oracle.moe_backward as OB
 import routing_dispatch_expert_router_amd as moe
 from moe_inputs import generate, bf16_bits_from_f32
 from moe_inputs.configs import MoEConfig
-from tests.gpu_util import log, dev, f64, empty_act, i32, f32, tol, weights_dev, routing_margin
+from tests.gpu_util import log, dev, f64, empty_act, i32, f32, tol, weights_dev, routing_margin, check_keep
 from tests.test_gpu_backward import _transposed, _grads
 
 N_CASES = 24
@@ -130,6 +133,11 @@ def test_random_layer_forward_backward(cfg):
         keys = out["p"] + np.asarray(inp.sel_bias, np.float64)[None, :]
         assert np.all(routing_margin(cfg, keys)[diff] < 1e-5), "choices differ away from a near-tie"
         log(f"  near-tie tokens: {len(diff)}")
+    # the keep rule on the GPU's own choices and gates, exactly; where the
+    # choices match the oracle's, keep decisions differ only at gate near-ties
+    flips = check_keep(cfg, io, out, near_ties=len(diff) == 0)
+    if len(flips):
+        log(f"  keep decisions at gate near-ties: {len(flips)}")
     kept = io["row_of"].cpu().numpy().reshape(-1) >= 0
     P = OB.params_of(inp)
 
