@@ -536,7 +536,9 @@ template <typename TIN, typename TW, int NF, int MW> struct RouteRegs {
   static constexpr int D = (BUDGET / V) < 2 ? 2 : ((BUDGET / V) > 8 ? 8 : (BUDGET / V));
 };
 
-template <typename TIN, typename TW, int NPL, int NF, int MW, bool ST>
+// EPLK > 0: the selection with that many register slots per lane only (the
+// launch's own form: a kernel holding every form is sized for the largest)
+template <typename TIN, typename TW, int NPL, int NF, int MW, bool ST, int EPLK = 0>
 __global__ __launch_bounds__(256, (ST ? 2 : RouteRegs<TIN, TW, NF, MW>::OCC)) void route_kernel(RouteArgs a) {
   // LDS: [WK][TB][Eh] partial scores (then scores, probabilities), [Eh]
   // counts, [Eh] bias, and (staged scores) the chunk ring
@@ -676,7 +678,8 @@ __global__ __launch_bounds__(256, (ST ? 2 : RouteRegs<TIN, TW, NF, MW>::OCC)) vo
 
   route_scores(a, part, part, bsh, tb0);
   __syncthreads();
-  route_select(a, part, sbias, cnt, tb0);
+  if constexpr (EPLK > 0) route_select_n<EPLK>(a, part, sbias, cnt, tb0);
+  else route_select(a, part, sbias, cnt, tb0);
   __syncthreads();
   route_block_stats(a, part, cnt, tb0);
   }
@@ -889,10 +892,10 @@ size_t route_ws_bytes(const Shape &s) {
 
 #define LAUNCH_CHECK() do { if (int rc_ = launch_status("route")) return rc_; } while (0)
 
-template <typename TIN, typename TW, int NPL, int NF, int MW, bool ST>
+template <typename TIN, typename TW, int NPL, int NF, int MW, bool ST, int EPLK = 0>
 static int launch_one(const RouteArgs &a, const RouteGeom &g, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((route_kernel<TIN, TW, NPL, NF, MW, ST>), dim3((unsigned)g.nbx, (unsigned)a.H), dim3(256), lds,
-                     st, a);
+  hipLaunchKernelGGL((route_kernel<TIN, TW, NPL, NF, MW, ST, EPLK>), dim3((unsigned)g.nbx, (unsigned)a.H), dim3(256),
+                     lds, st, a);
   return 0;
 }
 
@@ -903,6 +906,16 @@ static int launch_route_t(const RouteArgs &a, const RouteGeom &g, size_t lds, hi
   constexpr bool kST = NPL == 1 && NF >= 4;
   if constexpr (sizeof(TIN) == 2 && (kST || NF <= 10)) {
     if (g.mw == 2) return launch_one<TIN, TW, NPL, NF, 2, kST>(a, g, lds, st);
+  }
+  // one expert fragment per head (E_h <= 16: many heads, or few experts):
+  // kernels with the launch's own selection form (measured on the multi-head
+  // workload: 89 instead of 124 VGPRs, router 27.9 -> 27.0 us cold; a form
+  // held to 64 VGPRs for eight waves per SIMD, four k-steps in flight, took
+  // 43.8 us)
+  if constexpr (!kST && NF == 1) {
+    if (g.epl == 1) return launch_one<TIN, TW, NPL, NF, 1, kST, 1>(a, g, lds, st);
+    if (g.epl == 2) return launch_one<TIN, TW, NPL, NF, 1, kST, 2>(a, g, lds, st);
+    if (g.epl == 4) return launch_one<TIN, TW, NPL, NF, 1, kST, 4>(a, g, lds, st);
   }
   return launch_one<TIN, TW, NPL, NF, 1, kST>(a, g, lds, st);
 }
