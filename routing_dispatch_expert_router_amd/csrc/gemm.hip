@@ -12,7 +12,8 @@
 // [offsets[e], offsets[e+1]) of A and C; an optional extra group (shared
 // experts, or a plain dense product) has its own pointers and sizes.  Both
 // operands are K-contiguous.  Tiles: 256 x 256 outputs with 8 waves (tall
-// groups; a group's short tail goes to a second launch of 128 x 64 tiles) or
+// groups; a group's short tail goes to a second launch of 128 x 128 tiles, or
+// 128 x 64 ones for narrow products) or
 // 128 x 128 with 8 waves (SwiGLU: half the tile's B rows are gate rows, half
 // up rows, so the output tile is BN/2 hidden columns wide); k-chunks of 128
 // bytes per row in LDS rings with XOR-swizzled 16-byte slots, one barrier per
@@ -20,8 +21,11 @@
 //
 // What bounds it (measured on MI355X): with the global loads removed the MFMA
 // + LDS-read loop runs at 75-85 % of the bf16 peak; the global -> LDS stream
-// alone takes 70-90 % of the kernel's time, its L2 misses (the weights,
-// streamed once from HBM, and re-fetched row tiles) setting the pace.
+// alone takes 70-90 % of the kernel's time.  Per 64-k chunk a 256 x 256 tile
+// moves as many bytes through the LDS (fragment reads plus the direct-load
+// writes) as its MFMAs take cycles at 128 bytes per clock, the rate the bank
+// conflict counters point to; the 128 x 128 tiles move twice as many per
+// MFMA and keep the MFMA pipes busy about half as often.
 #include <type_traits>
 
 #include "common.h"
