@@ -155,6 +155,13 @@ typedef struct moe_layer_io {
   void *y_perm;             /* [R_max, d_head] act: expert outputs, same row order */
   void *shared_out;         /* [T, d_model] act: sum of the shared experts (n_shared > 0) */
   void *o;                  /* [T, H*d_head] act: combined head outputs (latent_proj only) */
+  void *gu;                 /* [R_max, 2*d_ff] (SwiGLU: gate, then up) or [R_max, d_ff] (ReLU) act,
+                               or NULL: the routed experts' pre-activations, rows as y_perm.
+                               moe_layer_fwd writes them and moe_layer_bwd reads them instead
+                               of recomputing the gate/up products, for layers whose routed
+                               experts run the grouped GEMM (not the fused narrow-expert MLP:
+                               bf16 with d_head 64, 128 or 256); ignored otherwise.  Pass the
+                               same buffer to both calls, or NULL to both. */
 } moe_layer_io;
 
 /* [host] Workspace bytes every call below needs for `cfg` (0 for an invalid cfg). */

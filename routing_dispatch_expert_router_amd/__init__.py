@@ -60,7 +60,7 @@ class MoeLayerIO(ctypes.Structure):
                 ("src_of", ctypes.c_void_p), ("aux_loss", ctypes.c_void_p), ("seq_loss", ctypes.c_void_p),
                 ("z", ctypes.c_void_p),
                 ("x_perm", ctypes.c_void_p), ("y_perm", ctypes.c_void_p), ("shared_out", ctypes.c_void_p),
-                ("o", ctypes.c_void_p)]
+                ("o", ctypes.c_void_p), ("gu", ctypes.c_void_p)]
 
 
 class MoeWeightsT(ctypes.Structure):

@@ -739,6 +739,93 @@ int launch_bwd_rows(const Shape &s, const void *dy, long ld_dy, const void *y_pe
   return launch_status("backward rows");
 }
 
+// The backward's activation step from the forward's kept pre-activations
+// (the forward's SwiGLU gate g and up u, or ReLU a, rounded to the act dtype
+// as the forward stored them): with the upstream dH, dA = dH u SiLU'(g) and
+// dB = dH SiLU(g) (dA|dB rows of 2 d_ff), H = SiLU(g) u; ReLU: dA = dH [a > 0],
+// H = max(a, 0).  The same arithmetic as the recompute GEMM's backward
+// epilogue, on the kept values instead of recomputed float32 products.  One
+// thread per four consecutive hidden units of a row (grid-stride; rows below
+// offsets[E]).
+// four consecutive elements as one 8-byte (bf16) or 16-byte (float32) access
+template <typename TE> struct Four;
+template <> struct Four<uint16_t> {
+  __device__ __forceinline__ static void load(const uint16_t *p, float o[4]) {
+    const uint2 u = *(const uint2 *)p;
+    o[0] = bf16_to_f32((uint16_t)(u.x & 0xFFFFu)); o[1] = bf16_to_f32((uint16_t)(u.x >> 16));
+    o[2] = bf16_to_f32((uint16_t)(u.y & 0xFFFFu)); o[3] = bf16_to_f32((uint16_t)(u.y >> 16));
+  }
+  __device__ __forceinline__ static void store(uint16_t *p, const float v[4]) {
+    uint2 u;
+    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *(uint2 *)p = u;
+  }
+};
+template <> struct Four<float> {
+  __device__ __forceinline__ static void load(const float *p, float o[4]) {
+    const float4 u = *(const float4 *)p;
+    o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w;
+  }
+  __device__ __forceinline__ static void store(float *p, const float v[4]) {
+    *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+template <typename TE, bool GLU>
+__global__ __launch_bounds__(256) void bwd_saved_act_kernel(const TE *__restrict__ gu, const TE *__restrict__ dH,
+                                                            TE *__restrict__ dAB, TE *__restrict__ H,
+                                                            const int32_t *__restrict__ offsets, int E, long dff) {
+  const long q4 = dff / 4;  // quads per row (d_ff is a multiple of 64)
+  const long total = (long)offsets[E] * q4;
+  const long mg = GLU ? 2 * dff : dff;
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const long r = i / q4, c = (i - r * q4) * 4;
+    float dh[4], a[4], b[4], da[4], db[4], h[4];
+    Four<TE>::load(dH + r * dff + c, dh);
+    Four<TE>::load(gu + r * mg + c, a);
+    if constexpr (GLU) Four<TE>::load(gu + r * mg + dff + c, b);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if constexpr (GLU) {
+        const float gt = a[v], up = b[v];
+        const float sg = 1.0f / (1.0f + __expf(-gt)), si = gt * sg;
+        da[v] = dh[v] * up * (sg * (1.0f + gt * (1.0f - sg)));
+        db[v] = dh[v] * si;
+        h[v] = si * up;
+      } else {
+        da[v] = a[v] > 0.0f ? dh[v] : 0.0f;
+        h[v] = fmaxf(a[v], 0.0f);
+      }
+    }
+    Four<TE>::store(dAB + r * mg + c, da);
+    if constexpr (GLU) Four<TE>::store(dAB + r * mg + dff + c, db);
+    Four<TE>::store(H + r * dff + c, h);
+  }
+}
+
+int launch_bwd_saved_act(const Shape &s, const void *gu, const void *dH, void *dAB, void *H, const int32_t *offsets,
+                         hipStream_t st) {
+  if (s.R_max == 0) return 0;
+  const long total = s.R_max * (long)s.dff / 4;
+  const unsigned grid = (unsigned)std::min<long>((total + 255) / 256, 16384);
+  const bool glu = s.act == 1;
+  if (s.act_f32) {
+    if (glu) hipLaunchKernelGGL((bwd_saved_act_kernel<float, true>), dim3(grid), dim3(256), 0, st, (const float *)gu,
+                                (const float *)dH, (float *)dAB, (float *)H, offsets, s.E, (long)s.dff);
+    else hipLaunchKernelGGL((bwd_saved_act_kernel<float, false>), dim3(grid), dim3(256), 0, st, (const float *)gu,
+                            (const float *)dH, (float *)dAB, (float *)H, offsets, s.E, (long)s.dff);
+  } else {
+    if (glu) hipLaunchKernelGGL((bwd_saved_act_kernel<uint16_t, true>), dim3(grid), dim3(256), 0, st,
+                                (const uint16_t *)gu, (const uint16_t *)dH, (uint16_t *)dAB, (uint16_t *)H, offsets,
+                                s.E, (long)s.dff);
+    else hipLaunchKernelGGL((bwd_saved_act_kernel<uint16_t, false>), dim3(grid), dim3(256), 0, st,
+                            (const uint16_t *)gu, (const uint16_t *)dH, (uint16_t *)dAB, (uint16_t *)H, offsets,
+                            s.E, (long)s.dff);
+  }
+  return launch_status("backward activation from kept pre-activations");
+}
+
 int launch_bwd_pad(const Shape &s, const int32_t *offsets, const int32_t *src_of, int32_t *poff, int32_t *pmap_r,
                    int32_t *pmap_x, long npad, hipStream_t st) {
   hipLaunchKernelGGL(bwd_poff_kernel, dim3(1), dim3(1024), 0, st, offsets, s.E, poff);

@@ -74,6 +74,8 @@ struct GemmArgs {
   int fixed_tiles;
   int G;
   int split;  // 0: all rows of a group; 1: rows [0, cut); 2: rows [cut, M); 3, 4: see row_window
+  void *gsave; long ldg;                      // EPI_SWIGLU / EPI_RELU, or NULL: the pre-activations (rows as
+                                              //   C): SwiGLU gate g at [row][col], up u at [row][N + col]; ReLU a
 };
 
 // Rows of a group a launch covers.  With split launches, a group's rows are
@@ -452,6 +454,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
   const TE *R = (EPI == EPI_RESID) ? (const TE *)p.res + (size_t)r0 * p.ldres : nullptr;
   const TE *DHp = (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) ? (const TE *)p.dh + (size_t)r0 * p.lddh : nullptr;
   TE *HO = (EPI == EPI_SWIGLU_BWD || EPI == EPI_RELU_BWD) ? (TE *)p.hout + (size_t)r0 * p.ldh : nullptr;
+  // the forward's pre-activations, kept for the backward when asked for
+  TE *GS = ((EPI == EPI_SWIGLU || EPI == EPI_RELU) && p.gsave) ? (TE *)p.gsave + (size_t)r0 * p.ldg : nullptr;
   // The epilogues that read a second operand (the residual; the backward's
   // upstream dH) issue all of the wave's loads before its first store: C may
   // alias that operand as far as the compiler knows, so a load placed after a
@@ -527,6 +531,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
         const int ct = wn * WN + f * 16 + 4 * cq;
         float o[4], r[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (EPI == EPI_RESID) Quad<TE>::decode(pre[i][f], r);
+        if constexpr (EPI == EPI_RELU) {
+          if (GS && m0 + rt < M && tn * BN_ + ct < N) {
+            const float a[4] = {acc[i][f][0], acc[i][f][1], acc[i][f][2], acc[i][f][3]};
+            Quad<TE>::store(GS + (size_t)(m0 + rt) * p.ldg + tn * BN_ + ct, a);
+          }
+        }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           o[v] = acc[i][f][v];
@@ -600,6 +610,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
           h[v] = gt / (1.0f + __expf(-gt)) * up;
         }
         Quad<TE>::store(C + (size_t)row * ldc + col, h);
+        if (GS) {
+          const float gq[4] = {acc[i][f][0], acc[i][f][1], acc[i][f][2], acc[i][f][3]};
+          const float uq[4] = {acc[i][f + NF / 2][0], acc[i][f + NF / 2][1], acc[i][f + NF / 2][2],
+                               acc[i][f + NF / 2][3]};
+          Quad<TE>::store(GS + (size_t)row * p.ldg + col, gq);
+          Quad<TE>::store(GS + (size_t)row * p.ldg + N + col, uq);
+        }
       }
     } else if (EPI == EPI_PIECE) {
 #pragma unroll
@@ -630,6 +647,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void grouped_gemm_kernel(GemmArgs p
         if (col >= N) continue;
         float o[4], r[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (EPI == EPI_RESID) Quad<TE>::decode(pre[i][f], r);
+        if constexpr (EPI == EPI_RELU) {
+          if (GS) {
+            const float a[4] = {acc[i][f][0], acc[i][f][1], acc[i][f][2], acc[i][f][3]};
+            Quad<TE>::store(GS + (size_t)row * p.ldg + col, a);
+          }
+        }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           o[v] = acc[i][f][v];
@@ -1085,7 +1108,7 @@ template <typename TE>
 static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets,
                      const void *w1, const void *w3, const void *w2, void *y_perm, const void *x_shared,
                      const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st,
-                     const FoldOut &fold) {
+                     const FoldOut &fold, void *gsave) {
   const int esz = sizeof(TE);
   char *p = (char *)ws;
   TE *H = (TE *)p;
@@ -1102,6 +1125,7 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
   // narrow experts: the fused MLP (no hidden round trip through HBM)
   const bool fused = sizeof(TE) == 2 && mlp_fused_supported(s);
   if (fold.o && !(fused && fold_supported(s))) return -2;
+  if (gsave && fused) return -2;  // the fused MLP keeps no pre-activations
   if (fused) {
     if (int rc = launch_mlp_fused(s, xin, gather, offsets, w1, w3, w2, y_perm, pre, st, fold)) return rc;
   }
@@ -1119,6 +1143,7 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
   a.gather = gather; a.gK = s.K; a.gEh = s.Eh; a.gdh = s.dh;
   a.B = w1; a.B2 = glu ? w3 : nullptr; a.ldb = s.dh; a.bstride = (long)s.dff * s.dh;
   a.C = H; a.ldc = s.dff;
+  a.gsave = gsave; a.ldg = glu ? 2L * s.dff : s.dff;
   a.offsets = offsets; a.E = s.E; a.N = s.dff; a.K = s.dh; a.Mr_bound = s.R_max;
   a.has_x = 0; a.G = s.E;
   // ---- GEMM 2: y_perm = H W2^T
@@ -1175,13 +1200,15 @@ static int ffn_typed(const Shape &s, const void *xin, const int32_t *gather, con
 int launch_expert_ffn(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets,
                       const void *w1, const void *w3, const void *w2, void *y_perm, const void *x_shared,
                       const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st,
-                      const FoldOut &fold) {
+                      const FoldOut &fold, void *gsave) {
   if (s.act_f32)
     return ffn_typed<float>(s, xin, gather, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws, st,
-                            fold);
+                            fold, gsave);
   return ffn_typed<uint16_t>(s, xin, gather, offsets, w1, w3, w2, y_perm, x_shared, ws1, ws3, ws2, shared_out, ws,
-                             st, fold);
+                             st, fold, gsave);
 }
+
+bool ffn_grouped(const Shape &s) { return s.act_f32 || !mlp_fused_supported(s); }
 
 size_t dense_ws_bytes() { return 0; }  // the tile counts come from the host
 

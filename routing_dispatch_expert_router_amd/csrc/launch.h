@@ -116,6 +116,11 @@ int launch_transpose(bool f32, const void *src, long ld_src, long bs_src, const 
 int launch_bwd_rows(const Shape &s, const void *dy, long ld_dy, const void *y_perm, const float *gates,
                     const int32_t *src_of, const int32_t *topk_idx, const int32_t *offsets, void *dY, float *dg,
                     hipStream_t st);
+// the backward's activation step from the forward's kept pre-activations gu
+// (see launch_expert_ffn): dA|dB [R][m d_ff] and H [R][d_ff] from gu and the
+// upstream dH [R][d_ff], for rows below offsets[E]
+int launch_bwd_saved_act(const Shape &s, const void *gu, const void *dH, void *dAB, void *H, const int32_t *offsets,
+                         hipStream_t st);
 int launch_bwd_pad(const Shape &s, const int32_t *offsets, const int32_t *src_of, int32_t *poff, int32_t *pmap_r,
                    int32_t *pmap_x, long npad, hipStream_t st);
 // float32 layers: the router weight gradient sums router_wgrad_split(s) token
@@ -180,11 +185,17 @@ size_t ffn_ws_bytes(const Shape &s);
 // else `xin` is the expert input x and row r is read from x[gather[r] / K]
 // at column offset (e / E_h) * d_head
 // fold.o != NULL (fold_supported(s) only): the combine folded into the
-// epilogue (see FoldOut); y_perm may then be NULL (not written)
+// epilogue (see FoldOut); y_perm may then be NULL (not written).  gsave !=
+// NULL (ffn_grouped(s) only): the routed gate/up products' pre-activations
+// are kept there, [R_max][2 d_ff] (SwiGLU: gate, then up) or [R_max][d_ff]
+// (ReLU), act dtype, rows as y_perm
 int launch_expert_ffn(const Shape &s, const void *xin, const int32_t *gather, const int32_t *offsets,
                       const void *w1, const void *w3, const void *w2, void *y_perm, const void *x_shared,
                       const void *ws1, const void *ws3, const void *ws2, void *shared_out, void *ws, hipStream_t st,
-                      const FoldOut &fold = FoldOut{});
+                      const FoldOut &fold = FoldOut{}, void *gsave = nullptr);
+// whether the routed experts run the grouped GEMM (not the fused MLP): the
+// layers whose forward can keep the pre-activations for the backward
+bool ffn_grouped(const Shape &s);
 // dense C[M,N] = A[M,K] B[N,K]^T (+ residual R[M,N]), act dtype, float32 accumulate
 size_t dense_ws_bytes();
 int launch_dense(bool f32, const void *A, const void *B, void *C, const void *residual, int M, int N, int K,

@@ -256,7 +256,8 @@ static bool misaligned_wt(const moe_weights_t *t) {
 }
 static bool misaligned_io(const moe_layer_io *io) {
   return misaligned({io->logits, io->topk_idx, io->topk_w, io->demand, io->counts, io->offsets, io->row_of,
-                     io->src_of, io->aux_loss, io->seq_loss, io->z, io->x_perm, io->y_perm, io->shared_out, io->o});
+                     io->src_of, io->aux_loss, io->seq_loss, io->z, io->x_perm, io->y_perm, io->shared_out, io->o,
+                     io->gu});
 }
 static bool misaligned_g(const moe_grads *g) {
   return misaligned({g->dx, g->dw_router, g->dbias, g->dw1, g->dw3, g->dw2, g->dws1, g->dws3, g->dws2, g->dw_in,
@@ -500,9 +501,11 @@ int moe_layer_fwd(const moe_config *cfg, const moe_weights *w, const void *x, vo
   const bool fold = moe::fold_supported(s);
   moe::FoldOut fo{};
   if (fold) fo = moe::FoldOut{o, topk_w, src_of};
+  // the routed pre-activations, kept for the backward when the caller gives a buffer
+  void *gsave = (io && io->gu && moe::ffn_grouped(s)) ? io->gu : nullptr;
   if ((rc = rc_of(moe::launch_expert_ffn(s, x_perm ? x_perm : xin, x_perm ? nullptr : src_of, offsets, w->w1,
                                          w->w3, w->w2, (fold && !io->y_perm) ? nullptr : y_perm, x, w->ws1, w->ws3,
-                                         w->ws2, shared, scratch, stream, fo))))
+                                         w->ws2, shared, scratch, stream, fo, gsave))))
     return rc;
   const void *res = (!s.latent && s.residual) ? x : nullptr;
   if (!fold && (rc = rc_of(moe::launch_combine(s, y_perm, row_of, topk_w, res, shared, s.latent ? o : y, stream))))
@@ -638,10 +641,15 @@ int moe_layer_bwd(const moe_config *cfg, const moe_weights *w, const moe_weights
   if ((rc = rc_of(moe::gemm_routed(s, moe::GEMM_EPI_PLAIN, dY, dh, nullptr, wt->w2t, nullptr, dh, dff * dh, dH, dff,
                                    (int)dff, (int)dh, offsets, nullptr, 0, nullptr, 0, prefix, stream))))
     return rc;
-  // recompute the gate/up products from u, with the backward epilogue: dA|dB, H
-  if ((rc = rc_of(moe::gemm_routed(s, epi_bwd, u, D, src_of, w->w1, glu ? w->w3 : nullptr, dh, dff * dh, dAB,
-                                   m * dff, (int)dff, (int)dh, offsets, dH, dff, Hr, dff, prefix, stream))))
-    return rc;
+  if (io->gu && moe::ffn_grouped(s)) {
+    // dA|dB and H from the pre-activations the forward kept
+    if ((rc = rc_of(moe::launch_bwd_saved_act(s, io->gu, dH, dAB, Hr, offsets, stream)))) return rc;
+  } else {
+    // recompute the gate/up products from u, with the backward epilogue: dA|dB, H
+    if ((rc = rc_of(moe::gemm_routed(s, epi_bwd, u, D, src_of, w->w1, glu ? w->w3 : nullptr, dh, dff * dh, dAB,
+                                     m * dff, (int)dff, (int)dh, offsets, dH, dff, Hr, dff, prefix, stream))))
+      return rc;
+  }
   // dX rows = [dA dB] [W1; W3]
   if ((rc = rc_of(moe::gemm_routed(s, moe::GEMM_EPI_PLAIN, dAB, m * dff, nullptr, wt->w13t, nullptr, m * dff,
                                    dh * m * dff, dXr, dh, (int)dh, (int)(m * dff), offsets, nullptr, 0, nullptr, 0,

@@ -50,7 +50,7 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-def _forward(cfg, inp, logits):
+def _forward(cfg, inp, logits, gu=False, want_y=False):
     T, K, E = cfg.T, cfg.k_total, cfg.n_experts
     Rm = moe.moe_rows_upper_bound(cfg)
     io = dict(logits=dev(logits), logits_mode=moe.MOE_LOGITS_LOAD, topk_idx=i32(T, K), topk_w=f32(T, K),
@@ -58,12 +58,14 @@ def _forward(cfg, inp, logits):
               y_perm=empty_act(cfg, max(Rm, 1), cfg.d_head),
               z=empty_act(cfg, T, cfg.d_latent) if cfg.latent_proj else None,
               o=empty_act(cfg, T, cfg.d_latent) if cfg.latent_proj else None)
+    if gu:  # the routed pre-activations, kept for the backward
+        io["gu"] = empty_act(cfg, max(Rm, 1), (2 if cfg.act == 1 else 1) * cfg.d_ff)
     W = weights_dev(cfg, inp)
     x = dev(inp.x)
     y = torch.empty_like(x)
     moe.moe_layer_fwd(cfg, W, x, y, io, moe.workspace(cfg))
     torch.cuda.synchronize()
-    return W, x, io
+    return (W, x, io, y) if want_y else (W, x, io)
 
 
 def _transposed(cfg, W):
@@ -168,3 +170,52 @@ def test_backward_rejects_aux_with_several_heads():
         moe.moe_layer_bwd(cfg, W, _transposed(cfg, W), x, dev(_dy(cfg)), 0.5, io, _grads(cfg),
                           moe.backward_workspace(cfg))
     assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+def _grouped(cfg):
+    """The routed experts run the grouped GEMM (not the fused narrow-expert MLP): the layers
+    whose forward keeps the pre-activations for the backward."""
+    return cfg.act_dtype == 0 or cfg.d_head not in (64, 128, 256)
+
+
+GU_CFGS = [c for c in CFGS if _grouped(c)] + [
+    # bf16 ReLU experts on the grouped GEMM (d_head 192)
+    MoEConfig("bwd_gu_relu_bf16", T=70, d_model=192, n_heads=1, d_head=192, n_experts=5, top_k=2, d_ff=128,
+              act=0, drop=1, capacity=20, tag=75),
+    # experts of about 1024 rows: 256-row tiles and their tails keep the pre-activations too
+    MoEConfig("bwd_gu_tall", T=2048, d_model=320, n_heads=1, d_head=320, n_experts=4, top_k=2, d_ff=128,
+              renorm=1, tag=76),
+]
+
+
+@pytest.mark.parametrize("cfg", GU_CFGS, ids=lambda c: c.name)
+def test_backward_with_kept_preactivations(cfg):
+    """moe_layer_fwd keeps the routed pre-activations in io.gu; moe_layer_bwd then reads them
+    instead of recomputing the gate/up products.  The forward's output is bitwise the same,
+    and every gradient meets the same bars against the backward oracle."""
+    log(f"backward with kept pre-activations {cfg.name}")
+    inp = _inputs(cfg)
+    out = oracle.forward(cfg, inp)
+    W, x, io0, y0 = _forward(cfg, inp, out["logits"], want_y=True)
+    _, _, io, y1 = _forward(cfg, inp, out["logits"], gu=True, want_y=True)
+    assert torch.equal(_bits(y0), _bits(y1))
+    wt = _transposed(cfg, W)
+    dy_h = _dy(cfg)
+    G = _grads(cfg)
+    lam = _lam(cfg)
+    moe.moe_layer_bwd(cfg, W, wt, x, dev(dy_h), lam, io, G, moe.backward_workspace(cfg))
+    torch.cuda.synchronize()
+    kept = io["row_of"].cpu().numpy().reshape(-1) >= 0
+    ref = OB.backward(cfg, OB.params_of(inp), io["topk_idx"].cpu().numpy(), kept, oracle.decode(dy_h), lam)
+    names = ["dx", "dw_router", "dbias", "dw1", "dw2"] + (["dw3"] if cfg.act == 1 else [])
+    if cfg.n_shared:
+        names += ["dws1", "dws2"] + (["dws3"] if cfg.act == 1 else [])
+    if cfg.latent_proj:
+        names += ["dw_in", "dw_out"]
+    for k in names:
+        got, want = f64(G[k]), ref[k]
+        scale = max(np.max(np.abs(want)), 1e-30)
+        err = np.max(np.abs(got - want))
+        log(f"  {k:10s} max|ref| {scale:.3g}  rel err {err / scale:.3g}")
+        assert np.all(np.isfinite(got)), k
+        assert err <= tol(cfg) * scale, k
