@@ -23,6 +23,13 @@ counters the runs hold: SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16,
 SQ_WAIT_INST_ANY, SQ_WAVE_CYCLES, SQ_LDS_BANK_CONFLICT, GRBM_GUI_ACTIVE,
 TCC_HIT_sum, TCC_MISS_sum, FETCH_SIZE, WRITE_SIZE.
 
+    python bench_profile.py backward --workload NAME --trace DIR [--bench-json FILE] [--commands FILE]
+
+writes profiles/moe_layer_bwd__NAME.md from a --kernel-trace run of bench.py
+with its backward timing: the launches of one moe_layer_bwd call (each call
+starts at its gate-gradient zeroing kernel, zero_f32_kernel; one-head
+layers), averaged over the traced calls, in launch order.
+
 An expert-FFN call is the run of dispatches that starts at its tile-prefix
 kernel (gemm_prep_kernel or mlp_prefix_kernel) and holds only FFN kernels
 (grouped_gemm_kernel, mlp_kernel); it is cold when the dispatch before it is
@@ -219,9 +226,60 @@ def counters_main(argv):
     print(f"{a.workload}: {len(order)} FFN kernels")
 
 
+def backward_main(argv):
+    ap = argparse.ArgumentParser(prog="bench_profile.py backward")
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--bench-json", default="")
+    ap.add_argument("--commands", default="")
+    a = ap.parse_args(argv)
+    tr = load_trace(a.trace)
+    starts = [i for i, r in enumerate(tr) if r[0].startswith("zero_f32_kernel")]
+    if not starts:
+        sys.exit("no backward call in the trace")
+    calls = []
+    for j, b in enumerate(starts):
+        e = starts[j + 1] if j + 1 < len(starts) else len(tr)
+        while e > b and (tr[e - 1][0].startswith("at::native") or tr[e - 1][0].startswith("__amd")):
+            e -= 1
+        calls.append((b, e))
+    # the backward calls are the ones with the most common launch sequence (the warm-up and timed calls)
+    shapes = {}
+    for b, e in calls:
+        shapes.setdefault(tuple((tr[k][0], tr[k][1]) for k in range(b, e)), []).append((b, e))
+    shape, cs = max(shapes.items(), key=lambda kv: len(kv[1]))
+    n = len(cs)
+    avg = [sum((tr[b + p][3] - tr[b + p][2]) / 1e3 for b, _ in cs) / n for p in range(len(shape))]
+    span = sum((tr[e - 1][3] - tr[b][2]) / 1e3 for b, e in cs) / n
+    lines = [f"# rocprofv3 summary: MoE layer backward (moe_layer_bwd), {a.workload}", "",
+             "Commands (from the repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`):", ""]
+    if a.commands:
+        lines += ["    " + c.strip() for c in open(a.commands) if c.strip()]
+    lines += ["    python bench_profile.py backward --workload " + a.workload + " --trace " + a.trace +
+              (f" --bench-json {a.bench_json}" if a.bench_json else ""), "",
+              f"{n} backward calls traced (warm-up + timed). Kernel durations below are averages over the calls,",
+              "in launch order; the span is first launch start to last launch end.", "",
+              "| # | kernel | grid (threads) | avg us |", "|---:|---|---:|---:|"]
+    lines += [f"| {p} | `{nm}` | {g} | {v:.1f} |" for p, ((nm, g), v) in enumerate(zip(shape, avg))]
+    bw = ""
+    if a.bench_json:
+        with open(a.bench_json) as f:
+            d = json.loads([l for l in f.read().splitlines() if l.strip().startswith("{")][-1])
+        b = d.get("backward") or {}
+        if b:
+            bw = (f"; bench.py's HIP-event figure for the same calls: {b['ms_per_step'] * 1e3:.1f} us per call"
+                  + (" (pre-activations kept by the forward)" if b.get("kept_preactivations") else ""))
+    lines += ["", f"Span of one call: {span:.1f} us{bw}.", ""]
+    with open(os.path.join(ROOT, "profiles", f"moe_layer_bwd__{a.workload}.md"), "w") as f:
+        f.write("\n".join(lines))
+    print(f"{a.workload}: backward span {span:.1f} us over {n} calls")
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "counters":
         return counters_main(sys.argv[2:])
+    if len(sys.argv) > 1 and sys.argv[1] == "backward":
+        return backward_main(sys.argv[2:])
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
     ap.add_argument("--trace", required=True)
