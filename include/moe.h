@@ -46,6 +46,14 @@
  *     be 256-byte aligned; its contents need not be initialised.
  *   - Every other device pointer must be 16-byte aligned (the kernels move
  *     16-byte vectors); a misaligned one returns MOE_ERR_ARG before any launch.
+ *   - The library reads every field of the structs below as laid out in this
+ *     header; fields are only ever appended, and each addition raises
+ *     MOE_ABI_VERSION.  Zero-initialise a struct and set the fields you use
+ *     (a NULL optional pointer is "not asked for").  A caller that may load a
+ *     library built from another version of this header compares
+ *     moe_abi_version() with its own MOE_ABI_VERSION before the first call:
+ *     a library that reads fields the caller's structs do not have would read
+ *     past them.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -174,6 +182,12 @@ int64_t moe_rows_upper_bound(const moe_config *cfg);
 
 /* [host] Static string naming a moe_status value. */
 const char *moe_status_str(int status);
+
+/* Layout version of the structs in this header (see the conventions above). */
+#define MOE_ABI_VERSION 1
+
+/* [host] The MOE_ABI_VERSION the library was built with. */
+int32_t moe_abi_version(void);
 
 /* [host] MOE_OK if `cfg` is valid and supported, else the error moe_* calls would return.
  * Supported sizes: T*K, T*max(d_model, H*d_head, m*d_ff, m*n_shared*d_ff),

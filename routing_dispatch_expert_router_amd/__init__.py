@@ -25,6 +25,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+# struct layout version of include/moe.h (MOE_ABI_VERSION); the loader refuses a library built with another
+MOE_ABI_VERSION = 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DROP_NONE, MOE_DROP_CAPACITY, MOE_DROP_AFFINITY = 0, 1, 2
@@ -39,7 +41,7 @@ CONFIG_FIELDS = ["T", "d_model", "n_heads", "d_head", "n_experts", "top_k", "n_g
 _OPTIONAL_FIELDS = {"route_mode", "sel_bias_gate", "seq_len"}
 
 # exported symbols, as declared in include/moe.h
-SYMBOLS = ["moe_workspace_bytes", "moe_rows_upper_bound", "moe_status_str", "moe_check_config",
+SYMBOLS = ["moe_workspace_bytes", "moe_rows_upper_bound", "moe_status_str", "moe_abi_version", "moe_check_config",
            "moe_route", "moe_route_ex", "moe_dispatch", "moe_dispatch_noalloc", "moe_check_topk", "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_layer_fwd",
            "moe_sel_bias_update", "moe_backward_workspace_bytes", "moe_transpose_weights", "moe_layer_bwd"]
 
@@ -88,6 +90,7 @@ def _load():
         "moe_workspace_bytes": (S, [Z]),
         "moe_rows_upper_bound": (ctypes.c_int64, [Z]),
         "moe_status_str": (ctypes.c_char_p, [I]),
+        "moe_abi_version": (ctypes.c_int32, []),
         "moe_check_config": (I, [Z]),
         "moe_route": (I, [Z, P, P, P, P, I, P, P, P, P, S, P]),
         "moe_route_ex": (I, [Z, P, P, P, P, P, I, P, P, P, P, P, S, P]),
@@ -107,6 +110,9 @@ def _load():
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
         f.restype, f.argtypes = res, args
+    if lib.moe_abi_version() != MOE_ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has struct layout version {lib.moe_abi_version()}, this binding "
+                          f"version {MOE_ABI_VERSION}: rebuild the library")
     return lib
 
 

@@ -278,6 +278,8 @@ int64_t moe_rows_upper_bound(const moe_config *cfg) {
   return s.R_max;
 }
 
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
 const char *moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";

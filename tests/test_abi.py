@@ -378,3 +378,26 @@ def test_check_topk_argument_checks():
     assert lib.moe_check_topk(ctypes.byref(c1), ctypes.c_void_p(0x1002), fake, None) == moe.MOE_ERR_ARG
     bad = moe.config_struct(CONFIGS[1].with_(n_experts=0))
     assert lib.moe_check_topk(ctypes.byref(bad), fake, fake, None) != moe.MOE_OK
+
+
+def _header_fields(struct):
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = src[src.index(f"typedef struct {struct} {{"):src.index(f"}} {struct};")]
+    body = body.split("{", 1)[1]
+    # declarations may list several names: "void *dw1, *dw3, *dw2;"
+    return [re.sub(r"[\s\*]", " ", n).split()[-1] for d in body.split(";") if d.strip() for n in d.split(",")]
+
+
+@pytest.mark.parametrize("struct,cls", [("moe_weights", "MoeWeights"), ("moe_layer_io", "MoeLayerIO"),
+                                        ("moe_weights_t", "MoeWeightsT"), ("moe_grads", "MoeGrads")])
+def test_struct_fields_match_header(struct, cls):
+    """The binding's ctypes structs name the header's fields in the header's order."""
+    names = [f[0] for f in getattr(moe, cls)._fields_]
+    assert names == _header_fields(struct)
+
+
+def test_abi_version():
+    """The header's MOE_ABI_VERSION, the binding's and the library's agree."""
+    src = open(HEADER).read()
+    v = int(re.search(r"#define\s+MOE_ABI_VERSION\s+(\d+)", src).group(1))
+    assert v == moe.MOE_ABI_VERSION == moe._lib.moe_abi_version()
