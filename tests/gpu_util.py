@@ -130,3 +130,57 @@ def check_keep(cfg, io, out, near_ties=True):
             assert abs(float(ow[a]) - float(thr)) <= 4 * float(np.spacing(np.float32(thr))), \
                 f"assignment {a} (expert {e}) kept differently away from a gate near-tie"
     return diff
+
+
+def relu_tie_allowance(cfg, P, topk_idx, kept, dy):
+    """Element-wise bounds on how far a ReLU layer's gradients may lie from the backward
+    oracle's because of the ReLU mask alone.
+
+    The mask [a > 0] of a pre-activation a = W1 v is a decision taken in floating point,
+    like the top-k choice: where the oracle's a lies within what the GPU's own a may
+    differ from it (float32 sums; with the latent projections also the expert input
+    z = x W_in^T, which the layer stores in its activation type and the experts read
+    from there), the GPU may take the other side, and its gradients then differ by that
+    element's whole term.  Returns (bounds, n) with bounds = {"dx", "dw1", "dw_in"}: the
+    sum of those terms' magnitudes over the near-zero elements (zero elsewhere), and n,
+    the number of such elements.  Zero bounds for SwiGLU layers (a smooth activation).
+    """
+    import oracle.moe_backward as OB
+    T, E, Eh, dh = cfg.T, cfg.n_experts, cfg.e_per_head, cfg.d_head
+    x = P["x"]
+    zero = dict(dx=np.zeros_like(x), dw1=np.zeros_like(P["w1"]),
+                dw_in=np.zeros_like(P["w_in"]) if cfg.latent_proj else None)
+    if cfg.act != 0:
+        return zero, 0
+    u = OB._u(cfg, P)
+    # |what the GPU's a may differ by| <= rel * sum_k |W1 v| (+ z's own rounding and sums)
+    rel_z = 2.0 ** -8 if cfg.act_dtype == 1 else 1e-5
+    su = np.abs(x) @ np.abs(P["w_in"]).T if cfg.latent_proj else None
+    idx = np.asarray(topk_idx, np.int64)
+    K = idx.shape[1]
+    keep2 = np.asarray(kept).reshape(T, K)
+    pc = np.take_along_axis(OB._probs(cfg, P, u), idx, axis=1)
+    g, _ = OB._gate_values(cfg, P, pc, idx)
+    do = np.asarray(dy, np.float64) @ P["w_out"] if cfg.latent_proj else np.asarray(dy, np.float64)
+    b_du = np.zeros((T, cfg.n_heads * dh))
+    b_dw1 = np.zeros_like(P["w1"])
+    n = 0
+    for e in range(E):
+        rows, cols = np.nonzero((idx == e) & keep2)
+        if len(rows) == 0:
+            continue
+        hs = slice((e // Eh) * dh, (e // Eh + 1) * dh)
+        v, W1 = u[rows, hs], P["w1"][e]
+        a = v @ W1.T
+        reach = 1e-5 * (np.abs(v) @ np.abs(W1).T)
+        if cfg.latent_proj:
+            reach += (rel_z * np.abs(v) + 1e-5 * su[rows, hs]) @ np.abs(W1).T
+        near = np.abs(a) <= reach
+        n += int(near.sum())
+        dhid = (g[rows, cols][:, None] * do[rows, hs]) @ P["w2"][e]
+        c = np.where(near, np.abs(dhid), 0.0)
+        b_dw1[e] += c.T @ np.abs(v)
+        np.add.at(b_du, (rows[:, None], np.arange(hs.start, hs.stop)[None, :]), c @ np.abs(W1))
+    if cfg.latent_proj:
+        return dict(dx=b_du @ np.abs(P["w_in"]), dw1=b_dw1, dw_in=b_du.T @ np.abs(x)), n
+    return dict(dx=b_du, dw1=b_dw1, dw_in=None), n

@@ -16,7 +16,10 @@ loaded and checks:
     mask), within 2e-2 (bf16) or 1e-4 (float32) of max|y|;
   * the per-sequence statistic within 1e-5 relative;
   * every gradient of moe_layer_bwd against the backward oracle for those
-    decisions, within the same bars.
+    decisions, within the same bars; for ReLU layers plus, element by element,
+    the terms of the pre-activations the oracle finds within float32 (and,
+    with the latent projections, the stored latent's) reach of 0, whose
+    mask the GPU may decide the other way.
 moe_route also runs on each case computing its own scores (the router
 product's shape variants): scores within 1e-5 of max|l|, choices equal up to
 near-ties, gates within 1e-5.
@@ -31,7 +34,8 @@ import oracle.moe_backward as OB
 import routing_dispatch_expert_router_amd as moe
 from moe_inputs import generate, bf16_bits_from_f32
 from moe_inputs.configs import MoEConfig
-from tests.gpu_util import log, dev, f64, empty_act, i32, f32, tol, weights_dev, routing_margin, check_keep
+from tests.gpu_util import (log, dev, f64, empty_act, i32, f32, tol, weights_dev, routing_margin, check_keep,
+                            relu_tie_allowance)
 from tests.test_gpu_backward import _transposed, _grads
 
 N_CASES = 24
@@ -84,7 +88,9 @@ def draw(i):
     return cfg
 
 
-CASES = [draw(i) for i in range(N_CASES)]
+# plus draws of ReLU layers with the latent projections (bf16 and float32; top-1 per
+# head with its folded combine among them), whose mask near-ties the check allows for
+CASES = [draw(i) for i in range(N_CASES)] + [draw(i) for i in (76, 85, 125, 166)]
 
 
 def test_draws_are_valid_and_varied():
@@ -164,6 +170,10 @@ def test_random_layer_forward_backward(cfg):
         names += ["dws1", "dws2"] + (["dws3"] if cfg.act == 1 else [])
     if cfg.latent_proj:
         names += ["dw_in", "dw_out"]
+    # ReLU layers: a pre-activation near 0 may take the other side of the mask on the GPU
+    ties, nties = relu_tie_allowance(cfg, P, idx, kept, oracle.decode(dy_h))
+    if nties:
+        log(f"  ReLU pre-activations near 0: {nties}")
     for n in names:
         got, want = f64(G[n]), ref[n]
         sc = max(np.max(np.abs(want)), 1e-30)
@@ -171,7 +181,11 @@ def test_random_layer_forward_backward(cfg):
         log(f"  {n:9s} rel err {e / sc:.3g}")
         assert np.all(np.isfinite(got)), n
         # router gradients are float32 throughout: an absolute floor covers a ~0 reference
-        assert e <= tol(cfg) * sc + (1e-6 if n in ("dw_router", "dbias") else 0.0), n
+        bound = tol(cfg) * sc + (1e-6 if n in ("dw_router", "dbias") else 0.0)
+        if ties.get(n) is not None:
+            assert np.all(np.abs(got - want) <= bound + ties[n]), n
+        else:
+            assert e <= bound, n
 
 
 @pytest.mark.gpu
