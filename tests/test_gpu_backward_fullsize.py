@@ -6,7 +6,9 @@ units (they decompose over hidden units).  Router gradients: every token's logit
 gradient sums to zero over the experts (softmax Jacobian), so sum_e dbias_e and
 every column sum of dW_router vanish.  The multi-head latent workload's experts are
 small, so the oracle's whole backward runs and every gradient is compared.  Plus
-finiteness and bitwise reproducibility.
+finiteness and bitwise reproducibility.  The workloads whose routed experts run the
+grouped GEMM run twice: recomputing the gate/up products, and (as the benchmark times
+them) with the forward keeping the pre-activations (io.gu) for the backward.
 """
 import numpy as np
 import pytest
@@ -21,6 +23,8 @@ from tests.gpu_util import log, dev, f64, tol, weights_dev, cached_inputs
 pytestmark = pytest.mark.gpu
 
 FULL = CONFIGS[1:]
+# (workload, pre-activations kept): kept only where the routed experts run the grouped GEMM
+CASES = [(c, False) for c in FULL] + [(c, True) for c in FULL if c.act_dtype == 0 or c.d_head not in (64, 128, 256)]
 
 
 def _lam(cfg):
@@ -32,9 +36,9 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
-def test_fullsize_backward(cfg):
-    log(f"full-size backward {cfg.name}")
+@pytest.mark.parametrize("cfg,keep", CASES, ids=[c.name + ("-kept" if k else "") for c, k in CASES])
+def test_fullsize_backward(cfg, keep):
+    log(f"full-size backward {cfg.name}" + (" (pre-activations kept)" if keep else ""))
     inp = cached_inputs(cfg)
     T, K, E, dh, F, d = cfg.T, cfg.k_total, cfg.n_experts, cfg.d_head, cfg.d_ff, cfg.d_model
     Rm = moe.moe_rows_upper_bound(cfg)
@@ -46,7 +50,8 @@ def test_fullsize_backward(cfg):
               topk_idx=e_(T, K, dt=torch.int32), topk_w=e_(T, K, dt=torch.float32), demand=e_(E, dt=torch.int32),
               counts=e_(E, dt=torch.int32), offsets=e_(E + 1, dt=torch.int32), row_of=e_(T, K, dt=torch.int32),
               src_of=e_(Rm, dt=torch.int32), y_perm=e_(Rm, dh),
-              z=e_(T, cfg.d_latent) if cfg.latent_proj else None, o=e_(T, cfg.d_latent) if cfg.latent_proj else None)
+              z=e_(T, cfg.d_latent) if cfg.latent_proj else None, o=e_(T, cfg.d_latent) if cfg.latent_proj else None,
+              gu=e_(max(Rm, 1), m * F) if keep else None)
     W = weights_dev(cfg, inp)
     x = dev(inp.x)
     y = torch.empty_like(x)
