@@ -25,7 +25,14 @@ moe_route also runs on each case computing its own scores (the router
 product's shape variants): scores within 1e-5 of max|l|, choices equal up to
 near-ties, gates within 1e-5.
 The draws are fixed (seed per case), so a failure names a reproducible case.
+Besides the small draws: larger layers (300-3000 tokens, widths up to 512: several
+row and column tiles per expert), larger layers of the routing variants, and small
+and large layers whose forward keeps the pre-activations for the backward; a few of
+each by default, N of each with the environment variable MOE_RANDOM_SWEEP=N (swept
+at N = 150-200 on MI355X).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -101,7 +108,7 @@ CASES = [draw(i) for i in range(N_CASES)] + [draw(i) for i in (76, 85, 125, 166)
 
 def test_draws_are_valid_and_varied():
     """Host-side: every draw is a supported configuration, and the draws cover the options."""
-    for c in CASES:
+    for c in CASES + LARGE + VARIANT:
         assert moe.moe_check_config(c) == moe.MOE_OK, c
         assert moe.moe_backward_workspace_bytes(c) > 0, c
     assert {c.n_heads for c in CASES} >= {1, 2}
@@ -111,15 +118,107 @@ def test_draws_are_valid_and_varied():
     assert {c.act_dtype for c in CASES} == {0, 1} and {c.act for c in CASES} == {0, 1}
 
 
+def draw_large(i):
+    """The i-th random layer of 300-3000 tokens and widths up to 512 (several row and
+    column tiles per expert: the 256-row tiles, their tails and the mixed launches)."""
+    rng = np.random.default_rng([4048, i])
+    H = int(rng.choice([1, 1, 2, 4]))
+    latent = int(H > 1 and rng.random() < 0.6)
+    dh = int(rng.choice([64, 128, 192, 256, 320, 512]))
+    d_model = H * dh if not latent else int(rng.choice([128, 256, 512]))
+    Eh = int(rng.integers(1, 17))
+    top_k = int(rng.integers(1, min(Eh, 8) + 1))
+    T = int(rng.integers(300, 3001))
+    drop = int(rng.integers(0, 3))
+    capacity = int(rng.integers(0, -(-T * top_k // Eh) * 2 + 2)) if drop == 1 else 0
+    f32_layer = rng.random() < 0.15
+    return MoEConfig(f"large{i:03d}", T=T, d_model=d_model, n_heads=H, d_head=dh, n_experts=H * Eh, top_k=top_k,
+                     renorm=int(rng.integers(0, 2)), drop=drop, capacity=capacity, keep_num=int(rng.integers(5, 11)),
+                     keep_den=10, d_ff=int(rng.choice([64, 128, 256, 512])), act=int(rng.integers(0, 2)),
+                     n_shared=int(rng.integers(0, 2)) if (H == 1 and not latent) else 0, latent_proj=latent,
+                     residual=int(rng.integers(0, 2)), act_dtype=0 if f32_layer else 1,
+                     router_dtype=0 if f32_layer else int(rng.integers(0, 2)),
+                     zipf_s=float(rng.choice([0.0, 1.0, 1.2])), tag=5000 + i)
+
+
+def draw_variant(i):
+    """The i-th random layer of 300-2500 tokens in one of five routing families:
+    group-limited with the affinity keep and shared experts, expert choice, the
+    balancing bias with the per-sequence statistic, multi-head latent top-1 per head
+    (the fused MLP's folded combine), multi-head latent with any k and keep rule."""
+    rng = np.random.default_rng([6060, i])
+    kind = int(rng.integers(0, 5))
+    T = int(rng.integers(300, 2501))
+    c = dict(renorm=0, drop=0, capacity=0, keep_num=9, keep_den=10, n_groups=0, topk_groups=0, route_mode=0,
+             sel_bias_gate=0, sel_bias_steps=0, seq_len=0, n_shared=0, latent_proj=0,
+             residual=int(rng.integers(0, 2)), act=int(rng.integers(0, 2)), act_dtype=1,
+             router_dtype=int(rng.integers(0, 2)), d_ff=int(rng.choice([64, 128, 256])),
+             zipf_s=float(rng.choice([0.0, 1.0])), tag=7000 + i)
+    if kind == 0:
+        Eh = int(rng.choice([8, 12, 16, 24, 32]))
+        ng = int(rng.choice([g for g in (2, 4, 8) if Eh % g == 0]))
+        k = int(rng.integers(1, 7))
+        need = -(-k // (Eh // ng))
+        dh = int(rng.choice([128, 256, 384]))
+        c.update(n_heads=1, d_head=dh, d_model=dh, n_experts=Eh, top_k=k, n_groups=ng,
+                 topk_groups=int(rng.integers(need, ng + 1)), drop=2, renorm=int(rng.integers(0, 2)),
+                 n_shared=int(rng.integers(0, 3)))
+    elif kind == 1:
+        E = int(rng.integers(2, 33))
+        dh = int(rng.choice([128, 256, 320]))
+        c.update(n_heads=1, d_head=dh, d_model=dh, n_experts=E, top_k=1, route_mode=1, drop=1,
+                 capacity=int(rng.integers(1, T + 10)))
+    elif kind == 2:
+        E = int(rng.integers(4, 65))
+        L = int(rng.integers(16, 257))
+        dh = int(rng.choice([128, 256]))
+        c.update(n_heads=1, d_head=dh, d_model=dh, n_experts=E, top_k=int(rng.integers(1, min(E, 8) + 1)),
+                 sel_bias_steps=5, sel_bias_gate=int(rng.integers(0, 2)), seq_len=L)
+        T = max(L, T // L * L)
+    elif kind == 3:
+        H = int(rng.choice([2, 4, 8]))
+        c.update(n_heads=H, d_head=int(rng.choice([64, 128, 256])), d_model=int(rng.choice([256, 512, 1024])),
+                 n_experts=H * int(rng.integers(2, 17)), top_k=1, latent_proj=1, residual=1)
+    else:
+        H = int(rng.choice([2, 4]))
+        Eh = int(rng.integers(2, 17))
+        k = int(rng.integers(1, min(Eh, 8) + 1))
+        drop = int(rng.integers(0, 3))
+        c.update(n_heads=H, d_head=int(rng.choice([64, 128, 192, 256])), d_model=int(rng.choice([256, 512])),
+                 n_experts=H * Eh, top_k=k, latent_proj=1, drop=drop,
+                 capacity=int(rng.integers(1, -(-T * k // Eh) * 2)) if drop == 1 else 0)
+    return MoEConfig(f"variant{i:03d}", T=T, **c)
+
+
+# A few of each larger family run by default; MOE_RANDOM_SWEEP=N runs N of each.
+N_SWEEP = int(os.environ.get("MOE_RANDOM_SWEEP", "0"))
+LARGE = [draw_large(i) for i in range(max(N_SWEEP, 6))]
+VARIANT = [draw_variant(i) for i in range(max(N_SWEEP, 10))]
+# the forward keeping the routed pre-activations for the backward
+KEPT = [draw(i) for i in range(max(N_SWEEP, 6))] + LARGE[:max(N_SWEEP, 6)]
+
+
 def _dy(cfg):
     a = np.random.default_rng([77, cfg.tag]).standard_normal((cfg.T, cfg.d_model)).astype(np.float32)
     return bf16_bits_from_f32(a) if cfg.act_dtype == 1 else a
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", CASES + LARGE + VARIANT, ids=lambda c: c.name)
 def test_random_layer_forward_backward(cfg):
-    log(f"random {cfg}")
+    check_layer(cfg)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("cfg", KEPT, ids=lambda c: c.name)
+def test_random_layer_kept_preactivations(cfg):
+    """The same checks with the forward keeping the routed pre-activations (io.gu) and
+    the backward reading them (ignored by layers on the fused narrow-expert MLP)."""
+    check_layer(cfg, keep=True)
+
+
+def check_layer(cfg, keep=False):
+    log(f"random {cfg}" + (" (pre-activations kept)" if keep else ""))
     inp = generate(cfg, threads=1)
     out = oracle.forward(cfg, inp)
     T, K, E = cfg.T, cfg.k_total, cfg.n_experts
@@ -130,7 +229,8 @@ def test_random_layer_forward_backward(cfg):
               aux_loss=f32(1) if cfg.n_heads == 1 else None,
               seq_loss=f32(T // cfg.seq_len) if cfg.seq_len else None,
               z=empty_act(cfg, T, cfg.d_latent) if cfg.latent_proj else None,
-              o=empty_act(cfg, T, cfg.d_latent) if cfg.latent_proj else None)
+              o=empty_act(cfg, T, cfg.d_latent) if cfg.latent_proj else None,
+              gu=empty_act(cfg, Rm, (2 if cfg.act == 1 else 1) * cfg.d_ff) if keep else None)
     W = weights_dev(cfg, inp)
     x = dev(inp.x)
     y = torch.empty_like(x)
@@ -200,7 +300,7 @@ def test_random_layer_forward_backward(cfg):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", CASES + VARIANT, ids=lambda c: c.name)
 def test_random_route_compute(cfg):
     """moe_route computing its own scores: within 1e-5 * max|l| of the oracle's; choices differ only at near-ties."""
     log(f"random route COMPUTE {cfg.name}")
