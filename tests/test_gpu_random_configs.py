@@ -203,10 +203,14 @@ def _dy(cfg):
     return bf16_bits_from_f32(a) if cfg.act_dtype == 1 else a
 
 
+# the larger draws also ask for x_perm: the dispatch's row copy and the expert FFN on it
+LAYER_CASES = [(c, False) for c in CASES + VARIANT] + [(c, True) for c in LARGE]
+
+
 @pytest.mark.gpu
-@pytest.mark.parametrize("cfg", CASES + LARGE + VARIANT, ids=lambda c: c.name)
-def test_random_layer_forward_backward(cfg):
-    check_layer(cfg)
+@pytest.mark.parametrize("cfg,xperm", LAYER_CASES, ids=[c.name + ("-xperm" if xp else "") for c, xp in LAYER_CASES])
+def test_random_layer_forward_backward(cfg, xperm):
+    check_layer(cfg, xperm=xperm)
 
 
 @pytest.mark.gpu
@@ -217,8 +221,8 @@ def test_random_layer_kept_preactivations(cfg):
     check_layer(cfg, keep=True)
 
 
-def check_layer(cfg, keep=False):
-    log(f"random {cfg}" + (" (pre-activations kept)" if keep else ""))
+def check_layer(cfg, keep=False, xperm=False):
+    log(f"random {cfg}" + (" (pre-activations kept)" if keep else "") + (" (x_perm)" if xperm else ""))
     inp = generate(cfg, threads=1)
     out = oracle.forward(cfg, inp)
     T, K, E = cfg.T, cfg.k_total, cfg.n_experts
@@ -230,7 +234,8 @@ def check_layer(cfg, keep=False):
               seq_loss=f32(T // cfg.seq_len) if cfg.seq_len else None,
               z=empty_act(cfg, T, cfg.d_latent) if cfg.latent_proj else None,
               o=empty_act(cfg, T, cfg.d_latent) if cfg.latent_proj else None,
-              gu=empty_act(cfg, Rm, (2 if cfg.act == 1 else 1) * cfg.d_ff) if keep else None)
+              gu=empty_act(cfg, Rm, (2 if cfg.act == 1 else 1) * cfg.d_ff) if keep else None,
+              x_perm=empty_act(cfg, Rm, cfg.d_head) if xperm else None)
     W = weights_dev(cfg, inp)
     x = dev(inp.x)
     y = torch.empty_like(x)
@@ -251,6 +256,15 @@ def check_layer(cfg, keep=False):
     if len(flips):
         log(f"  keep decisions at gate near-ties: {len(flips)}")
     kept = io["row_of"].cpu().numpy().reshape(-1) >= 0
+    if xperm:
+        # every x_perm row is a bitwise copy of its source row (the head's slice of x or z)
+        R = int(io["offsets"][-1])
+        a = io["src_of"][:R].long()
+        e_of = io["topk_idx"].reshape(-1).long()[a]
+        src = (io["z"] if cfg.latent_proj else x).view(T, cfg.n_heads, cfg.d_head)
+        want = src[a // K, e_of // cfg.e_per_head]
+        bits = (lambda t: t.view(torch.int16)) if want.dtype == torch.bfloat16 else (lambda t: t.view(torch.int32))
+        assert torch.equal(bits(io["x_perm"][:R]), bits(want)), "x_perm rows"
     P = OB.params_of(inp)
 
     y_ref, _ = OB.forward_fixed(cfg, P, idx, kept)
