@@ -243,9 +243,13 @@ def _gate_to_prob_grad(cfg, g, S, dg):
     return (dg - sdg) / S
 
 
-def backward(cfg, P, topk_idx, kept, dy, lam=0.0, seq_w=0.0):
+def backward(cfg, P, topk_idx, kept, dy, lam=0.0, seq_w=0.0, u=None):
     """Gradients of L = <dy, y> + lam * l_aux [+ seq_w * sum of the per-sequence balance
     terms] (see the module docstring), float64.
+
+    u: the expert and router input to use in place of x W_in^T (a latent layer whose
+    z is read at the precision it is stored in); its gradient du passes to W_in and x
+    unchanged.  None: u = x W_in^T (or x).
 
     Returns dict: dx, dw_router, dbias, dw1, dw3, dw2, dws1, dws3, dws2, dw_in, dw_out
     (None where absent), plus the intermediates dg [T, K] (gate gradients), dl [T, E]
@@ -255,7 +259,7 @@ def backward(cfg, P, topk_idx, kept, dy, lam=0.0, seq_w=0.0):
     x, T, E, Eh, dh = P["x"], cfg.T, cfg.n_experts, cfg.e_per_head, cfg.d_head
     k, K = _kh(cfg)
     dy = np.asarray(dy, np.float64)
-    u = _u(cfg, P)
+    u = _u(cfg, P) if u is None else np.asarray(u, np.float64)
     p = _probs(cfg, P, u)
     idx = topk_idx.astype(np.int64)
     pc = np.take_along_axis(p, idx, axis=1)

@@ -141,7 +141,8 @@ def relu_tie_allowance(cfg, P, topk_idx, kept, dy):
     differ from it (float32 sums; with the latent projections also the expert input
     z = x W_in^T, which the layer stores in its activation type and the experts read
     from there), the GPU may take the other side, and its gradients then differ by that
-    element's whole term.  Returns (bounds, n) with bounds = {"dx", "dw1", "dw_in"}: the
+    element's whole term.  Returns (bounds, n) with bounds = {"dx", "dw1", "dw_in" and, with
+    shared experts, "dws1"} (the shared experts' masks likewise): the
     sum of those terms' magnitudes over the near-zero elements (zero elsewhere), and n,
     the number of such elements.  Zero bounds for SwiGLU layers (a smooth activation).
     """
@@ -183,4 +184,15 @@ def relu_tie_allowance(cfg, P, topk_idx, kept, dy):
         np.add.at(b_du, (rows[:, None], np.arange(hs.start, hs.stop)[None, :]), c @ np.abs(W1))
     if cfg.latent_proj:
         return dict(dx=b_du @ np.abs(P["w_in"]), dw1=b_dw1, dw_in=b_du.T @ np.abs(x)), n
-    return dict(dx=b_du, dw1=b_dw1, dw_in=None), n
+    # shared experts (one head, no projections): input x, gate 1, upstream dy
+    b_dws1 = np.zeros_like(P["ws1"]) if cfg.n_shared else None
+    f = cfg.d_ff
+    for i in range(cfg.n_shared):
+        w1, _, w2 = OB._shared_slices(cfg, P, i)
+        a = x @ w1.T
+        near = np.abs(a) <= 1e-5 * (np.abs(x) @ np.abs(w1).T)
+        n += int(near.sum())
+        c = np.where(near, np.abs(np.asarray(dy, np.float64) @ w2), 0.0)
+        b_du += c @ np.abs(w1)
+        b_dws1[i * f:(i + 1) * f] += c.T @ np.abs(x)
+    return dict(dx=b_du, dw1=b_dw1, dw_in=None, dws1=b_dws1), n

@@ -43,7 +43,7 @@ import routing_dispatch_expert_router_amd as moe
 from moe_inputs import generate, bf16_bits_from_f32
 from moe_inputs.configs import MoEConfig
 from tests.gpu_util import (log, dev, f64, empty_act, i32, f32, tol, weights_dev, routing_margin, check_keep,
-                            relu_tie_allowance)
+                            relu_tie_allowance, act_round)
 from tests.test_gpu_backward import _transposed, _grads
 
 N_CASES = 24
@@ -283,7 +283,10 @@ def check_layer(cfg, keep=False, xperm=False):
     moe.moe_layer_bwd(cfg, W, _transposed(cfg, W), x, dev(dy_h), lam, io, G, moe.backward_workspace(cfg),
                       seq_weight=sw)
     torch.cuda.synchronize()
-    ref = OB.backward(cfg, P, idx, kept, oracle.decode(dy_h), lam, sw)
+    # a latent layer's router and experts read z as the layer stores it (its activation
+    # type): the oracle takes its own x W_in^T rounded the same way
+    u = oracle.decode(act_round(cfg, OB._u(cfg, P))) if cfg.latent_proj else None
+    ref = OB.backward(cfg, P, idx, kept, oracle.decode(dy_h), lam, sw, u=u)
     names = ["dx", "dw_router", "dw1", "dw2"] + (["dbias"] if inp.bias is not None else [])
     names += ["dw3"] if cfg.act == 1 else []
     if cfg.n_shared:
